@@ -1,0 +1,419 @@
+"""Plain fp64 CPU oracle for exact softmax attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check of the graft entry
+module and the CPU-baseline leg of the benchmark may import this module.  The
+product path (the HIP library and its Python binding) never calls it and shares
+no code with it.
+
+Sources (the pages this follows; cited by page title and section / equation):
+
+* "Chapter 33 推理计算优化" (faketrader.github.io, llm-from-scratch), §33.2:
+  eq 33.2 (single-query attention with additive bias/mask M_j), eq 33.3 (the
+  sufficient statistics m, ℓ, u of a non-empty legal key set), eqs 33.4-33.5
+  (the merge of two disjoint sets), the valid-flag rule for empty blocks and
+  fully masked rows, Algorithm 33.1 (single-query blocked exact attention) and
+  Example 25.1; §33.3 (the explicit T_q x T_k implementation, causal block
+  skipping, non-square causal alignment by logical position).
+* "Generation and Caching with the Same Model" (aihero.club), the KV-cache
+  section and its `causal_attention` listing: the [B, H, T, D] layout and the
+  rule that query row i sits at logical position q_offset + i and sees the
+  keys j <= q_offset + i.
+
+Two independent formulations live here:
+
+1. ``attention`` / ``attention_rows``: the definition written out.  The whole
+   T_q x T_k score matrix of one (batch, head) is materialised in fp64, the
+   illegal entries are set to -inf, and each row with at least one legal key
+   is normalised by its own maximum.  This is the explicit implementation of
+   §33.3, with the fully masked row defined as (O = +0, LSE = -inf) instead of
+   the NaN that a plain softmax of an all -inf row would give.
+2. ``block_stats`` / ``merge_stats`` / ``finalize`` / ``blocked_single_query``:
+   the pages' statistics and merge (eqs 33.3-33.5) and Algorithm 33.1 step by
+   step, generic over the arithmetic so that tests can run them in exact
+   rational arithmetic as well as in fp64.
+
+Readings taken where the pages leave a step open (each is listed in the design
+notes of the repository):
+
+* LSE of a row is ln sum_{legal j} e^{z_j} = m + ln ℓ (natural log, scale and
+  bias included).
+* A key is legal for row i iff it is causally visible (j <= q_offset + i, or
+  always when not causal) and its bias is not -inf.
+* A row with no legal key returns O = +0.0 and LSE = -inf (and a legal-key
+  count of 0); it is not an error.
+* Grouped heads: query head hq reads KV head hq // (H_q / H_kv).
+* A stored partial (o_s, lse_s) stands for the triple (lse_s, 1, o_s); a
+  partial with lse_s = -inf is empty and is skipped, never subtracted.
+* Split-KV partials cover contiguous key ranges [s*S, min((s+1)*S, T_k)).
+
+Nothing here is pinned by itself: the ``-m "not gpu"`` tests pin it against
+the printed example, closed forms, invariants, brute force over block
+partitions and an independent library softmax.
+"""
+
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+from typing import Callable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+NEG_INF = float("-inf")
+
+
+# ---------------------------------------------------------------------------
+# 1. The definition, materialised (eq 33.2, §33.3 explicit implementation)
+# ---------------------------------------------------------------------------
+
+def legal_keys(t_q: int, t_k: int, causal: bool, q_offset: int,
+               bias_rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Boolean [t_q, t_k]: key j is legal for query row i.
+
+    Row i sits at logical position q_offset + i (KV-cache section of
+    "Generation and Caching with the Same Model"); with causal masking it sees
+    key j iff j <= q_offset + i (§33.3, interface and correctness conditions:
+    alignment is by logical position, not by the top-left corner).  A bias of
+    -inf masks a key (eq 33.2: M_j is an additive bias or mask).
+    """
+    i = np.arange(t_q, dtype=np.int64)[:, None]
+    j = np.arange(t_k, dtype=np.int64)[None, :]
+    if causal:
+        legal = j <= (q_offset + i)
+    else:
+        legal = np.ones((t_q, t_k), dtype=bool)
+    if bias_rows is not None:
+        legal = legal & (bias_rows != NEG_INF)
+    return legal
+
+
+def softmax_rows(scores: np.ndarray, legal: np.ndarray,
+                 values: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Exact softmax-weighted average of ``values`` for each score row.
+
+    scores [R, T_k] fp64, legal [R, T_k] bool, values [T_k, d_v] fp64.
+    Returns (o [R, d_v], lse [R], n_legal [R] int64).  For a row with legal
+    keys: m = max legal score, w_j = e^{z_j - m} on legal keys and 0 elsewhere,
+    ℓ = sum w, o = sum w_j v_j / ℓ, lse = m + ln ℓ (eq 33.2).  A row with no
+    legal key gets o = +0.0, lse = -inf (§33.2 valid-flag rule).
+    """
+    r = scores.shape[0]
+    d_v = values.shape[1]
+    n_legal = legal.sum(axis=1).astype(np.int64)
+    o = np.zeros((r, d_v), dtype=np.float64)
+    lse = np.full(r, NEG_INF, dtype=np.float64)
+    live = n_legal > 0
+    if not live.any():
+        return o, lse, n_legal
+    s = np.where(legal[live], scores[live], NEG_INF)
+    m = s.max(axis=1)
+    w = np.exp(s - m[:, None])            # e^{-inf} = 0 on illegal keys
+    ell = w.sum(axis=1)
+    o[live] = (w @ values) / ell[:, None]
+    lse[live] = m + np.log(ell)
+    return o, lse, n_legal
+
+
+def _check_shapes(q, k, v, bias):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B, H, T, D]")
+    b, hq, _, d_h = q.shape
+    bk, hkv, t_k, d_hk = k.shape
+    if bk != b or v.shape[0] != b or v.shape[1] != hkv or v.shape[2] != t_k:
+        raise ValueError("k and v must be [B, H_kv, T_k, *] with q's batch")
+    if d_hk != d_h:
+        raise ValueError("q and k must share d_h")
+    if hkv == 0 or hq % hkv != 0:
+        raise ValueError("H_q must be a multiple of H_kv")
+    if bias is not None and bias.ndim != 4:
+        raise ValueError("bias must broadcast as [B, H_q, T_q, T_k]")
+
+
+def _bias_rows(bias: Optional[np.ndarray], b: int, hq: int, t_q: int,
+               t_k: int, rows=slice(None)) -> Optional[np.ndarray]:
+    if bias is None:
+        return None
+    bb = bias[b if bias.shape[0] > 1 else 0, hq if bias.shape[1] > 1 else 0]
+    return np.broadcast_to(bb, (t_q, t_k))[rows]
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
+              causal: bool, q_offset: int = 0,
+              bias: Optional[np.ndarray] = None,
+              key_range: Optional[Tuple[int, int]] = None):
+    """Materialised exact attention over every (batch, query head).
+
+    q [B, H_q, T_q, d_h], k [B, H_kv, T_k, d_h], v [B, H_kv, T_k, d_v] (any
+    real dtype; converted exactly to fp64), bias broadcastable to
+    [B, H_q, T_q, T_k] or None.  z_ij = scale * <q_i, k_j> + M_ij (eq 33.2;
+    the bias is added after scaling and is never scaled).  ``key_range``
+    restricts the legal set to keys [lo, hi) (used for split partials).
+
+    Returns (o [B, H_q, T_q, d_v], lse [B, H_q, T_q], n_legal [B, H_q, T_q]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if bias is not None:
+        bias = np.asarray(bias, dtype=np.float64)
+    _check_shapes(q, k, v, bias)
+    bsz, h_q, t_q, _ = q.shape
+    h_kv, t_k, d_v = k.shape[1], k.shape[2], v.shape[3]
+    group = h_q // h_kv
+    o = np.zeros((bsz, h_q, t_q, d_v))
+    lse = np.full((bsz, h_q, t_q), NEG_INF)
+    n = np.zeros((bsz, h_q, t_q), dtype=np.int64)
+    for b in range(bsz):
+        for hq in range(h_q):
+            kvh = hq // group
+            m_rows = _bias_rows(bias, b, hq, t_q, t_k)
+            s = scale * (q[b, hq] @ k[b, kvh].T)
+            if m_rows is not None:
+                s = s + np.where(m_rows == NEG_INF, 0.0, m_rows)
+            legal = legal_keys(t_q, t_k, causal, q_offset, m_rows)
+            if key_range is not None:
+                lo, hi = key_range
+                j = np.arange(t_k)[None, :]
+                legal = legal & (j >= lo) & (j < hi)
+            o[b, hq], lse[b, hq], n[b, hq] = softmax_rows(s, legal, v[b, kvh])
+    return o, lse, n
+
+
+def attention_rows(q, k, v, rows: Sequence[Tuple[int, int, int]], *,
+                   scale: float, causal: bool, q_offset: int = 0,
+                   bias=None):
+    """The same definition evaluated for selected rows (b, hq, i) only.
+
+    Each row is computed on its own from its query vector and every key of its
+    KV head, so full-size workloads can be checked on a sample of rows.  Inputs
+    may be torch CPU tensors or numpy arrays; only the needed slices are
+    converted to fp64.  Returns (o [R, d_v], lse [R], n_legal [R]).
+    """
+    def f64(x):
+        if hasattr(x, "detach"):
+            import torch  # only for the exact dtype conversion of a slice
+            return x.detach().to(torch.float64).numpy()
+        return np.asarray(x, dtype=np.float64)
+
+    h_q = q.shape[1]
+    h_kv = k.shape[1]
+    t_k = k.shape[2]
+    group = h_q // h_kv
+    outs_o, outs_l, outs_n = [], [], []
+    cache = {}
+    for (b, hq, i) in rows:
+        kvh = hq // group
+        key = (b, kvh)
+        if key not in cache:
+            cache.clear()
+            cache[key] = (f64(k[b, kvh]), f64(v[b, kvh]))
+        kk, vv = cache[key]
+        qi = f64(q[b, hq, i])
+        s = scale * (kk @ qi)
+        m_row = None
+        if bias is not None:
+            bb = bias[b if bias.shape[0] > 1 else 0, hq if bias.shape[1] > 1 else 0]
+            bi = bb[i if bb.shape[0] > 1 else 0]
+            m_row = np.broadcast_to(f64(bi), (t_k,))
+            s = s + np.where(m_row == NEG_INF, 0.0, m_row)
+        pos = q_offset + i
+        j = np.arange(t_k)
+        legal = (j <= pos) if causal else np.ones(t_k, dtype=bool)
+        if m_row is not None:
+            legal = legal & (m_row != NEG_INF)
+        o1, l1, n1 = softmax_rows(s[None, :], legal[None, :], vv)
+        outs_o.append(o1[0]); outs_l.append(l1[0]); outs_n.append(n1[0])
+    return np.array(outs_o), np.array(outs_l), np.array(outs_n, dtype=np.int64)
+
+
+def split_partials(q, k, v, *, scale: float, causal: bool, q_offset: int,
+                   split_size: int, bias=None):
+    """Per-split partial results for split-KV decode.
+
+    Split s covers keys [s*S, min((s+1)*S, T_k)); its partial is the
+    definition applied to that key range alone, stored as (o_s, lse_s), with
+    (0, -inf) for a split that holds no legal key.  Returns
+    (o_parts [B, H_q, T_q, n_splits, d_v], lse_parts [B, H_q, T_q, n_splits]).
+    """
+    t_k = np.asarray(k).shape[2]
+    n_splits = max(1, -(-t_k // split_size))
+    o_parts, l_parts = [], []
+    for s in range(n_splits):
+        o_s, l_s, _ = attention(q, k, v, scale=scale, causal=causal,
+                                q_offset=q_offset, bias=bias,
+                                key_range=(s * split_size,
+                                           min((s + 1) * split_size, t_k)))
+        o_parts.append(o_s); l_parts.append(l_s)
+    return np.stack(o_parts, axis=3), np.stack(l_parts, axis=3)
+
+
+# ---------------------------------------------------------------------------
+# 2. Statistics, merge and Algorithm 33.1 (eqs 33.3-33.5), arithmetic-generic
+# ---------------------------------------------------------------------------
+
+class Arith:
+    """The three scalar operations the statistics need.
+
+    ``exp_diff(a, b)`` = e^{a - b} for scores a <= b or any pair, ``log(x)`` the
+    natural log, ``gt(a, b)`` score comparison.  ``to_log`` maps an LSE-type
+    value back to the score domain of this arithmetic.
+    """
+
+    def __init__(self, exp_diff: Callable, log_plus: Callable, gt: Callable):
+        self.exp_diff = exp_diff
+        self.log_plus = log_plus      # (m, ell) -> m + ln(ell)
+        self.gt = gt
+
+
+FP64 = Arith(exp_diff=lambda a, b: math.exp(a - b),
+             log_plus=lambda m, ell: m + math.log(ell),
+             gt=lambda a, b: a > b)
+
+
+class LogOf:
+    """The score ln(a) of a positive rational a, kept exact as a Fraction.
+
+    e^{ln a - ln b} = a / b is then an exact rational, so the statistics and
+    the merge can be checked with no rounding at all.
+    """
+
+    __slots__ = ("a",)
+
+    def __init__(self, a):
+        self.a = Fraction(a)
+        if self.a <= 0:
+            raise ValueError("LogOf needs a positive rational")
+
+    def __repr__(self):
+        return f"ln({self.a})"
+
+    def __eq__(self, other):
+        return isinstance(other, LogOf) and self.a == other.a
+
+    def __hash__(self):
+        return hash(self.a)
+
+
+EXACT = Arith(exp_diff=lambda x, y: x.a / y.a,
+              log_plus=lambda m, ell: LogOf(m.a * ell),
+              gt=lambda x, y: x.a > y.a)
+
+
+def block_stats(z: Sequence, values: Sequence[Sequence], legal: Sequence[bool],
+                arith: Arith = FP64):
+    """(m, ℓ, u) of the legal keys of one block (eq 33.3), or None if empty.
+
+    m = max legal z_j, ℓ = sum e^{z_j - m}, u = sum e^{z_j - m} v_j.  An empty
+    block has no statistics at all (§33.2 valid-flag rule); no arithmetic is
+    done on the maximum of an empty set.
+    """
+    idx = [j for j, ok in enumerate(legal) if ok]
+    if not idx:
+        return None
+    m = z[idx[0]]
+    for j in idx[1:]:
+        if arith.gt(z[j], m):
+            m = z[j]
+    d_v = len(values[idx[0]])
+    ell = 0
+    u = [0] * d_v
+    for j in idx:
+        w = arith.exp_diff(z[j], m)
+        ell = ell + w
+        u = [u[d] + w * values[j][d] for d in range(d_v)]
+    return (m, ell, u)
+
+
+def merge_stats(a, b, arith: Arith = FP64):
+    """Merge two statistics of disjoint key sets (eqs 33.4-33.5).
+
+    m = max(m_A, m_B); ℓ = e^{m_A - m} ℓ_A + e^{m_B - m} ℓ_B;
+    u = e^{m_A - m} u_A + e^{m_B - m} u_B.  An empty side (None) contributes
+    nothing: the other side is returned as is (§33.2 valid flags, Exercise 33.3).
+    """
+    if a is None:
+        return b
+    if b is None:
+        return a
+    m_a, l_a, u_a = a
+    m_b, l_b, u_b = b
+    m = m_a if not arith.gt(m_b, m_a) else m_b
+    ca = arith.exp_diff(m_a, m)
+    cb = arith.exp_diff(m_b, m)
+    ell = ca * l_a + cb * l_b
+    u = [ca * x + cb * y for x, y in zip(u_a, u_b)]
+    return (m, ell, u)
+
+
+def finalize(state, d_v: int, arith: Arith = FP64):
+    """Output of a row: (u / ℓ, m + ln ℓ) or, with no legal key, (0, -inf)."""
+    if state is None:
+        return [0.0] * d_v, NEG_INF
+    m, ell, u = state
+    return [x / ell for x in u], arith.log_plus(m, ell)
+
+
+def blocked_single_query(z: Sequence, values: Sequence[Sequence],
+                         legal: Sequence[bool], blocks: Sequence[Sequence[int]],
+                         arith: Arith = FP64):
+    """Algorithm 33.1 for one query: keys read block by block.
+
+    Start with "no legal key yet"; for each block compute its scores' legal
+    subset, skip it if empty, store it if it is the first non-empty block,
+    otherwise merge (eqs 33.4-33.5); at the end return u/ℓ or the fully masked
+    row's defined output.  ``blocks`` lists key indices; together they must
+    partition the keys.
+    """
+    d_v = len(values[0]) if len(values) else 0
+    state = None
+    for blk in blocks:
+        zb = [z[j] for j in blk]
+        vb = [values[j] for j in blk]
+        lb = [legal[j] for j in blk]
+        st = block_stats(zb, vb, lb, arith)
+        if st is None:
+            continue
+        state = st if state is None else merge_stats(state, st, arith)
+    return finalize(state, d_v, arith)
+
+
+def merge_partials(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """Merge stored partials (o_s, lse_s) along the last state axis.
+
+    o_parts [..., S, d_v], lse_parts [..., S].  Each valid partial is the
+    triple (lse_s, 1, o_s) and the triples are folded with ``merge_stats``
+    (eqs 33.4-33.5); partials with lse_s = -inf are skipped.  Returns
+    (o [..., d_v], lse [...]).
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    lead = lse_parts.shape[:-1]
+    n_states = lse_parts.shape[-1]
+    d_v = o_parts.shape[-1]
+    o_flat = o_parts.reshape(-1, n_states, d_v)
+    l_flat = lse_parts.reshape(-1, n_states)
+    o_out = np.zeros((o_flat.shape[0], d_v))
+    l_out = np.full(o_flat.shape[0], NEG_INF)
+    for r in range(o_flat.shape[0]):
+        state = None
+        for s in range(n_states):
+            if l_flat[r, s] == NEG_INF:
+                continue
+            st = (float(l_flat[r, s]), 1.0, list(o_flat[r, s]))
+            state = st if state is None else merge_stats(state, st, FP64)
+        o_r, l_r = finalize(state, d_v, FP64)
+        o_out[r] = o_r
+        l_out[r] = l_r
+    return o_out.reshape(lead + (d_v,)), l_out.reshape(lead)
+
+
+def set_partitions(items: List[int]):
+    """Every set partition of ``items`` (Bell-number many), as lists of blocks."""
+    if not items:
+        yield []
+        return
+    first, rest = items[0], items[1:]
+    for part in set_partitions(rest):
+        for i in range(len(part)):
+            yield part[:i] + [[first] + part[i]] + part[i + 1:]
+        yield [[first]] + part

@@ -1,0 +1,432 @@
+"""Checks that pin the oracle to facts outside itself.
+
+Each ``check_*`` takes the oracle module (``oracle.reference`` or a mutated
+copy of it) and raises AssertionError when the oracle disagrees with the
+pages' printed values, a closed form, an invariant, a brute force over block
+partitions or an independent library softmax.  ``test_oracle_pins.py`` runs
+them on the real oracle; ``test_oracle_mutants.py`` runs them on copies with a
+planted mistake and expects at least one to fail.
+"""
+
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+
+from conftest import load_golden
+
+LN = math.log
+
+
+def _row_problem(bias_row, values, d_h=4):
+    """q = 0 so every score equals its bias: z_j = M_j (eq 33.2)."""
+    t_k = len(bias_row)
+    d_v = len(values[0])
+    q = np.zeros((1, 1, 1, d_h))
+    k = np.random.default_rng(7).standard_normal((1, 1, t_k, d_h))
+    v = np.array(values, dtype=np.float64).reshape(1, 1, t_k, d_v)
+    bias = np.array(bias_row, dtype=np.float64).reshape(1, 1, 1, t_k)
+    return q, k, v, bias
+
+
+# --- the pages' printed examples ------------------------------------------
+
+def check_example_25_1_exact(R):
+    g = load_golden("example_25_1.json")
+    z = [R.LogOf(a) for a in g["scores_are_log_of"]]
+    vals = [[Fraction(x)] for x in g["values"]]
+    legal = [True] * 3
+    blk_a, blk_b = g["blocks"]
+    st_a = R.block_stats([z[j] for j in blk_a], [vals[j] for j in blk_a],
+                         [True] * len(blk_a), R.EXACT)
+    st_b = R.block_stats([z[j] for j in blk_b], [vals[j] for j in blk_b],
+                         [True] * len(blk_b), R.EXACT)
+    for st, ref in ((st_a, g["block_A"]), (st_b, g["block_B"])):
+        m, ell, u = st
+        assert m == R.LogOf(ref["m_is_log_of"]), (m, ref)
+        assert ell == Fraction(ref["ell"]), (ell, ref)
+        assert u == [Fraction(ref["u"])], (u, ref)
+        o_loc, _ = R.finalize(st, 1, R.EXACT)
+        assert o_loc == [Fraction(ref["local_output"])]
+    merged = R.merge_stats(st_a, st_b, R.EXACT)
+    assert merged[0] == R.LogOf(g["merged"]["m_is_log_of"])
+    assert merged[1] == Fraction(g["merged"]["ell"])
+    assert merged[2] == [Fraction(g["merged"]["u"])]
+    o, lse = R.finalize(merged, 1, R.EXACT)
+    assert o == [Fraction(g["output"])]
+    # LSE is derived, not printed: ln(2 + 1 + 6) = ln 9.
+    assert lse == R.LogOf(9)
+    # The full computation the example prints: (2*1 + 1*4 + 6*5)/(2+1+6).
+    full = R.blocked_single_query(z, vals, legal, [[0, 1, 2]], R.EXACT)[0]
+    num = Fraction(g["full_computation"]["numerator"])
+    den = Fraction(g["full_computation"]["denominator"])
+    assert full == [num / den] == [Fraction(g["output"])]
+    # The wrong answers must not come out.
+    for wrong in g["wrong_answers"].values():
+        assert o != [Fraction(wrong)]
+    # eq 33.3 defines m as the block maximum whatever the key order.
+    st_rev = R.block_stats([z[1], z[0]], [vals[1], vals[0]], [True, True], R.EXACT)
+    assert st_rev == st_a, st_rev
+    # The merge scale of block A and the two global masses.
+    assert R.EXACT.exp_diff(st_a[0], merged[0]) == Fraction(g["scale_of_A_in_merge"])
+    masses = [R.EXACT.exp_diff(st[0], R.LogOf(1)) * st[1] for st in (st_a, st_b)]
+    assert masses == [Fraction(x) for x in g["global_masses"]]
+
+
+def check_example_25_1_fp64(R):
+    g = load_golden("example_25_1.json")
+    bias = [LN(a) for a in g["scores_are_log_of"]]
+    vals = [[float(x), 0.0] for x in g["values"]]
+    q, k, v, m = _row_problem(bias, vals)
+    o, lse, n = R.attention(q, k, v, scale=0.125, causal=False, bias=m)
+    assert abs(o[0, 0, 0, 0] - 4.0) <= 1e-15 * 4
+    assert o[0, 0, 0, 1] == 0.0
+    assert abs(lse[0, 0, 0] - LN(9)) <= 1e-15 * 3
+    assert n[0, 0, 0] == 3
+    # Split into blocks of two keys: partials (2, ln 3) and (5, ln 6).
+    op, lp = R.split_partials(q, k, v, scale=0.125, causal=False, q_offset=0,
+                              split_size=2, bias=m)
+    assert op.shape == (1, 1, 1, 2, 2)
+    assert abs(op[0, 0, 0, 0, 0] - 2.0) <= 1e-15 * 2
+    assert abs(op[0, 0, 0, 1, 0] - 5.0) <= 1e-15 * 5
+    assert abs(lp[0, 0, 0, 0] - LN(3)) <= 1e-15
+    assert abs(lp[0, 0, 0, 1] - LN(6)) <= 1e-15 * 2
+    om, lm = R.merge_partials(op, lp)
+    assert abs(om[0, 0, 0, 0] - 4.0) <= 1e-15 * 4
+    assert abs(lm[0, 0, 0] - LN(9)) <= 1e-15 * 3
+
+
+def check_exercise_33_2(R):
+    g = load_golden("exercise_33_2.json")
+    masses = [float(Fraction(x)) for x in g["block_masses"]]
+    vals = [float(Fraction(x)) for x in g["block_values"]]
+    want = float(Fraction(g["output"]))
+    o_parts = np.array([[[vals[0]], [vals[1]]]])
+    l_parts = np.array([[LN(masses[0]), LN(masses[1])]])
+    o, lse = R.merge_partials(o_parts, l_parts)
+    assert abs(o[0, 0] - want) <= 1e-15 * want
+    assert abs(o[0, 0] - float(Fraction(g["wrong_equal_weight_mean"]))) > 0.5
+    assert abs(lse[0] - LN(masses[0] + masses[1])) <= 1e-15
+    # The same through the materialised definition (two keys with z = ln mass).
+    q, k, v, m = _row_problem([LN(x) for x in masses], [[x] for x in vals])
+    o2, l2, _ = R.attention(q, k, v, scale=1.0, causal=False, bias=m)
+    assert abs(o2[0, 0, 0, 0] - want) <= 1e-15 * want
+    assert abs(l2[0, 0, 0] - LN(4)) <= 1e-15
+
+
+def check_kv_cache_vectors(R):
+    """Incremental (one query at position t over the first t+1 keys) equals
+    the full causal computation, with q = k = v = the page's vectors."""
+    g = load_golden("kv_cache_vectors.json")
+    vecs = np.array(g["vectors"])
+    x = vecs.reshape(1, 1, 4, 2)
+    scale = 1.0 / math.sqrt(2.0)
+    o_full, l_full, _ = R.attention(x, x, x, scale=scale, causal=True)
+    for t in range(4):
+        o_t, l_t, n_t = R.attention(x[:, :, t:t + 1], x[:, :, :t + 1],
+                                    x[:, :, :t + 1], scale=scale, causal=True,
+                                    q_offset=t)
+        assert n_t[0, 0, 0] == t + 1
+        assert np.max(np.abs(o_t[0, 0, 0] - o_full[0, 0, t])) < g["tolerance"]
+        # Brute force by hand on the tiny input: weights e^{s_j}/sum e^{s}.
+        s = [float(vecs[t] @ vecs[j]) * scale for j in range(t + 1)]
+        e = [math.exp(a) for a in s]
+        ref = [sum(e[j] * vecs[j][d] for j in range(t + 1)) / sum(e) for d in range(2)]
+        assert max(abs(a - b) for a, b in zip(ref, o_full[0, 0, t])) < g["tolerance"]
+        assert abs(l_full[0, 0, t] - math.log(sum(e))) < g["tolerance"]
+
+
+# --- closed forms and special cases ---------------------------------------
+
+def check_equal_scores_mean(R):
+    """q = 0, no bias: every legal score is 0, so causal row i averages
+    v_0..v_{q_offset+i} and its LSE is ln(q_offset + i + 1)."""
+    rng = np.random.default_rng(1)
+    t_q, t_k, d = 6, 11, 5
+    v = rng.standard_normal((1, 1, t_k, d))
+    k = rng.standard_normal((1, 1, t_k, d))
+    q = np.zeros((1, 1, t_q, d))
+    for off in (0, 3, t_k - t_q):
+        o, lse, n = R.attention(q, k, v, scale=0.3, causal=True, q_offset=off)
+        for i in range(t_q):
+            cnt = min(off + i + 1, t_k)
+            assert n[0, 0, i] == cnt
+            np.testing.assert_allclose(o[0, 0, i], v[0, 0, :cnt].mean(0), rtol=0, atol=1e-14)
+            assert abs(lse[0, 0, i] - math.log(cnt)) <= 1e-14
+    # A constant bias c shifts the LSE by c only.
+    bias = np.full((1, 1, t_q, t_k), 2.5)
+    o, lse, _ = R.attention(q, k, v, scale=0.3, causal=False, bias=bias)
+    np.testing.assert_allclose(o[0, 0, 0], v[0, 0].mean(0), rtol=0, atol=1e-14)
+    assert abs(lse[0, 0, 0] - (2.5 + math.log(t_k))) <= 1e-14
+
+
+def check_single_and_two_keys(R):
+    rng = np.random.default_rng(2)
+    t_k, d = 7, 3
+    v = rng.standard_normal((1, 1, t_k, d))
+    k = rng.standard_normal((1, 1, t_k, d))
+    q = np.zeros((1, 1, 1, d))
+    for j in range(t_k):
+        bias = np.full((1, 1, 1, t_k), -np.inf)
+        bias[..., j] = 1.75
+        o, lse, n = R.attention(q, k, v, scale=1.0, causal=False, bias=bias)
+        assert n[0, 0, 0] == 1
+        assert np.array_equal(o[0, 0, 0], v[0, 0, j])
+        assert lse[0, 0, 0] == 1.75
+    # Two legal keys whose scores differ by delta: logistic weights.
+    for delta in (-3.0, 0.0, 0.7, 5.0):
+        bias = np.full((1, 1, 1, t_k), -np.inf)
+        bias[..., 1] = 0.0
+        bias[..., 4] = delta
+        o, lse, _ = R.attention(q, k, v, scale=1.0, causal=False, bias=bias)
+        w4 = 1.0 / (1.0 + math.exp(-delta))
+        want = (1 - w4) * v[0, 0, 1] + w4 * v[0, 0, 4]
+        np.testing.assert_allclose(o[0, 0, 0], want, rtol=0, atol=1e-14)
+        assert abs(lse[0, 0, 0] - math.log1p(math.exp(delta))) <= 1e-14
+
+
+def check_invariants(R):
+    rng = np.random.default_rng(3)
+    b, hq, hkv, t_q, t_k, d_h, d_v = 1, 2, 1, 5, 9, 4, 3
+    q = rng.standard_normal((b, hq, t_q, d_h))
+    k = rng.standard_normal((b, hkv, t_k, d_h))
+    v = rng.standard_normal((b, hkv, t_k, d_v))
+    bias = rng.standard_normal((b, 1, t_q, t_k))
+    o, lse, _ = R.attention(q, k, v, scale=0.5, causal=False, bias=bias)
+    # Shift: +c on a row's scores leaves o and moves lse by c.
+    o2, lse2, _ = R.attention(q, k, v, scale=0.5, causal=False, bias=bias + 3.25)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse + 3.25, rtol=0, atol=1e-13)
+    # Key permutation (keys, values and bias together) changes nothing.
+    perm = rng.permutation(t_k)
+    o3, lse3, _ = R.attention(q, k[:, :, perm], v[:, :, perm], scale=0.5,
+                              causal=False, bias=bias[..., perm])
+    np.testing.assert_allclose(o3, o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse3, lse, rtol=0, atol=1e-13)
+    # Convex hull: each component lies between the legal values' extremes.
+    lo = v.min(axis=2)[:, :, None, :]
+    hi = v.max(axis=2)[:, :, None, :]
+    assert np.all(o >= lo - 1e-14) and np.all(o <= hi + 1e-14)
+
+
+def check_partitions_exact(R):
+    """Every set partition of 6 keys, blocks taken in every order (first 24
+    orders), equals the direct weighted average, exactly (eq 33.3-33.5 with
+    e^{z} = a rational mass)."""
+    masses = [Fraction(3), Fraction(1, 2), Fraction(7), Fraction(2), Fraction(5, 3), Fraction(1)]
+    vals = [[Fraction(2), Fraction(-1)], [Fraction(5)], [Fraction(-3)],
+            [Fraction(1, 4)], [Fraction(9)], [Fraction(0)]]
+    vals = [[x[0], x[0] * 2 - 1] for x in vals]
+    legal = [True, True, False, True, True, True]  # key 2 masked
+    z = [R.LogOf(a) for a in masses]
+    num = [sum(masses[j] * vals[j][d] for j in range(6) if legal[j]) for d in range(2)]
+    den = sum(masses[j] for j in range(6) if legal[j])
+    want = [x / den for x in num]
+    count = 0
+    for part in R.set_partitions(list(range(6))):
+        for order in itertools.islice(itertools.permutations(part), 24):
+            o, lse = R.blocked_single_query(z, vals, legal, list(order), R.EXACT)
+            assert o == want, (order, o, want)
+            assert lse == R.LogOf(den)
+            count += 1
+    assert count > 203  # Bell(6) partitions, several orders each
+
+
+def check_partitions_fp64(R):
+    """Every contiguous partition of 10 keys (2^9 of them) through Algorithm
+    33.1 equals the materialised definition within 1e-13."""
+    rng = np.random.default_rng(4)
+    t_k, d = 10, 3
+    z = list(rng.standard_normal(t_k) * 3)
+    vals = rng.standard_normal((t_k, d))
+    legal = [True] * t_k
+    legal[6] = False
+    o_ref, l_ref, _ = R.softmax_rows(np.array([z]), np.array([legal]), vals)
+    for cuts in range(1 << (t_k - 1)):
+        blocks, cur = [], [0]
+        for j in range(1, t_k):
+            if cuts >> (j - 1) & 1:
+                blocks.append(cur)
+                cur = []
+            cur.append(j)
+        blocks.append(cur)
+        o, lse = R.blocked_single_query(z, vals.tolist(), legal, blocks, R.FP64)
+        assert np.max(np.abs(np.array(o) - o_ref[0])) <= 1e-13
+        assert abs(lse - l_ref[0]) <= 1e-13
+
+
+def check_masked_blocks_and_rows(R):
+    rng = np.random.default_rng(5)
+    t_q, t_k, d = 4, 8, 3
+    q = rng.standard_normal((1, 1, t_q, d))
+    k = rng.standard_normal((1, 1, t_k, d))
+    v = rng.standard_normal((1, 1, t_k, d))
+    bias = np.zeros((1, 1, t_q, t_k))
+    bias[0, 0, 1, :] = -np.inf          # row 1: no legal key
+    bias[0, 0, 2, 2:6] = -np.inf        # row 2: a masked block in the middle
+    o, lse, n = R.attention(q, k, v, scale=0.7, causal=False, bias=bias)
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    assert np.all(o[0, 0, 1] == 0.0) and not np.signbit(o[0, 0, 1]).any()
+    assert lse[0, 0, 1] == -np.inf and n[0, 0, 1] == 0
+    keep = [0, 1, 6, 7]
+    o2, lse2, _ = R.attention(q[:, :, 2:3], k[:, :, keep], v[:, :, keep],
+                              scale=0.7, causal=False)
+    np.testing.assert_allclose(o[0, 0, 2], o2[0, 0, 0], rtol=0, atol=1e-14)
+    assert abs(lse[0, 0, 2] - lse2[0, 0, 0]) <= 1e-14
+    # Algorithm 33.1 over blocks that are all empty returns the defined row.
+    z = [0.0] * 4
+    o3, l3 = R.blocked_single_query(z, [[1.0]] * 4, [False] * 4, [[0, 1], [2, 3]])
+    assert o3 == [0.0] and l3 == -np.inf
+    # Causal rows before position 0 (negative offset) have no legal key.
+    o4, l4, n4 = R.attention(q, k, v, scale=0.7, causal=True, q_offset=-2)
+    assert np.all(n4[0, 0, :2] == 0) and np.all(l4[0, 0, :2] == -np.inf)
+    assert np.all(o4[0, 0, :2] == 0.0)
+    assert n4[0, 0, 2] == 1 and np.array_equal(o4[0, 0, 2], v[0, 0, 0])
+    # Empty key set: every row is masked.
+    o5, l5, n5 = R.attention(q, k[:, :, :0], v[:, :, :0], scale=0.7, causal=True)
+    assert np.all(o5 == 0.0) and np.all(l5 == -np.inf) and np.all(n5 == 0)
+
+
+def check_alignment(R):
+    """A cached decode query sits at the newest position: with the right
+    offset it equals non-causal attention; aligned at local index 0 it sees
+    key 0 only (the §33.3 pitfall) and must come out different."""
+    rng = np.random.default_rng(6)
+    t_k, d = 9, 4
+    q = rng.standard_normal((1, 1, 1, d))
+    k = rng.standard_normal((1, 1, t_k, d))
+    v = rng.standard_normal((1, 1, t_k, d))
+    o_right, l_right, _ = R.attention(q, k, v, scale=0.5, causal=True, q_offset=t_k - 1)
+    o_full, l_full, _ = R.attention(q, k, v, scale=0.5, causal=False)
+    np.testing.assert_allclose(o_right, o_full, rtol=0, atol=1e-15)
+    o_wrong, _, n_wrong = R.attention(q, k, v, scale=0.5, causal=True, q_offset=0)
+    assert n_wrong[0, 0, 0] == 1
+    assert np.array_equal(o_wrong[0, 0, 0], v[0, 0, 0])
+    assert np.max(np.abs(o_wrong - o_right)) > 1e-3
+    # Multi-query verify: row r at offset T_k-5+r sees keys 0..T_k-5+r.
+    q5 = rng.standard_normal((1, 1, 5, d))
+    o5, _, n5 = R.attention(q5, k, v, scale=0.5, causal=True, q_offset=t_k - 5)
+    assert list(n5[0, 0]) == [t_k - 4, t_k - 3, t_k - 2, t_k - 1, t_k]
+    for r in range(5):
+        keep = t_k - 4 + r
+        o_r, _, _ = R.attention(q5[:, :, r:r + 1], k[:, :, :keep], v[:, :, :keep],
+                                scale=0.5, causal=False)
+        np.testing.assert_allclose(o5[0, 0, r], o_r[0, 0, 0], rtol=0, atol=1e-14)
+    # An offset past the end makes every key visible.
+    o6, _, _ = R.attention(q5, k, v, scale=0.5, causal=True, q_offset=10 * t_k)
+    o7, _, _ = R.attention(q5, k, v, scale=0.5, causal=False)
+    np.testing.assert_allclose(o6, o7, rtol=0, atol=0)
+
+
+def check_gqa_mapping(R):
+    """Query head hq reads KV head hq // (H_q/H_kv): with q = 0 each output
+    is the mean of its KV head's values, which differ per KV head."""
+    t_k, d = 5, 2
+    hq, hkv = 6, 3
+    v = np.zeros((1, hkv, t_k, d))
+    for h in range(hkv):
+        v[0, h] = 10.0 * h + np.arange(t_k * d).reshape(t_k, d)
+    k = np.ones((1, hkv, t_k, d))
+    q = np.zeros((1, hq, 1, d))
+    o, _, _ = R.attention(q, k, v, scale=1.0, causal=False)
+    for h in range(hq):
+        np.testing.assert_allclose(o[0, h, 0], v[0, h // 2].mean(0), rtol=0, atol=1e-13)
+
+
+def check_split_merge(R):
+    rng = np.random.default_rng(8)
+    b, hq, hkv, t_q, t_k, d_h, d_v = 2, 4, 2, 3, 23, 5, 6
+    q = rng.standard_normal((b, hq, t_q, d_h))
+    k = rng.standard_normal((b, hkv, t_k, d_h))
+    v = rng.standard_normal((b, hkv, t_k, d_v))
+    bias = rng.standard_normal((b, 1, t_q, t_k))
+    bias[0, 0, 1, :] = -np.inf
+    for off, split in ((t_k - t_q, 5), (4, 4), (t_k + 3, 23), (0, 1)):
+        o, lse, _ = R.attention(q, k, v, scale=0.4, causal=True, q_offset=off, bias=bias)
+        op, lp = R.split_partials(q, k, v, scale=0.4, causal=True, q_offset=off,
+                                  split_size=split, bias=bias)
+        assert op.shape[3] == -(-t_k // split)
+        om, lm = R.merge_partials(op, lp)
+        np.testing.assert_allclose(om, o, rtol=0, atol=1e-13)
+        assert np.array_equal(np.isneginf(lm), np.isneginf(lse))
+        fin = ~np.isneginf(lse)
+        np.testing.assert_allclose(lm[fin], lse[fin], rtol=0, atol=1e-13)
+
+
+def check_rows_match_full(R):
+    rng = np.random.default_rng(9)
+    b, hq, hkv, t_q, t_k, d_h, d_v = 2, 4, 2, 6, 13, 4, 3
+    q = rng.standard_normal((b, hq, t_q, d_h))
+    k = rng.standard_normal((b, hkv, t_k, d_h))
+    v = rng.standard_normal((b, hkv, t_k, d_v))
+    bias = rng.standard_normal((b, 1, t_q, t_k))
+    bias[1, 0, 2] = -np.inf
+    o, lse, n = R.attention(q, k, v, scale=0.6, causal=True, q_offset=5, bias=bias)
+    rows = [(bb, h, i) for bb in range(b) for h in range(hq) for i in range(t_q)]
+    o2, l2, n2 = R.attention_rows(q, k, v, rows, scale=0.6, causal=True,
+                                  q_offset=5, bias=bias)
+    np.testing.assert_allclose(o2, o.reshape(-1, d_v), rtol=0, atol=1e-14)
+    assert np.array_equal(n2, n.reshape(-1))
+    assert np.array_equal(np.isneginf(l2), np.isneginf(lse.reshape(-1)))
+
+
+def check_library_softmax(R):
+    """Cross-check with torch's own float64 CPU attention and logsumexp, with
+    an explicit boolean mask and the KV heads expanded per group."""
+    import torch
+    rng = np.random.default_rng(10)
+    for (b, hq, hkv, t_q, t_k, d_h, d_v, off) in ((2, 6, 3, 7, 19, 8, 5, 9),
+                                                  (1, 2, 2, 12, 12, 6, 7, 0)):
+        q = rng.standard_normal((b, hq, t_q, d_h))
+        k = rng.standard_normal((b, hkv, t_k, d_h))
+        v = rng.standard_normal((b, hkv, t_k, d_v))
+        bias = rng.standard_normal((b, 1, t_q, t_k))
+        bias[rng.random(bias.shape) < 0.2] = -np.inf
+        bias[b - 1, 0, 4, :] = -np.inf
+        scale = 0.37
+        o, lse, n = R.attention(q, k, v, scale=scale, causal=True, q_offset=off, bias=bias)
+        tq = torch.from_numpy(q)
+        tk = torch.from_numpy(k).repeat_interleave(hq // hkv, dim=1)
+        tv = torch.from_numpy(v).repeat_interleave(hq // hkv, dim=1)
+        pos = torch.arange(t_q)[:, None] + off
+        vis = torch.arange(t_k)[None, :] <= pos
+        tb = torch.from_numpy(bias).expand(b, hq, t_q, t_k)
+        allowed = vis & torch.isfinite(tb)
+        addmask = torch.where(allowed, tb, torch.tensor(float("-inf"), dtype=torch.float64))
+        live = allowed.any(-1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, attn_mask=addmask, scale=scale)
+        scores = (tq @ tk.transpose(-1, -2).contiguous()) * scale + addmask
+        ref_lse = torch.logsumexp(scores, dim=-1)
+        o_t = torch.from_numpy(o)
+        assert torch.allclose(o_t[live], ref[live], rtol=0, atol=1e-12)
+        assert torch.allclose(torch.from_numpy(lse)[live], ref_lse[live], rtol=0, atol=1e-12)
+        assert torch.equal(torch.from_numpy(n), allowed.sum(-1))
+        assert bool((~live).any())  # the case holds at least one fully masked row
+        assert torch.all(o_t[~live] == 0)
+        assert torch.all(torch.from_numpy(lse)[~live] == float("-inf"))
+
+
+def check_bias_broadcast(R):
+    rng = np.random.default_rng(11)
+    b, hq, t_q, t_k, d = 2, 3, 4, 6, 3
+    q = rng.standard_normal((b, hq, t_q, d))
+    k = rng.standard_normal((b, hq, t_k, d))
+    v = rng.standard_normal((b, hq, t_k, d))
+    keyrow = rng.standard_normal((b, 1, 1, t_k))
+    keyrow[0, 0, 0, 1] = -np.inf
+    dense = np.broadcast_to(keyrow, (b, hq, t_q, t_k)).copy()
+    o1, l1, n1 = R.attention(q, k, v, scale=0.5, causal=True, q_offset=1, bias=keyrow)
+    o2, l2, n2 = R.attention(q, k, v, scale=0.5, causal=True, q_offset=1, bias=dense)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2) and np.array_equal(n1, n2)
+
+
+ALL_CHECKS = [
+    check_example_25_1_exact, check_example_25_1_fp64, check_exercise_33_2,
+    check_kv_cache_vectors, check_equal_scores_mean, check_single_and_two_keys,
+    check_invariants, check_partitions_exact, check_partitions_fp64,
+    check_masked_blocks_and_rows, check_alignment, check_gqa_mapping,
+    check_split_merge, check_rows_match_full, check_library_softmax,
+    check_bias_broadcast,
+]

@@ -1,0 +1,39 @@
+"""The seeded input generators: shapes, dtypes, determinism and the masking
+structure of the padded variable-length workload."""
+
+import torch
+
+from online_softmax_exact_amd import inputs
+
+
+def test_small_configs_shapes_and_determinism():
+    for k in (1, 4):
+        a = inputs.make_config(k)
+        b = inputs.make_config(k)
+        spec = inputs.SPECS[k]
+        assert a.q.shape == (spec["batch"], spec["heads_q"], spec["t_q"], spec["d_h"])
+        assert a.k.shape == (spec["batch"], spec["heads_kv"], spec["t_k"], spec["d_h"])
+        assert a.v.shape == (spec["batch"], spec["heads_kv"], spec["t_k"], spec["d_v"])
+        assert a.q.dtype == spec["dtype"]
+        assert torch.equal(a.q, b.q) and torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
+        assert a.scale == float(torch.tensor(spec["d_h"] ** -0.5, dtype=torch.float32))
+
+
+def test_padded_bias_structure():
+    gen = torch.Generator("cpu").manual_seed(123)
+    bias, lengths, rows = inputs.padded_bias(4, 64, 64, gen)
+    assert bias.shape == (4, 1, 64, 64) and bias.dtype == torch.float32
+    for b in range(4):
+        L = lengths[b]
+        assert 1 <= L <= 64
+        assert torch.all(torch.isneginf(bias[b, 0, :, L:]))
+        dead = torch.isneginf(bias[b, 0]).all(dim=1)
+        assert sorted(torch.nonzero(dead).flatten().tolist()) == sorted(rows[b])
+        assert len(set(rows[b])) == 2
+
+
+def test_random_bias_kinds():
+    for kind, shape in (("dense", (2, 4, 3, 5)), ("shared", (2, 1, 3, 5)),
+                        ("keys", (2, 1, 1, 5)), ("rows", (2, 1, 3, 1))):
+        w = inputs.make_random(2, 4, 2, 3, 5, 8, 8, bias=kind, seed=3)
+        assert w.bias.shape == shape

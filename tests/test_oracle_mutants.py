@@ -1,0 +1,61 @@
+"""Plant a plausible mistake in a copy of the oracle (on the CPU) and check
+that the pin suite catches it: the pins are strong enough to notice a dropped
+term, a wrong sign or index, or a transposed operand."""
+
+import importlib.util
+import os
+import sys
+import types
+
+import pytest
+
+from pin_checks import ALL_CHECKS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "reference.py")
+
+MUTANTS = {
+    "causal_off_by_one": ("legal = j <= (q_offset + i)", "legal = j < (q_offset + i)"),
+    "gqa_modulo": ("kvh = hq // group\n            m_rows", "kvh = hq % h_kv\n            m_rows"),
+    "scale_dropped": ("s = scale * (q[b, hq] @ k[b, kvh].T)", "s = (q[b, hq] @ k[b, kvh].T)"),
+    "bias_scaled": ("s = s + np.where(m_rows == NEG_INF, 0.0, m_rows)",
+                    "s = s + scale * np.where(m_rows == NEG_INF, 0.0, m_rows)"),
+    "lse_drops_max": ("lse[live] = m + np.log(ell)", "lse[live] = np.log(ell)"),
+    "exp_sign": ("w = np.exp(s - m[:, None])", "w = np.exp(s + m[:, None])"),
+    "no_normalise": ("o[live] = (w @ values) / ell[:, None]", "o[live] = (w @ values)"),
+    "transposed_kv": ("s = scale * (q[b, hq] @ k[b, kvh].T)", "s = scale * (q[b, hq] @ k[b, kvh].T).T[: q.shape[2], : k.shape[2]] if q.shape[2] == k.shape[2] else scale * (q[b, hq] @ k[b, kvh].T)"),
+    "merge_wrong_weight": ("cb = arith.exp_diff(m_b, m)", "cb = arith.exp_diff(m_a, m)"),
+    "merge_unweighted_u": ("u = [ca * x + cb * y for x, y in zip(u_a, u_b)]",
+                           "u = [x + y for x, y in zip(u_a, u_b)]"),
+    "merge_keeps_first_max": ("m = m_a if not arith.gt(m_b, m_a) else m_b", "m = m_a"),
+    "stats_first_key_max": ("        if arith.gt(z[j], m):\n            m = z[j]", "        pass"),
+    "masked_row_nan": ("live = n_legal > 0", "live = n_legal >= 0"),
+    "empty_block_not_skipped": ("        if st is None:\n            continue\n        state = st if",
+                                "        if st is None:\n            st = (0.0, 0.0, [0.0] * d_v)\n        state = st if"),
+    "split_range_inclusive": ("legal = legal & (j >= lo) & (j < hi)", "legal = legal & (j >= lo) & (j <= hi)"),
+    "rows_offset_ignored": ("pos = q_offset + i", "pos = i"),
+}
+
+
+def _load_mutant(name, old, new):
+    src = open(SRC, encoding="utf-8").read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    src = src.replace(old, new, 1)
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    mod.__file__ = SRC
+    sys.modules[mod.__name__] = mod
+    exec(compile(src, f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    old, new = MUTANTS[name]
+    mod = _load_mutant(name, old, new)
+    caught = []
+    for check in ALL_CHECKS:
+        try:
+            check(mod)
+        except Exception as e:  # AssertionError, or a crash the mistake causes
+            caught.append((check.__name__, type(e).__name__))
+    assert caught, f"planted mistake {name!r} passed every pin"
