@@ -1,0 +1,190 @@
+"""Benchmark of the hot path on one MI355X.
+
+One step = one causal bf16 prefill (batch 1, 32 heads, T = 8192, d = 128,
+through attn_fwd) plus one split-KV GQA decode (batch 16, 32 query heads on 8
+KV heads, T_k = 32768, d = 128, 64 splits of 512 keys, through
+attn_decode_splitkv: partial kernel + merge kernel).  Inputs are seeded
+synthetic tensors, resident in HBM before timing starts.  Each launch is
+bracketed by HIP events on the stream it runs on.
+
+Prints one JSON line.  ``value`` is the prefill's algorithmic TFLOP/s
+(2 (d_h + d_v) flops per legal query-key pair); the decode's algorithmic
+KV GB/s (Q + K + V + O + LSE bytes once) is reported beside it.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill attention TFLOP/s + decode KV GB/s, as % of MI355X peak"
+PEAK_BF16_TFLOPS = 2516.6     # dense bf16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def prefill_counts(t: int, heads: int, batch: int, d_h: int, d_v: int):
+    pairs = batch * heads * t * (t + 1) // 2          # causal, offset 0
+    flops = 2 * (d_h + d_v) * pairs
+    bytes_ = batch * heads * t * (d_h + d_h + d_v + d_v) * 2 + batch * heads * t * 4
+    return pairs, flops, bytes_
+
+
+def decode_counts(batch, hq, hkv, t_q, t_k, d_h, d_v):
+    kv = batch * hkv * t_k * (d_h + d_v) * 2
+    qo = batch * hq * t_q * (d_h + d_v) * 2 + batch * hq * t_q * 4
+    pairs = batch * hq * t_q * t_k
+    return kv + qo, 2 * (d_h + d_v) * pairs
+
+
+def timed(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(wl, heads: int):
+    """The fp64 oracle as it stands, on `heads` heads of the prefill workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    q = wl.q[:, :heads].double().numpy()
+    k = wl.k[:, :heads].double().numpy()
+    v = wl.v[:, :heads].double().numpy()
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, scale=wl.scale, causal=True, q_offset=0)
+    dt = time.perf_counter() - t0
+    t = q.shape[2]
+    _, flops, _ = prefill_counts(t, heads, 1, q.shape[3], v.shape[3])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} of 32 heads of the causal prefill (T=8192, d=128), fp64 numpy, "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-heads", type=int, default=8,
+                    help="heads of the prefill the CPU oracle baseline times")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import online_softmax_exact_amd as attn
+    from online_softmax_exact_amd import _lib, inputs
+
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    print("bench: generating inputs", file=sys.stderr, flush=True)
+    pre = inputs.make_config(2)
+    dec = inputs.make_config(3)
+    pq, pk, pv = (t.to(dev) for t in (pre.q, pre.k, pre.v))
+    dq, dk, dv_ = (t.to(dev) for t in (dec.q, dec.k, dec.v))
+    po = torch.empty_like(pq)
+    pl = torch.empty(pq.shape[:3], dtype=torch.float32, device=dev)
+    do = torch.empty_like(dq)
+    dl = torch.empty(dq.shape[:3], dtype=torch.float32, device=dev)
+    ws_bytes = attn.attn_decode_workspace_bytes(dq, dk, dv_, split_size=dec.split_size,
+                                                scale=dec.scale, q_offset=dec.q_offset)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def run_prefill():
+        attn.attn_fwd(pq, pk, pv, scale=pre.scale, causal=True, q_offset=0, out=po, lse=pl)
+
+    def run_decode():
+        attn.attn_decode_splitkv(dq, dk, dv_, split_size=dec.split_size, scale=dec.scale,
+                                 causal=True, q_offset=dec.q_offset, workspace=ws, out=do,
+                                 lse=dl)
+
+    print("bench: timing", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        run_prefill()
+        run_decode()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for e in ev:
+        e[0].record(stream)
+        run_prefill()
+        e[1].record(stream)
+        run_decode()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    pre_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    dec_ms = [b.elapsed_time(c) for _, b, c in ev]
+    step_ms = [a.elapsed_time(c) for a, _, c in ev]
+
+    _, p_flops, p_bytes = prefill_counts(8192, 32, 1, 128, 128)
+    d_bytes, d_flops = decode_counts(16, 32, 8, 1, 32768, 128, 128)
+    p_avg = sum(pre_ms) / len(pre_ms)
+    d_avg = sum(dec_ms) / len(dec_ms)
+    p_tflops = p_flops / (p_avg * 1e-3) / 1e12
+    d_gbs = d_bytes / (d_avg * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(p_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sum(step_ms) / len(step_ms), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), resident in HBM)",
+        "config": {"workload": "causal prefill B=1 H=32 T=8192 d=128 (attn_fwd) + "
+                               "GQA split-KV decode B=16 Hq=32 Hkv=8 Tk=32768 d=128 S=512 "
+                               "(attn_decode_splitkv)",
+                   "prefill_ms": round(p_avg, 4), "prefill_ms_min": round(min(pre_ms), 4),
+                   "decode_ms": round(d_avg, 4), "decode_ms_min": round(min(dec_ms), 4),
+                   "wall_s": round(wall, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_fwd prefill",
+                     "per_launch_flops": p_flops, "per_launch_bytes": p_bytes},
+        "decode": {"value": round(d_gbs, 1), "unit": "GB/s", "ms": round(d_avg, 4),
+                   "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(d_gbs / PEAK_HBM_GBS, 4),
+                                "traffic": None, "per_launch_bytes": d_bytes,
+                                "per_launch_flops": d_flops}},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(pre, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+/*
+ * attn_mi355x.h - C ABI of an exact blocked attention library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The library computes scaled-dot-product attention exactly, key block by key
+ * block, carrying per query row the online-softmax statistics of the keys seen
+ * so far: the maximum score m, the scaled exponential sum l and the scaled
+ * value sum u.  Two disjoint key sets merge by m = max(m_A, m_B),
+ * l = e^{m_A-m} l_A + e^{m_B-m} l_B, u = e^{m_A-m} u_A + e^{m_B-m} u_B, and a
+ * row's output is o = u / l.  Sources: "Chapter 33 推理计算优化"
+ * (faketrader.github.io, llm-from-scratch), §33.2 eq 33.2 (the operation),
+ * eq 33.3 (statistics), eqs 33.4-33.5 (merge), the valid-flag rule and
+ * Algorithm 33.1; §33.3 (blocking, causal block skipping, interface
+ * consistency: mask polarity, non-square causal alignment, head grouping,
+ * scale, strides).  Query positions follow the KV-cache section of
+ * "Generation and Caching with the Same Model" (aihero.club): query row i is
+ * at logical position q_offset + i and, when causal, sees keys j <= q_offset + i.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *   allocates no device memory and keeps no mutable global state, so calls on
+ *   different streams may run concurrently.
+ * - Layout is [B, H, T, D] with the innermost (D) dimension contiguous; the
+ *   three outer strides are given in ELEMENTS, must be >= 0, and may be 0 to
+ *   broadcast.  LSE and n_legal are contiguous [B, H_q, T_q].
+ * - Every call is asynchronous on the given stream (a hipStream_t passed as
+ *   void*; NULL = the null stream).  The library never synchronises and
+ *   never reads device memory on the host.
+ * - Arguments are validated before anything is launched; on an error nothing
+ *   is written and a negative attn_status_t is returned.  ATTN_E_HIP reports a
+ *   failed launch; faults inside a kernel surface at the caller's next
+ *   synchronisation.
+ * - A row with no legal key (every key causally invisible or masked by a
+ *   -inf bias, or T_k = 0) is NOT an error: its output row is +0.0 (all bits
+ *   zero) and its LSE is -inf (0xFF800000), its n_legal 0.  No NaN is formed.
+ * - A pointer may be NULL only when the tensor it stands for has no elements.
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_NULL = -1,        /* a required pointer is NULL */
+  ATTN_E_SHAPE = -2,       /* negative size, H_q % H_kv != 0, bad split size */
+  ATTN_E_DTYPE = -3,       /* unknown element type */
+  ATTN_E_UNSUPPORTED = -4, /* d_h or d_v outside [1, 256], non-finite scale */
+  ATTN_E_STRIDE = -5,      /* a negative stride */
+  ATTN_E_WORKSPACE = -6,   /* decode workspace missing or too small */
+  ATTN_E_HIP = -7          /* the HIP runtime refused a launch */
+} attn_status_t;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+/* Problem description (eq 33.2 of §33.2 with the symbols of Table 33.1).
+ * z_ij = scale * <q_i, k_j> + M_ij, where M is the optional additive bias
+ * (never scaled).  Key j is LEGAL for row i iff it is causally visible
+ * (causal == 0, or j <= q_offset + i) and M_ij != -inf.  Query head hq reads
+ * KV head hq / (heads_q / heads_kv) (contiguous head groups). */
+typedef struct {
+  int64_t batch;          /* B >= 0 */
+  int64_t heads_q;        /* H_q >= 1, a multiple of heads_kv */
+  int64_t heads_kv;       /* H_kv >= 1 */
+  int64_t t_q;            /* T_q >= 0 query rows */
+  int64_t t_k;            /* T_k >= 0 keys */
+  int64_t d_h;            /* key/query head size, 1..256 */
+  int64_t d_v;            /* value head size, 1..256 */
+  int64_t q_offset;       /* logical position of query row 0; any value */
+  int64_t q_stride[3];    /* Q [B, H_q, T_q, d_h]: strides of b, h, t */
+  int64_t k_stride[3];    /* K [B, H_kv, T_k, d_h] */
+  int64_t v_stride[3];    /* V [B, H_kv, T_k, d_v] */
+  int64_t o_stride[3];    /* O [B, H_q, T_q, d_v] */
+  int64_t bias_stride[4]; /* bias over [b, hq, i, j]; 0 broadcasts */
+  const float* bias;      /* fp32 additive bias/mask, NULL = none; -inf masks;
+                             +inf and NaN are outside the contract */
+  float scale;            /* finite; usually 1/sqrt(d_h) */
+  int32_t dtype;          /* attn_dtype_t of Q, K, V and O */
+  int32_t causal;         /* 0 or 1 */
+  int32_t reserved;       /* must be 0 */
+} attn_params_t;
+
+/* sizeof(attn_params_t), so that bindings can check their mirror of it. */
+size_t attn_params_sizeof(void);
+int attn_abi_version(void);
+const char* attn_strerror(int status);
+
+/* Exact attention over all query rows (prefill, non-square causal, verify).
+ * Implements Algorithm 33.1 of §33.2 for every (b, hq, i) with the keys read
+ * in tiles; tiles that no row of a query tile can see are skipped (§33.3).
+ * Outputs: o [B, H_q, T_q, d_v] in p->dtype (bf16 rounded to nearest even),
+ * lse [B, H_q, T_q] fp32 = ln sum_{legal j} e^{z_ij} (natural log), and
+ * optionally n_legal [B, H_q, T_q] int32 = number of legal keys (NULL to
+ * skip).  Returns ATTN_OK or a negative attn_status_t. */
+int attn_fwd(const attn_params_t* p, const void* q, const void* k,
+             const void* v, void* o, float* lse, int32_t* n_legal,
+             void* stream);
+
+/* Bytes of device workspace that attn_decode_splitkv needs for this problem
+ * and split size: fp32 partial outputs [B, H_q, T_q, S, d_v] followed by fp32
+ * partial LSEs [B, H_q, T_q, S] (each array 256-byte aligned), where
+ * S = ceil(T_k / split_size) (at least 1).  Returns 0 on invalid arguments. */
+size_t attn_decode_workspace_bytes(const attn_params_t* p, int64_t split_size);
+
+/* Split-KV attention for few query rows over a long KV cache (decode).
+ * Keys are cut into contiguous ranges [s*S, min((s+1)*S, T_k)); for each
+ * (b, kv head, range) one partial (o_s, lse_s) per query row is written to
+ * the workspace (the range's own exact attention; o_s = 0 and lse_s = -inf if
+ * the range holds no legal key), then the partials of every row are merged by
+ * eqs 33.4-33.5 of §33.2 taking (lse_s, 1, o_s) as each range's statistics.
+ * Same outputs and conventions as attn_fwd (no n_legal).  split_size >= 1.
+ * workspace must hold attn_decode_workspace_bytes(p, split_size) bytes
+ * (256-byte aligned); its contents after the call are the partials in the
+ * layout above. */
+int attn_decode_splitkv(const attn_params_t* p, int64_t split_size,
+                        const void* q, const void* k_cache,
+                        const void* v_cache, void* o, float* lse,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Merge n_states partial results per row (eqs 33.4-33.5 of §33.2).
+ * Row r, state s: o_states[r*o_row_stride + s*o_state_stride + d] (fp32, d <
+ * d_v) and lse_states[r*lse_row_stride + s*lse_state_stride] (fp32, natural
+ * log; -inf marks an empty state, which is skipped).  Each valid state stands
+ * for the triple (m, l, u) = (lse_s, 1, o_s).  Output row r:
+ * o_out[r*o_out_row_stride + d] in out_dtype and lse_out[r] (contiguous);
+ * a row with no valid state gets (+0.0, -inf).  n_states >= 1 unless
+ * n_rows == 0; 1 <= d_v <= 256; strides >= 0. */
+int attn_merge_states(int64_t n_rows, int64_t n_states, int64_t d_v,
+                      const float* o_states, int64_t o_row_stride,
+                      int64_t o_state_stride, const float* lse_states,
+                      int64_t lse_row_stride, int64_t lse_state_stride,
+                      int32_t out_dtype, void* o_out,
+                      int64_t o_out_row_stride, float* lse_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_H */

@@ -1,0 +1,234 @@
+"""ctypes binding of ``libattn_mi355x.so`` (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; this module
+only turns torch tensors into pointers, strides and sizes, allocates outputs
+through torch, passes torch's current stream, and raises on a negative
+status.  There is no fallback: if the library is missing, the first call
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn_mi355x.so")
+
+ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_E_HIP = -7
+_DTYPES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
+
+EXPORTED = ("attn_params_sizeof", "attn_abi_version", "attn_strerror", "attn_fwd",
+            "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_merge_states")
+
+
+class Params(ctypes.Structure):
+    """Mirror of attn_params_t (field order and types as in the header)."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("heads_q", ctypes.c_int64), ("heads_kv", ctypes.c_int64),
+        ("t_q", ctypes.c_int64), ("t_k", ctypes.c_int64), ("d_h", ctypes.c_int64),
+        ("d_v", ctypes.c_int64), ("q_offset", ctypes.c_int64),
+        ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+        ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+        ("bias_stride", ctypes.c_int64 * 4), ("bias", ctypes.c_void_p),
+        ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load the HIP library (once) and declare its signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"HIP attention library not built: {p} is missing "
+                           "(run __graft_entry__.build() or python -m online_softmax_exact_amd.build)")
+    lib = ctypes.CDLL(p)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    pp = ctypes.POINTER(Params)
+    lib.attn_params_sizeof.restype = sz
+    lib.attn_params_sizeof.argtypes = []
+    lib.attn_abi_version.restype = ctypes.c_int
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_strerror.argtypes = [ctypes.c_int]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
+    lib.attn_decode_workspace_bytes.restype = sz
+    lib.attn_decode_workspace_bytes.argtypes = [pp, i64]
+    lib.attn_decode_splitkv.restype = ctypes.c_int
+    lib.attn_decode_splitkv.argtypes = [pp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.attn_merge_states.restype = ctypes.c_int
+    lib.attn_merge_states.argtypes = [i64, i64, i64, vp, i64, i64, vp, i64, i64,
+                                      ctypes.c_int32, vp, i64, vp, vp]
+    if lib.attn_params_sizeof() != ctypes.sizeof(Params):
+        raise RuntimeError("attn_params_t layout mismatch between header and binding")
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load_library().attn_strerror(status).decode()
+
+
+def _check(status: int):
+    if status == 0:
+        return
+    msg = strerror(status)
+    if status == ATTN_E_HIP:
+        raise RuntimeError(msg)
+    raise ValueError(msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None or t.numel() == 0 else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device, stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _outer_strides(t: torch.Tensor, name: str):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, T, D]")
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError(f"{name} must have a contiguous innermost dimension")
+    return tuple(int(x) for x in t.stride()[:3])
+
+
+def make_params(q, k, v, o, *, scale, causal, q_offset, bias) -> Params:
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    b, hq, tq, dh = q.shape
+    p = Params()
+    p.batch, p.heads_q, p.heads_kv = b, hq, k.shape[1]
+    p.t_q, p.t_k, p.d_h, p.d_v = tq, k.shape[2], dh, v.shape[3]
+    if k.shape[0] != b or v.shape[0] != b or v.shape[1] != k.shape[1] or v.shape[2] != k.shape[2]:
+        raise ValueError("k and v must be [B, H_kv, T_k, *] with the batch of q")
+    if k.shape[3] != dh:
+        raise ValueError("q and k must share d_h")
+    p.q_offset = int(q_offset)
+    p.q_stride[:] = _outer_strides(q, "q")
+    p.k_stride[:] = _outer_strides(k, "k")
+    p.v_stride[:] = _outer_strides(v, "v")
+    p.o_stride[:] = _outer_strides(o, "o")
+    p.scale = float(1.0 / math.sqrt(dh) if scale is None else scale)
+    p.dtype = _DTYPES[q.dtype]
+    p.causal = 1 if causal else 0
+    p.reserved = 0
+    if bias is not None:
+        if bias.dtype != torch.float32 or bias.device != q.device:
+            raise ValueError("bias must be a float32 tensor on the device of q")
+        full = bias.expand(b, hq, tq, k.shape[2])
+        p.bias_stride[:] = tuple(int(x) for x in full.stride())
+        p.bias = full.data_ptr() if full.numel() else None
+    return p
+
+
+def _outputs(q, d_v, out, lse):
+    b, hq, tq, _ = q.shape
+    if out is None:
+        out = torch.empty((b, hq, tq, d_v), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((b, hq, tq), dtype=torch.float32, device=q.device)
+    elif not lse.is_contiguous() or lse.shape != (b, hq, tq):
+        raise ValueError("lse must be a contiguous [B, H_q, T_q] float32 tensor")
+    return out, lse
+
+
+def attn_fwd(q, k, v, *, scale=None, causal=True, q_offset=0, bias=None,
+             out=None, lse=None, return_n_legal=False, stream=None):
+    """Exact attention; returns (o, lse) or (o, lse, n_legal)."""
+    lib = load_library()
+    out, lse = _outputs(q, v.shape[3], out, lse)
+    p = make_params(q, k, v, out, scale=scale, causal=causal, q_offset=q_offset, bias=bias)
+    n_legal = None
+    if return_n_legal:
+        n_legal = torch.empty(lse.shape, dtype=torch.int32, device=q.device)
+    _check(lib.attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                        _ptr(n_legal), _stream(q.device, stream)))
+    return (out, lse, n_legal) if return_n_legal else (out, lse)
+
+
+def attn_decode_workspace_bytes(q, k_cache, v_cache, *, split_size, scale=None,
+                                causal=True, q_offset=None, bias=None) -> int:
+    lib = load_library()
+    o = torch.empty((q.shape[0], q.shape[1], q.shape[2], v_cache.shape[3]),
+                    dtype=q.dtype, device="meta")
+    off = k_cache.shape[2] - q.shape[2] if q_offset is None else q_offset
+    p = make_params(q, k_cache, v_cache, o, scale=scale, causal=causal, q_offset=off, bias=bias)
+    return int(lib.attn_decode_workspace_bytes(ctypes.byref(p), int(split_size)))
+
+
+def attn_decode_splitkv(q, k_cache, v_cache, *, split_size, scale=None, causal=True,
+                        q_offset=None, bias=None, workspace=None, out=None, lse=None,
+                        stream=None):
+    """Split-KV decode + merge; returns (o, lse, workspace).
+
+    ``q_offset`` defaults to T_k - T_q (the queries are the newest positions).
+    ``workspace`` is a uint8 device tensor of at least
+    ``attn_decode_workspace_bytes`` bytes; allocated here when None."""
+    lib = load_library()
+    out, lse = _outputs(q, v_cache.shape[3], out, lse)
+    off = k_cache.shape[2] - q.shape[2] if q_offset is None else q_offset
+    p = make_params(q, k_cache, v_cache, out, scale=scale, causal=causal, q_offset=off, bias=bias)
+    need = int(lib.attn_decode_workspace_bytes(ctypes.byref(p), int(split_size)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_decode_splitkv(ctypes.byref(p), int(split_size), _ptr(q), _ptr(k_cache),
+                                   _ptr(v_cache), _ptr(out), _ptr(lse),
+                                   ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                   _stream(q.device, stream)))
+    return out, lse, workspace
+
+
+def split_workspace_views(workspace, q, v_cache, split_size):
+    """(o_parts [B, H_q, T_q, S, d_v], lse_parts [B, H_q, T_q, S]) views of a
+    decode workspace, in the layout the header documents."""
+    b, hq, tq, _ = q.shape
+    t_k, d_v = v_cache.shape[2], v_cache.shape[3]
+    n_splits = max(1, -(-t_k // split_size))
+    rows = b * hq * tq
+    o_bytes = rows * n_splits * d_v * 4
+    lse_off = (o_bytes + 255) // 256 * 256
+    o = workspace[:o_bytes].view(torch.float32).view(b, hq, tq, n_splits, d_v)
+    l = workspace[lse_off:lse_off + rows * n_splits * 4].view(torch.float32).view(b, hq, tq, n_splits)
+    return o, l
+
+
+def attn_merge_states(o_states, lse_states, *, out_dtype=torch.float32, out=None,
+                      lse_out=None, stream=None):
+    """Merge partials o_states [R, S, d_v] / lse_states [R, S] (fp32) into
+    (o [R, d_v], lse [R])."""
+    lib = load_library()
+    if o_states.dtype != torch.float32 or lse_states.dtype != torch.float32:
+        raise ValueError("partials must be float32")
+    if o_states.dim() != 3 or lse_states.dim() != 2:
+        raise ValueError("o_states must be [R, S, d_v] and lse_states [R, S]")
+    r, s, d_v = o_states.shape
+    if lse_states.shape != (r, s):
+        raise ValueError("lse_states must be [R, S]")
+    if d_v > 1 and o_states.stride(2) != 1:
+        raise ValueError("o_states must have a contiguous innermost dimension")
+    if out is None:
+        out = torch.empty((r, d_v), dtype=out_dtype, device=o_states.device)
+    if lse_out is None:
+        lse_out = torch.empty((r,), dtype=torch.float32, device=o_states.device)
+    if out.dim() != 2 or (d_v > 1 and out.stride(1) != 1) or not lse_out.is_contiguous():
+        raise ValueError("out must be [R, d_v] with a contiguous row; lse_out contiguous")
+    _check(lib.attn_merge_states(r, s, d_v, _ptr(o_states), o_states.stride(0),
+                                 o_states.stride(1), _ptr(lse_states), lse_states.stride(0),
+                                 lse_states.stride(1), _DTYPES[out.dtype], _ptr(out),
+                                 out.stride(0), _ptr(lse_out), _stream(o_states.device, stream)))
+    return out, lse_out

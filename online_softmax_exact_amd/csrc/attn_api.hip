@@ -1,0 +1,182 @@
+// Host side of the C ABI: argument validation (before any launch, without
+// touching device memory), kernel choice and launches on the caller's stream.
+// Validation mirrors the interface conditions of §33.3 of "Chapter 33
+// 推理计算优化" (mask polarity, non-square causal alignment, head grouping,
+// scale, strides must be consistent) and rejects input it cannot honour
+// instead of proceeding, as the cached forward of "Generation and Caching
+// with the Same Model" does for inconsistent caches.
+#include <math.h>
+#include <string.h>
+
+#include "attn_internal.h"
+#include "kernels.h"
+
+namespace attn {
+
+SplitLayout split_layout(const Problem& pb, int64_t split_size) {
+  SplitLayout L{};
+  L.split_size = split_size;
+  L.rows = pb.batch * pb.heads_q * pb.t_q;
+  L.n_splits = pb.t_k > 0 ? pb.t_k / split_size + (pb.t_k % split_size != 0) : 1;
+  const size_t o_bytes = static_cast<size_t>(L.rows) * L.n_splits * pb.d_v * sizeof(float);
+  L.o_bytes = o_bytes;
+  L.lse_offset = (o_bytes + 255) & ~static_cast<size_t>(255);
+  L.total = L.lse_offset + ((static_cast<size_t>(L.rows) * L.n_splits * sizeof(float) + 255) &
+                            ~static_cast<size_t>(255));
+  return L;
+}
+
+namespace {
+
+constexpr int64_t kMaxHead = 256;
+constexpr int64_t kMaxDim = int64_t(1) << 40;     // any size or row count
+constexpr int64_t kMaxOffset = int64_t(1) << 60;  // |q_offset|
+
+bool product_ok(int64_t a, int64_t b, int64_t c) {
+  const __int128 x = static_cast<__int128>(a) * b * c;
+  return x <= kMaxDim;
+}
+
+bool numel_nonzero(int64_t a, int64_t b, int64_t c, int64_t d) {
+  return a > 0 && b > 0 && c > 0 && d > 0;
+}
+
+int validate(const attn_params_t* p, Problem* pb) {
+  if (p == nullptr) return ATTN_E_NULL;
+  if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16) return ATTN_E_DTYPE;
+  if (p->batch < 0 || p->t_q < 0 || p->t_k < 0 || p->heads_q < 1 || p->heads_kv < 1)
+    return ATTN_E_SHAPE;
+  if (p->batch > kMaxDim || p->t_q > kMaxDim || p->t_k > kMaxDim || p->heads_q > kMaxDim)
+    return ATTN_E_SHAPE;
+  if (p->heads_q % p->heads_kv != 0) return ATTN_E_SHAPE;
+  // Row counts must stay far from int64 overflow in the index math.
+  if (!product_ok(p->batch, p->heads_q, p->t_q) || !product_ok(p->batch, p->heads_kv, p->t_k))
+    return ATTN_E_SHAPE;
+  if (p->causal != 0 && p->causal != 1) return ATTN_E_SHAPE;
+  if (p->reserved != 0) return ATTN_E_SHAPE;
+  if (p->q_offset > kMaxOffset || p->q_offset < -kMaxOffset) return ATTN_E_SHAPE;
+  if (p->d_h < 1 || p->d_h > kMaxHead || p->d_v < 1 || p->d_v > kMaxHead) return ATTN_E_UNSUPPORTED;
+  if (!isfinite(p->scale)) return ATTN_E_UNSUPPORTED;
+  for (int i = 0; i < 3; ++i)
+    if (p->q_stride[i] < 0 || p->k_stride[i] < 0 || p->v_stride[i] < 0 || p->o_stride[i] < 0)
+      return ATTN_E_STRIDE;
+  for (int i = 0; i < 4; ++i)
+    if (p->bias_stride[i] < 0) return ATTN_E_STRIDE;
+
+  pb->batch = p->batch; pb->heads_q = p->heads_q; pb->heads_kv = p->heads_kv;
+  pb->t_q = p->t_q; pb->t_k = p->t_k; pb->d_h = p->d_h; pb->d_v = p->d_v;
+  pb->q_offset = p->q_offset;
+  memcpy(pb->qs, p->q_stride, sizeof(pb->qs));
+  memcpy(pb->ks, p->k_stride, sizeof(pb->ks));
+  memcpy(pb->vs, p->v_stride, sizeof(pb->vs));
+  memcpy(pb->os, p->o_stride, sizeof(pb->os));
+  memcpy(pb->bs, p->bias_stride, sizeof(pb->bs));
+  pb->bias = p->bias;
+  pb->scale_log2 = p->scale * kLog2e;
+  pb->causal = p->causal;
+  pb->group = static_cast<int32_t>(p->heads_q / p->heads_kv);
+  return ATTN_OK;
+}
+
+// Pointers of tensors with elements must be non-NULL.
+int check_pointers(const Problem& pb, const void* q, const void* k, const void* v,
+                   const void* o, const void* lse) {
+  const bool rows = numel_nonzero(pb.batch, pb.heads_q, pb.t_q, 1);
+  const bool keys = numel_nonzero(pb.batch, pb.heads_kv, pb.t_k, 1);
+  if (rows && (q == nullptr || o == nullptr || lse == nullptr)) return ATTN_E_NULL;
+  if (rows && keys && (k == nullptr || v == nullptr)) return ATTN_E_NULL;
+  return ATTN_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
+
+}  // namespace
+}  // namespace attn
+
+using namespace attn;
+
+extern "C" {
+
+size_t attn_params_sizeof(void) { return sizeof(attn_params_t); }
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_NULL: return "a required pointer is NULL";
+    case ATTN_E_SHAPE: return "invalid shape (negative size, heads_q not a multiple of heads_kv, bad flag or split size)";
+    case ATTN_E_DTYPE: return "unknown element type";
+    case ATTN_E_UNSUPPORTED: return "unsupported head size (d_h and d_v must be 1..256) or non-finite scale";
+    case ATTN_E_STRIDE: return "negative stride";
+    case ATTN_E_WORKSPACE: return "decode workspace missing or too small";
+    case ATTN_E_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v,
+             void* o, float* lse, int32_t* n_legal, void* stream) {
+  Problem pb;
+  int st = validate(p, &pb);
+  if (st != ATTN_OK) return st;
+  if ((st = check_pointers(pb, q, k, v, o, lse)) != ATTN_OK) return st;
+  if (pb.batch == 0 || pb.t_q == 0) return ATTN_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_fast_fwd(pb, p->dtype, q, k, v, o, lse, n_legal, s, &st)) return st;
+  return hip_status(launch_generic(pb, p->dtype, q, k, v, o, lse, n_legal, 0, nullptr, nullptr, s));
+}
+
+size_t attn_decode_workspace_bytes(const attn_params_t* p, int64_t split_size) {
+  Problem pb;
+  if (validate(p, &pb) != ATTN_OK || split_size < 1) return 0;
+  return split_layout(pb, split_size).total;
+}
+
+int attn_decode_splitkv(const attn_params_t* p, int64_t split_size, const void* q,
+                        const void* k_cache, const void* v_cache, void* o, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  Problem pb;
+  int st = validate(p, &pb);
+  if (st != ATTN_OK) return st;
+  if (split_size < 1) return ATTN_E_SHAPE;
+  if ((st = check_pointers(pb, q, k_cache, v_cache, o, lse)) != ATTN_OK) return st;
+  if (pb.batch == 0 || pb.t_q == 0) return ATTN_OK;
+  const SplitLayout L = split_layout(pb, split_size);
+  if (workspace == nullptr || workspace_bytes < L.total) return ATTN_E_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return ATTN_E_WORKSPACE;
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_l = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse_offset);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (!launch_fast_decode_partials(pb, p->dtype, q, k_cache, v_cache, L, ws_o, ws_l, s, &e))
+    e = launch_generic(pb, p->dtype, q, k_cache, v_cache, nullptr, nullptr, nullptr,
+                       split_size, ws_o, ws_l, s);
+  if (e != hipSuccess) return ATTN_E_HIP;
+  const int64_t out_strides[3] = {pb.os[0], pb.os[1], pb.os[2]};
+  return hip_status(launch_merge(L.rows, L.n_splits, pb.d_v, ws_o, L.n_splits * pb.d_v, pb.d_v,
+                                 ws_l, L.n_splits, 1, p->dtype, o, pb.heads_q, pb.t_q,
+                                 out_strides, lse, s));
+}
+
+int attn_merge_states(int64_t n_rows, int64_t n_states, int64_t d_v, const float* o_states,
+                      int64_t o_row_stride, int64_t o_state_stride, const float* lse_states,
+                      int64_t lse_row_stride, int64_t lse_state_stride, int32_t out_dtype,
+                      void* o_out, int64_t o_out_row_stride, float* lse_out, void* stream) {
+  if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_E_DTYPE;
+  if (n_rows < 0 || n_states < 0 || n_rows > (int64_t(1) << 32)) return ATTN_E_SHAPE;
+  if (d_v < 1 || d_v > kMaxHead) return ATTN_E_UNSUPPORTED;
+  if (o_row_stride < 0 || o_state_stride < 0 || lse_row_stride < 0 || lse_state_stride < 0 ||
+      o_out_row_stride < 0)
+    return ATTN_E_STRIDE;
+  if (n_rows == 0) return ATTN_OK;
+  if (n_states < 1) return ATTN_E_SHAPE;
+  if (o_states == nullptr || lse_states == nullptr || o_out == nullptr || lse_out == nullptr)
+    return ATTN_E_NULL;
+  const int64_t out_strides[3] = {o_out_row_stride, 0, 0};
+  return hip_status(launch_merge(n_rows, n_states, d_v, o_states, o_row_stride, o_state_stride,
+                                 lse_states, lse_row_stride, lse_state_stride, out_dtype, o_out,
+                                 1, 1, out_strides, lse_out, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Internal declarations shared by the host library and the kernels.
+// Device code targets gfx950 (CDNA4) only: wave64, MFMA, 160 KiB LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_mi355x.h"
+
+namespace attn {
+
+// ---------------------------------------------------------------------------
+// Problem description after validation (plain values, passed by value to the
+// kernels).  Scores are handled in the base-2 domain: z2 = z * log2(e), so a
+// weight e^{z - m} is exp2(z2 - m2) on the hardware's v_exp_f32.
+// ---------------------------------------------------------------------------
+struct Problem {
+  int64_t batch, heads_q, heads_kv, t_q, t_k, d_h, d_v, q_offset;
+  int64_t qs[3], ks[3], vs[3], os[3], bs[4];
+  const float* bias;
+  float scale_log2;   // scale * log2(e)
+  int32_t causal;
+  int32_t group;      // heads_q / heads_kv
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Workspace layout of split-KV decode: fp32 o partials [rows, S, d_v], then
+// fp32 lse partials [rows, S], where rows = B * H_q * T_q in (b, hq, i) order.
+struct SplitLayout {
+  int64_t rows, n_splits, split_size;
+  size_t o_bytes, lse_offset, total;
+};
+SplitLayout split_layout(const Problem& pb, int64_t split_size);
+
+// ---- launchers (return hipSuccess or the launch error) --------------------
+hipError_t launch_generic(const Problem& pb, int dtype, const void* q,
+                          const void* k, const void* v, void* o, float* lse,
+                          int32_t* n_legal, int64_t split_size, float* ws_o,
+                          float* ws_lse, hipStream_t stream);
+
+hipError_t launch_merge(int64_t n_rows, int64_t n_states, int64_t d_v,
+                        const float* o_states, int64_t o_row_stride,
+                        int64_t o_state_stride, const float* lse_states,
+                        int64_t lse_row_stride, int64_t lse_state_stride,
+                        int out_dtype, void* o_out, int64_t rows_per_b,
+                        int64_t rows_per_h, const int64_t out_strides[3],
+                        float* lse_out, hipStream_t stream);
+
+// ---- device helpers -------------------------------------------------------
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest even; inputs here are finite (no NaN is ever formed).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
+__device__ __forceinline__ float fast_log2(float x) {
+  return __builtin_amdgcn_logf(x);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ static void store(float* p, int64_t i, float x) { p[i] = x; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ static float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  __device__ static void store(uint16_t* p, int64_t i, float x) { p[i] = f32_to_bf16(x); }
+};
+
+#endif
+
+}  // namespace attn

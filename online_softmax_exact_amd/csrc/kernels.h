@@ -1,0 +1,19 @@
+// Fast-path launchers.  Each returns true when it took the problem (and then
+// stores the launch status in *status / *err) and false when the problem is
+// outside its specialisation, in which case the generic kernel runs.
+#pragma once
+
+#include "attn_internal.h"
+
+namespace attn {
+
+bool launch_fast_fwd(const Problem& pb, int dtype, const void* q, const void* k,
+                     const void* v, void* o, float* lse, int32_t* n_legal,
+                     hipStream_t stream, int* status);
+
+bool launch_fast_decode_partials(const Problem& pb, int dtype, const void* q,
+                                 const void* k, const void* v, const SplitLayout& L,
+                                 float* ws_o, float* ws_lse, hipStream_t stream,
+                                 hipError_t* err);
+
+}  // namespace attn

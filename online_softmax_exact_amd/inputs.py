@@ -2,11 +2,13 @@
 
 This module draws random tensors and fixes shapes; it holds none of the
 attention arithmetic, so both the HIP path's tests and the CPU oracle can take
-their inputs from it.  Every draw uses its own ``torch.Generator`` on the CPU
-(a local generator, as the KV-cache page of "Generation and Caching with the
-Same Model" recommends), in a fixed order: Q, K, V, then the extras of the
-padded variable-length workload.  bf16 tensors are fp32 N(0, 1) draws rounded
-to nearest-even by ``Tensor.to(torch.bfloat16)``.
+their inputs from it.  Every draw uses its own local ``torch.Generator`` on the
+CPU (as the KV-cache page of "Generation and Caching with the Same Model"
+recommends).  Tensor number t of a workload (Q = 0, K = 1, V = 2, bias = 3)
+is drawn in chunks along its two outer dimensions; chunk c comes from a
+generator seeded with ``derive_seed(seed, t, c)``, so the values do not depend
+on how many threads draw them.  bf16 tensors are fp32 N(0, 1) draws rounded to
+nearest-even by ``Tensor.to(torch.bfloat16)``.
 
 Workloads (the shapes of the pages' sizing example and of the cached-decode,
 speculative-verify and padded-batch uses the pages describe):
@@ -27,7 +29,9 @@ speculative-verify and padded-batch uses the pages describe):
 
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
+import os
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -82,41 +86,66 @@ def default_scale(d_h: int) -> float:
     return float(torch.tensor(1.0 / math.sqrt(d_h), dtype=torch.float32))
 
 
-def _draw(shape, gen, dtype):
-    x = torch.randn(shape, generator=gen, dtype=torch.float32)
-    return x if dtype == torch.float32 else x.to(dtype)
+def derive_seed(seed: int, tensor: int, chunk: int) -> int:
+    return (seed * 1_000_003 + tensor * 7_919 + chunk * 104_729 + 1) % (1 << 62)
+
+
+def _draw(shape, seed: int, tensor: int, dtype) -> torch.Tensor:
+    """N(0, 1) tensor of ``shape``; chunk c = (i0, i1) of the two outer dims."""
+    shape = tuple(int(x) for x in shape)
+    out = torch.empty(shape, dtype=dtype)
+    n0, n1 = shape[0], shape[1]
+    inner = shape[2:]
+
+    def one(c):
+        i0, i1 = divmod(c, n1)
+        g = torch.Generator("cpu").manual_seed(derive_seed(seed, tensor, c))
+        x = torch.randn(inner, generator=g, dtype=torch.float32)
+        out[i0, i1] = x if dtype == torch.float32 else x.to(dtype)
+
+    chunks = n0 * n1
+    workers = min(16, os.cpu_count() or 1, max(1, chunks))
+    if workers == 1 or out.numel() < (1 << 20):
+        for c in range(chunks):
+            one(c)
+    else:
+        with cf.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one, range(chunks)))
+    return out
 
 
 def make_config(k: int, seed: Optional[int] = None) -> Workload:
     """Workload k (1..5) at its full size, drawn from seed 1000 + k."""
     spec = SPECS[k]
-    gen = torch.Generator("cpu").manual_seed(1000 + k if seed is None else seed)
+    seed = 1000 + k if seed is None else seed
     b, hq, hkv = spec["batch"], spec["heads_q"], spec["heads_kv"]
     tq, tk, dh, dv = spec["t_q"], spec["t_k"], spec["d_h"], spec["d_v"]
     dt = spec["dtype"]
-    q = _draw((b, hq, tq, dh), gen, dt)
-    kk = _draw((b, hkv, tk, dh), gen, dt)
-    v = _draw((b, hkv, tk, dv), gen, dt)
+    q = _draw((b, hq, tq, dh), seed, 0, dt)
+    kk = _draw((b, hkv, tk, dh), seed, 1, dt)
+    v = _draw((b, hkv, tk, dv), seed, 2, dt)
     wl = Workload(name=spec["name"], q=q, k=kk, v=v, scale=default_scale(dh),
                   causal=spec["causal"], q_offset=spec["q_offset"],
                   split_size=spec.get("split_size"))
     if spec.get("bias"):
-        bias, lengths, rows = padded_bias(b, tq, tk, gen)
+        bias, lengths, rows = padded_bias(b, tq, tk, seed)
         wl.bias = bias
         wl.extras = dict(lengths=lengths, masked_rows=rows)
     return wl
 
 
-def padded_bias(batch: int, t_q: int, t_k: int, gen: torch.Generator):
+def padded_bias(batch: int, t_q: int, t_k: int, seed: int):
     """fp32 bias [batch, 1, t_q, t_k] for a padded variable-length batch.
 
-    Draw order: lengths L_b ~ U{1..t_k}; bias ~ N(0, 1); then, per sequence,
-    two distinct rows among the first max(L_b, 2).  Keys j >= L_b get -inf
-    (padding masks keys only) and the two chosen rows get -inf on every key,
-    so each sequence has exactly two rows with no legal key.
+    bias ~ N(0, 1) (tensor number 3 of the workload); then, from one generator
+    seeded with ``derive_seed(seed, 4, 0)``: lengths L_b ~ U{1..t_k} and, per
+    sequence, two distinct rows among the first max(L_b, 2).  Keys j >= L_b
+    get -inf (padding masks keys only) and the two chosen rows get -inf on
+    every key, so each sequence has exactly two rows with no legal key.
     """
+    bias = _draw((batch, 1, t_q, t_k), seed, 3, torch.float32)
+    gen = torch.Generator("cpu").manual_seed(derive_seed(seed, 4, 0))
     lengths = torch.randint(1, t_k + 1, (batch,), generator=gen)
-    bias = torch.randn((batch, 1, t_q, t_k), generator=gen, dtype=torch.float32)
     rows = []
     for b in range(batch):
         L = int(lengths[b])
@@ -141,10 +170,10 @@ def make_random(batch: int, heads_q: int, heads_kv: int, t_q: int, t_k: int,
     broadcast over queries and heads); "rows" ([B, 1, T_q, 1], broadcast over
     keys).  ``masked_frac`` sets that fraction of bias entries to -inf.
     """
-    gen = torch.Generator("cpu").manual_seed(seed)
-    q = _draw((batch, heads_q, t_q, d_h), gen, dtype)
-    k = _draw((batch, heads_kv, t_k, d_h), gen, dtype)
-    v = _draw((batch, heads_kv, t_k, d_v), gen, dtype)
+    q = _draw((batch, heads_q, t_q, d_h), seed, 0, dtype)
+    k = _draw((batch, heads_kv, t_k, d_h), seed, 1, dtype)
+    v = _draw((batch, heads_kv, t_k, d_v), seed, 2, dtype)
+    gen = torch.Generator("cpu").manual_seed(derive_seed(seed, 3, 0))
     shapes = {"dense": (batch, heads_q, t_q, t_k), "shared": (batch, 1, t_q, t_k),
               "keys": (batch, 1, 1, t_k), "rows": (batch, 1, t_q, 1)}
     m = None

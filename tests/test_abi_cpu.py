@@ -1,0 +1,135 @@
+"""The C-ABI library on the CPU: it loads without a GPU, exports every entry
+point the header declares, and rejects invalid arguments before launching
+anything (only calls that fail validation, or have nothing to do, are made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from online_softmax_exact_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_mi355x.h")
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return _lib.load_library()
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_params_layout(lib):
+    assert lib.attn_abi_version() == 1
+    assert lib.attn_params_sizeof() == ctypes.sizeof(_lib.Params) == 216
+
+
+def test_strerror(lib):
+    for code in range(-7, 1):
+        assert lib.attn_strerror(code)
+    assert b"unknown" in lib.attn_strerror(-99)
+
+
+def good_params(**kw):
+    p = _lib.Params()
+    p.batch, p.heads_q, p.heads_kv, p.t_q, p.t_k, p.d_h, p.d_v = 2, 4, 2, 8, 16, 64, 64
+    p.q_stride[:] = (4 * 8 * 64, 8 * 64, 64)
+    p.k_stride[:] = (2 * 16 * 64, 16 * 64, 64)
+    p.v_stride[:] = (2 * 16 * 64, 16 * 64, 64)
+    p.o_stride[:] = (4 * 8 * 64, 8 * 64, 64)
+    p.scale, p.dtype, p.causal = 0.125, _lib.ATTN_BF16, 1
+    for key, val in kw.items():
+        setattr(p, key, val)
+    return p
+
+
+def fwd(lib, p, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE):
+    return lib.attn_fwd(ctypes.byref(p) if p is not None else None, q, k, v, o, lse, None, None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("dtype", 7, -3), ("heads_q", 3, -2), ("heads_kv", 0, -2), ("batch", -1, -2),
+    ("t_q", -5, -2), ("t_k", -1, -2), ("d_h", 0, -4), ("d_h", 257, -4), ("d_v", 300, -4),
+    ("causal", 2, -2), ("reserved", 1, -2), ("scale", float("nan"), -4),
+    ("scale", float("inf"), -4), ("q_offset", 1 << 62, -2), ("batch", 1 << 41, -2),
+])
+def test_fwd_rejects(lib, field, value, code):
+    assert fwd(lib, good_params(**{field: value})) == code
+
+
+def test_fwd_rejects_strides_and_nulls(lib):
+    p = good_params()
+    p.k_stride[1] = -1
+    assert fwd(lib, p) == -5
+    p = good_params()
+    p.bias_stride[3] = -2
+    assert fwd(lib, p) == -5
+    assert fwd(lib, None) == -1
+    assert fwd(lib, good_params(), q=None) == -1
+    assert fwd(lib, good_params(), v=None) == -1
+    assert fwd(lib, good_params(), lse=None) == -1
+
+
+def test_fwd_nothing_to_do(lib):
+    # T_q = 0 and B = 0 are successful no-ops (nothing launched, NULLs allowed).
+    assert fwd(lib, good_params(t_q=0), q=None, o=None, lse=None) == 0
+    assert fwd(lib, good_params(batch=0), q=None, k=None, v=None, o=None, lse=None) == 0
+
+
+def test_decode_workspace_bytes(lib):
+    p = good_params(t_q=1, t_k=1000)
+    rows, s, dv = 2 * 4 * 1, -(-1000 // 96), 64
+    o_bytes = rows * s * dv * 4
+    want = (o_bytes + 255) // 256 * 256 + (rows * s * 4 + 255) // 256 * 256
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(p), 96) == want
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(p), 0) == 0
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(good_params(dtype=9)), 96) == 0
+    huge = lib.attn_decode_workspace_bytes(ctypes.byref(p), 1 << 62)  # one split
+    assert huge == (rows * dv * 4 + 255) // 256 * 256 + 256
+
+
+def test_decode_rejects(lib):
+    p = good_params(t_q=1, t_k=1000)
+    need = lib.attn_decode_workspace_bytes(ctypes.byref(p), 128)
+    call = lambda split, ws, nbytes, **kw: lib.attn_decode_splitkv(
+        ctypes.byref(p), split, FAKE, FAKE, FAKE, FAKE, FAKE, ws, nbytes, None)
+    assert call(0, FAKE, need) == -2
+    assert call(-3, FAKE, need) == -2
+    assert call(128, None, need) == -6
+    assert call(128, FAKE, need - 1) == -6
+    assert call(128, ctypes.c_void_p(0x100010), need) == -6  # not 256-byte aligned
+    bad = good_params(t_q=1, t_k=1000, heads_q=5)
+    assert lib.attn_decode_splitkv(ctypes.byref(bad), 128, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, need, None) == -2
+
+
+def test_merge_rejects(lib):
+    m = lambda **kw: lib.attn_merge_states(
+        kw.get("rows", 4), kw.get("states", 3), kw.get("dv", 64), kw.get("o", FAKE), 192, 64,
+        kw.get("l", FAKE), 3, 1, kw.get("dtype", 0), kw.get("out", FAKE), 64,
+        kw.get("lo", FAKE), None)
+    assert m(dtype=5) == -3
+    assert m(rows=-1) == -2
+    assert m(states=0) == -2
+    assert m(dv=0) == -4
+    assert m(dv=257) == -4
+    assert m(o=None) == -1
+    assert m(lo=None) == -1
+    assert m(rows=0, o=None, l=None, out=None, lo=None) == 0

@@ -1,0 +1,135 @@
+"""GPU parity on the five full-size workloads, through the same entry points
+and launch configuration the benchmark times.  Where the whole oracle would
+take too long, it is evaluated row by row on a sample of rows (first and last
+rows, tile edges, random rows, every fully masked row), and properties that
+hold for every row are checked on all of them."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import online_softmax_exact_amd as attn
+from online_softmax_exact_amd import inputs
+from gpu_util import assert_close, ensure_built, f64, oracle_full, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    ensure_built()
+
+
+def sample_rows(b, hq, tq, n_random, seed, extra=()):
+    g = np.random.default_rng(seed)
+    rows = set(extra)
+    edges = sorted({0, 1, 63, 64, 127, 128, 255, 256, tq // 2, tq - 129, tq - 128, tq - 2, tq - 1})
+    for i in edges:
+        if 0 <= i < tq:
+            rows.add((0, 0, i))
+            rows.add((b - 1, hq - 1, i))
+    for _ in range(n_random):
+        rows.add((int(g.integers(b)), int(g.integers(hq)), int(g.integers(tq))))
+    return sorted(rows)
+
+
+def check_sampled(wl, o, lse, rows, dtype):
+    o_ref, l_ref, n_ref = oracle.attention_rows(
+        wl.q, wl.k, wl.v, rows, scale=wl.scale, causal=wl.causal, q_offset=wl.q_offset,
+        bias=wl.bias)
+    idx = tuple(np.array(rows).T)
+    og = o.detach().cpu()[idx]
+    lg = lse.detach().cpu()[idx]
+    assert_close(og, lg, o_ref, l_ref, dtype, what="sampled rows")
+    return n_ref
+
+
+def test_config1_fp32_full():
+    wl = inputs.make_config(1)
+    print("config 1", wl.name, flush=True)
+    q, k, v, _ = to_dev(wl)
+    o, lse, n = attn.attn_fwd(q, k, v, scale=wl.scale, causal=True, q_offset=0,
+                              return_n_legal=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref, n_ref = oracle_full(wl)
+    assert_close(o, lse, o_ref, l_ref, torch.float32)
+    assert np.array_equal(n.cpu().numpy(), n_ref)
+
+
+def test_config2_causal_prefill():
+    wl = inputs.make_config(2)
+    print("config 2", wl.name, flush=True)
+    q, k, v, _ = to_dev(wl)
+    o, lse, n = attn.attn_fwd(q, k, v, scale=wl.scale, causal=True, q_offset=0,
+                              return_n_legal=True)
+    torch.cuda.synchronize()
+    # Properties of every row: finite, no NaN, exact legal-key counts i + 1.
+    assert not torch.isnan(o).any() and torch.isfinite(lse).all()
+    want_n = torch.arange(1, 8193, dtype=torch.int32, device=n.device).expand_as(n)
+    assert torch.equal(n, want_n)
+    rows = sample_rows(1, 32, 8192, 48, seed=2)
+    check_sampled(wl, o, lse, rows, torch.bfloat16)
+
+
+def test_config3_gqa_decode():
+    wl = inputs.make_config(3)
+    print("config 3", wl.name, flush=True)
+    q, k, v, _ = to_dev(wl)
+    o, lse, ws = attn.attn_decode_splitkv(q, k, v, split_size=wl.split_size, scale=wl.scale,
+                                          causal=True, q_offset=wl.q_offset)
+    torch.cuda.synchronize()
+    rows = [(b, h, 0) for b in range(16) for h in range(32)]   # every row
+    check_sampled(wl, o, lse, rows, torch.bfloat16)
+    # Sampled partials of the workspace: split s of row (b, h) is the exact
+    # attention over keys [512 s, 512 s + 512).
+    o_parts, l_parts = attn.split_workspace_views(ws, q, v, wl.split_size)
+    for (b, h, s) in ((0, 0, 0), (3, 17, 31), (15, 31, 63)):
+        lo, hi = s * 512, s * 512 + 512
+        sub = inputs.Workload(name="split", q=wl.q[b:b + 1, h:h + 1], k=wl.k[b:b + 1, h // 4:h // 4 + 1],
+                              v=wl.v[b:b + 1, h // 4:h // 4 + 1], scale=wl.scale, causal=True,
+                              q_offset=wl.q_offset)
+        o_ref, l_ref, _ = oracle_full(sub, key_range=(lo, hi))
+        assert_close(f64(o_parts[b, h, 0, s]), f64(l_parts[b, h, 0, s:s + 1]),
+                     o_ref[0, 0, 0], l_ref[0, 0], torch.bfloat16, what=f"partial {b},{h},{s}")
+
+
+def test_config4_verify():
+    wl = inputs.make_config(4)
+    print("config 4", wl.name, flush=True)
+    q, k, v, _ = to_dev(wl)
+    o, lse, n = attn.attn_fwd(q, k, v, scale=wl.scale, causal=True, q_offset=wl.q_offset,
+                              return_n_legal=True)
+    torch.cuda.synchronize()
+    want_n = torch.arange(4092, 4097, dtype=torch.int32, device=n.device).expand_as(n)
+    assert torch.equal(n, want_n)
+    rows = [(b, h, i) for b in range(0, 32, 3) for h in range(32) for i in range(5)]
+    check_sampled(wl, o, lse, rows, torch.bfloat16)
+
+
+def test_config5_padded_bias():
+    wl = inputs.make_config(5)
+    print("config 5", wl.name, "lengths", wl.extras["lengths"], flush=True)
+    q, k, v, m = to_dev(wl)
+    o, lse, n = attn.attn_fwd(q, k, v, scale=wl.scale, causal=True, q_offset=0, bias=m,
+                              return_n_legal=True)
+    torch.cuda.synchronize()
+    # Exact legal-key counts for every row, from the oracle's legality rule.
+    n_cpu = n.cpu().numpy()
+    for b in range(8):
+        legal = oracle.legal_keys(4096, 4096, True, 0, f64(wl.bias[b, 0]))
+        counts = legal.sum(axis=1)
+        assert np.array_equal(n_cpu[b], np.broadcast_to(counts, (16, 4096))), f"n_legal batch {b}"
+    # Exactly the two seeded rows per sequence are masked: +0.0 and -inf.
+    dead = torch.isneginf(lse).cpu()
+    assert int(dead.sum()) == 8 * 2 * 16
+    for b, rows in enumerate(wl.extras["masked_rows"]):
+        for r in rows:
+            assert bool(dead[b, :, r].all())
+            assert bool((o[b, :, r].view(torch.int16) == 0).all())
+    assert not torch.isnan(o).any()
+    extra = [(b, h, r) for b, rows in enumerate(wl.extras["masked_rows"]) for r in rows
+             for h in (0, 15)]
+    extra += [(b, 3, min(wl.extras["lengths"][b], 4095)) for b in range(8)]  # first padded row
+    rows = sample_rows(8, 16, 4096, 48, seed=5, extra=extra)
+    check_sampled(wl, o, lse, rows, torch.bfloat16)

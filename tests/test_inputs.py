@@ -20,8 +20,7 @@ def test_small_configs_shapes_and_determinism():
 
 
 def test_padded_bias_structure():
-    gen = torch.Generator("cpu").manual_seed(123)
-    bias, lengths, rows = inputs.padded_bias(4, 64, 64, gen)
+    bias, lengths, rows = inputs.padded_bias(4, 64, 64, 123)
     assert bias.shape == (4, 1, 64, 64) and bias.dtype == torch.float32
     for b in range(4):
         L = lengths[b]
@@ -37,3 +36,11 @@ def test_random_bias_kinds():
                         ("keys", (2, 1, 1, 5)), ("rows", (2, 1, 3, 1))):
         w = inputs.make_random(2, 4, 2, 3, 5, 8, 8, bias=kind, seed=3)
         assert w.bias.shape == shape
+
+
+def test_chunked_draw_is_thread_independent(monkeypatch):
+    a = inputs._draw((3, 5, 300, 40), 9, 1, torch.bfloat16)
+    monkeypatch.setattr(inputs.os, "cpu_count", lambda: 1)
+    b = inputs._draw((3, 5, 300, 40), 9, 1, torch.bfloat16)
+    assert torch.equal(a, b)
+    assert abs(float(a.float().mean())) < 0.01 and abs(float(a.float().std()) - 1) < 0.01
