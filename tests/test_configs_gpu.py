@@ -90,8 +90,8 @@ def test_config3_gqa_decode():
                               v=wl.v[b:b + 1, h // 4:h // 4 + 1], scale=wl.scale, causal=True,
                               q_offset=wl.q_offset)
         o_ref, l_ref, _ = oracle_full(sub, key_range=(lo, hi))
-        assert_close(f64(o_parts[b, h, 0, s]), f64(l_parts[b, h, 0, s:s + 1]),
-                     o_ref[0, 0, 0], l_ref[0, 0], torch.bfloat16, what=f"partial {b},{h},{s}")
+        assert_close(f64(o_parts[b, h, 0, s:s + 1]), f64(l_parts[b, h, 0, s:s + 1]),
+                     o_ref[0, 0], l_ref[0, 0], torch.bfloat16, what=f"partial {b},{h},{s}")
 
 
 def test_config4_verify():
