@@ -1,0 +1,395 @@
+// Few-query-row kernel for bf16 problems with d_h, d_v in {64, 128}: split-KV
+// decode partials (attn_decode_splitkv) and attn_fwd when H_q/H_kv * T_q is
+// small (cached decode, multi-query verification).
+//
+// What it computes: for one (batch, KV head, group of up to 32 query rows,
+// key range), the exact attention of every row over the legal keys of the
+// range (eq 33.2 of "Chapter 33 推理计算优化" §33.2), either as the final
+// output or as the partial (o_s, lse_s) of that range; partials are later
+// merged by eqs 33.4-33.5.  The rows of a workgroup are the T_q query rows of
+// every query head that shares the KV head, so each K/V byte of the range is
+// read from HBM exactly once for all of them.
+//
+// Mapping onto CDNA4 (gfx950): decode is bound by HBM bandwidth (each step
+// reads the whole cache), so the kernel is built to stream K and V once with
+// deep prefetch and keep the arithmetic off the critical path:
+// * The four wavefronts of a workgroup split the key range into four
+//   contiguous parts and each keeps its own statistics (m, l, u) per row.
+// * Per 32-key tile: S^T = K Q^T with v_mfma_f32_32x32x16_bf16; the K operand
+//   is loaded from HBM straight into registers in the MFMA layout (no LDS),
+//   Q^T stays in registers.  V goes through a wave-private LDS buffer and is
+//   read back transposed (ds_read_b64_tr_b16) as the A operand of
+//   O^T = V^T P^T.  The loads of tile t + 1 are issued before tile t is
+//   computed.
+// * At the end the four per-wave states are merged in LDS with eqs 33.4-33.5
+//   (a wave with no legal key for a row contributes nothing).
+#include "attn_internal.h"
+#include "kernels.h"
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr int kTile = 32;         // keys per tile
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 32;         // query rows per workgroup
+constexpr float kRescale = 8.0f;  // lazy-rescale threshold, base-2 units
+
+template <int DH, int DV>
+struct FCfg {
+  static constexpr int KS = DH / 16;
+  static constexpr int MO = DV / 32;
+  static constexpr int V_STRIDE = DV * 2 + 64;         // bytes per V row in LDS
+  static constexpr int VBUF = kTile * V_STRIDE;        // one wave's V tile
+  static constexpr int V_PER_LANE = kTile * DV / 8 / 64;
+  static constexpr int MERGE_O = kWaves * kRows * DV * 4;
+  static constexpr int MERGE = MERGE_O + 2 * kWaves * kRows * 4;
+  static constexpr int SMEM = MERGE > kWaves * VBUF ? MERGE : kWaves * VBUF;
+};
+
+struct FArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  float* ws_o;
+  float* ws_lse;
+  int64_t qs[3], ks[3], vs[3], os[3];
+  int64_t q_offset;
+  int64_t split_size;       // keys per work item
+  int32_t t_q, t_k, heads_q, heads_kv, group, rows, n_rg, n_splits;
+  float scale_log2;
+  int32_t causal;
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ u32x2 tr_read(const lds_char* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+template <int DH, int DV, bool SPLIT>
+__global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
+  using C = FCfg<DH, DV>;
+  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int lr = lane & 31;
+
+  // blockIdx -> (b, kvh, row group, split); the split varies fastest.
+  int64_t rest = blockIdx.x;
+  const int s = static_cast<int>(rest % a.n_splits); rest /= a.n_splits;
+  const int rg = static_cast<int>(rest % a.n_rg);    rest /= a.n_rg;
+  const int kvh = static_cast<int>(rest % a.heads_kv);
+  const int b = static_cast<int>(rest / a.heads_kv);
+
+  // This lane's row: n = 32 rg + lr -> query head kvh * group + n / T_q, row n % T_q.
+  const int n = rg * kRows + lr;
+  const bool row_ok = n < a.rows;
+  const int gq = row_ok ? n / a.t_q : 0;
+  const int qi = row_ok ? n % a.t_q : 0;
+  const int hq = kvh * a.group + gq;
+  const int64_t pos = a.q_offset + qi;
+
+  u32x4 qreg[C::KS];
+  {
+    const uint16_t* qp = a.q + b * a.qs[0] + hq * a.qs[1] + static_cast<int64_t>(qi) * a.qs[2];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      qreg[ks] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * ks + 8 * h) : u32x4{0, 0, 0, 0};
+  }
+
+  // Key range of the work item, cut at the last position any row can see.
+  int64_t lo = static_cast<int64_t>(s) * a.split_size;
+  int64_t hi = a.split_size < a.t_k - lo ? lo + a.split_size : a.t_k;
+  if (a.causal) {
+    const int64_t last = a.q_offset + a.t_q - 1;   // largest position of any row
+    if (last + 1 < hi) hi = last + 1;
+  }
+  // Four contiguous, tile-aligned parts, one per wave.
+  int64_t len = hi > lo ? hi - lo : 0;
+  const int64_t part = ((len + kWaves - 1) / kWaves + kTile - 1) / kTile * kTile;
+  int64_t wlo = lo + wave * part;
+  int64_t whi = wlo + part < hi ? wlo + part : hi;
+  if (whi < wlo) whi = wlo;
+  const int n_tiles = static_cast<int>((whi - wlo + kTile - 1) / kTile);
+
+  const uint16_t* kbase = a.k + b * a.ks[0] + kvh * a.ks[1];
+  const uint16_t* vbase = a.v + b * a.vs[0] + kvh * a.vs[1];
+  char* vl_w = smem + wave * C::VBUF;
+  const lds_char* vl = (const lds_char*)vl_w;
+
+  bool has = false;
+  float m2 = 0.0f;
+  float l_lane = 0.0f;
+  f32x16 oacc[C::MO];
+#pragma unroll
+  for (int i = 0; i < C::MO; ++i) oacc[i] = f32x16{};
+
+  u32x4 kreg[C::KS], vreg[C::V_PER_LANE];
+  auto load = [&](int t, u32x4* kr, u32x4* vr) {
+    const int64_t kb = wlo + static_cast<int64_t>(t) * kTile;
+    const int64_t key = kb + lr;
+    const bool kok = key < whi;
+    const uint16_t* kp = kbase + key * a.ks[2] + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      kr[ks] = kok ? *reinterpret_cast<const u32x4*>(kp + 16 * ks) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < C::V_PER_LANE; ++i) {
+      const int c = lane + 64 * i;
+      const int r = c / (DV / 8), col = c % (DV / 8);
+      const bool vok = kb + r < whi;
+      vr[i] = vok ? *reinterpret_cast<const u32x4*>(vbase + (kb + r) * a.vs[2] + col * 8)
+                  : u32x4{0, 0, 0, 0};
+    }
+  };
+
+  if (n_tiles > 0) load(0, kreg, vreg);
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int64_t kb = wlo + static_cast<int64_t>(t) * kTile;
+    // V tile -> this wave's LDS buffer (read back transposed below).
+#pragma unroll
+    for (int i = 0; i < C::V_PER_LANE; ++i) {
+      const int c = lane + 64 * i;
+      const int r = c / (DV / 8), col = c % (DV / 8);
+      *reinterpret_cast<u32x4*>(vl_w + r * C::V_STRIDE + col * 16) = vreg[i];
+    }
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[ks]), as_bf16x8(qreg[ks]), sacc, 0, 0, 0);
+    if (t + 1 < n_tiles) load(t + 1, kreg, vreg);
+
+    // Register r holds key kb + 8 (r / 4) + 4 h + (r % 4) of this lane's row.
+    int64_t lim64 = whi - 1 - kb;
+    if (a.causal && pos - kb < lim64) lim64 = pos - kb;
+    int lim = lim64 < -1 ? -1 : (lim64 > kTile ? kTile : static_cast<int>(lim64));
+    if (!row_ok) lim = -1;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = 8 * (r >> 2) + 4 * h + (r & 3);
+      const float z = j <= lim ? sacc[r] * a.scale_log2 : -INFINITY;
+      sacc[r] = z;
+      mx = fmaxf(mx, z);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+
+    bool need = false;
+    if (mx != -INFINITY) {
+      if (!has) {
+        has = true;
+        m2 = mx;
+      } else if (mx > m2 + kRescale) {
+        need = true;
+      }
+    }
+    if (__ballot(need) != 0) {
+      const float alpha = need ? fast_exp2(m2 - mx) : 1.0f;
+      if (need) m2 = mx;
+      l_lane *= alpha;
+#pragma unroll
+      for (int i = 0; i < C::MO; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+    }
+
+    unsigned pk[8];
+    {
+      float p[16];
+      float ls = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = fast_exp2(sacc[r] - m2);
+        ls += p[r];
+      }
+      l_lane += ls;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pk[i] = pack_bf16(p[2 * i], p[2 * i + 1]);
+    }
+
+    asm volatile("" ::: "memory");   // keep the V stores above the transposed reads
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const u32x4 bop = {pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]};
+      const int src_row = 16 * kk + 4 * h + ((lane & 15) >> 2);
+#pragma unroll
+      for (int mo = 0; mo < C::MO; ++mo) {
+        const int col = 32 * mo + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const lds_char* p0 = vl + src_row * C::V_STRIDE + col * 2;
+        const u32x2 x0 = tr_read(p0);
+        const u32x2 x1 = tr_read(p0 + 8 * C::V_STRIDE);
+        const u32x4 aop = {x0[0], x0[1], x1[0], x1[1]};
+        oacc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bop), oacc[mo], 0, 0, 0);
+      }
+    }
+    asm volatile("" ::: "memory");   // the next tile's V stores come after these reads
+  }
+
+  // ---- merge the four wave states (eqs 33.4-33.5) ----
+  const float l_row = l_lane + __shfl_xor(l_lane, 32, 64);
+  __syncthreads();                         // V buffers are free now
+  float* mo_area = reinterpret_cast<float*>(smem);
+  float* m_area = mo_area + kWaves * kRows * DV;
+  float* l_area = m_area + kWaves * kRows;
+  {
+    float* dst = mo_area + (wave * kRows + lr) * DV;
+#pragma unroll
+    for (int mo = 0; mo < C::MO; ++mo)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = {oacc[mo][4 * g], oacc[mo][4 * g + 1], oacc[mo][4 * g + 2], oacc[mo][4 * g + 3]};
+        *reinterpret_cast<f32x4*>(dst + 32 * mo + 8 * g + 4 * h) = x;
+      }
+    if (h == 0) {
+      m_area[wave * kRows + lr] = has ? m2 : -INFINITY;
+      l_area[wave * kRows + lr] = l_row;
+    }
+  }
+  __syncthreads();
+  const int rows_here = a.rows - rg * kRows < kRows ? a.rows - rg * kRows : kRows;
+  for (int e = tid; e < rows_here * DV; e += kThreads) {
+    const int rr = e / DV, d = e % DV;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m_area[w * kRows + rr]);
+    float num = 0.0f, den = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = m_area[w * kRows + rr];
+        if (mw == -INFINITY) continue;       // this wave saw no legal key
+        const float c = fast_exp2(mw - M);
+        num = fmaf(c, mo_area[(w * kRows + rr) * DV + d], num);
+        den = fmaf(c, l_area[w * kRows + rr], den);
+      }
+    }
+    const int nn = rg * kRows + rr;
+    const int ghq = kvh * a.group + nn / a.t_q;
+    const int gi = nn % a.t_q;
+    const int64_t ridx = (static_cast<int64_t>(b) * a.heads_q + ghq) * a.t_q + gi;
+    const bool live = M != -INFINITY;
+    const float val = live ? num / den : 0.0f;
+    if (SPLIT) {
+      a.ws_o[(ridx * a.n_splits + s) * DV + d] = val;
+      if (d == 0) a.ws_lse[ridx * a.n_splits + s] = live ? (M + fast_log2(den)) * kLn2 : -INFINITY;
+    } else {
+      uint16_t* op = a.o + b * a.os[0] + ghq * a.os[1] + static_cast<int64_t>(gi) * a.os[2];
+      op[d] = f32_to_bf16(val);
+      if (d == 0) a.lse[ridx] = live ? (M + fast_log2(den)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <int DH, int DV, bool SPLIT>
+hipError_t launch_f(const FArgs& a, int64_t blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <bool SPLIT>
+hipError_t launch_split(const FArgs& a, int64_t blocks, int d_h, int d_v, hipStream_t s) {
+  if (d_h == 128 && d_v == 128) return launch_f<128, 128, SPLIT>(a, blocks, s);
+  if (d_h == 64 && d_v == 128) return launch_f<64, 128, SPLIT>(a, blocks, s);
+  if (d_h == 128 && d_v == 64) return launch_f<128, 64, SPLIT>(a, blocks, s);
+  return launch_f<64, 64, SPLIT>(a, blocks, s);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+bool eligible(const Problem& pb, int dtype, const void* q, const void* k, const void* v,
+              const void* o) {
+  if (dtype != ATTN_BF16 || pb.bias != nullptr) return false;
+  if (!((pb.d_h == 64 || pb.d_h == 128) && (pb.d_v == 64 || pb.d_v == 128))) return false;
+  if (!(pb.scale_log2 > 0.0f)) return false;
+  if (pb.t_q >= (int64_t(1) << 30) || pb.t_k >= (int64_t(1) << 30)) return false;
+  if (pb.batch * pb.heads_kv >= (int64_t(1) << 30)) return false;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (o && !aligned16(o))) return false;
+  for (int i = 0; i < 3; ++i)
+    if ((pb.qs[i] | pb.ks[i] | pb.vs[i]) & 7) return false;
+  return true;
+}
+
+FArgs make_args(const Problem& pb, const void* q, const void* k, const void* v) {
+  FArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = pb.qs[i]; a.ks[i] = pb.ks[i]; a.vs[i] = pb.vs[i]; a.os[i] = pb.os[i];
+  }
+  a.q_offset = pb.q_offset;
+  a.t_q = static_cast<int32_t>(pb.t_q);
+  a.t_k = static_cast<int32_t>(pb.t_k);
+  a.heads_q = static_cast<int32_t>(pb.heads_q);
+  a.heads_kv = static_cast<int32_t>(pb.heads_kv);
+  a.group = pb.group;
+  a.rows = static_cast<int32_t>(pb.group * pb.t_q);
+  a.n_rg = (a.rows + kRows - 1) / kRows;
+  a.scale_log2 = pb.scale_log2;
+  a.causal = pb.causal;
+  return a;
+}
+
+}  // namespace
+
+bool launch_fewrow_fwd(const Problem& pb, int dtype, const void* q, const void* k,
+                       const void* v, void* o, float* lse, int32_t* n_legal,
+                       hipStream_t stream, int* status) {
+  if (n_legal != nullptr) return false;
+  if (!eligible(pb, dtype, q, k, v, o)) return false;
+  if (pb.group * pb.t_q > kRows) return false;   // many rows: the prefill kernel
+  for (int i = 0; i < 3; ++i)
+    if (pb.os[i] & 7) return false;
+  FArgs a = make_args(pb, q, k, v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.split_size = pb.t_k > 0 ? pb.t_k : 1;
+  a.n_splits = 1;
+  const int64_t blocks = pb.batch * pb.heads_kv * a.n_rg;
+  const hipError_t e = launch_split<false>(a, blocks, static_cast<int>(pb.d_h),
+                                           static_cast<int>(pb.d_v), stream);
+  *status = e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+  return true;
+}
+
+bool launch_fewrow_partials(const Problem& pb, int dtype, const void* q, const void* k,
+                            const void* v, const SplitLayout& L, float* ws_o, float* ws_lse,
+                            hipStream_t stream, hipError_t* err) {
+  if (!eligible(pb, dtype, q, k, v, nullptr)) return false;
+  if (L.n_splits >= (int64_t(1) << 30)) return false;
+  FArgs a = make_args(pb, q, k, v);
+  a.ws_o = ws_o;
+  a.ws_lse = ws_lse;
+  a.split_size = L.split_size;
+  a.n_splits = static_cast<int32_t>(L.n_splits);
+  const int64_t blocks = pb.batch * pb.heads_kv * a.n_rg * L.n_splits;
+  if (blocks >= (int64_t(1) << 31)) return false;
+  *err = launch_split<true>(a, blocks, static_cast<int>(pb.d_h), static_cast<int>(pb.d_v), stream);
+  return true;
+}
+
+}  // namespace attn

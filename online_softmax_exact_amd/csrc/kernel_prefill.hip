@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(Args a) {
 
     // Classify the tile for this wave.
     int kind = kPartial;
-    if (a.causal && kb > pos_w_last) kind = kSkip;
+    if (row0 >= a.t_q || (a.causal && kb > pos_w_last)) kind = kSkip;
     else if (!BIAS && kb + kBc <= a.t_k && (!a.causal || kb + kBc - 1 <= pos_w_first)) kind = kFull;
 
     if (kind != kSkip) {

@@ -105,6 +105,10 @@ def test_config4_verify():
     assert torch.equal(n, want_n)
     rows = [(b, h, i) for b in range(0, 32, 3) for h in range(32) for i in range(5)]
     check_sampled(wl, o, lse, rows, torch.bfloat16)
+    # The benchmarked call (no counts) takes the few-row kernel.
+    o2, lse2 = attn.attn_fwd(q, k, v, scale=wl.scale, causal=True, q_offset=wl.q_offset)
+    torch.cuda.synchronize()
+    check_sampled(wl, o2, lse2, rows, torch.bfloat16)
 
 
 def test_config5_padded_bias():

@@ -39,6 +39,11 @@ FWD_CASES = [
     (torch.bfloat16, 1, 2, 1, 64, 100, 128, 128, True, 10_000, "none", 0.0),
     (torch.bfloat16, 1, 3, 3, 33, 47, 40, 24, True, 14, "dense", 0.5),
     (torch.bfloat16, 3, 16, 2, 17, 1000, 128, 128, True, 983, "none", 0.0),
+    # few query rows per KV head (H_q/H_kv * T_q <= 32)
+    (torch.bfloat16, 2, 8, 2, 4, 300, 128, 128, True, 296, "none", 0.0),
+    (torch.bfloat16, 1, 32, 1, 1, 1000, 64, 64, True, 999, "none", 0.0),
+    (torch.bfloat16, 2, 4, 4, 3, 200, 128, 64, True, -1, "none", 0.0),
+    (torch.bfloat16, 2, 2, 2, 7, 70, 64, 128, False, 0, "none", 0.0),
 ]
 
 
@@ -52,8 +57,12 @@ def test_fwd_parity(case):
     o, lse, n = attn.attn_fwd(q, k, v, scale=wl.scale, causal=causal, q_offset=off, bias=m,
                               return_n_legal=True)
     torch.cuda.synchronize()
+    # Without the legal-key counts the entry point may take another kernel.
+    o2, lse2 = attn.attn_fwd(q, k, v, scale=wl.scale, causal=causal, q_offset=off, bias=m)
+    torch.cuda.synchronize()
     o_ref, l_ref, n_ref = oracle_full(wl)
     assert_close(o, lse, o_ref, l_ref, dt, what=str(case))
+    assert_close(o2, lse2, o_ref, l_ref, dt, what=str(case) + " (no counts)")
     assert np.array_equal(n.cpu().numpy(), n_ref), "n_legal differs"
 
 
@@ -147,6 +156,9 @@ DECODE_CASES = [
     (torch.bfloat16, 2, 4, 2, 4, 640, 128, 128, 64, 100, "none"),   # many splits beyond pos
     (torch.float32, 1, 2, 1, 1, 1000, 64, 64, 96, None, "keys"),
     (torch.bfloat16, 1, 4, 4, 2, 400, 64, 128, 128, None, "dense"),
+    (torch.bfloat16, 1, 8, 1, 5, 700, 128, 128, 128, None, "none"),   # 40 rows: 2 row groups
+    (torch.bfloat16, 2, 16, 2, 1, 3000, 128, 64, 1000, None, "none"),
+    (torch.bfloat16, 1, 2, 1, 2, 5, 64, 64, 3, None, "none"),
 ]
 
 
