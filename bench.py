@@ -42,19 +42,21 @@ def decode_counts(batch, hq, hkv, t_q, t_k, d_h, d_v):
     return kv + qo, 2 * (d_h + d_v) * pairs
 
 
-def timed(fn, steps, warmup, stream):
-    import torch
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for a, b in evs:
-        a.record(stream)
-        fn()
-        b.record(stream)
-    torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in evs]
+def recorded_traffic(key: str):
+    """HBM bytes per launch of kernel `key` from the committed rocprofv3 byte
+    counters (profiles/traffic.json), or None when the kernel's sources have
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))["kernels"][key]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        with open(os.path.join(ROOT, "online_softmax_exact_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return int(rec["traffic_bytes"]) if h.hexdigest() == rec["source_sha256"] else None
 
 
 def cpu_baseline(wl, heads: int):
@@ -87,6 +89,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="heads of the prefill the CPU oracle baseline times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after timing, run two device copies of this many MiB (a kernel of "
+                         "known traffic to scale hardware byte counters against)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -171,15 +176,24 @@ def main():
                    "wall_s": round(wall, 3)},
         "roofline": {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "attn_fwd prefill",
+                     "traffic": recorded_traffic("prefill"), "kernel": "attn_fwd prefill",
                      "per_launch_flops": p_flops, "per_launch_bytes": p_bytes},
         "decode": {"value": round(d_gbs, 1), "unit": "GB/s", "ms": round(d_avg, 4),
                    "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": round(d_gbs / PEAK_HBM_GBS, 4),
-                                "traffic": None, "per_launch_bytes": d_bytes,
+                                "traffic": recorded_traffic("decode_partials"),
+                                "per_launch_bytes": d_bytes,
                                 "per_launch_flops": d_flops}},
         "cpu_baseline": None,
     }
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(pre, args.cpu_heads)
