@@ -70,6 +70,14 @@ __device__ __forceinline__ float fast_log2(float x) {
   return __builtin_amdgcn_logf(x);
 }
 
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
+// return zeros, which the kernels use for key rows past the end of a range.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n,
+                                           0x00020000);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
