@@ -21,9 +21,13 @@
 //   The key order inside a 16-key MFMA step is the order in which the score
 //   registers hold them; any order is valid for a contraction as long as both
 //   operands agree.
-// * K/V tiles are double-buffered in LDS: global loads of tile t + 1 are in
-//   flight while tile t is computed.  Row strides are padded so that the
-//   16-byte K reads and the transposed V reads are free of bank conflicts.
+// * K/V tiles are double-buffered in LDS and filled by buffer_load ... lds
+//   (HBM -> LDS without registers); tile t + 2 is in flight while tile t is
+//   computed.  16-byte chunks are XOR-swizzled per row so that the 16-byte K
+//   reads and the transposed V reads are free of bank conflicts.
+// * Within a tile the two 32-key halves are software-pipelined: half 0's
+//   softmax (VALU) runs while half 1's score MFMAs execute, and half 1's
+//   softmax while half 0's P V MFMAs execute.
 // * Rescaling is lazy: the reference maximum m of a row only moves when a
 //   tile's maximum exceeds it by more than 8 (base-2 units); the merge rule
 //   holds for any reference value, so o = u / l is unchanged, and the weights
@@ -59,16 +63,28 @@ template <int DH, int DV>
 struct Cfg {
   static constexpr int KS = DH / 16;             // k-steps of K Q^T
   static constexpr int MO = DV / 32;             // 32-row slices of O^T
-  static constexpr int K_STRIDE = DH * 2 + 16;   // bytes per K row in LDS
-  static constexpr int V_STRIDE = DV * 2 + 64;   // bytes per V row in LDS
-  static constexpr int K_BYTES = kBc * K_STRIDE;
-  static constexpr int V_BYTES = kBc * V_STRIDE;
-  static constexpr int BUF = K_BYTES + V_BYTES;
-  static constexpr int K_CHUNKS = kBc * DH / 8;  // 16-byte chunks per tile
-  static constexpr int V_CHUNKS = kBc * DV / 8;
-  static constexpr int K_PER_T = K_CHUNKS / kThreads;
-  static constexpr int V_PER_T = V_CHUNKS / kThreads;
+  static constexpr int K_RB = DH * 2;            // bytes per K row (LDS, unpadded)
+  static constexpr int V_RB = DV * 2;            // bytes per V row
+  static constexpr int K_BYTES = kBc * K_RB;
+  static constexpr int V_BYTES = kBc * V_RB;
+  static constexpr int K_DMA = K_BYTES / 1024 / kWaves;   // 1 KB DMA writes per wave per tile
+  static constexpr int V_DMA = V_BYTES / 1024 / kWaves;
 };
+
+// LDS layouts.  Tiles are written by buffer_load ... lds (each wave
+// instruction fills 1 KB in lane order), so rows cannot be padded; instead the
+// 16-byte chunk c of row r is stored at chunk slot c ^ swz(r).  The K swizzle
+// makes the 16-byte MFMA-operand reads (16 lanes = 16 rows, one chunk each)
+// hit distinct banks; the V swizzle does the same for ds_read_b64_tr_b16
+// (32 lanes = 4 rows x 64 bytes).
+template <int RB>
+__device__ __forceinline__ int swz_k(int r) {
+  return (r / (256 / RB)) % (RB / 16);
+}
+template <int RB>
+__device__ __forceinline__ int swz_v(int r) {
+  return RB == 256 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
 
 struct Args {
   const uint16_t* q;
@@ -118,10 +134,12 @@ __device__ __forceinline__ int isum_xor32(int x) {
 
 template <int DH, int DV, bool BIAS, bool COUNT>
 __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kernel(Args a) {
+  // The host pass only needs this kernel's signature (its launch stub); the
+  // body is device code (it otherwise drops the stub of this template).
+#if defined(__HIP_DEVICE_COMPILE__)
   using C = Cfg<DH, DV>;
-  // K ring of two tiles, then V ring of two tiles.  K runs one tile ahead of
-  // V: while tile t's softmax and P V run, tile t + 1's scores are computed.
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::K_BYTES + 2 * C::V_BYTES];
+  // Two K slots then two V slots; tile t lives in slot t & 1.
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::K_BYTES + 2 * C::V_BYTES];
   char* const kring = smem;
   char* const vring = smem + 2 * C::K_BYTES;
 
@@ -180,6 +198,7 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     if (tf < t_full) t_full = tf;
   }
   if (BIAS) t_full = 0;
+  if (t_full > n_w) t_full = n_w;
 
   const uint16_t* kbase = a.k + b * a.ks[0] + kvh * a.ks[1];
   const uint16_t* vbase = a.v + b * a.vs[0] + kvh * a.vs[1];
@@ -206,251 +225,232 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
 #pragma unroll
   for (int i = 0; i < C::MO; ++i) oacc[i] = f32x16{};
 
-  // ---- tile movement: HBM -> registers (buffer loads) -> LDS ----
-  // Thread tid moves 16-byte chunks c = tid + i * kThreads of a tile: row
-  // c / (D / 8), column chunk c % (D / 8).  Rows past T_k read as zeros.
-  u32x4 kpre[C::K_PER_T], vpre[C::V_PER_T];
-  // Chunk i of this thread lies kThreads / (D / 8) rows below chunk i - 1:
-  // one offset register per thread, the row step goes into the descriptor.
-  const int koff = (tid / (DH / 8)) * k_row_bytes + (tid % (DH / 8)) * 16;
-  const int voff = (tid / (DV / 8)) * v_row_bytes + (tid % (DV / 8)) * 16;
-  constexpr int K_ROWS_PER_I = kThreads / (DH / 8);
-  constexpr int V_ROWS_PER_I = kThreads / (DV / 8);
-  auto gload_k = [&](int t) {
+  // ---- tile movement: HBM -> LDS by buffer_load ... lds ----
+  // DMA instruction j of this wave fills LDS bytes [1024 (wave * n + j), +1024)
+  // of the slot; lane l writes the 16 bytes at l * 16 of that block, i.e. one
+  // row and chunk slot of the swizzled layout, so it loads the row's chunk
+  // slot ^ swz(row).  The descriptor starts at the tile's first key and ends
+  // at T_k, so rows past T_k are filled with zeros.
+  int koff[C::K_DMA], voff[C::V_DMA];
 #pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      const int r0i = t * kBc + i * K_ROWS_PER_I;
-      const auto rs = make_rsrc(reinterpret_cast<const char*>(kbase) + static_cast<int64_t>(r0i) * k_row_bytes,
-                                static_cast<int64_t>(a.t_k - r0i) * k_row_bytes);
-      kpre[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, koff, 0, 0);
-    }
+  for (int j = 0; j < C::K_DMA; ++j) {
+    const int byte = (wave * C::K_DMA + j) * 1024 + lane * 16;
+    const int r = byte / C::K_RB, sl = (byte % C::K_RB) / 16;
+    koff[j] = r * k_row_bytes + (sl ^ swz_k<C::K_RB>(r)) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < C::V_DMA; ++j) {
+    const int byte = (wave * C::V_DMA + j) * 1024 + lane * 16;
+    const int r = byte / C::V_RB, sl = (byte % C::V_RB) / 16;
+    voff[j] = r * v_row_bytes + (sl ^ swz_v<C::V_RB>(r)) * 16;
+  }
+  auto gload = [&](int t) {
+    const int kb = t * kBc;
+    const int slot = t & 1;
+    const auto krs = make_rsrc(reinterpret_cast<const char*>(kbase) + static_cast<int64_t>(kb) * k_row_bytes,
+                               static_cast<int64_t>(a.t_k - kb) * k_row_bytes);
+    const auto vrs = make_rsrc(reinterpret_cast<const char*>(vbase) + static_cast<int64_t>(kb) * v_row_bytes,
+                               static_cast<int64_t>(a.t_k - kb) * v_row_bytes);
+#pragma unroll
+    for (int j = 0; j < C::K_DMA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          krs, (__attribute__((address_space(3))) void*)(kring + slot * C::K_BYTES + (wave * C::K_DMA + j) * 1024),
+          16, koff[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < C::V_DMA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vrs, (__attribute__((address_space(3))) void*)(vring + slot * C::V_BYTES + (wave * C::V_DMA + j) * 1024),
+          16, voff[j], 0, 0, 0);
   };
-  auto gload_v = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-      const int r0i = t * kBc + i * V_ROWS_PER_I;
-      const auto rs = make_rsrc(reinterpret_cast<const char*>(vbase) + static_cast<int64_t>(r0i) * v_row_bytes,
-                                static_cast<int64_t>(a.t_k - r0i) * v_row_bytes);
-      vpre[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
-    }
-  };
-  auto sstore_k = [&](int slot) {
-    char* kl = kring + slot * C::K_BYTES;
-#pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c / (DH / 8), col = c % (DH / 8);
-      *reinterpret_cast<u32x4*>(kl + r * C::K_STRIDE + col * 16) = kpre[i];
-    }
-  };
-  auto sstore_v = [&](int slot) {
-    char* vl = vring + slot * C::V_BYTES;
-#pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c / (DV / 8), col = c % (DV / 8);
-      *reinterpret_cast<u32x4*>(vl + r * C::V_STRIDE + col * 16) = vpre[i];
-    }
+  // Wait for this wave's DMA writes, then the workgroup barrier.
+  auto dma_barrier = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   };
 
-  // S^T of the K tile in `slot` for the two 32-key halves.
-  auto scores = [&](int slot, f32x16& s0, f32x16& s1) {
-    const char* kl = kring + slot * C::K_BYTES;
-    s0 = f32x16{};
-    s1 = f32x16{};
+  // S^T of one 32-key half of the K tile in `slot`.  Register r of the result
+  // holds key 32 half + 8 (r / 4) + 4 h + (r % 4) (tile-relative) of this
+  // lane's row.
+  auto scores_half = [&](int slot, int half, f32x16& sacc) {
+    const char* kl = kring + slot * C::K_BYTES + (32 * half + lr) * C::K_RB;
+    const int kx = swz_k<C::K_RB>(lr);          // rows lr and 32 + lr share it
+    sacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
-      const u32x4 k0 = *reinterpret_cast<const u32x4*>(kl + lr * C::K_STRIDE + 32 * s + 16 * h);
-      const u32x4 k1 = *reinterpret_cast<const u32x4*>(kl + (32 + lr) * C::K_STRIDE + 32 * s + 16 * h);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), as_bf16x8(qreg[s]), s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), as_bf16x8(qreg[s]), s1, 0, 0, 0);
+      const u32x4 kop = *reinterpret_cast<const u32x4*>(kl + ((2 * s + h) ^ kx) * 16);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop), as_bf16x8(qreg[s]), sacc, 0, 0, 0);
     }
   };
 
-  // Softmax statistics of tile t and O^T += V^T P^T.
-  auto softmax_pv = [&](int t, f32x16& s0, f32x16& s1) {
-    const int kb = t * kBc;
-    const bool full = t < t_full;
-    // Register r of half mt holds key kb + 32 mt + 8 (r / 4) + 4 h + (r % 4).
-    float tmax;
-    if (full) {
-      float mx = fmaxf(s0[0], s0[1]);
+  // O^T += V^T P^T for one 32-key half (two 16-key MFMA steps).  The B
+  // operand of step kk2 is pk[4 kk2 .. 4 kk2 + 3]: keys base + (0..3) and
+  // base + 8 + (0..3) with base = 32 half + 16 kk2 + 4 h, which is where the
+  // transposed reads fetch V from.
+  auto pv_half = [&](int slot, int half, const unsigned* pk) {
+    const lds_char* vl = (const lds_char*)(vring + slot * C::V_BYTES);
 #pragma unroll
-      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s0[r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
-      tmax = max_xor32(mx) * a.scale_log2;
-      if (COUNT) count += 32;
-    } else {
-      // Legal iff key < T_k, causally visible, and bias != -inf.
-      int lim = a.causal ? pos_row - kb : kBc;
-      if (a.t_k - 1 - kb < lim) lim = a.t_k - 1 - kb;   // keys past T_k do not exist
-      if (lim < -1) lim = -1;
-      if (!row_ok) lim = -1;   // rows past T_q: nothing legal, no bias read
-      // Bias of this lane's row for its 32 keys (contiguous along keys):
-      // 16-byte loads of the 4 consecutive keys each register group holds.
-      float mb0[16], mb1[16];
-      if (BIAS) {
-        const auto rs = make_rsrc(bias_w + kb, bias_w_bytes - static_cast<int64_t>(kb) * 4);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 x0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, bias_off + 32 * g, 0, 0));
-          const f32x4 x1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, bias_off + 128 + 32 * g, 0, 0));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            mb0[4 * g + e] = x0[e];
-            mb1[4 * g + e] = x1[e];
-          }
-        }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j0 = 8 * (r >> 2) + 4 * h + (r & 3);
-        const int j1 = 32 + j0;
-        float z0 = s0[r] * a.scale_log2, z1 = s1[r] * a.scale_log2;
-        bool ok0 = j0 <= lim, ok1 = j1 <= lim;
-        if (BIAS) {
-          ok0 = ok0 && mb0[r] != -INFINITY;
-          ok1 = ok1 && mb1[r] != -INFINITY;
-          z0 = fmaf(mb0[r], kLog2e, z0);
-          z1 = fmaf(mb1[r], kLog2e, z1);
-        }
-        if (COUNT) count += static_cast<int>(ok0) + static_cast<int>(ok1);
-        s0[r] = ok0 ? z0 : -INFINITY;
-        s1[r] = ok1 ? z1 : -INFINITY;
-        mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-      }
-      tmax = max_xor32(mx);
-    }
-
-    // Update the running reference maximum (lazy) and rescale if it moved.
-    bool need = false;
-    if (tmax != -INFINITY) {
-      if (!has) {
-        has = true;
-        m2 = tmax;
-      } else if (tmax > m2 + kRescale) {
-        need = true;
-      }
-    }
-    if (__ballot(need) != 0) {
-      const float alpha = need ? fast_exp2(m2 - tmax) : 1.0f;
-      if (need) m2 = tmax;
-      l_lane *= alpha;
-#pragma unroll
-      for (int i = 0; i < C::MO; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-    }
-
-    // P = exp2(z - m2); illegal entries hold -inf and give 0.  l sums the
-    // fp32 weights (the LSE keeps fp32 accuracy); V is multiplied by their
-    // bf16 roundings.
-    unsigned pk0[8], pk1[8];
-    {
-      if (full) {
-        const float nm = -m2;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s0[r] = fast_exp2(fmaf(s0[r], a.scale_log2, nm));
-          s1[r] = fast_exp2(fmaf(s1[r], a.scale_log2, nm));
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s0[r] = fast_exp2(s0[r] - m2);
-          s1[r] = fast_exp2(s1[r] - m2);
-        }
-      }
-      float ps[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ps[r] = s0[r] + s1[r];
-#pragma unroll
-      for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-        for (int r = 0; r < w; ++r) ps[r] += ps[r + w];
-      l_lane += ps[0];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pk0[i] = pack_bf16(s0[2 * i], s0[2 * i + 1]);
-        pk1[i] = pack_bf16(s1[2 * i], s1[2 * i + 1]);
-      }
-    }
-
-    // O^T += V^T P^T over four 16-key steps.
-    const lds_char* vl = (const lds_char*)(vring + (t & 1) * C::V_BYTES);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const unsigned* pk = (kk < 2) ? pk0 : pk1;
-      const int off = 4 * (kk & 1);
-      const u32x4 bop = {pk[off], pk[off + 1], pk[off + 2], pk[off + 3]};
-      // Keys of this step for this lane: base + (0..3) and base + 8 + (0..3).
-      const int key_base = 32 * (kk >> 1) + 16 * (kk & 1) + 4 * h;
-      const int src_row = key_base + ((lane & 15) >> 2);
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
+      const u32x4 bop = {pk[4 * kk2], pk[4 * kk2 + 1], pk[4 * kk2 + 2], pk[4 * kk2 + 3]};
+      const int src_row = 32 * half + 16 * kk2 + 4 * h + ((lane & 15) >> 2);
 #pragma unroll
       for (int mo = 0; mo < C::MO; ++mo) {
-        const int col = 32 * mo + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        const lds_char* p0 = vl + src_row * C::V_STRIDE + col * 2;
+        const int cb = 64 * mo + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);   // byte column
+        const int c = cb >> 4, hb = cb & 15;
+        const lds_char* p0 = vl + src_row * C::V_RB + ((c ^ swz_v<C::V_RB>(src_row)) << 4) + hb;
+        const lds_char* p1 = vl + (src_row + 8) * C::V_RB + ((c ^ swz_v<C::V_RB>(src_row + 8)) << 4) + hb;
         const u32x2 lo = tr_read(p0);
-        const u32x2 hi = tr_read(p0 + 8 * C::V_STRIDE);
+        const u32x2 hi = tr_read(p1);
         const u32x4 aop = {lo[0], lo[1], hi[0], hi[1]};
         oacc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bop), oacc[mo], 0, 0, 0);
       }
     }
   };
 
-  // One pipeline step: scores of tile t + 1 (into sn) are issued before the
-  // softmax and P V of tile t (in sc), so the MFMAs run while the VALU works;
-  // then the tiles for the next step are stored to LDS and the global loads
-  // two tiles ahead are issued.
-  // With a bias the extra score registers do not fit: tile t's scores are
-  // then computed right before its softmax, and K runs one tile ahead (like
-  // V) instead of two.  Ring slots: K(t) and V(t) live in slot t & 1; a slot
-  // is only rewritten after the barrier that follows its last reader.
-  constexpr bool kPipe = !BIAS;
-  constexpr int kAhead = kPipe ? 2 : 1;     // K tiles held in LDS beyond the current one
-  auto step = [&](int t, f32x16& sc0, f32x16& sc1, f32x16& sn0, f32x16& sn1) {
-    if (kPipe) {
-      if (t + 1 < n_w) scores((t + 1) & 1, sn0, sn1);
-    } else {
-      if (t < n_w) scores(t & 1, sc0, sc1);
+  // Rescale O and l when a row's reference maximum moved (wave-uniform test).
+  auto rescale = [&](float m_new, float alpha) {
+    if (__ballot(m_new != m2) != 0) {
+#pragma unroll
+      for (int i = 0; i < C::MO; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
     }
-    if (t < n_w) softmax_pv(t, sc0, sc1);
-    // kPipe: K(t + 2) replaces K(t), read in the previous step.
-    // otherwise: K(t + 1) replaces K(t - 1).  V(t + 1) replaces V(t - 1).
-    if (t + kAhead < n_tiles) sstore_k((t + kAhead) & 1);
-    if (t + 1 < n_tiles) sstore_v((t + 1) & 1);
-    __syncthreads();
-    if (t + kAhead + 1 < n_tiles) gload_k(t + kAhead + 1);
-    if (t + 2 < n_tiles) gload_v(t + 2);
+    m2 = m_new;
   };
 
-  // Prologue: K(0 .. kAhead - 1) and V(0) in LDS; K(kAhead), V(1) in flight;
-  // with the prefetch, the scores of tile 0.
-  if (n_tiles > 0) {
-    gload_k(0);
-    sstore_k(0);
-    gload_v(0);
-    sstore_v(0);
-  }
-  if (kPipe && n_tiles > 1) {
-    gload_k(1);
-    sstore_k(1);
-  }
-  __syncthreads();
-  if (n_tiles > kAhead) gload_k(kAhead);
-  if (n_tiles > 1) gload_v(1);
-  f32x16 sa0 = f32x16{}, sa1 = f32x16{}, sb0 = f32x16{}, sb1 = f32x16{};
-  if (kPipe && n_w > 0) scores(0, sa0, sa1);
-  __syncthreads();   // with the prefetch, K slot 0 is rewritten in step 0
+  // Softmax of a half with every key legal for every row and every row
+  // already holding statistics: branch-free (tile max, new reference, weights,
+  // sums, bf16 packing), so it can run under independent MFMAs.
+  auto fast_half = [&](const f32x16& sv, unsigned* pk, float& m_new, float& alpha) {
+    float mx = fmaxf(sv[0], sv[1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sv[r]);
+    const float tmax = max_xor32(mx) * a.scale_log2;
+    m_new = tmax > m2 + kRescale ? tmax : m2;
+    alpha = fast_exp2(m2 - m_new);
+    const float nm = -m_new;
+    float ps0 = 0.0f, ps1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p0 = fast_exp2(fmaf(sv[2 * i], a.scale_log2, nm));
+      const float p1 = fast_exp2(fmaf(sv[2 * i + 1], a.scale_log2, nm));
+      pk[i] = pack_bf16(p0, p1);
+      ps0 += p0;
+      ps1 += p1;
+    }
+    l_lane = fmaf(l_lane, alpha, ps0 + ps1);
+    if (COUNT) count += 16;
+  };
 
+  // General softmax of a half (masks, bias, first statistics of a row).
+  // Legal iff key < T_k, causally visible, and bias != -inf; illegal scores
+  // become -inf and give weight 0; a half with no legal key changes nothing.
+  auto general_half = [&](int t, int half, f32x16& sv, unsigned* pk) {
+    const int kb = t * kBc + 32 * half;
+    int lim = a.causal ? pos_row - kb : 32;
+    if (a.t_k - 1 - kb < lim) lim = a.t_k - 1 - kb;   // keys past T_k do not exist
+    if (lim < -1) lim = -1;
+    if (!row_ok) lim = -1;   // rows past T_q: nothing legal, no bias read
+    float mb[16];
+    if (BIAS) {
+      // 16-byte loads of the 4 consecutive keys each register group holds.
+      const auto rs = make_rsrc(bias_w + t * kBc, bias_w_bytes - static_cast<int64_t>(t) * kBc * 4);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, bias_off + 128 * half + 32 * g, 0, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mb[4 * g + e] = x[e];
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = 8 * (r >> 2) + 4 * h + (r & 3);
+      float z = sv[r] * a.scale_log2;
+      bool ok = j <= lim;
+      if (BIAS) {
+        ok = ok && mb[r] != -INFINITY;
+        z = fmaf(mb[r], kLog2e, z);
+      }
+      if (COUNT) count += static_cast<int>(ok);
+      sv[r] = ok ? z : -INFINITY;
+      mx = fmaxf(mx, sv[r]);
+    }
+    const float tmax = max_xor32(mx);
+    // First legal key of a row: store; later: lazy reference update.
+    float m_new = m2;
+    if (tmax != -INFINITY) {
+      if (!has) {
+        has = true;
+        m2 = tmax;
+        m_new = tmax;
+      } else if (tmax > m2 + kRescale) {
+        m_new = tmax;
+      }
+    }
+    const float alpha = fast_exp2(m2 - m_new);
+    rescale(m_new, alpha);
+    l_lane *= alpha;
+    float ps0 = 0.0f, ps1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p0 = fast_exp2(sv[2 * i] - m2);
+      const float p1 = fast_exp2(sv[2 * i + 1] - m2);
+      pk[i] = pack_bf16(p0, p1);
+      ps0 += p0;
+      ps1 += p1;
+    }
+    l_lane += ps0 + ps1;
+  };
+
+  // End of step t: wait for the DMA of tile t + 1 (issued one step ago),
+  // barrier (every wave is done with slot t & 1), then DMA tile t + 2 into it.
+  auto advance = [&](int t) {
+    dma_barrier();
+    if (t + 2 < n_tiles) gload(t + 2);
+  };
+
+  // Prologue: tiles 0 and 1 in flight.
+  if (n_tiles > 0) gload(0);
+  if (n_tiles > 1) gload(1);
+  dma_barrier();
+
+  // Tile 0 (first statistics), then the run of full tiles on the fast path,
+  // then the rest (diagonal / masked / skipped tiles).
+  auto general_step = [&](int t) {
+    if (t < n_w) {
+      f32x16 s0, s1;
+      unsigned pk[8];
+      scores_half(t & 1, 0, s0);
+      scores_half(t & 1, 1, s1);
+      general_half(t, 0, s0, pk);
+      pv_half(t & 1, 0, pk);
+      general_half(t, 1, s1, pk);
+      pv_half(t & 1, 1, pk);
+    }
+    advance(t);
+  };
   int t = 0;
-  for (; t + 1 < n_tiles; t += 2) {
-    step(t, sa0, sa1, sb0, sb1);
-    step(t + 1, sb0, sb1, sa0, sa1);
+  if (n_tiles > 0) general_step(t++);
+  if (t < t_full && __ballot(!has) == 0) {
+    for (; t < t_full; ++t) {
+      f32x16 s0, s1;
+      unsigned pk0[8], pk1[8];
+      float mn, al;
+      // Block 1: the 16 score MFMAs; half 0's softmax runs under half 1's.
+      scores_half(t & 1, 0, s0);
+      scores_half(t & 1, 1, s1);
+      fast_half(s0, pk0, mn, al);
+      rescale(mn, al);
+      // Block 2: half 0's P V MFMAs with half 1's softmax under them.
+      pv_half(t & 1, 0, pk0);
+      fast_half(s1, pk1, mn, al);
+      rescale(mn, al);
+      pv_half(t & 1, 1, pk1);
+      advance(t);
+    }
   }
-  if (t < n_tiles) step(t, sa0, sa1, sb0, sb1);
+  for (; t < n_tiles; ++t) general_step(t);
 
   // ---- finalise: o = u / l, LSE = m + ln l; rows with no legal key -> (+0, -inf) ----
   const float l_row = sum_xor32(l_lane);
@@ -474,6 +474,7 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     a.lse[ridx] = has ? (m2 + fast_log2(l_row)) * kLn2 : -INFINITY;
     if (COUNT) a.n_legal[ridx] = count;
   }
+#endif
 }
 
 template <int DH, int DV, bool BIAS, bool COUNT>
