@@ -84,8 +84,9 @@ def cpu_baseline(wl, heads: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=60,
+                    help="untimed steps; ~60 brings the GPU clock to its steady state")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="heads of the prefill the CPU oracle baseline times")
     ap.add_argument("--no-cpu-baseline", action="store_true")

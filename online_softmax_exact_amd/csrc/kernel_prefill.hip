@@ -25,9 +25,9 @@
 //   (HBM -> LDS without registers); tile t + 2 is in flight while tile t is
 //   computed.  16-byte chunks are XOR-swizzled per row so that the 16-byte K
 //   reads and the transposed V reads are free of bank conflicts.
-// * Within a tile the two 32-key halves are software-pipelined: half 0's
-//   softmax (VALU) runs while half 1's score MFMAs execute, and half 1's
-//   softmax while half 0's P V MFMAs execute.
+// * Within a tile the 32-key blocks are software-pipelined: block q's
+//   softmax (VALU) runs while the score MFMAs of block q + 1 and the P V
+//   MFMAs of block q - 1 execute.
 // * Rescaling is lazy: the reference maximum m of a row only moves when a
 //   tile's maximum exceeds it by more than 8 (base-2 units); the merge rule
 //   holds for any reference value, so o = u / l is unchanged, and the weights
@@ -50,11 +50,24 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kBc = 64;            // keys per tile
-constexpr int kWaves = 4;
+#ifndef PREFILL_BLOCKS
+#define PREFILL_BLOCKS 2               // 32-key blocks per key tile (one barrier per tile)
+#endif
+constexpr int kNQ = PREFILL_BLOCKS;
+constexpr int kBc = 32 * kNQ;      // keys per tile
+#ifndef PREFILL_XCD_MAP
+#define PREFILL_XCD_MAP 0              // 1: keep one head per XCD at a time (see the work order)
+#endif
+#ifndef PREFILL_WAVES
+#define PREFILL_WAVES 4                // wavefronts (32 query rows each) per workgroup
+#endif
+constexpr int kWaves = PREFILL_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;   // query rows per workgroup
 constexpr float kRescale = 8.0f;   // lazy-rescale threshold, base-2 units
+#ifndef PREFILL_SCHED
+#define PREFILL_SCHED 0                // VALU ops placed after each MFMA in the full-tile loop (0: compiler's order)
+#endif
 #ifndef PREFILL_WAVES_PER_SIMD
 #define PREFILL_WAVES_PER_SIMD 2       // resident waves per SIMD the kernel is built for
 #endif
@@ -149,10 +162,21 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
   const int h = lane >> 5;        // which half of the wave
   const int lr = lane & 31;       // this lane's query row within the wave
 
-  // Heaviest query tiles first (with causal masking, later tiles see more keys).
+  // Work order.  Heaviest query tiles first (with causal masking, later
+  // tiles see more keys).  Consecutive workgroup ids go round-robin to the 8
+  // XCDs (each with its own L2); when the (batch, head) count is a multiple of
+  // 8, XCD x works through heads x, x + 8, ... one at a time, so the K/V of
+  // the head it is on stays in its L2.
   const int bid = blockIdx.x;
-  const int qt = a.n_qtiles - 1 - bid / a.batch_heads;
-  const int bh = bid % a.batch_heads;
+  int qt, bh;
+  if (PREFILL_XCD_MAP && a.batch_heads % 8 == 0) {
+    const int xcd = bid & 7, local = bid >> 3;
+    qt = a.n_qtiles - 1 - local % a.n_qtiles;
+    bh = xcd + 8 * (local / a.n_qtiles);
+  } else {
+    qt = a.n_qtiles - 1 - bid / a.batch_heads;
+    bh = bid % a.batch_heads;
+  }
   const int b = bh / a.heads_q;
   const int hq = bh % a.heads_q;
   const int kvh = hq / a.group;
@@ -268,11 +292,11 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     __syncthreads();
   };
 
-  // S^T of one 32-key half of the K tile in `slot`.  Register r of the result
-  // holds key 32 half + 8 (r / 4) + 4 h + (r % 4) (tile-relative) of this
+  // S^T of 32-key block q of the K tile in `slot`.  Register r of the result
+  // holds key 32 q + 8 (r / 4) + 4 h + (r % 4) (tile-relative) of this
   // lane's row.
-  auto scores_half = [&](int slot, int half, f32x16& sacc) {
-    const char* kl = kring + slot * C::K_BYTES + (32 * half + lr) * C::K_RB;
+  auto scores_q = [&](int slot, int q, f32x16& sacc) {
+    const char* kl = kring + slot * C::K_BYTES + (32 * q + lr) * C::K_RB;
     const int kx = swz_k<C::K_RB>(lr);          // rows lr and 32 + lr share it
     sacc = f32x16{};
 #pragma unroll
@@ -282,16 +306,16 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     }
   };
 
-  // O^T += V^T P^T for one 32-key half (two 16-key MFMA steps).  The B
+  // O^T += V^T P^T for 32-key block q (two 16-key MFMA steps).  The B
   // operand of step kk2 is pk[4 kk2 .. 4 kk2 + 3]: keys base + (0..3) and
-  // base + 8 + (0..3) with base = 32 half + 16 kk2 + 4 h, which is where the
+  // base + 8 + (0..3) with base = 32 q + 16 kk2 + 4 h, which is where the
   // transposed reads fetch V from.
-  auto pv_half = [&](int slot, int half, const unsigned* pk) {
+  auto pv_q = [&](int slot, int q, const unsigned* pk) {
     const lds_char* vl = (const lds_char*)(vring + slot * C::V_BYTES);
 #pragma unroll
     for (int kk2 = 0; kk2 < 2; ++kk2) {
       const u32x4 bop = {pk[4 * kk2], pk[4 * kk2 + 1], pk[4 * kk2 + 2], pk[4 * kk2 + 3]};
-      const int src_row = 32 * half + 16 * kk2 + 4 * h + ((lane & 15) >> 2);
+      const int src_row = 32 * q + 16 * kk2 + 4 * h + ((lane & 15) >> 2);
 #pragma unroll
       for (int mo = 0; mo < C::MO; ++mo) {
         const int cb = 64 * mo + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);   // byte column
@@ -317,10 +341,10 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     m2 = m_new;
   };
 
-  // Softmax of a half with every key legal for every row and every row
+  // Softmax of a block with every key legal for every row and every row
   // already holding statistics: branch-free (tile max, new reference, weights,
   // sums, bf16 packing), so it can run under independent MFMAs.
-  auto fast_half = [&](const f32x16& sv, unsigned* pk, float& m_new, float& alpha) {
+  auto fast_q = [&](const f32x16& sv, unsigned* pk, float& m_new, float& alpha) {
     float mx = fmaxf(sv[0], sv[1]);
 #pragma unroll
     for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sv[r]);
@@ -341,11 +365,11 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     if (COUNT) count += 16;
   };
 
-  // General softmax of a half (masks, bias, first statistics of a row).
+  // General softmax of a block (masks, bias, first statistics of a row).
   // Legal iff key < T_k, causally visible, and bias != -inf; illegal scores
-  // become -inf and give weight 0; a half with no legal key changes nothing.
-  auto general_half = [&](int t, int half, f32x16& sv, unsigned* pk) {
-    const int kb = t * kBc + 32 * half;
+  // become -inf and give weight 0; a block with no legal key changes nothing.
+  auto general_q = [&](int t, int q, f32x16& sv, unsigned* pk) {
+    const int kb = t * kBc + 32 * q;
     int lim = a.causal ? pos_row - kb : 32;
     if (a.t_k - 1 - kb < lim) lim = a.t_k - 1 - kb;   // keys past T_k do not exist
     if (lim < -1) lim = -1;
@@ -357,7 +381,7 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 x = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, bias_off + 128 * half + 32 * g, 0, 0));
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, bias_off + 128 * q + 32 * g, 0, 0));
 #pragma unroll
         for (int e = 0; e < 4; ++e) mb[4 * g + e] = x[e];
       }
@@ -416,17 +440,19 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
   dma_barrier();
 
   // Tile 0 (first statistics), then the run of full tiles on the fast path,
-  // then the rest (diagonal / masked / skipped tiles).
+  // then the rest (diagonal / masked / skipped tiles).  On a general tile the
+  // blocks past the wave's last visible key are skipped.
   auto general_step = [&](int t) {
     if (t < n_w) {
-      f32x16 s0, s1;
-      unsigned pk[8];
-      scores_half(t & 1, 0, s0);
-      scores_half(t & 1, 1, s1);
-      general_half(t, 0, s0, pk);
-      pv_half(t & 1, 0, pk);
-      general_half(t, 1, s1, pk);
-      pv_half(t & 1, 1, pk);
+#pragma unroll
+      for (int q = 0; q < kNQ; ++q) {
+        if (a.causal && t * kBc + 32 * q > pos_w_last) break;
+        f32x16 sv;
+        unsigned pk[8];
+        scores_q(t & 1, q, sv);
+        general_q(t, q, sv, pk);
+        pv_q(t & 1, q, pk);
+      }
     }
     advance(t);
   };
@@ -434,19 +460,21 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
   if (n_tiles > 0) general_step(t++);
   if (t < t_full && __ballot(!has) == 0) {
     for (; t < t_full; ++t) {
-      f32x16 s0, s1;
-      unsigned pk0[8], pk1[8];
+      // Software pipeline over the 32-key blocks of the tile: block q's
+      // softmax (VALU) runs under the score MFMAs of block q + 1 and the P V
+      // MFMAs of block q - 1, which are independent of it.
+      f32x16 sv[2];
+      unsigned pk[2][8];
       float mn, al;
-      // Block 1: the 16 score MFMAs; half 0's softmax runs under half 1's.
-      scores_half(t & 1, 0, s0);
-      scores_half(t & 1, 1, s1);
-      fast_half(s0, pk0, mn, al);
-      rescale(mn, al);
-      // Block 2: half 0's P V MFMAs with half 1's softmax under them.
-      pv_half(t & 1, 0, pk0);
-      fast_half(s1, pk1, mn, al);
-      rescale(mn, al);
-      pv_half(t & 1, 1, pk1);
+      scores_q(t & 1, 0, sv[0]);
+#pragma unroll
+      for (int q = 0; q < kNQ; ++q) {
+        if (q + 1 < kNQ) scores_q(t & 1, q + 1, sv[(q + 1) & 1]);
+        if (q > 0) pv_q(t & 1, q - 1, pk[(q - 1) & 1]);
+        fast_q(sv[q & 1], pk[q & 1], mn, al);
+        rescale(mn, al);
+      }
+      pv_q(t & 1, kNQ - 1, pk[(kNQ - 1) & 1]);
       advance(t);
     }
   }
