@@ -87,7 +87,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=60,
                     help="untimed steps; ~60 brings the GPU clock to its steady state")
-    ap.add_argument("--cpu-heads", type=int, default=8,
+    ap.add_argument("--cpu-heads", type=int, default=32,
                     help="heads of the prefill the CPU oracle baseline times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
