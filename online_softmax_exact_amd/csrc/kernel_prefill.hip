@@ -66,7 +66,10 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;   // query rows per workgroup
 constexpr float kRescale = 8.0f;   // lazy-rescale threshold, base-2 units
 #ifndef PREFILL_SCHED
-#define PREFILL_SCHED 0                // VALU ops placed after each MFMA in the full-tile loop (0: compiler's order)
+#define PREFILL_SCHED 8                // VALU instructions placed after each MFMA of a full tile (0: compiler's order)
+#endif
+#ifndef PREFILL_PIN
+#define PREFILL_PIN 1                  // 1: full-tile weights computed before the rescale branch
 #endif
 #ifndef PREFILL_WAVES_PER_SIMD
 #define PREFILL_WAVES_PER_SIMD 2       // resident waves per SIMD the kernel is built for
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
   const int h = lane >> 5;        // which half of the wave
   const int lr = lane & 31;       // this lane's query row within the wave
 
@@ -292,17 +295,44 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     __syncthreads();
   };
 
+  // LDS read addresses, fixed per lane; the slot and block enter as
+  // immediate offsets where they are compile-time constants.
+  // K operand of k-step s: row lr (+ 32 q) of the tile, chunk (2 s + h) ^ swz,
+  // where the swizzle of rows lr and 32 q + lr is the same.
+  const lds_char* kp[C::KS];
+  {
+    const int kx = swz_k<C::K_RB>(lr);
+#pragma unroll
+    for (int s2 = 0; s2 < C::KS; ++s2)
+      kp[s2] = (const lds_char*)kring + lr * C::K_RB + (((2 * s2 + h) ^ kx) << 4);
+  }
+  // V^T operand of output slice mo: the transposed read of rows src + 8 e
+  // (e = 0, 1) with src = 32 q + 16 kk2 + 4 h + (lane % 16) / 4; the swizzle
+  // depends only on src % 16, so q and kk2 are immediate offsets.
+  const lds_char* vp[2][C::MO];
+  {
+    const int src = 4 * h + ((lane & 15) >> 2);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int mo = 0; mo < C::MO; ++mo) {
+        const int cb = 64 * mo + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);   // byte column
+        const int c = cb >> 4, hb = cb & 15;
+        vp[e][mo] = (const lds_char*)vring + (src + 8 * e) * C::V_RB +
+                    ((c ^ swz_v<C::V_RB>(src + 8 * e)) << 4) + hb;
+      }
+  }
+
   // S^T of 32-key block q of the K tile in `slot`.  Register r of the result
   // holds key 32 q + 8 (r / 4) + 4 h + (r % 4) (tile-relative) of this
   // lane's row.
   auto scores_q = [&](int slot, int q, f32x16& sacc) {
-    const char* kl = kring + slot * C::K_BYTES + (32 * q + lr) * C::K_RB;
-    const int kx = swz_k<C::K_RB>(lr);          // rows lr and 32 + lr share it
+    const int off = slot * C::K_BYTES + 32 * q * C::K_RB;
     sacc = f32x16{};
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      const u32x4 kop = *reinterpret_cast<const u32x4*>(kl + ((2 * s + h) ^ kx) * 16);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop), as_bf16x8(qreg[s]), sacc, 0, 0, 0);
+    for (int s2 = 0; s2 < C::KS; ++s2) {
+      const u32x4 kop = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(kp[s2] + off);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop), as_bf16x8(qreg[s2]), sacc, 0, 0, 0);
     }
   };
 
@@ -311,19 +341,14 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
   // base + 8 + (0..3) with base = 32 q + 16 kk2 + 4 h, which is where the
   // transposed reads fetch V from.
   auto pv_q = [&](int slot, int q, const unsigned* pk) {
-    const lds_char* vl = (const lds_char*)(vring + slot * C::V_BYTES);
 #pragma unroll
     for (int kk2 = 0; kk2 < 2; ++kk2) {
       const u32x4 bop = {pk[4 * kk2], pk[4 * kk2 + 1], pk[4 * kk2 + 2], pk[4 * kk2 + 3]};
-      const int src_row = 32 * q + 16 * kk2 + 4 * h + ((lane & 15) >> 2);
+      const int off = slot * C::V_BYTES + (32 * q + 16 * kk2) * C::V_RB;
 #pragma unroll
       for (int mo = 0; mo < C::MO; ++mo) {
-        const int cb = 64 * mo + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);   // byte column
-        const int c = cb >> 4, hb = cb & 15;
-        const lds_char* p0 = vl + src_row * C::V_RB + ((c ^ swz_v<C::V_RB>(src_row)) << 4) + hb;
-        const lds_char* p1 = vl + (src_row + 8) * C::V_RB + ((c ^ swz_v<C::V_RB>(src_row + 8)) << 4) + hb;
-        const u32x2 lo = tr_read(p0);
-        const u32x2 hi = tr_read(p1);
+        const u32x2 lo = tr_read(vp[0][mo] + off);
+        const u32x2 hi = tr_read(vp[1][mo] + off);
         const u32x4 aop = {lo[0], lo[1], hi[0], hi[1]};
         oacc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bop), oacc[mo], 0, 0, 0);
       }
@@ -458,25 +483,51 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
   };
   int t = 0;
   if (n_tiles > 0) general_step(t++);
-  if (t < t_full && __ballot(!has) == 0) {
-    for (; t < t_full; ++t) {
-      // Software pipeline over the 32-key blocks of the tile: block q's
-      // softmax (VALU) runs under the score MFMAs of block q + 1 and the P V
-      // MFMAs of block q - 1, which are independent of it.
-      f32x16 sv[2];
-      unsigned pk[2][8];
-      float mn, al;
-      scores_q(t & 1, 0, sv[0]);
+  // Software pipeline over the 32-key blocks of a full tile: block q's
+  // softmax (VALU) runs under the score MFMAs of block q + 1 and the P V
+  // MFMAs of block q - 1, which are independent of it.
+  auto fast_step = [&](int t, int slot) {
+    f32x16 sv[2];
+    unsigned pk[2][8];
+    float mn, al;
+    scores_q(slot, 0, sv[0]);
+    // Nothing of this tile can overlap block 0's score MFMAs.
+    if (PREFILL_SCHED > 0) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 0; q < kNQ; ++q) {
-        if (q + 1 < kNQ) scores_q(t & 1, q + 1, sv[(q + 1) & 1]);
-        if (q > 0) pv_q(t & 1, q - 1, pk[(q - 1) & 1]);
-        fast_q(sv[q & 1], pk[q & 1], mn, al);
-        rescale(mn, al);
+    for (int q = 0; q < kNQ; ++q) {
+      if (q + 1 < kNQ) scores_q(slot, q + 1, sv[(q + 1) & 1]);
+      if (q > 0) pv_q(slot, q - 1, pk[(q - 1) & 1]);
+      fast_q(sv[q & 1], pk[q & 1], mn, al);
+      if (PREFILL_PIN) {
+        // Keep the block's weights ahead of the rescale branch, so they are
+        // scheduled under the MFMAs issued before it rather than sunk past it.
+        const unsigned* w = pk[q & 1];
+        asm volatile("" ::"v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]),
+                     "v"(w[7]), "v"(l_lane));
       }
-      pv_q(t & 1, kNQ - 1, pk[(kNQ - 1) & 1]);
-      advance(t);
+      if (PREFILL_SCHED > 0) {
+        // One MFMA, then PREFILL_SCHED VALU instructions of the softmax, so
+        // the in-order issue never waits on the matrix pipe with VALU work
+        // behind it.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, PREFILL_SCHED, 0);
+        }
+      }
+      rescale(mn, al);
     }
+    pv_q(slot, kNQ - 1, pk[(kNQ - 1) & 1]);
+    advance(t);
+  };
+  // The run of full tiles starts at t = 1 (tile 0 is always general), so its
+  // tiles alternate between slots 1 and 0.
+  if (t < t_full && __ballot(!has) == 0) {
+    for (; t + 1 < t_full; t += 2) {
+      fast_step(t, 1);
+      fast_step(t + 1, 0);
+    }
+    if (t < t_full) fast_step(t++, 1);
   }
   for (; t < n_tiles; ++t) general_step(t);
 
