@@ -36,19 +36,12 @@
 //   v_exp_f32; LSE is converted back to natural-log units at the end.
 #include "attn_internal.h"
 #include "kernels.h"
+#include "prefill_common.h"
 
 namespace attn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) char lds_char;
+using namespace pf;
 
 #ifndef PREFILL_BLOCKS
 #define PREFILL_BLOCKS 2               // 32-key blocks per key tile (one barrier per tile)
@@ -64,7 +57,6 @@ constexpr int kBc = 32 * kNQ;      // keys per tile
 constexpr int kWaves = PREFILL_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;   // query rows per workgroup
-constexpr float kRescale = 8.0f;   // lazy-rescale threshold, base-2 units
 #ifndef PREFILL_SCHED
 #define PREFILL_SCHED 8                // VALU instructions placed after each MFMA of a full tile (0: compiler's order)
 #endif
@@ -86,67 +78,6 @@ struct Cfg {
   static constexpr int K_DMA = K_BYTES / 1024 / kWaves;   // 1 KB DMA writes per wave per tile
   static constexpr int V_DMA = V_BYTES / 1024 / kWaves;
 };
-
-// LDS layouts.  Tiles are written by buffer_load ... lds (each wave
-// instruction fills 1 KB in lane order), so rows cannot be padded; instead the
-// 16-byte chunk c of row r is stored at chunk slot c ^ swz(r).  The K swizzle
-// makes the 16-byte MFMA-operand reads (16 lanes = 16 rows, one chunk each)
-// hit distinct banks; the V swizzle does the same for ds_read_b64_tr_b16
-// (32 lanes = 4 rows x 64 bytes).
-template <int RB>
-__device__ __forceinline__ int swz_k(int r) {
-  return (r / (256 / RB)) % (RB / 16);
-}
-template <int RB>
-__device__ __forceinline__ int swz_v(int r) {
-  return RB == 256 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-}
-
-struct Args {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  uint16_t* o;
-  float* lse;
-  int32_t* n_legal;
-  const float* bias;
-  int64_t qs[3], ks[3], vs[3], os[3], bs[4];
-  int64_t q_offset;
-  int32_t t_q, t_k, heads_q, group, n_qtiles, batch_heads;
-  float scale_log2;
-  int32_t causal;
-};
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
-
-__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
-  f32x2 v = {a, b};
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
-}
-
-__device__ __forceinline__ u32x2 tr_read(const lds_char* p) {
-  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(p));
-  return __builtin_bit_cast(u32x2, v);
-}
-
-// Tile classification for one wavefront.
-enum : int { kSkip = 0, kFull = 1, kPartial = 2 };
-
-// max / sum of a value and the same value in lane ^ 32 (v_permlane32_swap
-// exchanges the two 32-lane halves, so each lane sees both values).
-__device__ __forceinline__ float max_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ int isum_xor32(int x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(x), static_cast<unsigned>(x), false, false);
-  return static_cast<int>(r[0]) + static_cast<int>(r[1]);
-}
 
 template <int DH, int DV, bool BIAS, bool COUNT>
 __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kernel(Args a) {
