@@ -13,7 +13,9 @@ Sources (the pages this follows; cited by page title and section / equation):
   (the merge of two disjoint sets), the valid-flag rule for empty blocks and
   fully masked rows, Algorithm 33.1 (single-query blocked exact attention) and
   Example 25.1; §33.3 (the explicit T_q x T_k implementation, causal block
-  skipping, non-square causal alignment by logical position).
+  skipping, non-square causal alignment by logical position); §33.7, the
+  sliding-window paragraph (only keys in a prescribed range stay visible) and
+  eq 33.16 (the error bound against full attention).
 * "Generation and Caching with the Same Model" (aihero.club), the KV-cache
   section and its `causal_attention` listing: the [B, H, T, D] layout and the
   rule that query row i sits at logical position q_offset + i and sees the
@@ -38,7 +40,10 @@ notes of the repository):
 * LSE of a row is ln sum_{legal j} e^{z_j} = m + ln ℓ (natural log, scale and
   bias included).
 * A key is legal for row i iff it is causally visible (j <= q_offset + i, or
-  always when not causal) and its bias is not -inf.
+  always when not causal), inside the sliding window when there is one
+  (j >= q_offset + i - W + 1: the W positions ending at the row's own; the
+  window is a lower bound only, also without causal masking) and its bias is
+  not -inf.
 * A row with no legal key returns O = +0.0 and LSE = -inf (and a legal-key
   count of 0); it is not an error.
 * Grouped heads: query head hq reads KV head hq // (H_q / H_kv).
@@ -67,14 +72,19 @@ NEG_INF = float("-inf")
 # ---------------------------------------------------------------------------
 
 def legal_keys(t_q: int, t_k: int, causal: bool, q_offset: int,
-               bias_rows: Optional[np.ndarray] = None) -> np.ndarray:
+               bias_rows: Optional[np.ndarray] = None,
+               window: int = 0) -> np.ndarray:
     """Boolean [t_q, t_k]: key j is legal for query row i.
 
     Row i sits at logical position q_offset + i (KV-cache section of
     "Generation and Caching with the Same Model"); with causal masking it sees
     key j iff j <= q_offset + i (§33.3, interface and correctness conditions:
     alignment is by logical position, not by the top-left corner).  A bias of
-    -inf masks a key (eq 33.2: M_j is an additive bias or mask).
+    -inf masks a key (eq 33.2: M_j is an additive bias or mask).  A sliding
+    window of W >= 1 keys (§33.7, the sliding-window paragraph with eq 33.16:
+    only keys inside the prescribed range stay visible) keeps the W positions
+    ending at the row's own, j >= q_offset + i - W + 1; window 0 means no
+    window.
     """
     i = np.arange(t_q, dtype=np.int64)[:, None]
     j = np.arange(t_k, dtype=np.int64)[None, :]
@@ -82,6 +92,8 @@ def legal_keys(t_q: int, t_k: int, causal: bool, q_offset: int,
         legal = j <= (q_offset + i)
     else:
         legal = np.ones((t_q, t_k), dtype=bool)
+    if window > 0:
+        legal = legal & (j >= q_offset + i - window + 1)
     if bias_rows is not None:
         legal = legal & (bias_rows != NEG_INF)
     return legal
@@ -140,14 +152,16 @@ def _bias_rows(bias: Optional[np.ndarray], b: int, hq: int, t_q: int,
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
               causal: bool, q_offset: int = 0,
               bias: Optional[np.ndarray] = None,
-              key_range: Optional[Tuple[int, int]] = None):
+              key_range: Optional[Tuple[int, int]] = None,
+              window: int = 0):
     """Materialised exact attention over every (batch, query head).
 
     q [B, H_q, T_q, d_h], k [B, H_kv, T_k, d_h], v [B, H_kv, T_k, d_v] (any
     real dtype; converted exactly to fp64), bias broadcastable to
     [B, H_q, T_q, T_k] or None.  z_ij = scale * <q_i, k_j> + M_ij (eq 33.2;
     the bias is added after scaling and is never scaled).  ``key_range``
-    restricts the legal set to keys [lo, hi) (used for split partials).
+    restricts the legal set to keys [lo, hi) (used for split partials);
+    ``window`` is the sliding window of ``legal_keys``.
 
     Returns (o [B, H_q, T_q, d_v], lse [B, H_q, T_q], n_legal [B, H_q, T_q]).
     """
@@ -170,7 +184,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
             s = scale * (q[b, hq] @ k[b, kvh].T)
             if m_rows is not None:
                 s = s + np.where(m_rows == NEG_INF, 0.0, m_rows)
-            legal = legal_keys(t_q, t_k, causal, q_offset, m_rows)
+            legal = legal_keys(t_q, t_k, causal, q_offset, m_rows, window)
             if key_range is not None:
                 lo, hi = key_range
                 j = np.arange(t_k)[None, :]
@@ -181,7 +195,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
 
 def attention_rows(q, k, v, rows: Sequence[Tuple[int, int, int]], *,
                    scale: float, causal: bool, q_offset: int = 0,
-                   bias=None):
+                   bias=None, window: int = 0):
     """The same definition evaluated for selected rows (b, hq, i) only.
 
     Each row is computed on its own from its query vector and every key of its
@@ -219,6 +233,8 @@ def attention_rows(q, k, v, rows: Sequence[Tuple[int, int, int]], *,
         pos = q_offset + i
         j = np.arange(t_k)
         legal = (j <= pos) if causal else np.ones(t_k, dtype=bool)
+        if window > 0:
+            legal = legal & (j >= pos - window + 1)
         if m_row is not None:
             legal = legal & (m_row != NEG_INF)
         o1, l1, n1 = softmax_rows(s[None, :], legal[None, :], vv)
@@ -227,7 +243,7 @@ def attention_rows(q, k, v, rows: Sequence[Tuple[int, int, int]], *,
 
 
 def split_partials(q, k, v, *, scale: float, causal: bool, q_offset: int,
-                   split_size: int, bias=None):
+                   split_size: int, bias=None, window: int = 0):
     """Per-split partial results for split-KV decode.
 
     Split s covers keys [s*S, min((s+1)*S, T_k)); its partial is the
@@ -242,7 +258,8 @@ def split_partials(q, k, v, *, scale: float, causal: bool, q_offset: int,
         o_s, l_s, _ = attention(q, k, v, scale=scale, causal=causal,
                                 q_offset=q_offset, bias=bias,
                                 key_range=(s * split_size,
-                                           min((s + 1) * split_size, t_k)))
+                                           min((s + 1) * split_size, t_k)),
+                                window=window)
         o_parts.append(o_s); l_parts.append(l_s)
     return np.stack(o_parts, axis=3), np.stack(l_parts, axis=3)
 

@@ -422,11 +422,113 @@ def check_bias_broadcast(R):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2) and np.array_equal(n1, n2)
 
 
+# --- sliding window (§33.7, the sliding-window paragraph and eq 33.16) ------
+
+def _window_count(pos, window, t_k, causal):
+    """Integers j in [0, t_k) with pos - window + 1 <= j (<= pos if causal)."""
+    lo = max(0, pos - window + 1)
+    hi = min(pos, t_k - 1) if causal else t_k - 1
+    return max(0, hi - lo + 1)
+
+
+def check_window_counts(R):
+    rng = np.random.default_rng(12)
+    t_q, t_k, d = 9, 17, 3
+    q = rng.standard_normal((1, 2, t_q, d))
+    k = rng.standard_normal((1, 2, t_k, d))
+    v = rng.standard_normal((1, 2, t_k, d))
+    for causal in (True, False):
+        for off in (-4, 0, 5, t_k - t_q, t_k + 2):
+            for w in (1, 2, 5, 16, 40):
+                _, lse, n = R.attention(q, k, v, scale=0.3, causal=causal, q_offset=off, window=w)
+                want = np.array([_window_count(off + i, w, t_k, causal) for i in range(t_q)])
+                assert np.array_equal(n[0, 0], want), (causal, off, w)
+                assert np.array_equal(np.isneginf(lse[0, 0]), want == 0)
+                rows = [(0, 1, i) for i in range(t_q)]
+                _, _, n2 = R.attention_rows(q, k, v, rows, scale=0.3, causal=causal, q_offset=off, window=w)
+                assert np.array_equal(n2, want), (causal, off, w)
+
+
+def check_window_single_key(R):
+    """W = 1 with causal masking leaves exactly the row's own position."""
+    rng = np.random.default_rng(13)
+    t_q, t_k, d_h, d_v = 6, 8, 4, 3
+    q = rng.standard_normal((1, 1, t_q, d_h))
+    k = rng.standard_normal((1, 1, t_k, d_h))
+    v = rng.standard_normal((1, 1, t_k, d_v))
+    for off in (-2, 0, 3, 5):
+        o, lse, n = R.attention(q, k, v, scale=0.7, causal=True, q_offset=off, window=1)
+        for i in range(t_q):
+            pos = off + i
+            if 0 <= pos < t_k:
+                np.testing.assert_allclose(o[0, 0, i], v[0, 0, pos], rtol=0, atol=1e-15)
+                assert abs(lse[0, 0, i] - 0.7 * float(q[0, 0, i] @ k[0, 0, pos])) < 1e-14
+                assert n[0, 0, i] == 1
+            else:
+                assert n[0, 0, i] == 0 and lse[0, 0, i] == -np.inf and np.all(o[0, 0, i] == 0)
+
+
+def check_window_as_bias(R):
+    """A window is the -inf bias on keys j < q_offset + i - W + 1."""
+    rng = np.random.default_rng(14)
+    b, hq, hkv, t_q, t_k, d_h, d_v = 2, 4, 2, 7, 21, 5, 4
+    q = rng.standard_normal((b, hq, t_q, d_h))
+    k = rng.standard_normal((b, hkv, t_k, d_h))
+    v = rng.standard_normal((b, hkv, t_k, d_v))
+    for causal, off, w in ((True, 14, 6), (True, 3, 2), (False, 10, 9), (True, -3, 4)):
+        i = np.arange(t_q)[:, None]
+        j = np.arange(t_k)[None, :]
+        bias = np.where(j >= off + i - w + 1, 0.0, -np.inf).reshape(1, 1, t_q, t_k)
+        o1, l1, n1 = R.attention(q, k, v, scale=0.5, causal=causal, q_offset=off, window=w)
+        o2, l2, n2 = R.attention(q, k, v, scale=0.5, causal=causal, q_offset=off, bias=bias)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2) and np.array_equal(n1, n2)
+
+
+def check_window_truncation_bound(R):
+    """eq 33.16 and its proof: with delta the full-attention mass of the keys
+    the window drops, o = (1 - delta) o' + delta o_drop, so
+    ||o - o'|| <= 2 delta M when every ||v_j|| <= M."""
+    rng = np.random.default_rng(15)
+    t_k, d_h, d_v = 40, 6, 5
+    k = rng.standard_normal((1, 1, t_k, d_h))
+    v = rng.standard_normal((1, 1, t_k, d_v))
+    big_m = float(np.linalg.norm(v[0, 0], axis=1).max())
+    for pos, w, temp in ((39, 10, 1.0), (25, 3, 2.0), (30, 29, 0.3), (12, 1, 1.5)):
+        q = temp * rng.standard_normal((1, 1, 1, d_h))
+        o, lse, _ = R.attention(q, k, v, scale=1.0, causal=True, q_offset=pos)
+        o_w, lse_w, _ = R.attention(q, k, v, scale=1.0, causal=True, q_offset=pos, window=w)
+        lo = pos - w + 1
+        o_d, lse_d, _ = R.attention(q, k, v, scale=1.0, causal=True, q_offset=pos, key_range=(0, lo))
+        delta = math.exp(lse_d[0, 0, 0] - lse[0, 0, 0])
+        assert abs(math.exp(lse_w[0, 0, 0] - lse[0, 0, 0]) + delta - 1.0) < 1e-12
+        np.testing.assert_allclose(o[0, 0, 0], (1 - delta) * o_w[0, 0, 0] + delta * o_d[0, 0, 0],
+                                   rtol=0, atol=1e-12)
+        assert 0 < delta < 1
+        assert np.linalg.norm(o[0, 0, 0] - o_w[0, 0, 0]) <= 2 * delta * big_m + 1e-12
+
+
+def check_window_split_merge(R):
+    rng = np.random.default_rng(16)
+    b, hq, hkv, t_q, t_k, d_h, d_v = 1, 4, 2, 3, 37, 4, 3
+    q = rng.standard_normal((b, hq, t_q, d_h))
+    k = rng.standard_normal((b, hkv, t_k, d_h))
+    v = rng.standard_normal((b, hkv, t_k, d_v))
+    for off, w, split in ((34, 9, 4), (34, 30, 7), (20, 2, 5)):
+        o, lse, _ = R.attention(q, k, v, scale=0.4, causal=True, q_offset=off, window=w)
+        op, lp = R.split_partials(q, k, v, scale=0.4, causal=True, q_offset=off,
+                                  split_size=split, window=w)
+        om, lm = R.merge_partials(op, lp)
+        np.testing.assert_allclose(om, o, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lm, lse, rtol=0, atol=1e-13)
+        assert bool(np.isneginf(lp).any())   # splits wholly outside the window are empty
+
+
 ALL_CHECKS = [
     check_example_25_1_exact, check_example_25_1_fp64, check_exercise_33_2,
     check_kv_cache_vectors, check_equal_scores_mean, check_single_and_two_keys,
     check_invariants, check_partitions_exact, check_partitions_fp64,
     check_masked_blocks_and_rows, check_alignment, check_gqa_mapping,
     check_split_merge, check_rows_match_full, check_library_softmax,
-    check_bias_broadcast,
+    check_bias_broadcast, check_window_counts, check_window_single_key,
+    check_window_as_bias, check_window_truncation_bound, check_window_split_merge,
 ]

@@ -34,6 +34,14 @@ MUTANTS = {
                                 "        if st is None:\n            st = (0.0, 0.0, [0.0] * d_v)\n        state = st if"),
     "split_range_inclusive": ("legal = legal & (j >= lo) & (j < hi)", "legal = legal & (j >= lo) & (j <= hi)"),
     "rows_offset_ignored": ("pos = q_offset + i", "pos = i"),
+    "window_off_by_one": ("legal = legal & (j >= q_offset + i - window + 1)",
+                          "legal = legal & (j > q_offset + i - window + 1)"),
+    "window_ignores_offset": ("legal = legal & (j >= q_offset + i - window + 1)",
+                              "legal = legal & (j >= i - window + 1)"),
+    "window_rows_off_by_one": ("legal = legal & (j >= pos - window + 1)",
+                               "legal = legal & (j >= pos - window)"),
+    "window_split_dropped": ("                                window=window)",
+                             "                                window=0)"),
 }
 
 
