@@ -46,12 +46,12 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef enum {
   ATTN_OK = 0,
   ATTN_E_NULL = -1,        /* a required pointer is NULL */
-  ATTN_E_SHAPE = -2,       /* negative size, H_q % H_kv != 0, bad split size */
+  ATTN_E_SHAPE = -2,       /* negative size or window, H_q % H_kv != 0, bad split size */
   ATTN_E_DTYPE = -3,       /* unknown element type */
   ATTN_E_UNSUPPORTED = -4, /* d_h or d_v outside [1, 256], non-finite scale */
   ATTN_E_STRIDE = -5,      /* a negative stride */
@@ -64,8 +64,11 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
 /* Problem description (eq 33.2 of §33.2 with the symbols of Table 33.1).
  * z_ij = scale * <q_i, k_j> + M_ij, where M is the optional additive bias
  * (never scaled).  Key j is LEGAL for row i iff it is causally visible
- * (causal == 0, or j <= q_offset + i) and M_ij != -inf.  Query head hq reads
- * KV head hq / (heads_q / heads_kv) (contiguous head groups). */
+ * (causal == 0, or j <= q_offset + i), inside the sliding window when one is
+ * set (window W >= 1: j >= q_offset + i - W + 1, the W positions ending at
+ * the row's own; §33.7, the sliding-window paragraph with eq 33.16) and
+ * M_ij != -inf.  Query head hq reads KV head hq / (heads_q / heads_kv)
+ * (contiguous head groups). */
 typedef struct {
   int64_t batch;          /* B >= 0 */
   int64_t heads_q;        /* H_q >= 1, a multiple of heads_kv */
@@ -85,7 +88,7 @@ typedef struct {
   float scale;            /* finite; usually 1/sqrt(d_h) */
   int32_t dtype;          /* attn_dtype_t of Q, K, V and O */
   int32_t causal;         /* 0 or 1 */
-  int32_t reserved;       /* must be 0 */
+  int32_t window;         /* sliding window W >= 1 keys, 0 = none; < 0 is an error */
 } attn_params_t;
 
 /* sizeof(attn_params_t), so that bindings can check their mirror of it. */

@@ -37,7 +37,7 @@ class Params(ctypes.Structure):
         ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
         ("bias_stride", ctypes.c_int64 * 4), ("bias", ctypes.c_void_p),
         ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("window", ctypes.c_int32),
     ]
 
 
@@ -107,7 +107,7 @@ def _outer_strides(t: torch.Tensor, name: str):
     return tuple(int(x) for x in t.stride()[:3])
 
 
-def make_params(q, k, v, o, *, scale, causal, q_offset, bias) -> Params:
+def make_params(q, k, v, o, *, scale, causal, q_offset, bias, window=0) -> Params:
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype float32 or bfloat16")
     b, hq, tq, dh = q.shape
@@ -126,7 +126,9 @@ def make_params(q, k, v, o, *, scale, causal, q_offset, bias) -> Params:
     p.scale = float(1.0 / math.sqrt(dh) if scale is None else scale)
     p.dtype = _DTYPES[q.dtype]
     p.causal = 1 if causal else 0
-    p.reserved = 0
+    if window is None or int(window) < 0 or int(window) >= 1 << 31:
+        raise ValueError("window must be an int in [0, 2^31)")
+    p.window = int(window)
     if bias is not None:
         if bias.dtype != torch.float32 or bias.device != q.device:
             raise ValueError("bias must be a float32 tensor on the device of q")
@@ -147,12 +149,14 @@ def _outputs(q, d_v, out, lse):
     return out, lse
 
 
-def attn_fwd(q, k, v, *, scale=None, causal=True, q_offset=0, bias=None,
+def attn_fwd(q, k, v, *, scale=None, causal=True, q_offset=0, bias=None, window=0,
              out=None, lse=None, return_n_legal=False, stream=None):
-    """Exact attention; returns (o, lse) or (o, lse, n_legal)."""
+    """Exact attention; returns (o, lse) or (o, lse, n_legal).  ``window`` > 0
+    keeps only keys j >= q_offset + i - window + 1 for row i."""
     lib = load_library()
     out, lse = _outputs(q, v.shape[3], out, lse)
-    p = make_params(q, k, v, out, scale=scale, causal=causal, q_offset=q_offset, bias=bias)
+    p = make_params(q, k, v, out, scale=scale, causal=causal, q_offset=q_offset, bias=bias,
+                    window=window)
     n_legal = None
     if return_n_legal:
         n_legal = torch.empty(lse.shape, dtype=torch.int32, device=q.device)
@@ -162,17 +166,18 @@ def attn_fwd(q, k, v, *, scale=None, causal=True, q_offset=0, bias=None,
 
 
 def attn_decode_workspace_bytes(q, k_cache, v_cache, *, split_size, scale=None,
-                                causal=True, q_offset=None, bias=None) -> int:
+                                causal=True, q_offset=None, bias=None, window=0) -> int:
     lib = load_library()
     o = torch.empty((q.shape[0], q.shape[1], q.shape[2], v_cache.shape[3]),
                     dtype=q.dtype, device="meta")
     off = k_cache.shape[2] - q.shape[2] if q_offset is None else q_offset
-    p = make_params(q, k_cache, v_cache, o, scale=scale, causal=causal, q_offset=off, bias=bias)
+    p = make_params(q, k_cache, v_cache, o, scale=scale, causal=causal, q_offset=off, bias=bias,
+                    window=window)
     return int(lib.attn_decode_workspace_bytes(ctypes.byref(p), int(split_size)))
 
 
 def attn_decode_splitkv(q, k_cache, v_cache, *, split_size, scale=None, causal=True,
-                        q_offset=None, bias=None, workspace=None, out=None, lse=None,
+                        q_offset=None, bias=None, window=0, workspace=None, out=None, lse=None,
                         stream=None):
     """Split-KV decode + merge; returns (o, lse, workspace).
 
@@ -182,7 +187,8 @@ def attn_decode_splitkv(q, k_cache, v_cache, *, split_size, scale=None, causal=T
     lib = load_library()
     out, lse = _outputs(q, v_cache.shape[3], out, lse)
     off = k_cache.shape[2] - q.shape[2] if q_offset is None else q_offset
-    p = make_params(q, k_cache, v_cache, out, scale=scale, causal=causal, q_offset=off, bias=bias)
+    p = make_params(q, k_cache, v_cache, out, scale=scale, causal=causal, q_offset=off, bias=bias,
+                    window=window)
     need = int(lib.attn_decode_workspace_bytes(ctypes.byref(p), int(split_size)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

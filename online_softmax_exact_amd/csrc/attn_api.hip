@@ -53,7 +53,7 @@ int validate(const attn_params_t* p, Problem* pb) {
   if (!product_ok(p->batch, p->heads_q, p->t_q) || !product_ok(p->batch, p->heads_kv, p->t_k))
     return ATTN_E_SHAPE;
   if (p->causal != 0 && p->causal != 1) return ATTN_E_SHAPE;
-  if (p->reserved != 0) return ATTN_E_SHAPE;
+  if (p->window < 0) return ATTN_E_SHAPE;
   if (p->q_offset > kMaxOffset || p->q_offset < -kMaxOffset) return ATTN_E_SHAPE;
   if (p->d_h < 1 || p->d_h > kMaxHead || p->d_v < 1 || p->d_v > kMaxHead) return ATTN_E_UNSUPPORTED;
   if (!isfinite(p->scale)) return ATTN_E_UNSUPPORTED;
@@ -75,6 +75,7 @@ int validate(const attn_params_t* p, Problem* pb) {
   pb->scale_log2 = p->scale * kLog2e;
   pb->causal = p->causal;
   pb->group = static_cast<int32_t>(p->heads_q / p->heads_kv);
+  pb->window = p->window;
   return ATTN_OK;
 }
 
@@ -105,7 +106,7 @@ const char* attn_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_E_NULL: return "a required pointer is NULL";
-    case ATTN_E_SHAPE: return "invalid shape (negative size, heads_q not a multiple of heads_kv, bad flag or split size)";
+    case ATTN_E_SHAPE: return "invalid shape (negative size or window, heads_q not a multiple of heads_kv, bad flag or split size)";
     case ATTN_E_DTYPE: return "unknown element type";
     case ATTN_E_UNSUPPORTED: return "unsupported head size (d_h and d_v must be 1..256) or non-finite scale";
     case ATTN_E_STRIDE: return "negative stride";

@@ -21,6 +21,7 @@ struct Problem {
   float scale_log2;   // scale * log2(e)
   int32_t causal;
   int32_t group;      // heads_q / heads_kv
+  int64_t window;     // sliding window (keys j >= q_offset + i - window + 1), 0 = none
 };
 
 constexpr float kLog2e = 1.4426950408889634f;

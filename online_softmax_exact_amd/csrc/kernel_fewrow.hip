@@ -67,6 +67,7 @@ struct FArgs {
   float* ws_lse;
   int64_t qs[3], ks[3], vs[3], os[3];
   int64_t q_offset;
+  int64_t window;           // sliding window, 0 = none
   int64_t split_size;       // keys per work item
   int32_t t_q, t_k, heads_q, heads_kv, group, rows, n_rg, n_splits;
   float scale_log2;
@@ -125,6 +126,10 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
   if (a.causal) {
     const int64_t last = a.q_offset + a.t_q - 1;   // largest position of any row
     if (last + 1 < hi) hi = last + 1;
+  }
+  if (a.window > 0) {
+    const int64_t first = a.q_offset - a.window + 1;   // smallest window start of any row
+    if (first > lo) lo = first;
   }
   // Four contiguous, tile-aligned parts, one per wave.
   int64_t len = hi > lo ? hi - lo : 0;
@@ -189,11 +194,14 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
     if (a.causal && pos - kb < lim64) lim64 = pos - kb;
     int lim = lim64 < -1 ? -1 : (lim64 > kTile ? kTile : static_cast<int>(lim64));
     if (!row_ok) lim = -1;
+    // Window: keys below pos - window + 1 are not legal.
+    int64_t first64 = a.window > 0 ? pos - a.window + 1 - kb : 0;
+    const int first = first64 < 0 ? 0 : (first64 > kTile ? kTile : static_cast<int>(first64));
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = 8 * (r >> 2) + 4 * h + (r & 3);
-      const float z = j <= lim ? sacc[r] * a.scale_log2 : -INFINITY;
+      const float z = (j <= lim && j >= first) ? sacc[r] * a.scale_log2 : -INFINITY;
       sacc[r] = z;
       mx = fmaxf(mx, z);
     }
@@ -344,6 +352,7 @@ FArgs make_args(const Problem& pb, const void* q, const void* k, const void* v) 
     a.qs[i] = pb.qs[i]; a.ks[i] = pb.ks[i]; a.vs[i] = pb.vs[i]; a.os[i] = pb.os[i];
   }
   a.q_offset = pb.q_offset;
+  a.window = pb.window;
   a.t_q = static_cast<int32_t>(pb.t_q);
   a.t_k = static_cast<int32_t>(pb.t_k);
   a.heads_q = static_cast<int32_t>(pb.heads_q);

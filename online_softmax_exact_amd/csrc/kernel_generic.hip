@@ -46,6 +46,7 @@ __global__ __launch_bounds__(256) void generic_kernel(
       int64_t lo = s * split_size;
       int64_t hi = split_size < pb.t_k - lo ? lo + split_size : pb.t_k;
       if (pb.causal && pos + 1 < hi) hi = pos + 1;  // causal block skipping
+      if (pb.window > 0 && pos - pb.window + 1 > lo) lo = pos - pb.window + 1;  // sliding window
       const T* kbase = k + b * pb.ks[0] + kvh * pb.ks[1];
       const T* vbase = v + b * pb.vs[0] + kvh * pb.vs[1];
       const float* brow = HAS_BIAS ? pb.bias + b * pb.bs[0] + hq * pb.bs[1] + i * pb.bs[2] : nullptr;

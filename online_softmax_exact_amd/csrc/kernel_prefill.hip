@@ -135,6 +135,16 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
   const int pos_row = clamp_pos(a.q_offset + row);          // this lane's position
   const int pos_w_first = clamp_pos(a.q_offset + row0);     // first row of the wave
   const int pos_w_last = clamp_pos(a.q_offset + row0 + 31); // last row of the wave
+  // First key inside the sliding window of a row at logical row r (0 without a
+  // window), clamped to [0, T_k]; keys below it are not legal.
+  auto win_lo = [&](int64_t r) -> int {
+    if (a.window <= 0) return 0;
+    const int64_t lo = a.q_offset + r - a.window + 1;
+    return lo < 0 ? 0 : (lo > a.t_k ? a.t_k : static_cast<int>(lo));
+  };
+  const int lo_row = win_lo(row);
+  const int lo_w_first = win_lo(row0);
+  const int lo_w_last = win_lo(row0 + 31);
 
   // Tiles the workgroup streams: keys [0, k_end).  Tiles the wave computes:
   // the first n_w of them (every later one is above the wave's diagonal).
@@ -142,6 +152,13 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
   const int wg_last = clamp_pos(a.q_offset + static_cast<int64_t>(qt) * kBr + kBr - 1);
   const int k_end = a.causal ? (wg_last + 1 < a.t_k ? wg_last + 1 : a.t_k) : a.t_k;
   const int n_tiles = k_end > 0 ? (k_end + kBc - 1) / kBc : 0;
+  // The workgroup streams tiles [t_begin, n_tiles): below t_begin every key is
+  // outside the window of its first row (and so of every row).
+  const int t_begin = win_lo(static_cast<int64_t>(qt) * kBr) / kBc;
+  // Tiles below t_w_begin hold no key inside the window of any row of the wave.
+  const int t_w_begin = lo_w_first / kBc;
+  // Tiles from t_lo_full on lie inside the window of every row of the wave.
+  const int t_lo_full = (lo_w_last + kBc - 1) / kBc;
   int n_w = n_tiles;
   if (row0 >= a.t_q) {
     n_w = 0;
@@ -330,6 +347,7 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     if (a.t_k - 1 - kb < lim) lim = a.t_k - 1 - kb;   // keys past T_k do not exist
     if (lim < -1) lim = -1;
     if (!row_ok) lim = -1;   // rows past T_q: nothing legal, no bias read
+    const int first = lo_row - kb;   // keys below the window are not legal
     float mb[16];
     if (BIAS) {
       // 16-byte loads of the 4 consecutive keys each register group holds.
@@ -347,7 +365,7 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     for (int r = 0; r < 16; ++r) {
       const int j = 8 * (r >> 2) + 4 * h + (r & 3);
       float z = sv[r] * a.scale_log2;
-      bool ok = j <= lim;
+      bool ok = j <= lim && j >= first;
       if (BIAS) {
         ok = ok && mb[r] != -INFINITY;
         z = fmaf(mb[r], kLog2e, z);
@@ -390,19 +408,20 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     if (t + 2 < n_tiles) gload(t + 2);
   };
 
-  // Prologue: tiles 0 and 1 in flight.
-  if (n_tiles > 0) gload(0);
-  if (n_tiles > 1) gload(1);
+  // Prologue: the first two streamed tiles in flight.
+  if (t_begin < n_tiles) gload(t_begin);
+  if (t_begin + 1 < n_tiles) gload(t_begin + 1);
   dma_barrier();
 
   // Tile 0 (first statistics), then the run of full tiles on the fast path,
   // then the rest (diagonal / masked / skipped tiles).  On a general tile the
   // blocks past the wave's last visible key are skipped.
   auto general_step = [&](int t) {
-    if (t < n_w) {
+    if (t < n_w && t >= t_w_begin) {
 #pragma unroll
       for (int q = 0; q < kNQ; ++q) {
         if (a.causal && t * kBc + 32 * q > pos_w_last) break;
+        if (t * kBc + 32 * q + 31 < lo_w_first) continue;   // below every row's window
         f32x16 sv;
         unsigned pk[8];
         scores_q(t & 1, q, sv);
@@ -412,8 +431,12 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     }
     advance(t);
   };
-  int t = 0;
-  if (n_tiles > 0) general_step(t++);
+  // General tiles up to the wave's first tile inside every row's window, then
+  // one more (it gives every row its first statistics), the run of full
+  // tiles on the fast path, the rest general (diagonal / masked / skipped).
+  int t = t_begin;
+  while (t < t_lo_full && t < n_tiles) general_step(t++);
+  if (t < n_tiles) general_step(t++);
   // Software pipeline over the 32-key blocks of a full tile: block q's
   // softmax (VALU) runs under the score MFMAs of block q + 1 and the P V
   // MFMAs of block q - 1, which are independent of it.
@@ -451,9 +474,9 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     pv_q(slot, kNQ - 1, pk[(kNQ - 1) & 1]);
     advance(t);
   };
-  // The run of full tiles starts at t = 1 (tile 0 is always general), so its
-  // tiles alternate between slots 1 and 0.
+  // Tile t lives in slot t & 1; the slot is an immediate in each copy.
   if (t < t_full && __ballot(!has) == 0) {
+    if ((t & 1) == 0) fast_step(t++, 0);
     for (; t + 1 < t_full; t += 2) {
       fast_step(t, 1);
       fast_step(t + 1, 0);
@@ -536,6 +559,7 @@ bool launch_prefill_mfma(const Problem& pb, int dtype, const void* q, const void
   }
   for (int i = 0; i < 4; ++i) a.bs[i] = pb.bs[i];
   a.q_offset = pb.q_offset;
+  a.window = pb.window;
   a.t_q = static_cast<int32_t>(pb.t_q);
   a.t_k = static_cast<int32_t>(pb.t_k);
   a.heads_q = static_cast<int32_t>(pb.heads_q);

@@ -30,6 +30,7 @@ struct Args {
   const float* bias;
   int64_t qs[3], ks[3], vs[3], os[3], bs[4];
   int64_t q_offset;
+  int64_t window;   // sliding window (keys j >= q_offset + i - window + 1), 0 = none
   int32_t t_q, t_k, heads_q, group, n_qtiles, batch_heads;
   float scale_log2;
   int32_t causal;

@@ -28,11 +28,11 @@ def f64(t):
     return t.detach().cpu().to(torch.float64).numpy()
 
 
-def oracle_full(wl, key_range=None):
+def oracle_full(wl, key_range=None, window=0):
     return oracle.attention(f64(wl.q), f64(wl.k), f64(wl.v), scale=wl.scale, causal=wl.causal,
                             q_offset=wl.q_offset,
                             bias=None if wl.bias is None else f64(wl.bias),
-                            key_range=key_range)
+                            key_range=key_range, window=window)
 
 
 def to_dev(wl):

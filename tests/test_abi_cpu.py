@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_params_layout(lib):
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
     assert lib.attn_params_sizeof() == ctypes.sizeof(_lib.Params) == 216
 
 
@@ -67,7 +67,7 @@ def fwd(lib, p, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE):
 @pytest.mark.parametrize("field,value,code", [
     ("dtype", 7, -3), ("heads_q", 3, -2), ("heads_kv", 0, -2), ("batch", -1, -2),
     ("t_q", -5, -2), ("t_k", -1, -2), ("d_h", 0, -4), ("d_h", 257, -4), ("d_v", 300, -4),
-    ("causal", 2, -2), ("reserved", 1, -2), ("scale", float("nan"), -4),
+    ("causal", 2, -2), ("window", -1, -2), ("scale", float("nan"), -4),
     ("scale", float("inf"), -4), ("q_offset", 1 << 62, -2), ("batch", 1 << 41, -2),
 ])
 def test_fwd_rejects(lib, field, value, code):
