@@ -9,7 +9,10 @@ bracketed by HIP events on the stream it runs on.
 
 Prints one JSON line.  ``value`` is the prefill's algorithmic TFLOP/s
 (2 (d_h + d_v) flops per legal query-key pair); the decode's algorithmic
-KV GB/s (Q + K + V + O + LSE bytes once) is reported beside it.
+KV GB/s (Q + K + V + O + LSE bytes once) is reported beside it.  After the
+timed steps, the same prefill and decode are timed once more with a sliding
+window (``--window``, keys j >= pos - W + 1) and reported under
+``sliding_window`` with their own algorithmic counts.
 """
 
 from __future__ import annotations
@@ -40,6 +43,21 @@ def decode_counts(batch, hq, hkv, t_q, t_k, d_h, d_v):
     qo = batch * hq * t_q * (d_h + d_v) * 2 + batch * hq * t_q * 4
     pairs = batch * hq * t_q * t_k
     return kv + qo, 2 * (d_h + d_v) * pairs
+
+
+def window_prefill_counts(t: int, heads: int, d_h: int, d_v: int, w: int):
+    """Causal prefill with a sliding window of w keys: row i has min(i + 1, w)
+    legal keys; each of Q, K, V, O and LSE is moved once."""
+    pairs = heads * sum(min(i + 1, w) for i in range(t))
+    return 2 * (d_h + d_v) * pairs, heads * t * (2 * d_h + 2 * d_v) * 2 + heads * t * 4
+
+
+def window_decode_counts(batch, hq, hkv, t_q, w, d_h, d_v):
+    """Decode with a sliding window of w keys: only the K/V rows inside the
+    window are read (each KV head once)."""
+    kv = batch * hkv * w * (d_h + d_v) * 2
+    qo = batch * hq * t_q * (d_h + d_v) * 2 + batch * hq * t_q * 4
+    return kv + qo, 2 * (d_h + d_v) * batch * hq * t_q * w
 
 
 def recorded_traffic(key: str):
@@ -90,6 +108,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="heads of the prefill the CPU oracle baseline times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--window", type=int, default=4096,
+                    help="sliding window of the extra windowed prefill/decode measurement (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, run two device copies of this many MiB (a kernel of "
                          "known traffic to scale hardware byte counters against)")
@@ -187,6 +207,50 @@ def main():
                                 "per_launch_flops": d_flops}},
         "cpu_baseline": None,
     }
+    if args.window > 0:
+        w = args.window
+        ww = torch.empty(attn.attn_decode_workspace_bytes(dq, dk, dv_, split_size=dec.split_size,
+                                                          scale=dec.scale, q_offset=dec.q_offset,
+                                                          window=w), dtype=torch.uint8, device=dev)
+
+        def timed(fn, n=20):
+            for _ in range(10):
+                fn()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+            for a_, b_ in evs:
+                a_.record(stream)
+                fn()
+                b_.record(stream)
+            torch.cuda.synchronize()
+            return sum(a_.elapsed_time(b_) for a_, b_ in evs) / n
+
+        wp_ms = timed(lambda: attn.attn_fwd(pq, pk, pv, scale=pre.scale, causal=True, window=w,
+                                            out=po, lse=pl))
+        wd_ms = timed(lambda: attn.attn_decode_splitkv(dq, dk, dv_, split_size=dec.split_size,
+                                                       scale=dec.scale, causal=True,
+                                                       q_offset=dec.q_offset, window=w,
+                                                       workspace=ww, out=do, lse=dl))
+        wp_flops, wp_bytes = window_prefill_counts(8192, 32, 128, 128, w)
+        wd_bytes, wd_flops = window_decode_counts(16, 32, 8, 1, w, 128, 128)
+        wp_t = wp_flops / (wp_ms * 1e-3) / 1e12
+        wd_g = wd_bytes / (wd_ms * 1e-3) / 1e9
+        out["sliding_window"] = {
+            "window": w,
+            "prefill": {"workload": f"causal prefill B=1 H=32 T=8192 d=128, window {w} (attn_fwd)",
+                        "ms": round(wp_ms, 4), "value": round(wp_t, 2), "unit": "TFLOP/s",
+                        "roofline": {"bound": "mfma", "achieved": round(wp_t, 2),
+                                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                     "frac": round(wp_t / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                                     "per_launch_flops": wp_flops, "per_launch_bytes": wp_bytes}},
+            "decode": {"workload": f"GQA split-KV decode B=16 Hq=32 Hkv=8 Tk=32768 d=128 S=512, "
+                                   f"window {w} (attn_decode_splitkv)",
+                       "ms": round(wd_ms, 4), "value": round(wd_g, 1), "unit": "GB/s",
+                       "roofline": {"bound": "hbm", "achieved": round(wd_g, 1), "peak": PEAK_HBM_GBS,
+                                    "unit": "GB/s", "frac": round(wd_g / PEAK_HBM_GBS, 4),
+                                    "traffic": None, "per_launch_bytes": wd_bytes,
+                                    "per_launch_flops": wd_flops}},
+        }
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)

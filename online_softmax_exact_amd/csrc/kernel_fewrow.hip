@@ -70,6 +70,7 @@ struct FArgs {
   int64_t window;           // sliding window, 0 = none
   int64_t split_size;       // keys per work item
   int32_t t_q, t_k, heads_q, heads_kv, group, rows, n_rg, n_splits;
+  int32_t split0, n_active;   // the grid covers splits [split0, split0 + n_active)
   float scale_log2;
   int32_t causal;
 };
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
 
   // blockIdx -> (b, kvh, row group, split); the split varies fastest.
   int64_t rest = blockIdx.x;
-  const int s = static_cast<int>(rest % a.n_splits); rest /= a.n_splits;
+  const int s = a.split0 + static_cast<int>(rest % a.n_active); rest /= a.n_active;
   const int rg = static_cast<int>(rest % a.n_rg);    rest /= a.n_rg;
   const int kvh = static_cast<int>(rest % a.heads_kv);
   const int b = static_cast<int>(rest / a.heads_kv);
@@ -112,14 +113,6 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
   const int hq = kvh * a.group + gq;
   const int64_t pos = a.q_offset + qi;
 
-  u32x4 qreg[C::KS];
-  {
-    const uint16_t* qp = a.q + b * a.qs[0] + hq * a.qs[1] + static_cast<int64_t>(qi) * a.qs[2];
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      qreg[ks] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * ks + 8 * h) : u32x4{0, 0, 0, 0};
-  }
-
   // Key range of the work item, cut at the last position any row can see.
   int64_t lo = static_cast<int64_t>(s) * a.split_size;
   int64_t hi = a.split_size < a.t_k - lo ? lo + a.split_size : a.t_k;
@@ -131,6 +124,36 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
     const int64_t first = a.q_offset - a.window + 1;   // smallest window start of any row
     if (first > lo) lo = first;
   }
+  // A work item with no key any of its rows may see (a split wholly past the
+  // last position or before the first window, or T_k = 0) only writes its
+  // empty result: O = +0 and LSE = -inf (the valid-flag rule of §33.2).
+  if (hi <= lo) {
+    const int rows_here = a.rows - rg * kRows < kRows ? a.rows - rg * kRows : kRows;
+    for (int e = tid; e < rows_here * DV; e += kThreads) {
+      const int rr = e / DV, d = e % DV;
+      const int nn = rg * kRows + rr;
+      const int ghq = kvh * a.group + nn / a.t_q;
+      const int gi = nn % a.t_q;
+      const int64_t ridx = (static_cast<int64_t>(b) * a.heads_q + ghq) * a.t_q + gi;
+      if (SPLIT) {
+        a.ws_o[(ridx * a.n_splits + s) * DV + d] = 0.0f;
+        if (d == 0) a.ws_lse[ridx * a.n_splits + s] = -INFINITY;
+      } else {
+        a.o[b * a.os[0] + ghq * a.os[1] + static_cast<int64_t>(gi) * a.os[2] + d] = 0;
+        if (d == 0) a.lse[ridx] = -INFINITY;
+      }
+    }
+    return;
+  }
+
+  u32x4 qreg[C::KS];
+  {
+    const uint16_t* qp = a.q + b * a.qs[0] + hq * a.qs[1] + static_cast<int64_t>(qi) * a.qs[2];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      qreg[ks] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * ks + 8 * h) : u32x4{0, 0, 0, 0};
+  }
+
   // Four contiguous, tile-aligned parts, one per wave.
   int64_t len = hi > lo ? hi - lo : 0;
   const int64_t part = ((len + kWaves - 1) / kWaves + kTile - 1) / kTile * kTile;
@@ -343,6 +366,22 @@ bool eligible(const Problem& pb, int dtype, const void* q, const void* k, const 
   return true;
 }
 
+// Partials (o_s, lse_s) = (0, -inf) of the splits in [0, s0) and [s1, n_splits),
+// which hold no key any row may see.
+__global__ __launch_bounds__(256) void empty_partials_kernel(float* ws_o, float* ws_lse, int64_t rows,
+                                                             int64_t n_splits, int64_t s0, int64_t s1,
+                                                             int64_t d_v) {
+  const int64_t n_inactive = n_splits - (s1 - s0);
+  const int64_t total = rows * n_inactive * (d_v + 1);
+  for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < total; e += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t c = e % (d_v + 1), rest = e / (d_v + 1);
+    const int64_t j = rest % n_inactive, r = rest / n_inactive;
+    const int64_t sp = j < s0 ? j : j + (s1 - s0);
+    if (c < d_v) ws_o[(r * n_splits + sp) * d_v + c] = 0.0f;
+    else ws_lse[r * n_splits + sp] = -INFINITY;
+  }
+}
+
 FArgs make_args(const Problem& pb, const void* q, const void* k, const void* v) {
   FArgs a{};
   a.q = static_cast<const uint16_t*>(q);
@@ -380,6 +419,8 @@ bool launch_fewrow_fwd(const Problem& pb, int dtype, const void* q, const void* 
   a.lse = lse;
   a.split_size = pb.t_k > 0 ? pb.t_k : 1;
   a.n_splits = 1;
+  a.split0 = 0;
+  a.n_active = 1;
   const int64_t blocks = pb.batch * pb.heads_kv * a.n_rg;
   const hipError_t e = launch_split<false>(a, blocks, static_cast<int>(pb.d_h),
                                            static_cast<int>(pb.d_v), stream);
@@ -397,9 +438,33 @@ bool launch_fewrow_partials(const Problem& pb, int dtype, const void* q, const v
   a.ws_lse = ws_lse;
   a.split_size = L.split_size;
   a.n_splits = static_cast<int32_t>(L.n_splits);
-  const int64_t blocks = pb.batch * pb.heads_kv * a.n_rg * L.n_splits;
+  // Splits any row may see: keys [k_lo, k_hi) with k_hi = last position + 1
+  // (causal) and k_lo = first window start; the others are filled as empty
+  // partials without running the attention kernel on them.
+  int64_t k_lo = 0, k_hi = pb.t_k;
+  if (pb.causal && pb.q_offset + pb.t_q < k_hi) k_hi = pb.q_offset + pb.t_q;
+  if (pb.window > 0 && pb.q_offset - pb.window + 1 > k_lo) k_lo = pb.q_offset - pb.window + 1;
+  int64_t s0 = 0, s1 = 0;
+  if (k_hi > k_lo) {
+    s0 = k_lo / L.split_size;
+    s1 = (k_hi - 1) / L.split_size + 1;
+    if (s1 > L.n_splits) s1 = L.n_splits;
+    if (s0 > s1) s0 = s1;
+  }
+  a.split0 = static_cast<int32_t>(s0);
+  a.n_active = static_cast<int32_t>(s1 - s0);
+  const int64_t blocks = pb.batch * pb.heads_kv * a.n_rg * a.n_active;
   if (blocks >= (int64_t(1) << 31)) return false;
-  *err = launch_split<true>(a, blocks, static_cast<int>(pb.d_h), static_cast<int>(pb.d_v), stream);
+  *err = hipSuccess;
+  if (blocks > 0)
+    *err = launch_split<true>(a, blocks, static_cast<int>(pb.d_h), static_cast<int>(pb.d_v), stream);
+  if (*err == hipSuccess && a.n_active < L.n_splits && L.rows > 0) {
+    const int64_t total = L.rows * (L.n_splits - a.n_active) * (pb.d_v + 1);
+    const int64_t grid = total / 256 + 1 < 4096 ? total / 256 + 1 : 4096;
+    hipLaunchKernelGGL(empty_partials_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, ws_o,
+                       ws_lse, L.rows, L.n_splits, s0, s1, pb.d_v);
+    *err = hipGetLastError();
+  }
   return true;
 }
 
