@@ -15,7 +15,10 @@ Sources (the pages this follows; cited by page title and section / equation):
   Example 25.1; §33.3 (the explicit T_q x T_k implementation, causal block
   skipping, non-square causal alignment by logical position); §33.7, the
   sliding-window paragraph (only keys in a prescribed range stay visible) and
-  eq 33.16 (the error bound against full attention).
+  eq 33.16 (the error bound against full attention); §33.3, "block size,
+  parallelism and backward recomputation": eqs 33.6-33.8 (gradients from the
+  recomputed probabilities) and Exercise 33.4 (the row-mean term from the
+  softmax Jacobian).
 * "Generation and Caching with the Same Model" (aihero.club), the KV-cache
   section and its `causal_attention` listing: the [B, H, T, D] layout and the
   rule that query row i sits at logical position q_offset + i and sees the
@@ -50,6 +53,10 @@ notes of the repository):
 * A stored partial (o_s, lse_s) stands for the triple (lse_s, 1, o_s); a
   partial with lse_s = -inf is empty and is skipped, never subtracted.
 * Split-KV partials cover contiguous key ranges [s*S, min((s+1)*S, T_k)).
+* Backward (eqs 33.6-33.8): the score scale replaces 1/sqrt(d_h) in eq 33.8
+  (its trailing "." is a garble); the bias gets no gradient; illegal keys and
+  fully masked rows have P = 0 and so contribute no gradient; the K and V
+  gradients of a KV head sum over the query heads that read it.
 
 Nothing here is pinned by itself: the ``-m "not gpu"`` tests pin it against
 the printed example, closed forms, invariants, brute force over block
@@ -262,6 +269,65 @@ def split_partials(q, k, v, *, scale: float, causal: bool, q_offset: int,
                                 window=window)
         o_parts.append(o_s); l_parts.append(l_s)
     return np.stack(o_parts, axis=3), np.stack(l_parts, axis=3)
+
+
+def attention_backward(q, k, v, d_o, *, scale: float, causal: bool,
+                       q_offset: int = 0, bias=None, window: int = 0):
+    """Gradients of O = softmax(S) V with respect to Q, K and V for an upstream
+    gradient G_O (§33.3, "block size, parallelism and backward recomputation":
+    eqs 33.6-33.8).
+
+    Per (batch, query head) the probabilities are rebuilt from the definition
+    (eq 33.2, the legal set of ``legal_keys``): P_ij = e^{z_ij - m_i} / ℓ_i on
+    legal keys, 0 on illegal keys and on rows with no legal key.  Then
+
+        G_V = P^T G_O,  G_P = G_O V^T                       (eq 33.6)
+        (G_S)_ij = P_ij [(G_P)_ij - sum_k P_ik (G_P)_ik]    (eq 33.7)
+        G_Q = scale * G_S K,  G_K = scale * G_S^T Q         (eq 33.8)
+
+    with the score scale in place of 1/sqrt(d_h) (z = scale <q, k> + M).  The
+    bias M is a constant input (mask or additive bias) and gets no gradient.
+    G_K and G_V of a KV head sum the contributions of every query head of its
+    group.  Returns (dq [B, H_q, T_q, d_h], dk [B, H_kv, T_k, d_h],
+    dv [B, H_kv, T_k, d_v]).
+    """
+    def f64(x):
+        if hasattr(x, "detach"):
+            import torch  # exact dtype conversion of torch CPU inputs only
+            return x.detach().to(torch.float64).numpy()
+        return np.asarray(x, dtype=np.float64)
+
+    q, k, v, d_o = f64(q), f64(k), f64(v), f64(d_o)
+    if bias is not None:
+        bias = f64(bias)
+    _check_shapes(q, k, v, bias)
+    bsz, h_q, t_q, _ = q.shape
+    h_kv, t_k = k.shape[1], k.shape[2]
+    group = h_q // h_kv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(bsz):
+        for hq in range(h_q):
+            kvh = hq // group
+            m_rows = _bias_rows(bias, b, hq, t_q, t_k)
+            s = scale * (q[b, hq] @ k[b, kvh].T)
+            if m_rows is not None:
+                s = s + np.where(m_rows == NEG_INF, 0.0, m_rows)
+            legal = legal_keys(t_q, t_k, causal, q_offset, m_rows, window)
+            p = np.zeros((t_q, t_k))
+            live = legal.any(axis=1)
+            if live.any():
+                z = np.where(legal[live], s[live], NEG_INF)
+                w = np.exp(z - z.max(axis=1, keepdims=True))
+                p[live] = w / w.sum(axis=1, keepdims=True)
+            g_o = d_o[b, hq]
+            dv[b, kvh] += p.T @ g_o                                   # eq 33.6
+            g_p = g_o @ v[b, kvh].T                                   # eq 33.6
+            g_s = p * (g_p - (p * g_p).sum(axis=1, keepdims=True))    # eq 33.7
+            dq[b, hq] = scale * (g_s @ k[b, kvh])                     # eq 33.8
+            dk[b, kvh] += scale * (g_s.T @ q[b, hq])                  # eq 33.8
+    return dq, dk, dv
 
 
 # ---------------------------------------------------------------------------

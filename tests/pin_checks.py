@@ -523,6 +523,101 @@ def check_window_split_merge(R):
         assert bool(np.isneginf(lp).any())   # splits wholly outside the window are empty
 
 
+# --- backward (eqs 33.6-33.8, Exercise 33.4) --------------------------------
+
+def _bwd_problem(seed, b=1, hq=2, hkv=1, t_q=4, t_k=6, d_h=3, d_v=2):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((b, hq, t_q, d_h)), rng.standard_normal((b, hkv, t_k, d_h)),
+            rng.standard_normal((b, hkv, t_k, d_v)), rng.standard_normal((b, hq, t_q, d_v)))
+
+
+def check_backward_finite_differences(R):
+    """Central differences of L = sum(G_O * O) through the forward oracle."""
+    q, k, v, g = _bwd_problem(20)
+    bias = np.random.default_rng(21).standard_normal((1, 2, 4, 6))
+    bias[0, 0, 1, 2] = -np.inf
+    bias[0, 1, 0, :] = -np.inf            # one fully masked row
+    for kw in (dict(causal=True, q_offset=2, bias=bias), dict(causal=True, q_offset=3, window=2),
+               dict(causal=False, q_offset=0)):
+        def loss(q_, k_, v_):
+            o, _, _ = R.attention(q_, k_, v_, scale=0.7, **kw)
+            return float((g * o).sum())
+        dq, dk, dv = R.attention_backward(q, k, v, g, scale=0.7, **kw)
+        for x, dx in ((q, dq), (k, dk), (v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                old = x[idx]
+                x[idx] = old + 1e-6
+                up = loss(q, k, v)
+                x[idx] = old - 1e-6
+                dn = loss(q, k, v)
+                x[idx] = old
+                num[idx] = (up - dn) / 2e-6
+            np.testing.assert_allclose(dx, num, rtol=0, atol=1e-7)
+
+
+def check_backward_shift_direction(R):
+    """Exercise 33.4: the row-mean term makes the gradient along a common
+    shift of a row's scores zero; with every key equal, all scores of a row
+    are equal, so G_Q = scale * sum_j (G_S)_ij k = 0."""
+    q, k, v, g = _bwd_problem(22, t_q=5, t_k=7)
+    k[:] = k[:, :, :1, :]
+    dq, dk, _ = R.attention_backward(q, k, v, g, scale=0.9, causal=True, q_offset=2)
+    assert np.abs(dq).max() < 1e-14
+    assert np.abs(dk).max() > 1e-3          # K itself still gets a gradient
+
+
+def check_backward_identities(R):
+    """sum <G_Q, Q> = sum <G_K, K> (both scale * sum_ij (G_S)_ij <q_i, k_j>),
+    and sum_j G_V_j = sum of G_O over rows with a legal key (rows of P sum to 1)."""
+    q, k, v, g = _bwd_problem(23, b=2, hq=4, hkv=2, t_q=5, t_k=9, d_h=4, d_v=3)
+    for off, w in ((0, 0), (4, 3), (-2, 0)):
+        dq, dk, dv = R.attention_backward(q, k, v, g, scale=0.5, causal=True, q_offset=off, window=w)
+        _, lse, _ = R.attention(q, k, v, scale=0.5, causal=True, q_offset=off, window=w)
+        for bb in range(2):
+            for kvh in range(2):
+                heads = [2 * kvh, 2 * kvh + 1]
+                lhs = sum(float((dq[bb, h] * q[bb, h]).sum()) for h in heads)
+                rhs = float((dk[bb, kvh] * k[bb, kvh]).sum())
+                assert abs(lhs - rhs) < 1e-12
+                live = sum(g[bb, h][~np.isneginf(lse[bb, h])].sum(axis=0) for h in heads)
+                np.testing.assert_allclose(dv[bb, kvh].sum(axis=0), live, rtol=0, atol=1e-12)
+
+
+def check_backward_single_key(R):
+    """A window of one key: P is one-hot, so G_S = 0 (G_Q = G_K = 0) and G_V
+    of key j is the upstream gradient of the row at position j."""
+    q, k, v, g = _bwd_problem(24, t_q=4, t_k=6)
+    dq, dk, dv = R.attention_backward(q, k, v, g, scale=1.1, causal=True, q_offset=1, window=1)
+    assert np.abs(dq).max() < 1e-15 and np.abs(dk).max() < 1e-15
+    want = np.zeros_like(dv)
+    for i in range(4):
+        want[0, 0, 1 + i] += g[0, 0, i] + g[0, 1, i]
+    np.testing.assert_allclose(dv, want, rtol=0, atol=1e-15)
+
+
+def check_backward_library_autograd(R):
+    """torch's float64 autograd through an explicitly masked softmax attention
+    (rows with at least one legal key; KV heads expanded per group)."""
+    import torch
+    q, k, v, g = _bwd_problem(25, b=2, hq=4, hkv=2, t_q=6, t_k=11, d_h=5, d_v=4)
+    off, w, scale = 5, 7, 0.45
+    dq, dk, dv = R.attention_backward(q, k, v, g, scale=scale, causal=True, q_offset=off, window=w)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    i = torch.arange(6)[:, None] + off
+    j = torch.arange(11)[None, :]
+    allowed = (j <= i) & (j >= i - w + 1)
+    assert bool(allowed.any(-1).all())
+    kk = tk.repeat_interleave(2, dim=1)
+    vv = tv.repeat_interleave(2, dim=1)
+    s = scale * tq @ kk.transpose(-1, -2)
+    p = torch.softmax(s.masked_fill(~allowed, float("-inf")), dim=-1)
+    (p @ vv * torch.tensor(g)).sum().backward()
+    assert np.allclose(tq.grad.numpy(), dq, rtol=0, atol=1e-12)
+    assert np.allclose(tk.grad.numpy(), dk, rtol=0, atol=1e-12)
+    assert np.allclose(tv.grad.numpy(), dv, rtol=0, atol=1e-12)
+
+
 ALL_CHECKS = [
     check_example_25_1_exact, check_example_25_1_fp64, check_exercise_33_2,
     check_kv_cache_vectors, check_equal_scores_mean, check_single_and_two_keys,
@@ -531,4 +626,6 @@ ALL_CHECKS = [
     check_split_merge, check_rows_match_full, check_library_softmax,
     check_bias_broadcast, check_window_counts, check_window_single_key,
     check_window_as_bias, check_window_truncation_bound, check_window_split_merge,
+    check_backward_finite_differences, check_backward_shift_direction, check_backward_identities,
+    check_backward_single_key, check_backward_library_autograd,
 ]

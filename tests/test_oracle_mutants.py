@@ -42,6 +42,14 @@ MUTANTS = {
                                "legal = legal & (j >= pos - window)"),
     "window_split_dropped": ("                                window=window)",
                              "                                window=0)"),
+    "bwd_no_row_mean": ("g_s = p * (g_p - (p * g_p).sum(axis=1, keepdims=True))", "g_s = p * g_p"),
+    "bwd_row_mean_unweighted": ("g_s = p * (g_p - (p * g_p).sum(axis=1, keepdims=True))",
+                                "g_s = p * (g_p - g_p.mean(axis=1, keepdims=True))"),
+    "bwd_dq_scale_dropped": ("dq[b, hq] = scale * (g_s @ k[b, kvh])", "dq[b, hq] = (g_s @ k[b, kvh])"),
+    "bwd_dk_from_dq_side": ("dk[b, kvh] += scale * (g_s.T @ q[b, hq])",
+                            "dk[b, kvh] += scale * (p.T @ q[b, hq])"),
+    "bwd_gqa_overwrites": ("dv[b, kvh] += p.T @ g_o", "dv[b, kvh] = p.T @ g_o"),
+    "bwd_dp_uses_k": ("g_p = g_o @ v[b, kvh].T", "g_p = g_o @ v[b, kvh].T[:, ::-1]"),
 }
 
 
