@@ -144,6 +144,29 @@ int attn_merge_states(int64_t n_rows, int64_t n_states, int64_t d_v,
                       int32_t out_dtype, void* o_out,
                       int64_t o_out_row_stride, float* lse_out, void* stream);
 
+/* Bytes of device workspace that attn_bwd needs: fp32 D_i = <dO_i, O_i> for
+ * every query row [B, H_q, T_q] (256-byte aligned).  Returns 0 on invalid
+ * arguments. */
+size_t attn_bwd_workspace_bytes(const attn_params_t* p);
+
+/* Gradients of attn_fwd's attention with respect to Q, K and V by
+ * recomputation from the saved LSE (eqs 33.6-33.8 of §33.3 and Exercise
+ * 33.4): with P_ij = e^{z_ij - LSE_i} on legal keys (0 elsewhere),
+ * dV = P^T dO, dP = dO V^T, dS_ij = P_ij (dP_ij - <dO_i, O_i>),
+ * dQ = scale dS K, dK = scale dS^T Q.  Inputs: q, k, v as for attn_fwd, the
+ * forward outputs o and lse of the same call, and the upstream gradient d_o
+ * [B, H_q, T_q, d_v].  Outputs (overwritten, never accumulated): d_q
+ * [B, H_q, T_q, d_h], d_k [B, H_kv, T_k, d_h], d_v [B, H_kv, T_k, d_v]; dK and
+ * dV of a KV head sum over the query heads of its group.  Each gradient and
+ * d_o use the element type and the strides of their forward tensor (d_o and o
+ * share o_stride, d_q q_stride, d_k k_stride, d_v v_stride).  The bias (if
+ * any) is a constant input and gets no gradient; rows with no legal key (LSE
+ * = -inf) contribute nothing.  workspace: attn_bwd_workspace_bytes(p) bytes,
+ * 256-byte aligned. */
+int attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v,
+             const void* o, const float* lse, const void* d_o, void* d_q, void* d_k,
+             void* d_v, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,8 @@ ATTN_E_HIP = -7
 _DTYPES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
 
 EXPORTED = ("attn_params_sizeof", "attn_abi_version", "attn_strerror", "attn_fwd",
-            "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_merge_states")
+            "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_merge_states",
+            "attn_bwd_workspace_bytes", "attn_bwd")
 
 
 class Params(ctypes.Structure):
@@ -70,6 +71,10 @@ def load_library(path: Optional[str] = None):
     lib.attn_merge_states.restype = ctypes.c_int
     lib.attn_merge_states.argtypes = [i64, i64, i64, vp, i64, i64, vp, i64, i64,
                                       ctypes.c_int32, vp, i64, vp, vp]
+    lib.attn_bwd_workspace_bytes.restype = sz
+    lib.attn_bwd_workspace_bytes.argtypes = [pp]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     if lib.attn_params_sizeof() != ctypes.sizeof(Params):
         raise RuntimeError("attn_params_t layout mismatch between header and binding")
     if path is None:
@@ -197,6 +202,36 @@ def attn_decode_splitkv(q, k_cache, v_cache, *, split_size, scale=None, causal=T
                                    ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                    _stream(q.device, stream)))
     return out, lse, workspace
+
+
+def attn_bwd(q, k, v, o, lse, d_o, *, scale=None, causal=True, q_offset=0, bias=None, window=0,
+             d_q=None, d_k=None, d_v=None, workspace=None, stream=None):
+    """Gradients (d_q, d_k, d_v) of attn_fwd's attention for the upstream
+    gradient ``d_o``, recomputed from the forward's ``o`` and ``lse``.  Each
+    gradient gets the shape, strides and dtype of its forward tensor; ``d_o``
+    must have the strides of ``o``."""
+    lib = load_library()
+    if d_o.shape != o.shape or d_o.stride() != o.stride() or d_o.dtype != o.dtype:
+        raise ValueError("d_o must have the shape, strides and dtype of o")
+    if not lse.is_contiguous() or lse.shape != o.shape[:3] or lse.dtype != torch.float32:
+        raise ValueError("lse must be the contiguous float32 [B, H_q, T_q] LSE of the forward")
+    p = make_params(q, k, v, o, scale=scale, causal=causal, q_offset=q_offset, bias=bias,
+                    window=window)
+    grads = []
+    for t, g in ((q, d_q), (k, d_k), (v, d_v)):
+        if g is None:
+            g = torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
+        elif g.shape != t.shape or g.stride() != t.stride() or g.dtype != t.dtype:
+            raise ValueError("gradients must have the shape, strides and dtype of their tensors")
+        grads.append(g)
+    need = int(lib.attn_bwd_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o),
+                        _ptr(grads[0]), _ptr(grads[1]), _ptr(grads[2]),
+                        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                        _stream(q.device, stream)))
+    return tuple(grads)
 
 
 def split_workspace_views(workspace, q, v_cache, split_size):

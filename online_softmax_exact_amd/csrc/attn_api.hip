@@ -128,6 +128,32 @@ int attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v
   return hip_status(launch_generic(pb, p->dtype, q, k, v, o, lse, n_legal, 0, nullptr, nullptr, s));
 }
 
+size_t attn_bwd_workspace_bytes(const attn_params_t* p) {
+  Problem pb;
+  if (validate(p, &pb) != ATTN_OK) return 0;
+  const size_t rows = static_cast<size_t>(pb.batch * pb.heads_q * pb.t_q);
+  return ((rows > 0 ? rows : 1) * sizeof(float) + 255) & ~static_cast<size_t>(255);
+}
+
+int attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* d_o, void* d_q, void* d_k, void* d_v, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  Problem pb;
+  int st = validate(p, &pb);
+  if (st != ATTN_OK) return st;
+  if ((st = check_pointers(pb, q, k, v, o, lse)) != ATTN_OK) return st;
+  const bool rows = numel_nonzero(pb.batch, pb.heads_q, pb.t_q, 1);
+  const bool keys = numel_nonzero(pb.batch, pb.heads_kv, pb.t_k, 1);
+  if (rows && (d_o == nullptr || d_q == nullptr)) return ATTN_E_NULL;
+  if (keys && (k == nullptr || v == nullptr || d_k == nullptr || d_v == nullptr)) return ATTN_E_NULL;
+  if (!rows && !keys) return ATTN_OK;
+  if (workspace == nullptr || workspace_bytes < attn_bwd_workspace_bytes(p)) return ATTN_E_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return ATTN_E_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(launch_bwd_generic(pb, p->dtype, q, k, v, o, lse, d_o, d_q, d_k, d_v,
+                                       static_cast<float*>(workspace), s));
+}
+
 size_t attn_decode_workspace_bytes(const attn_params_t* p, int64_t split_size) {
   Problem pb;
   if (validate(p, &pb) != ATTN_OK || split_size < 1) return 0;

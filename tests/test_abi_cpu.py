@@ -133,3 +133,33 @@ def test_merge_rejects(lib):
     assert m(o=None) == -1
     assert m(lo=None) == -1
     assert m(rows=0, o=None, l=None, out=None, lo=None) == 0
+
+
+def test_bwd_workspace_bytes(lib):
+    p = good_params()
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(p)) == (2 * 4 * 8 * 4 + 255) // 256 * 256
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(good_params(t_q=0))) == 256
+    assert lib.attn_bwd_workspace_bytes(ctypes.byref(good_params(dtype=9))) == 0
+
+
+def test_bwd_rejects(lib):
+    p = good_params()
+    need = lib.attn_bwd_workspace_bytes(ctypes.byref(p))
+    def call(params=p, ws=FAKE, nbytes=need, **kw):
+        ptr = lambda name: kw.get(name, FAKE)
+        return lib.attn_bwd(ctypes.byref(params) if params is not None else None, ptr("q"), ptr("k"),
+                            ptr("v"), ptr("o"), ptr("lse"), ptr("d_o"), ptr("d_q"), ptr("d_k"),
+                            ptr("d_v"), ws, nbytes, None)
+    assert call(params=None) == -1
+    assert call(params=good_params(heads_q=3)) == -2
+    assert call(params=good_params(window=-2)) == -2
+    assert call(params=good_params(dtype=4)) == -3
+    assert call(params=good_params(d_v=0)) == -4
+    for name in ("q", "k", "v", "o", "lse", "d_o", "d_q", "d_k", "d_v"):
+        assert call(**{name: None}) == -1, name
+    assert call(ws=None) == -6
+    assert call(nbytes=need - 1) == -6
+    assert call(ws=ctypes.c_void_p(0x100010)) == -6
+    # Nothing to do: no rows and no keys.
+    assert call(params=good_params(batch=0), q=None, k=None, v=None, o=None, lse=None, d_o=None,
+                d_q=None, d_k=None, d_v=None, ws=None, nbytes=0) == 0
