@@ -150,8 +150,12 @@ int attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v
   if (workspace == nullptr || workspace_bytes < attn_bwd_workspace_bytes(p)) return ATTN_E_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return ATTN_E_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(launch_bwd_generic(pb, p->dtype, q, k, v, o, lse, d_o, d_q, d_k, d_v,
-                                       static_cast<float*>(workspace), s));
+  float* ws_d = static_cast<float*>(workspace);
+  hipError_t e = launch_bwd_rowdot(pb, p->dtype, o, d_o, ws_d, s);
+  if (e == hipSuccess && !launch_bwd_dq_mfma(pb, p->dtype, q, k, v, lse, d_o, ws_d, d_q, s, &e))
+    e = launch_bwd_dq_generic(pb, p->dtype, q, k, v, lse, d_o, ws_d, d_q, s);
+  if (e == hipSuccess) e = launch_bwd_dkdv_generic(pb, p->dtype, q, k, v, lse, d_o, ws_d, d_k, d_v, s);
+  return hip_status(e);
 }
 
 size_t attn_decode_workspace_bytes(const attn_params_t* p, int64_t split_size) {

@@ -41,9 +41,15 @@ hipError_t launch_generic(const Problem& pb, int dtype, const void* q,
                           int32_t* n_legal, int64_t split_size, float* ws_o,
                           float* ws_lse, hipStream_t stream);
 
-hipError_t launch_bwd_generic(const Problem& pb, int dtype, const void* q, const void* k,
-                              const void* v, const void* o, const float* lse, const void* d_o,
-                              void* d_q, void* d_k, void* d_v, float* ws_d, hipStream_t stream);
+// Backward: D_i = <dO_i, O_i>, then dQ and dK/dV (generic kernels).
+hipError_t launch_bwd_rowdot(const Problem& pb, int dtype, const void* o, const void* d_o, float* ws_d,
+                             hipStream_t stream);
+hipError_t launch_bwd_dq_generic(const Problem& pb, int dtype, const void* q, const void* k,
+                                 const void* v, const float* lse, const void* d_o, const float* ws_d,
+                                 void* d_q, hipStream_t stream);
+hipError_t launch_bwd_dkdv_generic(const Problem& pb, int dtype, const void* q, const void* k,
+                                   const void* v, const float* lse, const void* d_o, const float* ws_d,
+                                   void* d_k, void* d_v, hipStream_t stream);
 
 hipError_t launch_merge(int64_t n_rows, int64_t n_states, int64_t d_v,
                         const float* o_states, int64_t o_row_stride,

@@ -219,37 +219,68 @@ int64_t grid_for(int64_t items) {
   return wgs < 65536 ? (wgs > 0 ? wgs : 1) : 65536;
 }
 
-template <typename T, bool HAS_BIAS>
-hipError_t launch_t(const Problem& pb, const void* q, const void* k, const void* v, const void* o,
-                    const float* lse, const void* d_o, void* d_q, void* d_k, void* d_v, float* ws_d,
-                    hipStream_t stream) {
+}  // namespace
+
+hipError_t launch_bwd_rowdot(const Problem& pb, int dtype, const void* o, const void* d_o, float* ws_d,
+                             hipStream_t stream) {
   const int64_t rows = pb.batch * pb.heads_q * pb.t_q;
-  const int64_t keys = pb.batch * pb.heads_kv * pb.t_k;
-  if (rows > 0) {
-    hipLaunchKernelGGL((bwd_rowdot_kernel<T>), dim3(grid_for(rows)), dim3(256), 0, stream, pb,
-                       static_cast<const T*>(o), static_cast<const T*>(d_o), ws_d, rows);
-    hipLaunchKernelGGL((bwd_dq_kernel<T, HAS_BIAS>), dim3(grid_for(rows)), dim3(256), 0, stream, pb,
-                       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), lse,
-                       static_cast<const T*>(d_o), ws_d, static_cast<T*>(d_q), rows);
-  }
-  if (keys > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, HAS_BIAS>), dim3(grid_for(keys)), dim3(256), 0, stream, pb,
-                       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), lse,
-                       static_cast<const T*>(d_o), ws_d, static_cast<T*>(d_k), static_cast<T*>(d_v), keys);
+  if (rows == 0) return hipSuccess;
+  if (dtype == ATTN_F32)
+    hipLaunchKernelGGL((bwd_rowdot_kernel<float>), dim3(grid_for(rows)), dim3(256), 0, stream, pb,
+                       static_cast<const float*>(o), static_cast<const float*>(d_o), ws_d, rows);
+  else
+    hipLaunchKernelGGL((bwd_rowdot_kernel<uint16_t>), dim3(grid_for(rows)), dim3(256), 0, stream, pb,
+                       static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(d_o), ws_d, rows);
   return hipGetLastError();
 }
 
+namespace {
+template <typename T, bool HAS_BIAS>
+void dq_t(const Problem& pb, const void* q, const void* k, const void* v, const float* lse,
+          const void* d_o, const float* ws_d, void* d_q, int64_t rows, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_dq_kernel<T, HAS_BIAS>), dim3(grid_for(rows)), dim3(256), 0, stream, pb,
+                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), lse,
+                     static_cast<const T*>(d_o), ws_d, static_cast<T*>(d_q), rows);
+}
+template <typename T, bool HAS_BIAS>
+void dkdv_t(const Problem& pb, const void* q, const void* k, const void* v, const float* lse,
+            const void* d_o, const float* ws_d, void* d_k, void* d_v, int64_t keys, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, HAS_BIAS>), dim3(grid_for(keys)), dim3(256), 0, stream, pb,
+                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), lse,
+                     static_cast<const T*>(d_o), ws_d, static_cast<T*>(d_k), static_cast<T*>(d_v), keys);
+}
 }  // namespace
 
-hipError_t launch_bwd_generic(const Problem& pb, int dtype, const void* q, const void* k, const void* v,
-                              const void* o, const float* lse, const void* d_o, void* d_q, void* d_k,
-                              void* d_v, float* ws_d, hipStream_t stream) {
+hipError_t launch_bwd_dq_generic(const Problem& pb, int dtype, const void* q, const void* k,
+                                 const void* v, const float* lse, const void* d_o, const float* ws_d,
+                                 void* d_q, hipStream_t stream) {
+  const int64_t rows = pb.batch * pb.heads_q * pb.t_q;
+  if (rows == 0) return hipSuccess;
   const bool bias = pb.bias != nullptr;
-  if (dtype == ATTN_F32)
-    return bias ? launch_t<float, true>(pb, q, k, v, o, lse, d_o, d_q, d_k, d_v, ws_d, stream)
-                : launch_t<float, false>(pb, q, k, v, o, lse, d_o, d_q, d_k, d_v, ws_d, stream);
-  return bias ? launch_t<uint16_t, true>(pb, q, k, v, o, lse, d_o, d_q, d_k, d_v, ws_d, stream)
-              : launch_t<uint16_t, false>(pb, q, k, v, o, lse, d_o, d_q, d_k, d_v, ws_d, stream);
+  if (dtype == ATTN_F32) {
+    if (bias) dq_t<float, true>(pb, q, k, v, lse, d_o, ws_d, d_q, rows, stream);
+    else dq_t<float, false>(pb, q, k, v, lse, d_o, ws_d, d_q, rows, stream);
+  } else {
+    if (bias) dq_t<uint16_t, true>(pb, q, k, v, lse, d_o, ws_d, d_q, rows, stream);
+    else dq_t<uint16_t, false>(pb, q, k, v, lse, d_o, ws_d, d_q, rows, stream);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_generic(const Problem& pb, int dtype, const void* q, const void* k,
+                                   const void* v, const float* lse, const void* d_o, const float* ws_d,
+                                   void* d_k, void* d_v, hipStream_t stream) {
+  const int64_t keys = pb.batch * pb.heads_kv * pb.t_k;
+  if (keys == 0) return hipSuccess;
+  const bool bias = pb.bias != nullptr;
+  if (dtype == ATTN_F32) {
+    if (bias) dkdv_t<float, true>(pb, q, k, v, lse, d_o, ws_d, d_k, d_v, keys, stream);
+    else dkdv_t<float, false>(pb, q, k, v, lse, d_o, ws_d, d_k, d_v, keys, stream);
+  } else {
+    if (bias) dkdv_t<uint16_t, true>(pb, q, k, v, lse, d_o, ws_d, d_k, d_v, keys, stream);
+    else dkdv_t<uint16_t, false>(pb, q, k, v, lse, d_o, ws_d, d_k, d_v, keys, stream);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace attn

@@ -1,0 +1,393 @@
+// MFMA backward kernels for bf16 Q/K/V/O/dO, d_h and d_v in {64, 128}, no
+// bias: gradients of the attention of attn_fwd by recomputing the
+// probabilities from the saved LSE, eqs 33.6-33.8 of "Chapter 33 推理计算优化"
+// §33.3 (block size, parallelism and backward recomputation):
+//   P_ij = e^{z_ij - LSE_i} on legal keys, dP = dO V^T,
+//   dS_ij = P_ij (dP_ij - D_i) with D_i = <dO_i, O_i> (Exercise 33.4),
+//   dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO.
+// No running maximum is needed: the saved LSE is the exact normaliser.
+//
+// dQ kernel: the forward kernel's mapping.  A workgroup of 4 wavefronts owns
+// 128 query rows; K/V tiles of 64 keys stream HBM -> LDS (buffer_load ... lds
+// into two-slot rings).  Per 32-key block: S^T = K Q^T and dP^T = V dO^T
+// (A = 16-byte reads of K / V rows, B = Q^T / dO^T resident in registers),
+// so each lane holds 16 entries of one query row; dS^T is packed to bf16 and
+// is the B operand of dQ^T += K^T dS^T, whose A operand K^T comes from
+// ds_read_b64_tr_b16 of the row-major K tile.
+//
+// dK/dV kernel: a workgroup of 4 wavefronts owns 128 keys of one (batch, KV
+// head); wavefront w owns keys 32 w .. 32 w + 31, with K^T (and V^T for dK)
+// resident in registers.  Q/dO tiles of 64 rows of every query head of the
+// group stream HBM -> LDS.  Per 32-row block: S = Q K^T (and dP = dO V^T),
+// so each lane holds 16 entries of one key column; P (dV) or dS (dK) is
+// packed to bf16 and is the B operand of dV^T += dO^T P or dK^T += Q^T dS,
+// with A = dO^T / Q^T from transposed reads of the row-major tile.  One launch
+// per output (dV, then dK): each keeps one accumulator set and two operand
+// sets in registers.
+//
+// Tiles are 64 rows; all rows of a tile use the XOR swizzle of the transposed
+// reads (16-byte row reads are conflict-free with it too: 16 consecutive rows
+// map chunk c to 16 distinct chunks).
+#include "attn_internal.h"
+#include "kernels.h"
+#include "prefill_common.h"
+
+namespace attn {
+namespace {
+
+using namespace pf;
+
+constexpr int kW = 4;
+constexpr int kThreads = 64 * kW;
+constexpr int kRowsW = 32;              // rows (dQ) or keys (dK/dV) per wavefront
+constexpr int kBr = kRowsW * kW;        // per workgroup
+constexpr int kBc = 64;                 // streamed tile rows
+
+struct BArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* d_o;
+  const float* lse;
+  const float* dd;          // D_i = <dO_i, O_i>, [B, H_q, T_q]
+  uint16_t* out;            // dQ, dK or dV
+  int64_t qs[3], ks[3], vs[3], os[3];
+  int64_t q_offset;
+  int64_t window;
+  int32_t t_q, t_k, heads_q, heads_kv, group, n_tiles_grid, n_units;
+  float scale_log2;
+  int32_t causal;
+};
+
+template <int DH, int DV>
+struct BCfg {
+  static constexpr int KS = DH / 16;     // k-steps over d_h
+  static constexpr int MS = DV / 16;     // k-steps over d_v
+  static constexpr int MQ = DH / 32;     // 32-wide slices of d_h
+  static constexpr int MV = DV / 32;     // 32-wide slices of d_v
+  static constexpr int H_RB = DH * 2;    // bytes per row of a d_h-wide tile
+  static constexpr int V_RB = DV * 2;    // bytes per row of a d_v-wide tile
+  static constexpr int H_BYTES = kBc * H_RB;
+  static constexpr int V_BYTES = kBc * V_RB;
+  static constexpr int H_DMA = H_BYTES / 1024 / kW;   // 1 KB copies per wavefront per tile
+  static constexpr int V_DMA = V_BYTES / 1024 / kW;
+};
+
+// Position helpers: logical position clamped to [-1, T_k].
+__device__ __forceinline__ int clamp_pos(const BArgs& a, int64_t p) {
+  return p < -1 ? -1 : (p > a.t_k ? a.t_k : static_cast<int>(p));
+}
+// First key inside the window of logical row r (0 without a window), in [0, T_k].
+__device__ __forceinline__ int win_lo(const BArgs& a, int64_t r) {
+  if (a.window <= 0) return 0;
+  const int64_t lo = a.q_offset + r - a.window + 1;
+  return lo < 0 ? 0 : (lo > a.t_k ? a.t_k : static_cast<int>(lo));
+}
+
+// Byte offsets (relative to a tile's first row) of the 16-byte chunks one
+// wavefront copies: copy j, lane l fills LDS bytes [1024 (wave n + j) + 16 l, +16)
+// of the slot, i.e. row r, chunk slot sl, which holds chunk sl ^ swz(r).
+template <int RB, int N>
+__device__ __forceinline__ void dma_offsets(int wave, int lane, int row_bytes, int* off) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const int byte = (wave * N + j) * 1024 + lane * 16;
+    const int r = byte / RB, sl = (byte % RB) / 16;
+    off[j] = r * row_bytes + (sl ^ swz_v<RB>(r)) * 16;
+  }
+}
+
+template <int RB, int N>
+__device__ __forceinline__ void dma_tile(const void* base, int64_t first_row, int64_t n_rows, int row_bytes,
+                                         char* slot, int wave, const int* off) {
+  const auto rs = make_rsrc(static_cast<const char*>(base) + first_row * row_bytes,
+                            (n_rows - first_row) * row_bytes);
+#pragma unroll
+  for (int j = 0; j < N; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(slot + (wave * N + j) * 1024), 16, off[j], 0, 0, 0);
+}
+
+// Address of the 16-byte chunk holding elements 16 s + 8 h .. + 7 of row r of
+// a swizzled tile (A operand of a 32x32x16 MFMA: lane = row, 8 elements).
+template <int RB>
+__device__ __forceinline__ const lds_char* row_chunk(const char* tile, int r, int s, int h) {
+  return (const lds_char*)tile + r * RB + (((2 * s + h) ^ swz_v<RB>(r)) << 4);
+}
+
+// Transposed-read address for operand step kk2 of rows base .. base + 15 and
+// output slice mo (32 columns) of a swizzled row-major tile: rows
+// src + 8 e with src = 16 kk2 + 4 h + (lane % 16) / 4 (+ base), byte column
+// 64 mo + 32 ((lane / 16) % 2) + 8 (lane % 4).
+template <int RB>
+__device__ __forceinline__ const lds_char* tr_addr(const char* tile, int base, int kk2, int mo, int e, int lane) {
+  const int h = lane >> 5;
+  const int src = base + 16 * kk2 + 4 * h + ((lane & 15) >> 2) + 8 * e;
+  const int cb = 64 * mo + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  return (const lds_char*)tile + src * RB + (((cb >> 4) ^ swz_v<RB>(src)) << 4) + (cb & 15);
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+template <int DH, int DV>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using C = BCfg<DH, DV>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::H_BYTES + 2 * C::V_BYTES];
+  char* const kring = smem;
+  char* const vring = smem + 2 * C::H_BYTES;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int lr = lane & 31;
+
+  // Heaviest query tiles first.
+  const int bid = blockIdx.x;
+  const int qt = a.n_tiles_grid - 1 - bid / a.n_units;
+  const int bh = bid % a.n_units;
+  const int b = bh / a.heads_q;
+  const int hq = bh % a.heads_q;
+  const int kvh = hq / a.group;
+
+  const int row0 = qt * kBr + wave * kRowsW;
+  const int row = row0 + lr;
+  const bool row_ok = row < a.t_q;
+  const int64_t ridx = (static_cast<int64_t>(b) * a.heads_q + hq) * a.t_q + row;
+
+  // Q^T and dO^T operands of this lane's row.
+  u32x4 qreg[C::KS], greg[C::MS];
+  {
+    const uint16_t* qp = a.q + b * a.qs[0] + hq * a.qs[1] + static_cast<int64_t>(row) * a.qs[2];
+    const uint16_t* gp = a.d_o + b * a.os[0] + hq * a.os[1] + static_cast<int64_t>(row) * a.os[2];
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s)
+      qreg[s] = row_ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < C::MS; ++s)
+      greg[s] = row_ok ? *reinterpret_cast<const u32x4*>(gp + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
+  }
+  const float lse2 = row_ok ? a.lse[ridx] * kLog2e : -INFINITY;
+  const float dd = row_ok ? a.dd[ridx] : 0.0f;
+
+  const int pos_row = clamp_pos(a, a.q_offset + row);
+  const int pos_w_first = clamp_pos(a, a.q_offset + row0);
+  const int pos_w_last = clamp_pos(a, a.q_offset + row0 + 31);
+  const int lo_row = win_lo(a, row);
+  const int lo_w_first = win_lo(a, row0);
+  const int lo_w_last = win_lo(a, row0 + 31);
+
+  const int wg_last = clamp_pos(a, a.q_offset + static_cast<int64_t>(qt) * kBr + kBr - 1);
+  const int k_end = a.causal ? (wg_last + 1 < a.t_k ? wg_last + 1 : a.t_k) : a.t_k;
+  const int n_tiles = k_end > 0 ? (k_end + kBc - 1) / kBc : 0;
+  const int t_begin = win_lo(a, static_cast<int64_t>(qt) * kBr) / kBc;
+  const int t_w_begin = lo_w_first / kBc;
+  const int t_lo_full = (lo_w_last + kBc - 1) / kBc;
+  int n_w = n_tiles;
+  if (row0 >= a.t_q) {
+    n_w = 0;
+  } else if (a.causal) {
+    const int last = pos_w_last < a.t_k - 1 ? pos_w_last : a.t_k - 1;
+    const int tw = last < 0 ? 0 : last / kBc + 1;
+    if (tw < n_w) n_w = tw;
+  }
+  // Tiles every row of the wave sees in full (and every row exists).
+  int t_full = a.t_k / kBc;
+  if (a.causal) {
+    const int tf = (pos_w_first + 1) / kBc;
+    if (tf < t_full) t_full = tf;
+  }
+  if (row0 + kRowsW > a.t_q) t_full = 0;
+  if (t_full > n_w) t_full = n_w;
+
+  const uint16_t* kbase = a.k + b * a.ks[0] + kvh * a.ks[1];
+  const uint16_t* vbase = a.v + b * a.vs[0] + kvh * a.vs[1];
+  const int k_row_bytes = static_cast<int>(a.ks[2]) * 2;
+  const int v_row_bytes = static_cast<int>(a.vs[2]) * 2;
+  int koff[C::H_DMA], voff[C::V_DMA];
+  dma_offsets<C::H_RB, C::H_DMA>(wave, lane, k_row_bytes, koff);
+  dma_offsets<C::V_RB, C::V_DMA>(wave, lane, v_row_bytes, voff);
+  auto gload = [&](int t) {
+    dma_tile<C::H_RB, C::H_DMA>(kbase, static_cast<int64_t>(t) * kBc, a.t_k, k_row_bytes,
+                                kring + (t & 1) * C::H_BYTES, wave, koff);
+    dma_tile<C::V_RB, C::V_DMA>(vbase, static_cast<int64_t>(t) * kBc, a.t_k, v_row_bytes,
+                                vring + (t & 1) * C::V_BYTES, wave, voff);
+  };
+
+  f32x16 qacc[C::MQ];
+#pragma unroll
+  for (int i = 0; i < C::MQ; ++i) qacc[i] = f32x16{};
+
+  // Block q of the tile in `slot`: S^T and dP^T (register r holds key
+  // 32 q + 8 (r / 4) + 4 h + (r % 4) of this lane's row).
+  auto s_and_dp = [&](int slot, int q, f32x16& sacc, f32x16& dacc) {
+    const char* kt = kring + slot * C::H_BYTES;
+    const char* vt = vring + slot * C::V_BYTES;
+    sacc = f32x16{};
+    dacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const u32x4 kop = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          row_chunk<C::H_RB>(kt, 32 * q + lr, s, h));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop), as_bf16x8(qreg[s]), sacc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < C::MS; ++s) {
+      const u32x4 vop = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          row_chunk<C::V_RB>(vt, 32 * q + lr, s, h));
+      dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop), as_bf16x8(greg[s]), dacc, 0, 0, 0);
+    }
+  };
+  // dQ^T += K^T dS^T for block q (B operand of step kk2: keys
+  // 32 q + 16 kk2 + 4 h + (0..3) and + 8 + (0..3), where the reads fetch K).
+  auto dq_acc = [&](int slot, int q, const unsigned* pk) {
+    const char* kt = kring + slot * C::H_BYTES;
+#pragma unroll
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
+      const u32x4 bop = {pk[4 * kk2], pk[4 * kk2 + 1], pk[4 * kk2 + 2], pk[4 * kk2 + 3]};
+#pragma unroll
+      for (int mo = 0; mo < C::MQ; ++mo) {
+        const u32x2 lo = tr_read(tr_addr<C::H_RB>(kt, 32 * q, kk2, mo, 0, lane));
+        const u32x2 hi = tr_read(tr_addr<C::H_RB>(kt, 32 * q, kk2, mo, 1, lane));
+        const u32x4 aop = {lo[0], lo[1], hi[0], hi[1]};
+        qacc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bop), qacc[mo], 0, 0, 0);
+      }
+    }
+  };
+  // dS of a block; MASK: apply causal / window / T_k limits per element.
+  auto ds_block = [&](bool mask, int t, int q, const f32x16& sacc, const f32x16& dacc, unsigned* pk) {
+    const int kb = t * kBc + 32 * q;
+    int lim = a.causal ? pos_row - kb : 32;
+    if (a.t_k - 1 - kb < lim) lim = a.t_k - 1 - kb;
+    if (!row_ok) lim = -1;
+    const int first = lo_row - kb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float d2[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 2 * i + e;
+        const int j = 8 * (r >> 2) + 4 * h + (r & 3);
+        float p = fast_exp2(fmaf(sacc[r], a.scale_log2, -lse2));
+        if (mask) p = (j <= lim && j >= first) ? p : 0.0f;
+        d2[e] = p * (dacc[r] - dd);                 // eq 33.7
+      }
+      pk[i] = pack_bf16(d2[0], d2[1]);
+    }
+  };
+
+  auto dma_barrier = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  auto advance = [&](int t) {
+    dma_barrier();
+    if (t + 2 < n_tiles) gload(t + 2);
+  };
+
+  if (t_begin < n_tiles) gload(t_begin);
+  if (t_begin + 1 < n_tiles) gload(t_begin + 1);
+  dma_barrier();
+
+  auto step = [&](int t, bool fast) {
+    if (t < n_w && t >= t_w_begin) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (!fast && a.causal && t * kBc + 32 * q > pos_w_last) break;
+        if (!fast && t * kBc + 32 * q + 31 < lo_w_first) continue;
+        f32x16 sacc, dacc;
+        unsigned pk[8];
+        s_and_dp(t & 1, q, sacc, dacc);
+        ds_block(!fast, t, q, sacc, dacc, pk);
+        dq_acc(t & 1, q, pk);
+      }
+    }
+    advance(t);
+  };
+  int t = t_begin;
+  const int f0 = t_lo_full > t_begin ? t_lo_full : t_begin;
+  for (; t < f0 && t < n_tiles; ++t) step(t, false);
+  for (; t < t_full; ++t) step(t, true);
+  for (; t < n_tiles; ++t) step(t, false);
+
+  // dQ = scale dS K (eq 33.8).
+  if (!row_ok) return;
+  const float sc = a.scale_log2 * kLn2;
+  uint16_t* op = a.out + b * a.qs[0] + hq * a.qs[1] + static_cast<int64_t>(row) * a.qs[2];
+#pragma unroll
+  for (int mo = 0; mo < C::MQ; ++mo) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dcol = 32 * mo + 8 * g + 4 * h;
+      u32x2 w;
+      w[0] = pack_bf16(qacc[mo][4 * g] * sc, qacc[mo][4 * g + 1] * sc);
+      w[1] = pack_bf16(qacc[mo][4 * g + 2] * sc, qacc[mo][4 * g + 3] * sc);
+      *reinterpret_cast<u32x2*>(op + dcol) = w;
+    }
+  }
+#endif
+}
+
+template <int DH, int DV>
+hipError_t launch_dq(const BArgs& a, int64_t blocks, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_dq_mfma_kernel<DH, DV>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+// Takes bf16 problems without bias with d_h, d_v in {64, 128}, positive
+// scale, 16-byte aligned rows and sizes that fit 32-bit indices; launches the
+// dQ kernel (D must already be in dd).  Returns false when it does not apply.
+bool launch_bwd_dq_mfma(const Problem& pb, int dtype, const void* q, const void* k, const void* v,
+                        const float* lse, const void* d_o, const float* dd, void* d_q,
+                        hipStream_t stream, hipError_t* err) {
+  if (dtype != ATTN_BF16 || pb.bias != nullptr) return false;
+  if (!((pb.d_h == 64 || pb.d_h == 128) && (pb.d_v == 64 || pb.d_v == 128))) return false;
+  if (!(pb.scale_log2 > 0.0f)) return false;
+  if (pb.t_q >= (int64_t(1) << 30) || pb.t_k >= (int64_t(1) << 30)) return false;
+  if (pb.ks[2] >= (int64_t(1) << 24) || pb.vs[2] >= (int64_t(1) << 24)) return false;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(d_q)) return false;
+  for (int i = 0; i < 3; ++i)
+    if ((pb.qs[i] | pb.ks[i] | pb.vs[i] | pb.os[i]) & 7) return false;
+  const int64_t n_qtiles = (pb.t_q + kBr - 1) / kBr;
+  const int64_t blocks = n_qtiles * pb.batch * pb.heads_q;
+  if (blocks >= (int64_t(1) << 31) || pb.batch * pb.heads_q >= (int64_t(1) << 30)) return false;
+  BArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.d_o = static_cast<const uint16_t*>(d_o);
+  a.lse = lse;
+  a.dd = dd;
+  a.out = static_cast<uint16_t*>(d_q);
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = pb.qs[i]; a.ks[i] = pb.ks[i]; a.vs[i] = pb.vs[i]; a.os[i] = pb.os[i];
+  }
+  a.q_offset = pb.q_offset;
+  a.window = pb.window;
+  a.t_q = static_cast<int32_t>(pb.t_q);
+  a.t_k = static_cast<int32_t>(pb.t_k);
+  a.heads_q = static_cast<int32_t>(pb.heads_q);
+  a.heads_kv = static_cast<int32_t>(pb.heads_kv);
+  a.group = pb.group;
+  a.n_tiles_grid = static_cast<int32_t>(n_qtiles);
+  a.n_units = static_cast<int32_t>(pb.batch * pb.heads_q);
+  a.scale_log2 = pb.scale_log2;
+  a.causal = pb.causal;
+  if (blocks == 0) {
+    *err = hipSuccess;
+    return true;
+  }
+  if (pb.d_h == 128 && pb.d_v == 128) *err = launch_dq<128, 128>(a, blocks, stream);
+  else if (pb.d_h == 64 && pb.d_v == 128) *err = launch_dq<64, 128>(a, blocks, stream);
+  else if (pb.d_h == 128 && pb.d_v == 64) *err = launch_dq<128, 64>(a, blocks, stream);
+  else *err = launch_dq<64, 64>(a, blocks, stream);
+  return true;
+}
+
+}  // namespace attn

@@ -30,4 +30,9 @@ bool launch_fewrow_partials(const Problem& pb, int dtype, const void* q, const v
                             const void* v, const SplitLayout& L, float* ws_o, float* ws_lse,
                             hipStream_t stream, hipError_t* err);
 
+// MFMA backward dQ (bf16, d_h and d_v in {64, 128}, no bias); dd holds D.
+bool launch_bwd_dq_mfma(const Problem& pb, int dtype, const void* q, const void* k, const void* v,
+                        const float* lse, const void* d_o, const float* dd, void* d_q,
+                        hipStream_t stream, hipError_t* err);
+
 }  // namespace attn
