@@ -154,7 +154,8 @@ int attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v
   hipError_t e = launch_bwd_rowdot(pb, p->dtype, o, d_o, ws_d, s);
   if (e == hipSuccess && !launch_bwd_dq_mfma(pb, p->dtype, q, k, v, lse, d_o, ws_d, d_q, s, &e))
     e = launch_bwd_dq_generic(pb, p->dtype, q, k, v, lse, d_o, ws_d, d_q, s);
-  if (e == hipSuccess) e = launch_bwd_dkdv_generic(pb, p->dtype, q, k, v, lse, d_o, ws_d, d_k, d_v, s);
+  if (e == hipSuccess && !launch_bwd_dkdv_mfma(pb, p->dtype, q, k, v, lse, d_o, ws_d, d_k, d_v, s, &e))
+    e = launch_bwd_dkdv_generic(pb, p->dtype, q, k, v, lse, d_o, ws_d, d_k, d_v, s);
   return hip_status(e);
 }
 

@@ -330,6 +330,229 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a) {
 #endif
 }
 
+// ---------------------------------------------------------------------------
+// dK (WHICH = 1) or dV (WHICH = 0)
+// ---------------------------------------------------------------------------
+template <int DH, int DV, int WHICH>
+__global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using C = BCfg<DH, DV>;
+  constexpr bool DK = WHICH == 1;
+  constexpr int MOUT = DK ? C::MQ : C::MV;     // 32-wide output slices
+  // Q ring, dO ring (two slots each), then per slot 64 LSEs and 64 D values.
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::H_BYTES + 2 * C::V_BYTES + 1024];
+  char* const qring = smem;
+  char* const gring = smem + 2 * C::H_BYTES;
+  float* const sring = reinterpret_cast<float*>(smem + 2 * C::H_BYTES + 2 * C::V_BYTES);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int lr = lane & 31;
+
+  // Low key tiles first (with causal masking they are seen by more rows).
+  const int bid = blockIdx.x;
+  const int kt = bid / a.n_units;
+  const int bh = bid % a.n_units;
+  const int b = bh / a.heads_kv;
+  const int kvh = bh % a.heads_kv;
+
+  const int key0 = kt * kBr + wave * kRowsW;   // first key of this wave
+  const int key = key0 + lr;
+  const bool key_ok = key < a.t_k;
+
+  // K^T (and V^T) operands of this lane's key.
+  u32x4 kreg[C::KS], vreg[DK ? C::MS : 1];
+  {
+    const uint16_t* kp = a.k + b * a.ks[0] + kvh * a.ks[1] + static_cast<int64_t>(key) * a.ks[2];
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s)
+      kreg[s] = key_ok ? *reinterpret_cast<const u32x4*>(kp + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
+    if (DK) {
+      const uint16_t* vp = a.v + b * a.vs[0] + kvh * a.vs[1] + static_cast<int64_t>(key) * a.vs[2];
+#pragma unroll
+      for (int s = 0; s < C::MS; ++s)
+        vreg[s] = key_ok ? *reinterpret_cast<const u32x4*>(vp + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // Query rows that can see a key of the workgroup: pos_i >= first key
+  // (causal) and pos_i - W + 1 <= last key (window).
+  const int64_t wk0 = static_cast<int64_t>(kt) * kBr;
+  int64_t i_lo = 0, i_hi = a.t_q;
+  if (a.causal && wk0 - a.q_offset > i_lo) i_lo = wk0 - a.q_offset;
+  if (a.window > 0 && wk0 + kBr - 1 - a.q_offset + a.window < i_hi) i_hi = wk0 + kBr - 1 - a.q_offset + a.window;
+  if (i_lo > i_hi) i_lo = i_hi;
+  const int qt_lo = static_cast<int>(i_lo / kBc);
+  const int n_qt = i_hi > i_lo ? static_cast<int>((i_hi + kBc - 1) / kBc) - qt_lo : 0;
+  const int n_units = n_qt * a.group;          // (query head of the group, query tile)
+
+  const int q_row_bytes = static_cast<int>(a.qs[2]) * 2;
+  const int g_row_bytes = static_cast<int>(a.os[2]) * 2;
+  int qoff[C::H_DMA], goff[C::V_DMA];
+  dma_offsets<C::H_RB, C::H_DMA>(wave, lane, q_row_bytes, qoff);
+  dma_offsets<C::V_RB, C::V_DMA>(wave, lane, g_row_bytes, goff);
+  auto unit = [&](int u, int& hq, int& i0) {
+    hq = kvh * a.group + u / n_qt;
+    i0 = (qt_lo + u % n_qt) * kBc;
+  };
+  auto gload = [&](int u) {
+    int hq, i0;
+    unit(u, hq, i0);
+    const int slot = u & 1;
+    dma_tile<C::H_RB, C::H_DMA>(a.q + b * a.qs[0] + hq * a.qs[1], i0, a.t_q, q_row_bytes,
+                                qring + slot * C::H_BYTES, wave, qoff);
+    dma_tile<C::V_RB, C::V_DMA>(a.d_o + b * a.os[0] + hq * a.os[1], i0, a.t_q, g_row_bytes,
+                                gring + slot * C::V_BYTES, wave, goff);
+    if (wave == 0) {
+      // 64 LSEs and 64 D values of the tile's rows (4 bytes per lane; rows
+      // past T_q read as 0 and are masked).
+      const int64_t r0 = (static_cast<int64_t>(b) * a.heads_q + hq) * a.t_q + i0;
+      const int64_t n = a.t_q - i0;
+      const auto rl = make_rsrc(a.lse + r0, n * 4);
+      const auto rd = make_rsrc(a.dd + r0, n * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rl, (__attribute__((address_space(3))) void*)(sring + slot * 128), 4, lane * 4, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rd, (__attribute__((address_space(3))) void*)(sring + slot * 128 + 64), 4, lane * 4, 0, 0, 0);
+    }
+  };
+
+  f32x16 acc[MOUT];
+#pragma unroll
+  for (int i = 0; i < MOUT; ++i) acc[i] = f32x16{};
+
+  auto dma_barrier = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  if (n_units > 0) gload(0);
+  if (n_units > 1) gload(1);
+  dma_barrier();
+
+  const int last_key = key0 + kRowsW - 1;
+  for (int u = 0; u < n_units; ++u) {
+    int hq, i0;
+    unit(u, hq, i0);
+    const int slot = u & 1;
+    const char* qt_ = qring + slot * C::H_BYTES;
+    const char* gt_ = gring + slot * C::V_BYTES;
+    const float* st_ = sring + slot * 128;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r0 = i0 + 32 * q;                 // first row of the block
+      const int64_t pf = a.q_offset + r0, pl = a.q_offset + r0 + 31;
+      // Any legal (row, key) pair in the block for this wave?
+      bool any = key0 < a.t_k && r0 < a.t_q;
+      if (a.causal && pl < key0) any = false;
+      if (a.window > 0 && pf - a.window + 1 > last_key) any = false;
+      if (!any) continue;
+      // All pairs legal?
+      bool full = last_key < a.t_k && r0 + 31 < a.t_q;
+      if (a.causal && pf < last_key) full = false;
+      if (a.window > 0 && pl - a.window + 1 > key0) full = false;
+
+      // S = Q K^T (and dP = dO V^T): register r holds row
+      // r0 + 8 (r / 4) + 4 h + (r % 4) of this lane's key.
+      f32x16 sacc = f32x16{}, dacc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) {
+        const u32x4 qop = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            row_chunk<C::H_RB>(qt_, 32 * q + lr, s, h));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qop), as_bf16x8(kreg[s]), sacc, 0, 0, 0);
+      }
+      if (DK) {
+#pragma unroll
+        for (int s = 0; s < C::MS; ++s) {
+          const u32x4 gop = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+              row_chunk<C::V_RB>(gt_, 32 * q + lr, s, h));
+          dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(gop), as_bf16x8(vreg[s]), dacc, 0, 0, 0);
+        }
+      }
+      // LSE (and D) of the 16 rows this lane holds.
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        l4[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+            (const __attribute__((address_space(3))) char*)(st_) + (32 * q + 8 * g + 4 * h) * 4);
+        if (DK)
+          d4[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+              (const __attribute__((address_space(3))) char*)(st_) + 256 + (32 * q + 8 * g + 4 * h) * 4);
+      }
+      unsigned pk[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float w2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * i + e;
+          const int row = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          float p = fast_exp2(fmaf(sacc[r], a.scale_log2, -l4[r >> 2][r & 3] * kLog2e));
+          if (!full) {
+            const int64_t pos = a.q_offset + row;
+            bool ok = key_ok && row < a.t_q;
+            if (a.causal && key > pos) ok = false;
+            if (a.window > 0 && key < pos - a.window + 1) ok = false;
+            p = ok ? p : 0.0f;
+          }
+          w2[e] = DK ? p * (dacc[r] - d4[r >> 2][r & 3]) : p;   // dS (eq 33.7) or P
+        }
+        pk[i] = pack_bf16(w2[0], w2[1]);
+      }
+      // dV^T += dO^T P or dK^T += Q^T dS (A = transposed reads of the tile).
+      const char* at = DK ? qt_ : gt_;
+#pragma unroll
+      for (int kk2 = 0; kk2 < 2; ++kk2) {
+        const u32x4 bop = {pk[4 * kk2], pk[4 * kk2 + 1], pk[4 * kk2 + 2], pk[4 * kk2 + 3]};
+#pragma unroll
+        for (int mo = 0; mo < MOUT; ++mo) {
+          u32x2 lo, hi;
+          if (DK) {
+            lo = tr_read(tr_addr<C::H_RB>(at, 32 * q, kk2, mo, 0, lane));
+            hi = tr_read(tr_addr<C::H_RB>(at, 32 * q, kk2, mo, 1, lane));
+          } else {
+            lo = tr_read(tr_addr<C::V_RB>(at, 32 * q, kk2, mo, 0, lane));
+            hi = tr_read(tr_addr<C::V_RB>(at, 32 * q, kk2, mo, 1, lane));
+          }
+          const u32x4 aop = {lo[0], lo[1], hi[0], hi[1]};
+          acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bop), acc[mo], 0, 0, 0);
+        }
+      }
+    }
+    // End of unit u: this wave's copies of unit u + 1 are done, every wave is
+    // done with slot u & 1; copy unit u + 2 into it.
+    dma_barrier();
+    if (u + 2 < n_units) gload(u + 2);
+  }
+
+  // dK = scale dS^T Q (eq 33.8) or dV = P^T dO (eq 33.6); keys no row sees get 0.
+  if (!key_ok) return;
+  const float sc = DK ? a.scale_log2 * kLn2 : 1.0f;
+  uint16_t* op = DK ? a.out + b * a.ks[0] + kvh * a.ks[1] + static_cast<int64_t>(key) * a.ks[2]
+                    : a.out + b * a.vs[0] + kvh * a.vs[1] + static_cast<int64_t>(key) * a.vs[2];
+#pragma unroll
+  for (int mo = 0; mo < MOUT; ++mo) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dcol = 32 * mo + 8 * g + 4 * h;
+      u32x2 w;
+      w[0] = pack_bf16(acc[mo][4 * g] * sc, acc[mo][4 * g + 1] * sc);
+      w[1] = pack_bf16(acc[mo][4 * g + 2] * sc, acc[mo][4 * g + 3] * sc);
+      *reinterpret_cast<u32x2*>(op + dcol) = w;
+    }
+  }
+#endif
+}
+
+template <int DH, int DV, int WHICH>
+hipError_t launch_kv(const BArgs& a, int64_t blocks, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_kv_mfma_kernel<DH, DV, WHICH>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                     0, s, a);
+  return hipGetLastError();
+}
+
 template <int DH, int DV>
 hipError_t launch_dq(const BArgs& a, int64_t blocks, hipStream_t s) {
   hipLaunchKernelGGL((bwd_dq_mfma_kernel<DH, DV>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a);
@@ -387,6 +610,56 @@ bool launch_bwd_dq_mfma(const Problem& pb, int dtype, const void* q, const void*
   else if (pb.d_h == 64 && pb.d_v == 128) *err = launch_dq<64, 128>(a, blocks, stream);
   else if (pb.d_h == 128 && pb.d_v == 64) *err = launch_dq<128, 64>(a, blocks, stream);
   else *err = launch_dq<64, 64>(a, blocks, stream);
+  return true;
+}
+
+// dK and dV with the MFMA kernels (same conditions as launch_bwd_dq_mfma).
+bool launch_bwd_dkdv_mfma(const Problem& pb, int dtype, const void* q, const void* k, const void* v,
+                          const float* lse, const void* d_o, const float* dd, void* d_k, void* d_v,
+                          hipStream_t stream, hipError_t* err) {
+  if (dtype != ATTN_BF16 || pb.bias != nullptr) return false;
+  if (!((pb.d_h == 64 || pb.d_h == 128) && (pb.d_v == 64 || pb.d_v == 128))) return false;
+  if (!(pb.scale_log2 > 0.0f)) return false;
+  if (pb.t_q >= (int64_t(1) << 30) || pb.t_k >= (int64_t(1) << 30)) return false;
+  if (pb.qs[2] >= (int64_t(1) << 24) || pb.os[2] >= (int64_t(1) << 24)) return false;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(d_k) ||
+      !aligned16(d_v))
+    return false;
+  for (int i = 0; i < 3; ++i)
+    if ((pb.qs[i] | pb.ks[i] | pb.vs[i] | pb.os[i]) & 7) return false;
+  const int64_t n_ktiles = (pb.t_k + kBr - 1) / kBr;
+  const int64_t blocks = n_ktiles * pb.batch * pb.heads_kv;
+  if (blocks >= (int64_t(1) << 31) || pb.batch * pb.heads_kv >= (int64_t(1) << 30)) return false;
+  BArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.d_o = static_cast<const uint16_t*>(d_o);
+  a.lse = lse;
+  a.dd = dd;
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = pb.qs[i]; a.ks[i] = pb.ks[i]; a.vs[i] = pb.vs[i]; a.os[i] = pb.os[i];
+  }
+  a.q_offset = pb.q_offset;
+  a.window = pb.window;
+  a.t_q = static_cast<int32_t>(pb.t_q);
+  a.t_k = static_cast<int32_t>(pb.t_k);
+  a.heads_q = static_cast<int32_t>(pb.heads_q);
+  a.heads_kv = static_cast<int32_t>(pb.heads_kv);
+  a.group = pb.group;
+  a.n_tiles_grid = static_cast<int32_t>(n_ktiles);
+  a.n_units = static_cast<int32_t>(pb.batch * pb.heads_kv);
+  a.scale_log2 = pb.scale_log2;
+  a.causal = pb.causal;
+  *err = hipSuccess;
+  if (blocks == 0) return true;
+  for (int which = 0; which < 2 && *err == hipSuccess; ++which) {
+    a.out = static_cast<uint16_t*>(which ? d_k : d_v);
+    if (pb.d_h == 128 && pb.d_v == 128) *err = which ? launch_kv<128, 128, 1>(a, blocks, stream) : launch_kv<128, 128, 0>(a, blocks, stream);
+    else if (pb.d_h == 64 && pb.d_v == 128) *err = which ? launch_kv<64, 128, 1>(a, blocks, stream) : launch_kv<64, 128, 0>(a, blocks, stream);
+    else if (pb.d_h == 128 && pb.d_v == 64) *err = which ? launch_kv<128, 64, 1>(a, blocks, stream) : launch_kv<128, 64, 0>(a, blocks, stream);
+    else *err = which ? launch_kv<64, 64, 1>(a, blocks, stream) : launch_kv<64, 64, 0>(a, blocks, stream);
+  }
   return true;
 }
 

@@ -35,4 +35,8 @@ bool launch_bwd_dq_mfma(const Problem& pb, int dtype, const void* q, const void*
                         const float* lse, const void* d_o, const float* dd, void* d_q,
                         hipStream_t stream, hipError_t* err);
 
+bool launch_bwd_dkdv_mfma(const Problem& pb, int dtype, const void* q, const void* k, const void* v,
+                          const float* lse, const void* d_o, const float* dd, void* d_k, void* d_v,
+                          hipStream_t stream, hipError_t* err);
+
 }  // namespace attn

@@ -330,6 +330,65 @@ def attention_backward(q, k, v, d_o, *, scale: float, causal: bool,
     return dq, dk, dv
 
 
+def attention_backward_sampled(q, k, v, d_o, *, rows=(), keys=(), scale: float,
+                               causal: bool, q_offset: int = 0, window: int = 0):
+    """The gradients of ``attention_backward`` (eqs 33.6-33.8) at selected
+    places only, for full-size problems: G_Q of query rows (b, hq, i) and
+    G_K, G_V of keys (b, kv head, j).  A row needs its own probability row;
+    a key needs the probability column of every query head of its group, so
+    those heads' P and G_P are materialised one head at a time.  No bias.
+    Inputs may be torch CPU tensors or numpy arrays.  Returns
+    (dq [R, d_h], dk [K, d_h], dv [K, d_v])."""
+    def f64(x):
+        if hasattr(x, "detach"):
+            import torch  # exact dtype conversion of torch CPU inputs only
+            return x.detach().to(torch.float64).numpy()
+        return np.asarray(x, dtype=np.float64)
+
+    h_q, h_kv, t_q, t_k = q.shape[1], k.shape[1], q.shape[2], k.shape[2]
+    group = h_q // h_kv
+
+    def head(b, hq, row_sel):
+        kvh = hq // group
+        qq, kk, vv, gg = f64(q[b, hq][row_sel]), f64(k[b, kvh]), f64(v[b, kvh]), f64(d_o[b, hq][row_sel])
+        ii = np.arange(t_q)[row_sel]
+        s_ = scale * (qq @ kk.T)
+        j = np.arange(t_k)[None, :]
+        pos = (q_offset + ii)[:, None]
+        legal = (j <= pos) if causal else np.ones(s_.shape, dtype=bool)
+        if window > 0:
+            legal = legal & (j >= pos - window + 1)
+        p = np.zeros_like(s_)
+        live = legal.any(axis=1)
+        if live.any():
+            z = np.where(legal[live], s_[live], NEG_INF)
+            w = np.exp(z - z.max(axis=1, keepdims=True))
+            p[live] = w / w.sum(axis=1, keepdims=True)
+        g_p = gg @ vv.T                                               # eq 33.6
+        g_s = p * (g_p - (p * g_p).sum(axis=1, keepdims=True))        # eq 33.7
+        return qq, kk, gg, p, g_s
+
+    dq = []
+    for (b, hq, i) in rows:
+        _, kk, _, _, g_s = head(b, hq, slice(i, i + 1))
+        dq.append(scale * (g_s @ kk)[0])                              # eq 33.8
+    dk = {key: 0.0 for key in keys}
+    dv = {key: 0.0 for key in keys}
+    by_head = {}
+    for (b, kvh, j) in keys:
+        by_head.setdefault((b, kvh), []).append(j)
+    for (b, kvh), js in by_head.items():
+        for hq in range(kvh * group, (kvh + 1) * group):
+            qq, _, gg, p, g_s = head(b, hq, slice(None))
+            for j in js:
+                dv[(b, kvh, j)] = dv[(b, kvh, j)] + p[:, j] @ gg        # eq 33.6
+                dk[(b, kvh, j)] = dk[(b, kvh, j)] + scale * (g_s[:, j] @ qq)   # eq 33.8
+    d_h, d_v = q.shape[3], v.shape[3]
+    return (np.array(dq).reshape(len(rows), d_h),
+            np.array([dk[key] for key in keys]).reshape(len(keys), d_h),
+            np.array([dv[key] for key in keys]).reshape(len(keys), d_v))
+
+
 # ---------------------------------------------------------------------------
 # 2. Statistics, merge and Algorithm 33.1 (eqs 33.3-33.5), arithmetic-generic
 # ---------------------------------------------------------------------------

@@ -618,6 +618,18 @@ def check_backward_library_autograd(R):
     assert np.allclose(tv.grad.numpy(), dv, rtol=0, atol=1e-12)
 
 
+def check_backward_sampled_matches_full(R):
+    q, k, v, g = _bwd_problem(26, b=2, hq=4, hkv=2, t_q=7, t_k=12, d_h=4, d_v=3)
+    for kw in (dict(causal=True, q_offset=5), dict(causal=True, q_offset=6, window=4), dict(causal=False)):
+        dq, dk, dv = R.attention_backward(q, k, v, g, scale=0.6, **kw)
+        rows = [(1, 3, 6), (0, 0, 0), (0, 2, 3)]
+        keys = [(1, 1, 11), (0, 0, 0), (0, 1, 5)]
+        sq, sk, sv = R.attention_backward_sampled(q, k, v, g, rows=rows, keys=keys, scale=0.6, **kw)
+        np.testing.assert_allclose(sq, np.array([dq[r] for r in rows]), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(sk, np.array([dk[x] for x in keys]), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(sv, np.array([dv[x] for x in keys]), rtol=0, atol=1e-13)
+
+
 ALL_CHECKS = [
     check_example_25_1_exact, check_example_25_1_fp64, check_exercise_33_2,
     check_kv_cache_vectors, check_equal_scores_mean, check_single_and_two_keys,
@@ -627,5 +639,5 @@ ALL_CHECKS = [
     check_bias_broadcast, check_window_counts, check_window_single_key,
     check_window_as_bias, check_window_truncation_bound, check_window_split_merge,
     check_backward_finite_differences, check_backward_shift_direction, check_backward_identities,
-    check_backward_single_key, check_backward_library_autograd,
+    check_backward_single_key, check_backward_library_autograd, check_backward_sampled_matches_full,
 ]

@@ -31,6 +31,11 @@ BWD_CASES = [
     (torch.bfloat16, 1, 4, 2, 120, 180, 128, 64, False, 0, "none", 0.0, 0),
     (torch.bfloat16, 1, 2, 2, 260, 260, 128, 128, True, 0, "none", 0.0, 50),
     (torch.bfloat16, 1, 2, 1, 64, 90, 64, 64, True, -20, "rows", 0.3, 0),
+    # MFMA kernels: several 128-row / 128-key workgroup tiles, ragged tails
+    (torch.bfloat16, 1, 4, 1, 300, 450, 64, 64, True, 150, "none", 0.0, 0),
+    (torch.bfloat16, 2, 2, 2, 257, 257, 128, 128, True, 0, "none", 0.0, 130),
+    (torch.bfloat16, 1, 4, 4, 2048, 2048, 128, 128, True, 0, "none", 0.0, 0),
+    (torch.bfloat16, 1, 2, 2, 5, 700, 128, 128, True, 695, "none", 0.0, 0),
 ]
 
 
@@ -83,3 +88,28 @@ def test_backward_parity(case):
     tol = BWD_TOL[dt]
     for n, (mx, mean) in errs.items():
         assert mx <= tol["max"] and mean <= tol["mean"], f"{n}: {mx:.2e} / {mean:.2e} > {tol}"
+
+
+def test_backward_full_size_sampled():
+    """The causal prefill of the benchmark (B = 1, 32 heads, T = 8192,
+    d = 128) through the GPU forward and backward; dQ of sampled rows and
+    dK, dV of sampled keys against the oracle evaluated at those places."""
+    wl = inputs.make_config(2)
+    q, k, v, _ = to_dev(wl)
+    g = torch.randn(q.shape, generator=torch.Generator().manual_seed(4242)).to(torch.bfloat16)
+    d_o = g.to(q.device)
+    o, lse = attn.attn_fwd(q, k, v, scale=wl.scale, causal=True)
+    dq, dk, dv = attn.attn_bwd(q, k, v, o, lse, d_o, scale=wl.scale, causal=True)
+    torch.cuda.synchronize()
+    t = q.shape[2]
+    rows = [(0, h, i) for h in (0, 17) for i in (0, 1, 127, 128, 4095, 5000, t - 2, t - 1)]
+    keys = [(0, h, j) for h in (3, 31) for j in (0, 1, 64, 2047, 6000, t - 64, t - 1)]
+    rq, rk, rv = oracle.attention_backward_sampled(wl.q, wl.k, wl.v, g, rows=rows, keys=keys,
+                                                   scale=wl.scale, causal=True)
+    got_q = np.stack([f64(dq[r]) for r in rows])
+    got_k = np.stack([f64(dk[x]) for x in keys])
+    got_v = np.stack([f64(dv[x]) for x in keys])
+    for n, x, r in (("dq", got_q, rq), ("dk", got_k, rk), ("dv", got_v, rv)):
+        mx, mean = _rel(x, r)
+        print(n, "relative errors", mx, mean, flush=True)
+        assert mx <= BWD_TOL[torch.bfloat16]["max"] and mean <= BWD_TOL[torch.bfloat16]["mean"], n
