@@ -12,7 +12,8 @@ Prints one JSON line.  ``value`` is the prefill's algorithmic TFLOP/s
 KV GB/s (Q + K + V + O + LSE bytes once) is reported beside it.  After the
 timed steps, the same prefill and decode are timed once more with a sliding
 window (``--window``, keys j >= pos - W + 1) and reported under
-``sliding_window`` with their own algorithmic counts.
+``sliding_window``, and the prefill's backward (``attn_bwd``, upstream
+gradient N(0,1)) under ``backward``, each with its own algorithmic counts.
 """
 
 from __future__ import annotations
@@ -108,6 +109,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="heads of the prefill the CPU oracle baseline times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--window", type=int, default=4096,
                     help="sliding window of the extra windowed prefill/decode measurement (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -207,6 +209,35 @@ def main():
                                 "per_launch_flops": d_flops}},
         "cpu_baseline": None,
     }
+    if not args.no_backward:
+        gd = torch.randn(pq.shape, generator=torch.Generator().manual_seed(4242)).to(torch.bfloat16).to(dev)
+        run_prefill()                      # o and lse of the forward
+        gq, gk, gv = torch.empty_like(pq), torch.empty_like(pk), torch.empty_like(pv)
+        ws_b = torch.empty(32 * 8192 * 4, dtype=torch.uint8, device=dev)   # fp32 D per query row
+
+        def run_backward():
+            attn.attn_bwd(pq, pk, pv, po, pl, gd, scale=pre.scale, causal=True,
+                          d_q=gq, d_k=gk, d_v=gv, workspace=ws_b)
+
+        for _ in range(10):
+            run_backward()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for a_, b_ in evs:
+            a_.record(stream)
+            run_backward()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        b_ms = sum(a_.elapsed_time(b_) for a_, b_ in evs) / len(evs)
+        pairs, _, _ = prefill_counts(8192, 32, 1, 128, 128)
+        b_flops = 2 * (3 * 128 + 2 * 128) * pairs
+        b_t = b_flops / (b_ms * 1e-3) / 1e12
+        out["backward"] = {
+            "workload": "causal backward B=1 H=32 T=8192 d=128 (attn_bwd: D, dQ, dV, dK kernels)",
+            "ms": round(b_ms, 4), "value": round(b_t, 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(b_t, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(b_t / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                         "per_launch_flops": b_flops,
+                         "flops_per_pair": "2 (3 d_h + 2 d_v): recomputed scores, dP, dV, dQ, dK"}}
     if args.window > 0:
         w = args.window
         ww = torch.empty(attn.attn_decode_workspace_bytes(dq, dk, dv_, split_size=dec.split_size,
