@@ -18,7 +18,8 @@ Sources (the pages this follows; cited by page title and section / equation):
   eq 33.16 (the error bound against full attention); §33.3, "block size,
   parallelism and backward recomputation": eqs 33.6-33.8 (gradients from the
   recomputed probabilities) and Exercise 33.4 (the row-mean term from the
-  softmax Jacobian).
+  softmax Jacobian); §33.4, shape bucketing (the padding cost E[b(T)^2 - T^2]
+  that unpadded variable-length batches avoid).
 * "Generation and Caching with the Same Model" (aihero.club), the KV-cache
   section and its `causal_attention` listing: the [B, H, T, D] layout and the
   rule that query row i sits at logical position q_offset + i and sees the
@@ -53,6 +54,9 @@ notes of the repository):
 * A stored partial (o_s, lse_s) stands for the triple (lse_s, 1, o_s); a
   partial with lse_s = -inf is empty and is skipped, never subtracted.
 * Split-KV partials cover contiguous key ranges [s*S, min((s+1)*S, T_k)).
+* Unpadded variable-length batches: row i of packed sequence s sits at
+  q_offset + (L_k,s - L_q,s) + i, i.e. a sequence's rows are the last L_q
+  positions of its keys (the pages name the padding cost, not the layout).
 * Backward (eqs 33.6-33.8): the score scale replaces 1/sqrt(d_h) in eq 33.8
   (its trailing "." is a garble); the bias gets no gradient; illegal keys and
   fully masked rows have P = 0 and so contribute no gradient; the K and V
@@ -269,6 +273,39 @@ def split_partials(q, k, v, *, scale: float, causal: bool, q_offset: int,
                                 window=window)
         o_parts.append(o_s); l_parts.append(l_s)
     return np.stack(o_parts, axis=3), np.stack(l_parts, axis=3)
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, *, scale: float, causal: bool,
+                     q_offset: int = 0, window: int = 0):
+    """Unpadded variable-length batch (§33.4, shape bucketing: padding every
+    sequence to a bucket b(T) costs about E[b(T)^2 - T^2] extra score work for
+    dense attention; this is the result without that padding).
+
+    q [1, H_q, sum L_q, d_h], k and v [1, H_kv, sum L_k, *]: sequences packed
+    along the token axis; sequence s has query rows [cu_q[s], cu_q[s+1]) and
+    keys [cu_k[s], cu_k[s+1]).  Each sequence is exact attention on its own
+    rows and keys (``attention``), its rows being the last L_q positions of its
+    keys: row i of sequence s sits at q_offset + (L_k - L_q) + i.  Returns
+    (o [1, H_q, sum L_q, d_v], lse [1, H_q, sum L_q], n_legal likewise).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    cu_q = [int(x) for x in cu_q]
+    cu_k = [int(x) for x in cu_k]
+    h_q, t_q, d_v = q.shape[1], q.shape[2], v.shape[3]
+    o = np.zeros((1, h_q, t_q, d_v))
+    lse = np.full((1, h_q, t_q), NEG_INF)
+    n = np.zeros((1, h_q, t_q), dtype=np.int64)
+    for s in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[s], cu_q[s + 1], cu_k[s], cu_k[s + 1]
+        if q1 == q0:
+            continue
+        o_s, l_s, n_s = attention(q[:, :, q0:q1], k[:, :, k0:k1], v[:, :, k0:k1], scale=scale,
+                                  causal=causal, q_offset=q_offset + (k1 - k0) - (q1 - q0),
+                                  window=window)
+        o[:, :, q0:q1], lse[:, :, q0:q1], n[:, :, q0:q1] = o_s, l_s, n_s
+    return o, lse, n
 
 
 def attention_backward(q, k, v, d_o, *, scale: float, causal: bool,

@@ -630,6 +630,70 @@ def check_backward_sampled_matches_full(R):
         np.testing.assert_allclose(sv, np.array([dv[x] for x in keys]), rtol=0, atol=1e-13)
 
 
+# --- unpadded variable-length batches (§33.4, shape bucketing) ---------------
+
+def check_varlen_equals_padded(R):
+    """Packing the sequences equals the padded batch the pages describe: each
+    sequence padded to a bucket, padded keys masked by a -inf bias, the rows of
+    the sequence placed at the end of its key positions; the padded rows are
+    dropped.  Also the legal-pair saving: sum of n_legal over the padded rows
+    minus the unpadded sum is the work the bucket adds."""
+    rng = np.random.default_rng(30)
+    lq, lk = [3, 0, 7, 1, 5], [6, 4, 7, 9, 5]
+    hq, hkv, d_h, d_v, bucket = 4, 2, 5, 3, 10
+    cu_q = np.concatenate([[0], np.cumsum(lq)])
+    cu_k = np.concatenate([[0], np.cumsum(lk)])
+    q = rng.standard_normal((1, hq, cu_q[-1], d_h))
+    k = rng.standard_normal((1, hkv, cu_k[-1], d_h))
+    v = rng.standard_normal((1, hkv, cu_k[-1], d_v))
+    for causal, w in ((True, 0), (True, 3), (False, 0)):
+        o, lse, n = R.attention_varlen(q, k, v, cu_q, cu_k, scale=0.6, causal=causal, window=w)
+        nb = len(lq)
+        qp = np.zeros((nb, hq, bucket, d_h)); kp = np.zeros((nb, hkv, bucket, d_h))
+        vp = np.zeros((nb, hkv, bucket, d_v)); bias = np.zeros((nb, 1, bucket, bucket))
+        for s in range(nb):
+            # rows at the end of the bucket, keys at the start: row i sits at
+            # position (L_k - L_q) + i when q_offset = bucket - L_q and keys
+            # past L_k are masked; here every row is placed at bucket - L_q + i
+            # with keys shifted so that position p is key p.
+            qp[s, :, bucket - lq[s]:] = q[0, :, cu_q[s]:cu_q[s + 1]]
+            kp[s, :, :lk[s]] = k[0, :, cu_k[s]:cu_k[s + 1]]
+            vp[s, :, :lk[s]] = v[0, :, cu_k[s]:cu_k[s + 1]]
+            bias[s, 0, :, lk[s]:] = -np.inf
+        # q_offset per sequence differs (L_k - L_q - (bucket - L_q) = L_k - bucket),
+        # so run the padded batch one sequence at a time with that offset.
+        for s in range(nb):
+            op, lp, npad = R.attention(qp[s:s + 1], kp[s:s + 1], vp[s:s + 1], scale=0.6, causal=causal,
+                                       q_offset=lk[s] - bucket, bias=bias[s:s + 1], window=w)
+            rows = slice(bucket - lq[s], bucket)
+            np.testing.assert_allclose(o[0, :, cu_q[s]:cu_q[s + 1]], op[0, :, rows], rtol=0, atol=1e-14)
+            assert np.array_equal(np.isneginf(lse[0, :, cu_q[s]:cu_q[s + 1]]), np.isneginf(lp[0, :, rows]))
+            assert np.array_equal(n[0, :, cu_q[s]:cu_q[s + 1]], npad[0, :, rows])
+        if causal and w == 0:
+            # Row i of sequence s sees min(L_k - L_q + i + 1, L_k) keys.
+            want = np.concatenate([[min(lk[s] - lq[s] + i + 1, lk[s]) for i in range(lq[s])]
+                                   for s in range(nb)]).astype(np.int64)
+            assert np.array_equal(n[0, 0], want)
+
+
+def check_varlen_sequences_independent(R):
+    """Changing one sequence's values changes only that sequence's rows."""
+    rng = np.random.default_rng(31)
+    cu_q, cu_k = [0, 4, 9, 11], [0, 6, 9, 20]
+    q = rng.standard_normal((1, 2, 11, 4))
+    k = rng.standard_normal((1, 1, 20, 4))
+    v = rng.standard_normal((1, 1, 20, 3))
+    o1, l1, _ = R.attention_varlen(q, k, v, cu_q, cu_k, scale=0.5, causal=True)
+    v2 = v.copy(); v2[0, 0, 6:9] += 1.0
+    o2, l2, _ = R.attention_varlen(q, k, v2, cu_q, cu_k, scale=0.5, causal=True)
+    assert np.array_equal(l1, l2)
+    changed = np.any(o1 != o2, axis=(0, 1, 3))
+    # Sequence 1 has 5 rows over 3 keys: its first two rows sit before every
+    # key (causal), stay masked and cannot change.
+    assert not changed[:6].any() and changed[6:9].all() and not changed[9:].any()
+    assert np.isneginf(l1[0, :, 4:6]).all() and np.isfinite(l1[0, :, 6:9]).all()
+
+
 ALL_CHECKS = [
     check_example_25_1_exact, check_example_25_1_fp64, check_exercise_33_2,
     check_kv_cache_vectors, check_equal_scores_mean, check_single_and_two_keys,
@@ -640,4 +704,5 @@ ALL_CHECKS = [
     check_window_as_bias, check_window_truncation_bound, check_window_split_merge,
     check_backward_finite_differences, check_backward_shift_direction, check_backward_identities,
     check_backward_single_key, check_backward_library_autograd, check_backward_sampled_matches_full,
+    check_varlen_equals_padded, check_varlen_sequences_independent,
 ]

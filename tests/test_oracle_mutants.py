@@ -50,6 +50,9 @@ MUTANTS = {
                             "dk[b, kvh] += scale * (p.T @ q[b, hq])"),
     "bwd_gqa_overwrites": ("dv[b, kvh] += p.T @ g_o", "dv[b, kvh] = p.T @ g_o"),
     "bwd_dp_uses_k": ("g_p = g_o @ v[b, kvh].T", "g_p = g_o @ v[b, kvh].T[:, ::-1]"),
+    "varlen_top_left": ("causal=causal, q_offset=q_offset + (k1 - k0) - (q1 - q0),",
+                        "causal=causal, q_offset=q_offset,"),
+    "varlen_keys_shifted": ("k[:, :, k0:k1], v[:, :, k0:k1]", "k[:, :, q0:q0 + k1 - k0], v[:, :, k0:k1]"),
 }
 
 
