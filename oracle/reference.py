@@ -276,7 +276,7 @@ def split_partials(q, k, v, *, scale: float, causal: bool, q_offset: int,
 
 
 def attention_varlen(q, k, v, cu_q, cu_k, *, scale: float, causal: bool,
-                     q_offset: int = 0, window: int = 0):
+                     q_offset: int = 0, bias=None, window: int = 0):
     """Unpadded variable-length batch (§33.4, shape bucketing: padding every
     sequence to a bucket b(T) costs about E[b(T)^2 - T^2] extra score work for
     dense attention; this is the result without that padding).
@@ -285,8 +285,11 @@ def attention_varlen(q, k, v, cu_q, cu_k, *, scale: float, causal: bool,
     along the token axis; sequence s has query rows [cu_q[s], cu_q[s+1]) and
     keys [cu_k[s], cu_k[s+1]).  Each sequence is exact attention on its own
     rows and keys (``attention``), its rows being the last L_q positions of its
-    keys: row i of sequence s sits at q_offset + (L_k - L_q) + i.  Returns
-    (o [1, H_q, sum L_q, d_v], lse [1, H_q, sum L_q], n_legal likewise).
+    keys: row i of sequence s sits at q_offset + (L_k - L_q) + i.  The bias
+    (optional, [1, H_q or 1, sum L_q, sum L_k]) is indexed by packed row and
+    packed key, so sequence s reads its diagonal block.  Returns
+    (o [1, H_q, sum L_q, d_v], lse [1, H_q, sum L_q], n_legal likewise);
+    rows outside every sequence stay (0, -inf, 0).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -301,10 +304,44 @@ def attention_varlen(q, k, v, cu_q, cu_k, *, scale: float, causal: bool,
         q0, q1, k0, k1 = cu_q[s], cu_q[s + 1], cu_k[s], cu_k[s + 1]
         if q1 == q0:
             continue
+        b_s = None
+        if bias is not None:   # size-1 (broadcast) row or key dims are kept whole
+            bb = np.asarray(bias, dtype=np.float64)
+            b_s = bb[:, :, (slice(q0, q1) if bb.shape[2] != 1 else slice(None)),
+                     (slice(k0, k1) if bb.shape[3] != 1 else slice(None))]
         o_s, l_s, n_s = attention(q[:, :, q0:q1], k[:, :, k0:k1], v[:, :, k0:k1], scale=scale,
                                   causal=causal, q_offset=q_offset + (k1 - k0) - (q1 - q0),
-                                  window=window)
+                                  bias=b_s, window=window)
         o[:, :, q0:q1], lse[:, :, q0:q1], n[:, :, q0:q1] = o_s, l_s, n_s
+    return o, lse, n
+
+
+def attention_kvlens(q, k, v, kv_lens, *, scale: float, causal: bool,
+                     q_offset: int = 0, bias=None, window: int = 0):
+    """Per-batch KV lengths (the unpadded form of a batch of caches of
+    different lengths, §33.4 shape bucketing): batch b uses keys
+    [0, kv_lens[b]) of k and v [B, H_kv, T_k, *], and its row i sits at
+    q_offset + kv_lens[b] - T_q + i (the rows are the last T_q positions of
+    its keys).  Each batch is ``attention`` on its own keys; the bias, if any,
+    is [B, *, T_q, T_k] and only its first kv_lens[b] keys are read.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b_n, h_q, t_q, d_v = q.shape[0], q.shape[1], q.shape[2], v.shape[3]
+    o = np.zeros((b_n, h_q, t_q, d_v))
+    lse = np.full((b_n, h_q, t_q), NEG_INF)
+    n = np.zeros((b_n, h_q, t_q), dtype=np.int64)
+    for b in range(b_n):
+        n_k = int(kv_lens[b])
+        b_s = None
+        if bias is not None:   # a size-1 (broadcast) batch or key dim is kept whole
+            bb = np.asarray(bias, dtype=np.float64)
+            b_s = bb[(slice(b, b + 1) if bb.shape[0] != 1 else slice(None)), :, :,
+                     (slice(0, n_k) if bb.shape[3] != 1 else slice(None))]
+        o[b:b + 1], lse[b:b + 1], n[b:b + 1] = attention(
+            q[b:b + 1], k[b:b + 1, :, :n_k], v[b:b + 1, :, :n_k], scale=scale, causal=causal,
+            q_offset=q_offset + n_k - t_q, bias=b_s, window=window)
     return o, lse, n
 
 

@@ -646,8 +646,15 @@ def check_varlen_equals_padded(R):
     q = rng.standard_normal((1, hq, cu_q[-1], d_h))
     k = rng.standard_normal((1, hkv, cu_k[-1], d_h))
     v = rng.standard_normal((1, hkv, cu_k[-1], d_v))
-    for causal, w in ((True, 0), (True, 3), (False, 0)):
-        o, lse, n = R.attention_varlen(q, k, v, cu_q, cu_k, scale=0.6, causal=causal, window=w)
+    # A bias indexed by packed row and key, with -inf entries (masked pairs
+    # and one whole row), read only on each sequence's diagonal block.
+    mb = rng.standard_normal((1, hq, cu_q[-1], cu_k[-1]))
+    mb[rng.random(mb.shape) < 0.2] = -np.inf
+    mb[:, :, 2, :] = -np.inf
+    for causal, w, use_bias in ((True, 0, False), (True, 3, False), (False, 0, False),
+                                (True, 0, True), (False, 2, True)):
+        o, lse, n = R.attention_varlen(q, k, v, cu_q, cu_k, scale=0.6, causal=causal, window=w,
+                                       bias=mb if use_bias else None)
         nb = len(lq)
         qp = np.zeros((nb, hq, bucket, d_h)); kp = np.zeros((nb, hkv, bucket, d_h))
         vp = np.zeros((nb, hkv, bucket, d_v)); bias = np.zeros((nb, 1, bucket, bucket))
@@ -660,6 +667,10 @@ def check_varlen_equals_padded(R):
             kp[s, :, :lk[s]] = k[0, :, cu_k[s]:cu_k[s + 1]]
             vp[s, :, :lk[s]] = v[0, :, cu_k[s]:cu_k[s + 1]]
             bias[s, 0, :, lk[s]:] = -np.inf
+        if use_bias:
+            bias = np.broadcast_to(bias, (nb, hq, bucket, bucket)).copy()
+            for s in range(nb):
+                bias[s, :, bucket - lq[s]:, :lk[s]] = mb[0, :, cu_q[s]:cu_q[s + 1], cu_k[s]:cu_k[s + 1]]
         # q_offset per sequence differs (L_k - L_q - (bucket - L_q) = L_k - bucket),
         # so run the padded batch one sequence at a time with that offset.
         for s in range(nb):
@@ -669,7 +680,9 @@ def check_varlen_equals_padded(R):
             np.testing.assert_allclose(o[0, :, cu_q[s]:cu_q[s + 1]], op[0, :, rows], rtol=0, atol=1e-14)
             assert np.array_equal(np.isneginf(lse[0, :, cu_q[s]:cu_q[s + 1]]), np.isneginf(lp[0, :, rows]))
             assert np.array_equal(n[0, :, cu_q[s]:cu_q[s + 1]], npad[0, :, rows])
-        if causal and w == 0:
+        if use_bias:
+            assert np.isneginf(lse[0, :, 2]).all()   # the row the bias masks whole
+        if causal and w == 0 and not use_bias:
             # Row i of sequence s sees min(L_k - L_q + i + 1, L_k) keys.
             want = np.concatenate([[min(lk[s] - lq[s] + i + 1, lk[s]) for i in range(lq[s])]
                                    for s in range(nb)]).astype(np.int64)
@@ -694,6 +707,53 @@ def check_varlen_sequences_independent(R):
     assert np.isneginf(l1[0, :, 4:6]).all() and np.isfinite(l1[0, :, 6:9]).all()
 
 
+def check_varlen_key_bias_broadcast(R):
+    """A per-key bias [1, 1, 1, sum L_k] (one M_j per packed key) equals the
+    same values written out densely for every row."""
+    rng = np.random.default_rng(32)
+    cu_q, cu_k = [0, 3, 3, 8], [0, 5, 6, 14]
+    q = rng.standard_normal((1, 2, 8, 4))
+    k = rng.standard_normal((1, 2, 14, 4))
+    v = rng.standard_normal((1, 2, 14, 2))
+    mj = rng.standard_normal((1, 1, 1, 14))
+    mj[0, 0, 0, [1, 9]] = -np.inf
+    a = R.attention_varlen(q, k, v, cu_q, cu_k, scale=0.7, causal=True, bias=mj)
+    b = R.attention_varlen(q, k, v, cu_q, cu_k, scale=0.7, causal=True,
+                           bias=np.broadcast_to(mj, (1, 2, 8, 14)).copy())
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def check_kvlens_equals_padded(R):
+    """Per-batch KV lengths equal the padded cache the pages describe: keys
+    past L_b masked by a -inf bias, rows at positions L_b - T_q + i."""
+    rng = np.random.default_rng(33)
+    bsz, hq, hkv, t_q, t_k = 5, 4, 2, 3, 9
+    lens = [9, 0, 1, 4, 2]
+    q = rng.standard_normal((bsz, hq, t_q, 6))
+    k = rng.standard_normal((bsz, hkv, t_k, 6))
+    v = rng.standard_normal((bsz, hkv, t_k, 5))
+    for causal, w in ((True, 0), (False, 0), (True, 2)):
+        o, lse, n = R.attention_kvlens(q, k, v, lens, scale=0.4, causal=causal, window=w)
+        for b in range(bsz):
+            bias = np.zeros((1, 1, 1, t_k))
+            bias[..., lens[b]:] = -np.inf
+            op, lp, npad = R.attention(q[b:b + 1], k[b:b + 1], v[b:b + 1], scale=0.4, causal=causal,
+                                       q_offset=lens[b] - t_q, bias=bias, window=w)
+            np.testing.assert_allclose(o[b], op[0], rtol=0, atol=1e-14)
+            assert np.array_equal(np.isneginf(lse[b]), np.isneginf(lp[0]))
+            assert np.array_equal(n[b], npad[0])
+        assert np.isneginf(lse[1]).all() and (o[1] == 0).all()   # the empty cache
+        if causal and w == 0:
+            # Row i of batch b sees min(L_b - T_q + i + 1, L_b) keys (>= 0).
+            want = np.array([[max(0, min(L - t_q + i + 1, L)) for i in range(t_q)] for L in lens])
+            assert np.array_equal(n[:, 0], want)
+    # Full lengths: the dense problem with the rows at the end of the keys.
+    o, lse, _ = R.attention_kvlens(q, k, v, [t_k] * bsz, scale=0.4, causal=True)
+    od, ld, _ = R.attention(q, k, v, scale=0.4, causal=True, q_offset=t_k - t_q)
+    assert np.array_equal(o, od) and np.array_equal(lse, ld)
+
+
 ALL_CHECKS = [
     check_example_25_1_exact, check_example_25_1_fp64, check_exercise_33_2,
     check_kv_cache_vectors, check_equal_scores_mean, check_single_and_two_keys,
@@ -704,5 +764,6 @@ ALL_CHECKS = [
     check_window_as_bias, check_window_truncation_bound, check_window_split_merge,
     check_backward_finite_differences, check_backward_shift_direction, check_backward_identities,
     check_backward_single_key, check_backward_library_autograd, check_backward_sampled_matches_full,
-    check_varlen_equals_padded, check_varlen_sequences_independent,
+    check_varlen_equals_padded, check_varlen_sequences_independent, check_varlen_key_bias_broadcast,
+    check_kvlens_equals_padded,
 ]

@@ -53,6 +53,9 @@ MUTANTS = {
     "varlen_top_left": ("causal=causal, q_offset=q_offset + (k1 - k0) - (q1 - q0),",
                         "causal=causal, q_offset=q_offset,"),
     "varlen_keys_shifted": ("k[:, :, k0:k1], v[:, :, k0:k1]", "k[:, :, q0:q0 + k1 - k0], v[:, :, k0:k1]"),
+    "varlen_bias_rows_unshifted": ("(slice(q0, q1) if bb.shape[2] != 1", "(slice(0, q1 - q0) if bb.shape[2] != 1"),
+    "kvlens_top_left": ("q_offset=q_offset + n_k - t_q, bias=b_s", "q_offset=q_offset, bias=b_s"),
+    "kvlens_keeps_all_keys": ("k[b:b + 1, :, :n_k], v[b:b + 1, :, :n_k]", "k[b:b + 1], v[b:b + 1]"),
 }
 
 
