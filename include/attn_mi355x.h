@@ -46,14 +46,15 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 typedef enum {
   ATTN_OK = 0,
   ATTN_E_NULL = -1,        /* a required pointer is NULL */
   ATTN_E_SHAPE = -2,       /* negative size or window, H_q % H_kv != 0, bad split size */
   ATTN_E_DTYPE = -3,       /* unknown element type */
-  ATTN_E_UNSUPPORTED = -4, /* d_h or d_v outside [1, 256], non-finite scale */
+  ATTN_E_UNSUPPORTED = -4, /* d_h or d_v outside [1, 256], non-finite scale, or a
+                              variable-length field the entry point does not take */
   ATTN_E_STRIDE = -5,      /* a negative stride */
   ATTN_E_WORKSPACE = -6,   /* decode workspace missing or too small */
   ATTN_E_HIP = -7          /* the HIP runtime refused a launch */
@@ -89,6 +90,36 @@ typedef struct {
   int32_t dtype;          /* attn_dtype_t of Q, K, V and O */
   int32_t causal;         /* 0 or 1 */
   int32_t window;         /* sliding window W >= 1 keys, 0 = none; < 0 is an error */
+  /* Unpadded variable-length batches (§33.4, shape bucketing: padding every
+   * sequence to a bucket length b(T) costs dense attention about
+   * E[b(T)^2 - T^2] extra score work; these fields remove the padding).
+   *
+   * Packed sequences (attn_fwd only): with cu_seqlens_q != NULL, batch must
+   * be 1 and Q, O (rows) and K, V (keys) hold n_seqs sequences one after the
+   * other along T.  Sequence s owns query rows [cu_seqlens_q[s],
+   * cu_seqlens_q[s+1]) and keys [cu_seqlens_k[s], cu_seqlens_k[s+1]); with
+   * L_q and L_k its lengths, its row i sits at logical position
+   * q_offset + (L_k - L_q) + i (its rows are the last L_q positions of its
+   * keys) and sees only its own keys.  The bias, if any, is indexed by packed
+   * row and packed key (sequence s reads its diagonal block; stride 0
+   * broadcasts as usual, so bias_stride[2] = 0 gives one M_j per packed key).
+   * Both arrays are DEVICE int32 arrays of n_seqs + 1 entries, non-decreasing,
+   * from 0 up to T_q and T_k.  The library never reads them on the host; in a
+   * kernel each entry is clamped to [0, T] and a decreasing pair is an empty
+   * sequence, so no access leaves the tensors; rows outside every sequence are
+   * not written.  max_seqlen_q sizes the grid (one pass covers that many rows
+   * per sequence); any value >= 0 gives the same result, a smaller one than
+   * the longest L_q only costs time.  lse and n_legal are [1, H_q, T_q]. */
+  const int32_t* cu_seqlens_q; /* NULL = one dense batch */
+  const int32_t* cu_seqlens_k; /* required with cu_seqlens_q */
+  int64_t n_seqs;              /* >= 0 with cu_seqlens_q, else ignored */
+  int64_t max_seqlen_q;        /* >= 0 with cu_seqlens_q, else ignored */
+  /* Per-batch KV lengths (attn_fwd and attn_decode_splitkv, not with
+   * cu_seqlens_q): batch b uses keys [0, L_b) of K and V, L_b =
+   * seqlens_k[b] clamped to [0, T_k] in the kernel, and its row i sits at
+   * q_offset + L_b - T_q + i.  DEVICE int32 array of B entries; NULL = every
+   * batch uses all T_k keys at positions q_offset + i. */
+  const int32_t* seqlens_k;
 } attn_params_t;
 
 /* sizeof(attn_params_t), so that bindings can check their mirror of it. */
@@ -122,7 +153,8 @@ size_t attn_decode_workspace_bytes(const attn_params_t* p, int64_t split_size);
  * Same outputs and conventions as attn_fwd (no n_legal).  split_size >= 1.
  * workspace must hold attn_decode_workspace_bytes(p, split_size) bytes
  * (256-byte aligned); its contents after the call are the partials in the
- * layout above. */
+ * layout above.  With seqlens_k, ranges at or past L_b hold no legal key;
+ * cu_seqlens_q is not taken (ATTN_E_UNSUPPORTED). */
 int attn_decode_splitkv(const attn_params_t* p, int64_t split_size,
                         const void* q, const void* k_cache,
                         const void* v_cache, void* o, float* lse,
@@ -162,7 +194,8 @@ size_t attn_bwd_workspace_bytes(const attn_params_t* p);
  * share o_stride, d_q q_stride, d_k k_stride, d_v v_stride).  The bias (if
  * any) is a constant input and gets no gradient; rows with no legal key (LSE
  * = -inf) contribute nothing.  workspace: attn_bwd_workspace_bytes(p) bytes,
- * 256-byte aligned. */
+ * 256-byte aligned.  Variable-length fields (cu_seqlens_q, seqlens_k) are not
+ * taken: ATTN_E_UNSUPPORTED. */
 int attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v,
              const void* o, const float* lse, const void* d_o, void* d_q, void* d_k,
              void* d_v, void* workspace, size_t workspace_bytes, void* stream);

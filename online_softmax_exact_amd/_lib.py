@@ -39,6 +39,9 @@ class Params(ctypes.Structure):
         ("bias_stride", ctypes.c_int64 * 4), ("bias", ctypes.c_void_p),
         ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
         ("window", ctypes.c_int32),
+        ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+        ("n_seqs", ctypes.c_int64), ("max_seqlen_q", ctypes.c_int64),
+        ("seqlens_k", ctypes.c_void_p),
     ]
 
 
@@ -112,7 +115,15 @@ def _outer_strides(t: torch.Tensor, name: str):
     return tuple(int(x) for x in t.stride()[:3])
 
 
-def make_params(q, k, v, o, *, scale, causal, q_offset, bias, window=0) -> Params:
+def _int32_vector(t, n, name, device):
+    if t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] != n or not t.is_contiguous() \
+            or t.device != device:
+        raise ValueError(f"{name} must be a contiguous int32 vector of {n} entries on the device of q")
+    return t.data_ptr()
+
+
+def make_params(q, k, v, o, *, scale, causal, q_offset, bias, window=0, cu_seqlens_q=None,
+                cu_seqlens_k=None, max_seqlen_q=None, seqlens_k=None) -> Params:
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype float32 or bfloat16")
     b, hq, tq, dh = q.shape
@@ -140,6 +151,19 @@ def make_params(q, k, v, o, *, scale, causal, q_offset, bias, window=0) -> Param
         full = bias.expand(b, hq, tq, k.shape[2])
         p.bias_stride[:] = tuple(int(x) for x in full.stride())
         p.bias = full.data_ptr() if full.numel() else None
+    if cu_seqlens_q is not None or cu_seqlens_k is not None:
+        if cu_seqlens_q is None or cu_seqlens_k is None or b != 1:
+            raise ValueError("packed sequences need cu_seqlens_q and cu_seqlens_k and batch 1")
+        n = cu_seqlens_q.shape[0] - 1 if cu_seqlens_q.dim() == 1 else -1
+        if n < 0:
+            raise ValueError("cu_seqlens_q must hold n_seqs + 1 offsets")
+        p.cu_seqlens_q = _int32_vector(cu_seqlens_q, n + 1, "cu_seqlens_q", q.device)
+        p.cu_seqlens_k = _int32_vector(cu_seqlens_k, n + 1, "cu_seqlens_k", q.device)
+        p.n_seqs = n
+        # Without a caller's bound the grid covers the longest possible sequence.
+        p.max_seqlen_q = tq if max_seqlen_q is None else int(max_seqlen_q)
+    if seqlens_k is not None:
+        p.seqlens_k = _int32_vector(seqlens_k, b, "seqlens_k", q.device)
     return p
 
 
@@ -155,13 +179,22 @@ def _outputs(q, d_v, out, lse):
 
 
 def attn_fwd(q, k, v, *, scale=None, causal=True, q_offset=0, bias=None, window=0,
-             out=None, lse=None, return_n_legal=False, stream=None):
+             out=None, lse=None, return_n_legal=False, cu_seqlens_q=None, cu_seqlens_k=None,
+             max_seqlen_q=None, seqlens_k=None, stream=None):
     """Exact attention; returns (o, lse) or (o, lse, n_legal).  ``window`` > 0
-    keeps only keys j >= q_offset + i - window + 1 for row i."""
+    keeps only keys j >= q_offset + i - window + 1 for row i.
+
+    Packed sequences: q, k, v of batch 1 with ``cu_seqlens_q`` /
+    ``cu_seqlens_k`` (int32 device offsets, n_seqs + 1 each); row i of a
+    sequence sits at q_offset + (L_k - L_q) + i and sees only its own keys.
+    ``max_seqlen_q`` (a host int) sizes the grid; it defaults to T_q.
+    Per-batch KV lengths: ``seqlens_k`` (int32 device, one per batch); batch b
+    uses keys [0, L_b) and its row i sits at q_offset + L_b - T_q + i."""
     lib = load_library()
     out, lse = _outputs(q, v.shape[3], out, lse)
     p = make_params(q, k, v, out, scale=scale, causal=causal, q_offset=q_offset, bias=bias,
-                    window=window)
+                    window=window, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
+                    max_seqlen_q=max_seqlen_q, seqlens_k=seqlens_k)
     n_legal = None
     if return_n_legal:
         n_legal = torch.empty(lse.shape, dtype=torch.int32, device=q.device)
@@ -170,30 +203,41 @@ def attn_fwd(q, k, v, *, scale=None, causal=True, q_offset=0, bias=None, window=
     return (out, lse, n_legal) if return_n_legal else (out, lse)
 
 
+def _decode_offset(q, k_cache, q_offset, seqlens_k):
+    """Default query position: the newest T_q positions of the cache (with
+    per-batch lengths the library already places rows at the end of each)."""
+    if q_offset is not None:
+        return q_offset
+    return 0 if seqlens_k is not None else k_cache.shape[2] - q.shape[2]
+
+
 def attn_decode_workspace_bytes(q, k_cache, v_cache, *, split_size, scale=None,
-                                causal=True, q_offset=None, bias=None, window=0) -> int:
+                                causal=True, q_offset=None, bias=None, window=0,
+                                seqlens_k=None) -> int:
     lib = load_library()
     o = torch.empty((q.shape[0], q.shape[1], q.shape[2], v_cache.shape[3]),
                     dtype=q.dtype, device="meta")
-    off = k_cache.shape[2] - q.shape[2] if q_offset is None else q_offset
+    off = _decode_offset(q, k_cache, q_offset, seqlens_k)
     p = make_params(q, k_cache, v_cache, o, scale=scale, causal=causal, q_offset=off, bias=bias,
-                    window=window)
+                    window=window, seqlens_k=seqlens_k)
     return int(lib.attn_decode_workspace_bytes(ctypes.byref(p), int(split_size)))
 
 
 def attn_decode_splitkv(q, k_cache, v_cache, *, split_size, scale=None, causal=True,
-                        q_offset=None, bias=None, window=0, workspace=None, out=None, lse=None,
-                        stream=None):
+                        q_offset=None, bias=None, window=0, seqlens_k=None, workspace=None,
+                        out=None, lse=None, stream=None):
     """Split-KV decode + merge; returns (o, lse, workspace).
 
-    ``q_offset`` defaults to T_k - T_q (the queries are the newest positions).
+    ``q_offset`` defaults to T_k - T_q (the queries are the newest positions),
+    or to 0 with ``seqlens_k`` (int32 device KV length per batch: batch b
+    uses keys [0, L_b), its rows at q_offset + L_b - T_q + i).
     ``workspace`` is a uint8 device tensor of at least
     ``attn_decode_workspace_bytes`` bytes; allocated here when None."""
     lib = load_library()
     out, lse = _outputs(q, v_cache.shape[3], out, lse)
-    off = k_cache.shape[2] - q.shape[2] if q_offset is None else q_offset
+    off = _decode_offset(q, k_cache, q_offset, seqlens_k)
     p = make_params(q, k_cache, v_cache, out, scale=scale, causal=causal, q_offset=off, bias=bias,
-                    window=window)
+                    window=window, seqlens_k=seqlens_k)
     need = int(lib.attn_decode_workspace_bytes(ctypes.byref(p), int(split_size)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

@@ -62,6 +62,17 @@ int validate(const attn_params_t* p, Problem* pb) {
       return ATTN_E_STRIDE;
   for (int i = 0; i < 4; ++i)
     if (p->bias_stride[i] < 0) return ATTN_E_STRIDE;
+  // Variable-length fields: cu_seqlens entries and KV lengths are int32.
+  if (p->cu_seqlens_q != nullptr) {
+    if (p->cu_seqlens_k == nullptr) return ATTN_E_NULL;
+    if (p->batch != 1 || p->seqlens_k != nullptr) return ATTN_E_SHAPE;
+    if (p->n_seqs < 0 || p->n_seqs >= (int64_t(1) << 30)) return ATTN_E_SHAPE;
+    if (p->max_seqlen_q < 0 || p->max_seqlen_q > kMaxDim) return ATTN_E_SHAPE;
+    if (p->t_q >= (int64_t(1) << 31) || p->t_k >= (int64_t(1) << 31)) return ATTN_E_SHAPE;
+  } else if (p->cu_seqlens_k != nullptr) {
+    return ATTN_E_SHAPE;   // key offsets without row offsets
+  }
+  if (p->seqlens_k != nullptr && p->t_k >= (int64_t(1) << 31)) return ATTN_E_SHAPE;
 
   pb->batch = p->batch; pb->heads_q = p->heads_q; pb->heads_kv = p->heads_kv;
   pb->t_q = p->t_q; pb->t_k = p->t_k; pb->d_h = p->d_h; pb->d_v = p->d_v;
@@ -76,6 +87,11 @@ int validate(const attn_params_t* p, Problem* pb) {
   pb->causal = p->causal;
   pb->group = static_cast<int32_t>(p->heads_q / p->heads_kv);
   pb->window = p->window;
+  pb->cu_q = p->cu_seqlens_q;
+  pb->cu_k = p->cu_seqlens_q != nullptr ? p->cu_seqlens_k : nullptr;
+  pb->n_seqs = p->cu_seqlens_q != nullptr ? p->n_seqs : 0;
+  pb->max_seqlen_q = p->cu_seqlens_q != nullptr ? p->max_seqlen_q : 0;
+  pb->kv_lens = p->seqlens_k;
   return ATTN_OK;
 }
 
@@ -108,7 +124,7 @@ const char* attn_strerror(int status) {
     case ATTN_E_NULL: return "a required pointer is NULL";
     case ATTN_E_SHAPE: return "invalid shape (negative size or window, heads_q not a multiple of heads_kv, bad flag or split size)";
     case ATTN_E_DTYPE: return "unknown element type";
-    case ATTN_E_UNSUPPORTED: return "unsupported head size (d_h and d_v must be 1..256) or non-finite scale";
+    case ATTN_E_UNSUPPORTED: return "unsupported head size (d_h and d_v must be 1..256), non-finite scale, or a variable-length field this entry point does not take";
     case ATTN_E_STRIDE: return "negative stride";
     case ATTN_E_WORKSPACE: return "decode workspace missing or too small";
     case ATTN_E_HIP: return "HIP runtime error at launch";
@@ -123,6 +139,7 @@ int attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v
   if (st != ATTN_OK) return st;
   if ((st = check_pointers(pb, q, k, v, o, lse)) != ATTN_OK) return st;
   if (pb.batch == 0 || pb.t_q == 0) return ATTN_OK;
+  if (pb.cu_q != nullptr && pb.n_seqs == 0) return ATTN_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_fast_fwd(pb, p->dtype, q, k, v, o, lse, n_legal, s, &st)) return st;
   return hip_status(launch_generic(pb, p->dtype, q, k, v, o, lse, n_legal, 0, nullptr, nullptr, s));
@@ -142,6 +159,7 @@ int attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v
   int st = validate(p, &pb);
   if (st != ATTN_OK) return st;
   if ((st = check_pointers(pb, q, k, v, o, lse)) != ATTN_OK) return st;
+  if (pb.cu_q != nullptr || pb.kv_lens != nullptr) return ATTN_E_UNSUPPORTED;
   const bool rows = numel_nonzero(pb.batch, pb.heads_q, pb.t_q, 1);
   const bool keys = numel_nonzero(pb.batch, pb.heads_kv, pb.t_k, 1);
   if (rows && (d_o == nullptr || d_q == nullptr)) return ATTN_E_NULL;
@@ -173,6 +191,7 @@ int attn_decode_splitkv(const attn_params_t* p, int64_t split_size, const void* 
   if (st != ATTN_OK) return st;
   if (split_size < 1) return ATTN_E_SHAPE;
   if ((st = check_pointers(pb, q, k_cache, v_cache, o, lse)) != ATTN_OK) return st;
+  if (pb.cu_q != nullptr) return ATTN_E_UNSUPPORTED;
   if (pb.batch == 0 || pb.t_q == 0) return ATTN_OK;
   const SplitLayout L = split_layout(pb, split_size);
   if (workspace == nullptr || workspace_bytes < L.total) return ATTN_E_WORKSPACE;

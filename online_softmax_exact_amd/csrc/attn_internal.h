@@ -22,6 +22,14 @@ struct Problem {
   int32_t causal;
   int32_t group;      // heads_q / heads_kv
   int64_t window;     // sliding window (keys j >= q_offset + i - window + 1), 0 = none
+  // Variable-length batches (device arrays, never read on the host).
+  // Packed: sequence s owns rows [cu_q[s], cu_q[s+1]) and keys [cu_k[s],
+  // cu_k[s+1]), row i at q_offset + (L_k - L_q) + i.  Per-batch KV lengths:
+  // batch b uses keys [0, kv_lens[b]), row i at q_offset + kv_lens[b] - T_q + i.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int64_t n_seqs, max_seqlen_q;
+  const int32_t* kv_lens;
 };
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -73,6 +73,7 @@ struct FArgs {
   int32_t split0, n_active;   // the grid covers splits [split0, split0 + n_active)
   float scale_log2;
   int32_t causal;
+  const int32_t* kv_lens;     // per-batch KV lengths (device), NULL = T_k for every batch
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -104,6 +105,14 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
   const int rg = static_cast<int>(rest % a.n_rg);    rest /= a.n_rg;
   const int kvh = static_cast<int>(rest % a.heads_kv);
   const int b = static_cast<int>(rest / a.heads_kv);
+  // Per-batch KV length L_b (clamped to [0, T_k]): keys [0, L_b), rows at
+  // q_offset + L_b - T_q + i.
+  if (a.kv_lens != nullptr) {
+    const int raw = a.kv_lens[b];
+    const int lk = raw < 0 ? 0 : (raw > a.t_k ? a.t_k : raw);
+    a.q_offset += lk - a.t_q;
+    a.t_k = lk;
+  }
 
   // This lane's row: n = 32 rg + lr -> query head kvh * group + n / T_q, row n % T_q.
   const int n = rg * kRows + lr;
@@ -355,7 +364,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 bool eligible(const Problem& pb, int dtype, const void* q, const void* k, const void* v,
               const void* o) {
-  if (dtype != ATTN_BF16 || pb.bias != nullptr) return false;
+  if (dtype != ATTN_BF16 || pb.bias != nullptr || pb.cu_q != nullptr) return false;
   if (!((pb.d_h == 64 || pb.d_h == 128) && (pb.d_v == 64 || pb.d_v == 128))) return false;
   if (!(pb.scale_log2 > 0.0f)) return false;
   if (pb.t_q >= (int64_t(1) << 30) || pb.t_k >= (int64_t(1) << 30)) return false;
@@ -401,6 +410,7 @@ FArgs make_args(const Problem& pb, const void* q, const void* k, const void* v) 
   a.n_rg = (a.rows + kRows - 1) / kRows;
   a.scale_log2 = pb.scale_log2;
   a.causal = pb.causal;
+  a.kv_lens = pb.kv_lens;
   return a;
 }
 
@@ -445,7 +455,11 @@ bool launch_fewrow_partials(const Problem& pb, int dtype, const void* q, const v
   if (pb.causal && pb.q_offset + pb.t_q < k_hi) k_hi = pb.q_offset + pb.t_q;
   if (pb.window > 0 && pb.q_offset - pb.window + 1 > k_lo) k_lo = pb.q_offset - pb.window + 1;
   int64_t s0 = 0, s1 = 0;
-  if (k_hi > k_lo) {
+  if (pb.kv_lens != nullptr) {
+    // Positions depend on lengths the host does not read: every split runs
+    // (one past a batch's length only writes its empty partial).
+    s1 = L.n_splits;
+  } else if (k_hi > k_lo) {
     s0 = k_lo / L.split_size;
     s1 = (k_hi - 1) / L.split_size + 1;
     if (s1 > L.n_splits) s1 = L.n_splits;

@@ -33,8 +33,33 @@ __global__ __launch_bounds__(256) void generic_kernel(
     const int64_t hq = rest % pb.heads_q;
     const int64_t b = rest / pb.heads_q;
     const int64_t i = rb * kWaves + wave;
-    const bool row_ok = i < pb.t_q;
+    bool row_ok = i < pb.t_q;
     const int64_t kvh = hq / pb.group;
+
+    // This row's keys [k0, k0 + t_k) and logical position.  Packed sequences:
+    // the sequence holding row i (binary search over the clamped row offsets;
+    // a row outside every sequence is not written); per-batch KV lengths: the
+    // batch's own length; rows sit at the end of their keys in both.
+    int64_t k0 = 0, t_k = pb.t_k, pos = pb.q_offset + i;
+    if (pb.cu_q != nullptr && row_ok) {
+      auto cq = [&](int64_t x) { const int64_t y = pb.cu_q[x]; return y < 0 ? 0 : (y > pb.t_q ? pb.t_q : y); };
+      auto ck = [&](int64_t x) { const int64_t y = pb.cu_k[x]; return y < 0 ? 0 : (y > pb.t_k ? pb.t_k : y); };
+      int64_t s_lo = 0, s_hi = pb.n_seqs - 1;   // last sequence starting at or before row i
+      while (s_lo < s_hi) {
+        const int64_t mid = (s_lo + s_hi + 1) / 2;
+        if (cq(mid) <= i) s_lo = mid; else s_hi = mid - 1;
+      }
+      const int64_t q0 = cq(s_lo), q1 = cq(s_lo + 1) > q0 ? cq(s_lo + 1) : q0;
+      k0 = ck(s_lo);
+      const int64_t k1 = ck(s_lo + 1) > k0 ? ck(s_lo + 1) : k0;
+      row_ok = i >= q0 && i < q1;
+      t_k = k1 - k0;
+      pos = pb.q_offset + t_k - (q1 - q0) + (i - q0);
+    } else if (pb.kv_lens != nullptr) {
+      const int64_t raw = pb.kv_lens[b];
+      t_k = raw < 0 ? 0 : (raw > pb.t_k ? pb.t_k : raw);
+      pos = pb.q_offset + t_k - pb.t_q + i;
+    }
 
     const T* qrow = q + b * pb.qs[0] + hq * pb.qs[1] + i * pb.qs[2];
     for (int d = lane; d < kMaxD; d += 64)
@@ -42,14 +67,14 @@ __global__ __launch_bounds__(256) void generic_kernel(
     __syncthreads();
 
     if (row_ok) {
-      const int64_t pos = pb.q_offset + i;
       int64_t lo = s * split_size;
-      int64_t hi = split_size < pb.t_k - lo ? lo + split_size : pb.t_k;
+      int64_t hi = split_size < t_k - lo ? lo + split_size : t_k;
       if (pb.causal && pos + 1 < hi) hi = pos + 1;  // causal block skipping
       if (pb.window > 0 && pos - pb.window + 1 > lo) lo = pos - pb.window + 1;  // sliding window
-      const T* kbase = k + b * pb.ks[0] + kvh * pb.ks[1];
-      const T* vbase = v + b * pb.vs[0] + kvh * pb.vs[1];
-      const float* brow = HAS_BIAS ? pb.bias + b * pb.bs[0] + hq * pb.bs[1] + i * pb.bs[2] : nullptr;
+      const T* kbase = k + b * pb.ks[0] + kvh * pb.ks[1] + k0 * pb.ks[2];
+      const T* vbase = v + b * pb.vs[0] + kvh * pb.vs[1] + k0 * pb.vs[2];
+      const float* brow =
+          HAS_BIAS ? pb.bias + b * pb.bs[0] + hq * pb.bs[1] + i * pb.bs[2] + k0 * pb.bs[3] : nullptr;
 
       bool has = false;        // "no legal key yet" (Algorithm 33.1)
       float m2 = 0.0f;         // running max, base-2 domain, valid iff has

@@ -79,7 +79,7 @@ struct Cfg {
   static constexpr int V_DMA = V_BYTES / 1024 / kWaves;
 };
 
-template <int DH, int DV, bool BIAS, bool COUNT>
+template <int DH, int DV, bool BIAS, bool COUNT, bool VAR>
 __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kernel(Args a) {
   // The host pass only needs this kernel's signature (its launch stub); the
   // body is device code (it otherwise drops the stub of this template).
@@ -102,19 +102,58 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
   // 8, XCD x works through heads x, x + 8, ... one at a time, so the K/V of
   // the head it is on stays in its L2.
   const int bid = blockIdx.x;
-  int qt, bh;
+  int idx, bh;   // idx = 0 for the first-dispatched (heaviest) query tile
   if (PREFILL_XCD_MAP && a.batch_heads % 8 == 0) {
     const int xcd = bid & 7, local = bid >> 3;
-    qt = a.n_qtiles - 1 - local % a.n_qtiles;
+    idx = local % a.n_qtiles;
     bh = xcd + 8 * (local / a.n_qtiles);
   } else {
-    qt = a.n_qtiles - 1 - bid / a.batch_heads;
+    idx = bid / a.batch_heads;
     bh = bid % a.batch_heads;
   }
   const int b = bh / a.heads_q;
   const int hq = bh % a.heads_q;
   const int kvh = hq / a.group;
+  int qt = a.n_qtiles - 1 - idx;
 
+  // Variable-length batches.  Packed sequences: grid slot idx is sequence
+  // idx % n_seqs, round r = idx / n_seqs, i.e. every sequence's last (most
+  // keys, when causal) tile first; the workgroup then computes tiles
+  // n_tiles - 1 - r, that minus rounds, ... so any sequence length is
+  // covered.  Pointers are moved to the sequence's first row and key and the
+  // sizes become the sequence's own, with its rows at the end of its keys.
+  // Per-batch KV lengths: the batch's keys are [0, L_b) and its rows sit at
+  // q_offset + L_b - T_q + i.
+  const int32_t t_q_all = a.t_q;   // rows per head in LSE / n_legal
+  int32_t row_base = 0;            // packed row of this sequence's row 0
+  if (VAR) {
+    if (a.cu_q != nullptr) {
+      const int sq = idx % a.n_seqs, r = idx / a.n_seqs;
+      const int q0 = clamp_len(a.cu_q[sq], a.t_q);
+      const int q1 = max(q0, clamp_len(a.cu_q[sq + 1], a.t_q));
+      const int k0 = clamp_len(a.cu_k[sq], a.t_k);
+      const int k1 = max(k0, clamp_len(a.cu_k[sq + 1], a.t_k));
+      qt = (q1 - q0 + kBr - 1) / kBr - 1 - r;
+      if (qt < 0) return;   // whole workgroup: nothing of this sequence is left for it
+      a.q += static_cast<int64_t>(q0) * a.qs[2];
+      a.o += static_cast<int64_t>(q0) * a.os[2];
+      a.k += static_cast<int64_t>(k0) * a.ks[2];
+      a.v += static_cast<int64_t>(k0) * a.vs[2];
+      if (BIAS) a.bias += static_cast<int64_t>(q0) * a.bs[2] + static_cast<int64_t>(k0) * a.bs[3];
+      row_base = q0;
+      a.q_offset += (k1 - k0) - (q1 - q0);
+      a.t_q = q1 - q0;
+      a.t_k = k1 - k0;
+    } else {
+      const int lk = clamp_len(a.kv_lens[b], a.t_k);
+      a.q_offset += lk - a.t_q;
+      a.t_k = lk;
+    }
+  }
+
+  // One query tile (128 rows of one head); a packed-sequence workgroup runs
+  // it for several tiles in turn.
+  auto tile_body = [&](const int qt) {
   const int row0 = qt * kBr + wave * 32;   // first row of this wave
   const int row = row0 + lr;               // this lane's row
   const bool row_ok = row < a.t_q;
@@ -503,24 +542,40 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     }
   }
   if (h == 0) {
-    const int64_t ridx = (static_cast<int64_t>(b) * a.heads_q + hq) * a.t_q + row;
+    const int64_t ridx = (static_cast<int64_t>(b) * a.heads_q + hq) * t_q_all + row_base + row;
     a.lse[ridx] = has ? (m2 + fast_log2(l_row)) * kLn2 : -INFINITY;
     if (COUNT) a.n_legal[ridx] = count;
+  }
+  };   // tile_body
+
+  if (VAR && a.cu_q != nullptr) {
+    for (; qt >= 0; qt -= a.rounds) {
+      tile_body(qt);
+      __syncthreads();   // LDS rings are refilled by the next tile's prologue
+    }
+  } else {
+    tile_body(qt);
   }
 #endif
 }
 
-template <int DH, int DV, bool BIAS, bool COUNT>
+template <int DH, int DV, bool BIAS, bool COUNT, bool VAR>
 hipError_t launch_cfg(const Args& a, int64_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<DH, DV, BIAS, COUNT>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((prefill_kernel<DH, DV, BIAS, COUNT, VAR>), dim3(static_cast<unsigned>(blocks)),
                      dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
+template <int DH, int DV, bool VAR>
+hipError_t launch_var(const Args& a, int64_t blocks, bool bias, bool count, hipStream_t s) {
+  if (bias)
+    return count ? launch_cfg<DH, DV, true, true, VAR>(a, blocks, s) : launch_cfg<DH, DV, true, false, VAR>(a, blocks, s);
+  return count ? launch_cfg<DH, DV, false, true, VAR>(a, blocks, s) : launch_cfg<DH, DV, false, false, VAR>(a, blocks, s);
+}
+
 template <int DH, int DV>
-hipError_t launch_dims(const Args& a, int64_t blocks, bool bias, bool count, hipStream_t s) {
-  if (bias) return count ? launch_cfg<DH, DV, true, true>(a, blocks, s) : launch_cfg<DH, DV, true, false>(a, blocks, s);
-  return count ? launch_cfg<DH, DV, false, true>(a, blocks, s) : launch_cfg<DH, DV, false, false>(a, blocks, s);
+hipError_t launch_dims(const Args& a, int64_t blocks, bool bias, bool count, bool var, hipStream_t s) {
+  return var ? launch_var<DH, DV, true>(a, blocks, bias, count, s) : launch_var<DH, DV, false>(a, blocks, bias, count, s);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -542,7 +597,17 @@ bool launch_prefill_mfma(const Problem& pb, int dtype, const void* q, const void
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return false;
   for (int i = 0; i < 3; ++i)
     if ((pb.qs[i] | pb.ks[i] | pb.vs[i] | pb.os[i]) & 7) return false;
-  const int64_t n_qtiles = (pb.t_q + kBr - 1) / kBr;
+  // Packed sequences: `rounds` query tiles per sequence in the grid (from the
+  // caller's longest-sequence bound; longer sequences loop).
+  const bool packed = pb.cu_q != nullptr;
+  int64_t rounds = 1;
+  if (packed) {
+    rounds = (pb.max_seqlen_q + kBr - 1) / kBr;
+    if (rounds < 1) rounds = 1;
+    const int64_t cap = (pb.t_q + kBr - 1) / kBr;   // no sequence has more tiles than this
+    if (rounds > cap) rounds = cap > 0 ? cap : 1;
+  }
+  const int64_t n_qtiles = packed ? pb.n_seqs * rounds : (pb.t_q + kBr - 1) / kBr;
   const int64_t blocks = n_qtiles * pb.batch * pb.heads_q;
   if (blocks >= (int64_t(1) << 31) || pb.batch * pb.heads_q >= (int64_t(1) << 30)) return false;
 
@@ -568,14 +633,20 @@ bool launch_prefill_mfma(const Problem& pb, int dtype, const void* q, const void
   a.batch_heads = static_cast<int32_t>(pb.batch * pb.heads_q);
   a.scale_log2 = pb.scale_log2;
   a.causal = pb.causal;
+  a.cu_q = pb.cu_q;
+  a.cu_k = pb.cu_k;
+  a.kv_lens = pb.kv_lens;
+  a.n_seqs = static_cast<int32_t>(pb.n_seqs);
+  a.rounds = static_cast<int32_t>(rounds);
 
   const bool bias = pb.bias != nullptr;
   const bool count = n_legal != nullptr;
+  const bool var = packed || pb.kv_lens != nullptr;
   hipError_t e;
-  if (pb.d_h == 128 && pb.d_v == 128) e = launch_dims<128, 128>(a, blocks, bias, count, stream);
-  else if (pb.d_h == 64 && pb.d_v == 128) e = launch_dims<64, 128>(a, blocks, bias, count, stream);
-  else if (pb.d_h == 128 && pb.d_v == 64) e = launch_dims<128, 64>(a, blocks, bias, count, stream);
-  else e = launch_dims<64, 64>(a, blocks, bias, count, stream);
+  if (pb.d_h == 128 && pb.d_v == 128) e = launch_dims<128, 128>(a, blocks, bias, count, var, stream);
+  else if (pb.d_h == 64 && pb.d_v == 128) e = launch_dims<64, 128>(a, blocks, bias, count, var, stream);
+  else if (pb.d_h == 128 && pb.d_v == 64) e = launch_dims<128, 64>(a, blocks, bias, count, var, stream);
+  else e = launch_dims<64, 64>(a, blocks, bias, count, var, stream);
   *status = e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
   return true;
 }

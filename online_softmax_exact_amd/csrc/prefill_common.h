@@ -34,7 +34,17 @@ struct Args {
   int32_t t_q, t_k, heads_q, group, n_qtiles, batch_heads;
   float scale_log2;
   int32_t causal;
+  // Variable-length batches: packed sequences (cu_q, cu_k of n_seqs + 1
+  // entries; the grid holds `rounds` query tiles per sequence and head) or
+  // per-batch KV lengths (kv_lens); both NULL for a dense batch.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* kv_lens;
+  int32_t n_seqs, rounds;
 };
+
+// x clamped to [0, n] (device-side length and offset arrays are never trusted).
+__device__ __forceinline__ int clamp_len(int x, int n) { return x < 0 ? 0 : (x > n ? n : x); }
 
 // LDS layouts.  Tiles are written by buffer_load ... lds (each wave
 // instruction fills 1 KB in lane order), so rows cannot be padded; instead the

@@ -186,3 +186,43 @@ def make_random(batch: int, heads_q: int, heads_kv: int, t_q: int, t_k: int,
                     scale=default_scale(d_h) if scale is None else scale,
                     causal=causal, q_offset=q_offset, bias=m,
                     split_size=split_size)
+
+
+def varlen_lengths(n: int, max_len: int, seed: int):
+    """n sequence lengths uniform in [1, max_len]: the first draw of
+    ``padded_bias``'s generator, so workload 5's seed gives its own lengths."""
+    gen = torch.Generator("cpu").manual_seed(derive_seed(seed, 4, 0))
+    return [int(x) for x in torch.randint(1, max_len + 1, (n,), generator=gen)]
+
+
+def offsets(lengths):
+    """Packed offsets [0, L_0, L_0 + L_1, ...] as an int32 tensor."""
+    out = [0]
+    for n in lengths:
+        out.append(out[-1] + int(n))
+    return torch.tensor(out, dtype=torch.int32)
+
+
+def make_packed(lengths_q, lengths_k, heads_q: int, heads_kv: int, d_h: int, d_v: int, *,
+                dtype=torch.bfloat16, seed: int = 0, bias: str = "none",
+                masked_frac: float = 0.0):
+    """Packed variable-length batch: q [1, H_q, sum L_q, d_h], k [1, H_kv,
+    sum L_k, d_h], v [1, H_kv, sum L_k, d_v] (N(0, 1), drawn like
+    ``make_random``) with int32 offsets cu_q, cu_k.  ``bias``: "none";
+    "packed" (fp32 N(0, 1) [1, H_q, sum L_q, sum L_k], indexed by packed row
+    and key); "keys" ([1, 1, 1, sum L_k], one value per packed key).
+    ``masked_frac`` of the bias entries are -inf.  Returns
+    (q, k, v, bias, cu_q, cu_k)."""
+    cu_q, cu_k = offsets(lengths_q), offsets(lengths_k)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    q = _draw((1, heads_q, tq, d_h), seed, 0, dtype)
+    k = _draw((1, heads_kv, tk, d_h), seed, 1, dtype)
+    v = _draw((1, heads_kv, tk, d_v), seed, 2, dtype)
+    m = None
+    if bias != "none":
+        gen = torch.Generator("cpu").manual_seed(derive_seed(seed, 3, 0))
+        shape = {"packed": (1, heads_q, tq, tk), "keys": (1, 1, 1, tk)}[bias]
+        m = torch.randn(shape, generator=gen, dtype=torch.float32)
+        if masked_frac > 0:
+            m[torch.rand(shape, generator=gen) < masked_frac] = NEG_INF
+    return q, k, v, m, cu_q, cu_k

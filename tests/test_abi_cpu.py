@@ -37,8 +37,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_params_layout(lib):
-    assert lib.attn_abi_version() == 2
-    assert lib.attn_params_sizeof() == ctypes.sizeof(_lib.Params) == 216
+    assert lib.attn_abi_version() == 3
+    assert lib.attn_params_sizeof() == ctypes.sizeof(_lib.Params) == 256
 
 
 def test_strerror(lib):
@@ -163,3 +163,75 @@ def test_bwd_rejects(lib):
     # Nothing to do: no rows and no keys.
     assert call(params=good_params(batch=0), q=None, k=None, v=None, o=None, lse=None, d_o=None,
                 d_q=None, d_k=None, d_v=None, ws=None, nbytes=0) == 0
+
+
+def packed_params(**kw):
+    """One packed batch: 3 sequences in T_q = 8 rows and T_k = 16 keys."""
+    base = dict(batch=1, cu_seqlens_q=0x200000, cu_seqlens_k=0x300000, n_seqs=3, max_seqlen_q=4)
+    base.update(kw)
+    return good_params(**base)
+
+
+def test_varlen_rejects(lib):
+    # Packed sequences: key offsets required, batch 1, no per-batch lengths,
+    # sizes that fit the int32 offsets, n_seqs and max_seqlen_q >= 0.
+    assert fwd(lib, packed_params(cu_seqlens_k=None)) == -1
+    assert fwd(lib, packed_params(batch=2)) == -2
+    assert fwd(lib, packed_params(seqlens_k=0x400000)) == -2
+    assert fwd(lib, packed_params(n_seqs=-1)) == -2
+    assert fwd(lib, packed_params(max_seqlen_q=-1)) == -2
+    assert fwd(lib, packed_params(t_k=1 << 31)) == -2
+    # Key offsets without row offsets are ambiguous.
+    assert fwd(lib, good_params(cu_seqlens_k=0x300000)) == -2
+    # Per-batch lengths are int32.
+    assert fwd(lib, good_params(seqlens_k=0x400000, t_k=1 << 31)) == -2
+    # No sequences: nothing to do (device arrays are never read on the host).
+    assert fwd(lib, packed_params(n_seqs=0)) == 0
+
+
+def test_varlen_unsupported_entry_points(lib):
+    # Split-KV decode takes per-batch lengths but not packed sequences; the
+    # backward takes neither.
+    p = packed_params()
+    need = lib.attn_decode_workspace_bytes(ctypes.byref(p), 4)
+    assert lib.attn_decode_splitkv(ctypes.byref(p), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need,
+                                   None) == -4
+    for params in (packed_params(), good_params(seqlens_k=0x400000)):
+        need = lib.attn_bwd_workspace_bytes(ctypes.byref(params))
+        assert lib.attn_bwd(ctypes.byref(params), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, FAKE, need, None) == -4
+
+
+def test_binding_varlen_arguments():
+    # The binding checks the offset vectors before anything reaches the library.
+    import torch
+    q = torch.zeros(1, 2, 10, 64)
+    kv = torch.zeros(1, 2, 12, 64)
+    cu = torch.tensor([0, 4, 10], dtype=torch.int32)
+    cuk = torch.tensor([0, 5, 12], dtype=torch.int32)
+    p = _lib.make_params(q, kv, kv, q, scale=None, causal=True, q_offset=0, bias=None,
+                         cu_seqlens_q=cu, cu_seqlens_k=cuk, max_seqlen_q=6)
+    assert (p.n_seqs, p.max_seqlen_q) == (2, 6)
+    assert p.cu_seqlens_q == cu.data_ptr() and p.cu_seqlens_k == cuk.data_ptr()
+    assert _lib.make_params(q, kv, kv, q, scale=None, causal=True, q_offset=0, bias=None,
+                            cu_seqlens_q=cu, cu_seqlens_k=cuk).max_seqlen_q == 10
+    with pytest.raises(ValueError):
+        _lib.make_params(q, kv, kv, q, scale=None, causal=True, q_offset=0, bias=None,
+                         cu_seqlens_q=cu, cu_seqlens_k=cuk[:2])
+    with pytest.raises(ValueError):
+        _lib.make_params(q, kv, kv, q, scale=None, causal=True, q_offset=0, bias=None,
+                         cu_seqlens_q=cu.long(), cu_seqlens_k=cuk)
+    with pytest.raises(ValueError):
+        _lib.make_params(q, kv, kv, q, scale=None, causal=True, q_offset=0, bias=None,
+                         cu_seqlens_q=cu)
+    q2 = torch.zeros(2, 2, 10, 64)
+    kv2 = torch.zeros(2, 2, 12, 64)
+    with pytest.raises(ValueError):
+        _lib.make_params(q2, kv2, kv2, q2, scale=None, causal=True, q_offset=0, bias=None,
+                         cu_seqlens_q=cu, cu_seqlens_k=cuk)
+    lens = torch.tensor([3, 12], dtype=torch.int32)
+    assert _lib.make_params(q2, kv2, kv2, q2, scale=None, causal=True, q_offset=0, bias=None,
+                            seqlens_k=lens).seqlens_k == lens.data_ptr()
+    with pytest.raises(ValueError):
+        _lib.make_params(q2, kv2, kv2, q2, scale=None, causal=True, q_offset=0, bias=None,
+                         seqlens_k=lens[:1])

@@ -44,3 +44,17 @@ def test_chunked_draw_is_thread_independent(monkeypatch):
     b = inputs._draw((3, 5, 300, 40), 9, 1, torch.bfloat16)
     assert torch.equal(a, b)
     assert abs(float(a.float().mean())) < 0.01 and abs(float(a.float().std()) - 1) < 0.01
+
+
+def test_varlen_lengths_are_the_padded_workload_lengths():
+    _, lengths, _ = inputs.padded_bias(4, 64, 64, 123)
+    assert inputs.varlen_lengths(4, 64, 123) == lengths
+
+
+def test_make_packed_layout():
+    q, k, v, m, cu_q, cu_k = inputs.make_packed([3, 0, 5], [4, 2, 5], 4, 2, 8, 6, seed=1,
+                                                bias="keys", masked_frac=0.3)
+    assert cu_q.tolist() == [0, 3, 3, 8] and cu_k.tolist() == [0, 4, 6, 11]
+    assert q.shape == (1, 4, 8, 8) and k.shape == (1, 2, 11, 8) and v.shape == (1, 2, 11, 6)
+    assert m.shape == (1, 1, 1, 11) and m.dtype == torch.float32
+    assert cu_q.dtype == torch.int32
