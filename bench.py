@@ -12,8 +12,10 @@ Prints one JSON line.  ``value`` is the prefill's algorithmic TFLOP/s
 KV GB/s (Q + K + V + O + LSE bytes once) is reported beside it.  After the
 timed steps, the same prefill and decode are timed once more with a sliding
 window (``--window``, keys j >= pos - W + 1) and reported under
-``sliding_window``, and the prefill's backward (``attn_bwd``, upstream
-gradient N(0,1)) under ``backward``, each with its own algorithmic counts.
+``sliding_window``, the prefill's backward (``attn_bwd``, upstream
+gradient N(0,1)) under ``backward``, and unpadded variable-length batches
+(packed prefill against the padded batch, decode over per-batch KV lengths)
+under ``varlen``, each with its own algorithmic counts.
 """
 
 from __future__ import annotations
@@ -61,6 +63,83 @@ def window_decode_counts(batch, hq, hkv, t_q, w, d_h, d_v):
     return kv + qo, 2 * (d_h + d_v) * batch * hq * t_q * w
 
 
+def varlen_counts(lengths, heads: int, d_h: int, d_v: int):
+    """Packed causal prefill with every sequence's rows at its own keys
+    (L_q = L_k = L): sum L (L + 1) / 2 legal pairs per head; Q, K, V, O and
+    LSE of the packed tokens are moved once."""
+    pairs = heads * sum(n * (n + 1) // 2 for n in lengths)
+    tokens = sum(lengths)
+    return 2 * (d_h + d_v) * pairs, heads * tokens * (2 * d_h + 2 * d_v) * 2 + heads * tokens * 4
+
+
+def kvlens_decode_bytes(lengths, hq, hkv, t_q, d_h, d_v):
+    """Decode over per-batch KV lengths: each batch's first L_b K/V rows of
+    every KV head read once, plus Q, O and LSE."""
+    kv = hkv * sum(lengths) * (d_h + d_v) * 2
+    return kv + len(lengths) * hq * t_q * ((d_h + d_v) * 2 + 4)
+
+
+def varlen_section(torch, attn, inputs, dev, dk, dv_, dq, dec, ws, timed):
+    """Unpadded variable-length batches: the padded workload's eight lengths
+    (uniform in [1, 4096]) packed, against the same sequences padded to 4096
+    with a -inf bias on the padded keys; and the cached decode with per-batch
+    KV lengths uniform in [1, 32768]."""
+    lengths = inputs.varlen_lengths(8, 4096, 1005)
+    hq, d_h, d_v, t = 16, 64, 128, 4096
+    q, k, v, _, cu_q, cu_k = inputs.make_packed(lengths, lengths, hq, hq, d_h, d_v, seed=1005)
+    q, k, v, cu_q, cu_k = (x.to(dev) for x in (q, k, v, cu_q, cu_k))
+    o = torch.empty(1, hq, q.shape[2], d_v, dtype=q.dtype, device=dev)
+    lse = torch.empty(1, hq, q.shape[2], device=dev)
+    scale = inputs.default_scale(d_h)
+    packed_ms = timed(lambda: attn.attn_fwd(q, k, v, scale=scale, causal=True, out=o, lse=lse,
+                                            cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
+                                            max_seqlen_q=max(lengths)))
+    qp = torch.zeros(8, hq, t, d_h, dtype=q.dtype, device=dev)
+    kp = torch.zeros_like(qp)
+    vp = torch.zeros(8, hq, t, d_v, dtype=q.dtype, device=dev)
+    bias = torch.zeros(8, 1, 1, t, device=dev)
+    for b, n in enumerate(lengths):
+        s0 = int(cu_q[b])
+        qp[b, :, :n], kp[b, :, :n], vp[b, :, :n] = q[0, :, s0:s0 + n], k[0, :, s0:s0 + n], v[0, :, s0:s0 + n]
+        bias[b, 0, 0, n:] = float("-inf")
+    op = torch.empty(8, hq, t, d_v, dtype=q.dtype, device=dev)
+    lp = torch.empty(8, hq, t, device=dev)
+    padded_ms = timed(lambda: attn.attn_fwd(qp, kp, vp, scale=scale, causal=True, bias=bias, out=op, lse=lp))
+    flops, bytes_ = varlen_counts(lengths, hq, d_h, d_v)
+    pt = flops / (packed_ms * 1e-3) / 1e12
+    del qp, kp, vp, op, lp
+
+    kv_lens = inputs.varlen_lengths(16, 32768, 1003)
+    lens_t = torch.tensor(kv_lens, dtype=torch.int32, device=dev)
+    od = torch.empty(dq.shape[:3] + (dv_.shape[3],), dtype=dq.dtype, device=dev)
+    ld = torch.empty(dq.shape[:3], device=dev)
+    dec_ms = timed(lambda: attn.attn_decode_splitkv(dq, dk, dv_, split_size=dec.split_size, scale=dec.scale,
+                                                    causal=True, seqlens_k=lens_t, workspace=ws, out=od,
+                                                    lse=ld))
+    d_bytes = kvlens_decode_bytes(kv_lens, 32, 8, 1, 128, 128)
+    dg = d_bytes / (dec_ms * 1e-3) / 1e9
+    return {
+        "prefill": {"workload": f"packed causal prefill, 8 sequences of lengths {lengths}, H=16, "
+                                "d_h=64, d_v=128 (attn_fwd with cu_seqlens)",
+                    "ms": round(packed_ms, 4), "value": round(pt, 2), "unit": "TFLOP/s",
+                    "padded_ms": round(padded_ms, 4),
+                    "padded": "the same sequences padded to 4096 with a -inf bias on padded keys",
+                    "speedup_vs_padded": round(padded_ms / packed_ms, 3),
+                    "roofline": {"bound": "mfma", "achieved": round(pt, 2), "peak": PEAK_BF16_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(pt / PEAK_BF16_TFLOPS, 4),
+                                 "traffic": recorded_traffic("packed_prefill"),
+                                 "per_launch_flops": flops, "per_launch_bytes": bytes_}},
+        "decode": {"workload": "GQA split-KV decode B=16 Hq=32 Hkv=8 Tk<=32768 d=128 S=512 with per-batch "
+                               f"KV lengths uniform in [1, 32768] (sum {sum(kv_lens)}; attn_decode_splitkv "
+                               "with seqlens_k)",
+                   "ms": round(dec_ms, 4), "value": round(dg, 1), "unit": "GB/s",
+                   "roofline": {"bound": "hbm", "achieved": round(dg, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(dg / PEAK_HBM_GBS, 4),
+                                "traffic": recorded_traffic("kvlens_decode_partials"),
+                                "per_launch_bytes": d_bytes}},
+    }
+
+
 def recorded_traffic(key: str):
     """HBM bytes per launch of kernel `key` from the committed rocprofv3 byte
     counters (profiles/traffic.json), or None when the kernel's sources have
@@ -76,6 +155,13 @@ def recorded_traffic(key: str):
         with open(os.path.join(ROOT, "online_softmax_exact_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return int(rec["traffic_bytes"]) if h.hexdigest() == rec["source_sha256"] else None
+
+
+def backward_traffic():
+    """HBM bytes of one attn_bwd call: its dQ, dV and dK kernels' recorded
+    traffic (the D kernel reads O and dO once), or None if any is stale."""
+    parts = [recorded_traffic(k) for k in ("bwd_dq", "bwd_dv", "bwd_dk")]
+    return None if None in parts else sum(parts)
 
 
 def cpu_baseline(wl, heads: int):
@@ -110,6 +196,8 @@ def main():
                     help="heads of the prefill the CPU oracle baseline times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the variable-length (packed prefill, per-batch KV length decode) measurement")
     ap.add_argument("--window", type=int, default=4096,
                     help="sliding window of the extra windowed prefill/decode measurement (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -235,26 +323,28 @@ def main():
             "workload": "causal backward B=1 H=32 T=8192 d=128 (attn_bwd: D, dQ, dV, dK kernels)",
             "ms": round(b_ms, 4), "value": round(b_t, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(b_t, 2), "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(b_t / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                         "unit": "TFLOP/s", "frac": round(b_t / PEAK_BF16_TFLOPS, 4),
+                         "traffic": backward_traffic(),
                          "per_launch_flops": b_flops,
                          "flops_per_pair": "2 (3 d_h + 2 d_v): recomputed scores, dP, dV, dQ, dK"}}
+    def timed(fn, n=20):
+        """Average of n launches of fn (after 10 untimed), HIP events on the stream."""
+        for _ in range(10):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a_, b_ in evs:
+            a_.record(stream)
+            fn()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        return sum(a_.elapsed_time(b_) for a_, b_ in evs) / n
+
     if args.window > 0:
         w = args.window
         ww = torch.empty(attn.attn_decode_workspace_bytes(dq, dk, dv_, split_size=dec.split_size,
                                                           scale=dec.scale, q_offset=dec.q_offset,
                                                           window=w), dtype=torch.uint8, device=dev)
-
-        def timed(fn, n=20):
-            for _ in range(10):
-                fn()
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(n)]
-            for a_, b_ in evs:
-                a_.record(stream)
-                fn()
-                b_.record(stream)
-            torch.cuda.synchronize()
-            return sum(a_.elapsed_time(b_) for a_, b_ in evs) / n
 
         wp_ms = timed(lambda: attn.attn_fwd(pq, pk, pv, scale=pre.scale, causal=True, window=w,
                                             out=po, lse=pl))
@@ -282,6 +372,9 @@ def main():
                                     "traffic": None, "per_launch_bytes": wd_bytes,
                                     "per_launch_flops": wd_flops}},
         }
+    if not args.no_varlen:
+        print("bench: variable-length batches", file=sys.stderr, flush=True)
+        out["varlen"] = varlen_section(torch, attn, inputs, dev, dk, dv_, dq, dec, ws, timed)
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)

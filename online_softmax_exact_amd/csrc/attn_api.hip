@@ -207,7 +207,7 @@ int attn_decode_splitkv(const attn_params_t* p, int64_t split_size, const void* 
   const int64_t out_strides[3] = {pb.os[0], pb.os[1], pb.os[2]};
   return hip_status(launch_merge(L.rows, L.n_splits, pb.d_v, ws_o, L.n_splits * pb.d_v, pb.d_v,
                                  ws_l, L.n_splits, 1, p->dtype, o, pb.heads_q, pb.t_q,
-                                 out_strides, lse, s));
+                                 out_strides, lse, s, pb.kv_lens, split_size, pb.t_k));
 }
 
 int attn_merge_states(int64_t n_rows, int64_t n_states, int64_t d_v, const float* o_states,

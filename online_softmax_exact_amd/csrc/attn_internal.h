@@ -65,7 +65,9 @@ hipError_t launch_merge(int64_t n_rows, int64_t n_states, int64_t d_v,
                         int64_t lse_row_stride, int64_t lse_state_stride,
                         int out_dtype, void* o_out, int64_t rows_per_b,
                         int64_t rows_per_h, const int64_t out_strides[3],
-                        float* lse_out, hipStream_t stream);
+                        float* lse_out, hipStream_t stream,
+                        const int32_t* kv_lens = nullptr, int64_t split_size = 1,
+                        int64_t t_k = 0);
 
 // ---- device helpers -------------------------------------------------------
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)

@@ -71,6 +71,7 @@ struct FArgs {
   int64_t split_size;       // keys per work item
   int32_t t_q, t_k, heads_q, heads_kv, group, rows, n_rg, n_splits;
   int32_t split0, n_active;   // the grid covers splits [split0, split0 + n_active)
+  int32_t batch;
   float scale_log2;
   int32_t causal;
   const int32_t* kv_lens;     // per-batch KV lengths (device), NULL = T_k for every batch
@@ -88,7 +89,7 @@ __device__ __forceinline__ u32x2 tr_read(const lds_char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-template <int DH, int DV, bool SPLIT>
+template <int DH, int DV, bool SPLIT, bool VAR>
 __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
   using C = FCfg<DH, DV>;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
@@ -99,17 +100,36 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
   const int h = lane >> 5;
   const int lr = lane & 31;
 
-  // blockIdx -> (b, kvh, row group, split); the split varies fastest.
-  int64_t rest = blockIdx.x;
-  const int s = a.split0 + static_cast<int>(rest % a.n_active); rest /= a.n_active;
-  const int rg = static_cast<int>(rest % a.n_rg);    rest /= a.n_rg;
-  const int kvh = static_cast<int>(rest % a.heads_kv);
-  const int b = static_cast<int>(rest / a.heads_kv);
+  // blockIdx -> work item (group g = (b, row group, kvh), split s), split
+  // fastest.  Consecutive workgroups go round-robin to the 8 XCDs, so XCD x
+  // gets the splits s = x mod 8: balanced when every split holds keys.  With
+  // per-batch KV lengths only a prefix of each batch's splits does, so there
+  // (group count a multiple of 8) XCD x takes the groups g = x mod 8 (with 8
+  // KV heads: KV head x of every batch) with all their splits, split fastest:
+  // the same work on every XCD whatever the lengths, and the workgroups on
+  // one XCD stream different offsets of their K/V rows.
+  const int64_t n_groups = static_cast<int64_t>(a.n_rg) * a.heads_kv * a.batch;
+  int64_t g;
+  int s;
+  if (VAR && n_groups % 8 == 0) {
+    const int64_t x = blockIdx.x % 8, j = blockIdx.x / 8;
+    g = (j / a.n_active) * 8 + x;
+    s = a.split0 + static_cast<int>(j % a.n_active);
+  } else {
+    g = blockIdx.x / a.n_active;
+    s = a.split0 + static_cast<int>(blockIdx.x % a.n_active);
+  }
+  const int kvh = static_cast<int>(g % a.heads_kv);
+  const int rg = static_cast<int>((g / a.heads_kv) % a.n_rg);
+  const int b = static_cast<int>(g / a.heads_kv / a.n_rg);
   // Per-batch KV length L_b (clamped to [0, T_k]): keys [0, L_b), rows at
   // q_offset + L_b - T_q + i.
-  if (a.kv_lens != nullptr) {
+  if (VAR) {
     const int raw = a.kv_lens[b];
     const int lk = raw < 0 ? 0 : (raw > a.t_k ? a.t_k : raw);
+    // A range at or past L_b holds no key of this batch: nothing to write
+    // (the merge reads only the first ceil(L_b / split_size) partials).
+    if (SPLIT && static_cast<int64_t>(s) * a.split_size >= lk) return;
     a.q_offset += lk - a.t_q;
     a.t_k = lk;
   }
@@ -347,8 +367,12 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
 
 template <int DH, int DV, bool SPLIT>
 hipError_t launch_f(const FArgs& a, int64_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(kThreads), 0, stream, a);
+  if (a.kv_lens != nullptr)
+    hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT, true>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT, false>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -411,6 +435,7 @@ FArgs make_args(const Problem& pb, const void* q, const void* k, const void* v) 
   a.scale_log2 = pb.scale_log2;
   a.causal = pb.causal;
   a.kv_lens = pb.kv_lens;
+  a.batch = static_cast<int32_t>(pb.batch);
   return a;
 }
 

@@ -16,16 +16,32 @@ namespace {
 
 constexpr int kRows = 4;
 
+// Partials of row r that were written: all n_states, or with per-batch KV
+// lengths only the first ceil(L_b / split_size) (later ranges hold no key of
+// the batch and are not written), b = r / rows_per_b.
+struct StateCount {
+  const int32_t* kv_lens;
+  int64_t split_size, t_k, rows_per_b;
+  __device__ int64_t of(int64_t r, int64_t n_states) const {
+    if (kv_lens == nullptr) return n_states;
+    const int64_t raw = kv_lens[r / rows_per_b];
+    const int64_t len = raw < 0 ? 0 : (raw > t_k ? t_k : raw);
+    const int64_t n = (len + split_size - 1) / split_size;
+    return n < n_states ? n : n_states;
+  }
+};
+
 template <typename TO>
 __global__ __launch_bounds__(256) void merge_kernel(
     int64_t n_rows, int64_t n_states, int64_t d_v,
     const float* __restrict__ o_states, int64_t o_rs, int64_t o_ss,
     const float* __restrict__ lse_states, int64_t l_rs, int64_t l_ss,
     TO* __restrict__ out, int64_t heads, int64_t t_rows, int64_t os0,
-    int64_t os1, int64_t os2, float* __restrict__ lse_out) {
+    int64_t os1, int64_t os2, float* __restrict__ lse_out, StateCount sc) {
   const int lane = threadIdx.x & 63;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * kRows + (threadIdx.x >> 6);
   if (r >= n_rows) return;
+  n_states = sc.of(r, n_states);
   const float* lrow = lse_states + r * l_rs;
   const float* orow = o_states + r * o_rs;
   const int64_t ii = r % t_rows;
@@ -73,13 +89,14 @@ __global__ __launch_bounds__(256) void merge_wide_kernel(
     int64_t n_states, int d_v, const float* __restrict__ o_states, int64_t o_rs, int64_t o_ss,
     const float* __restrict__ lse_states, int64_t l_rs, int64_t l_ss, TO* __restrict__ out,
     int64_t heads, int64_t t_rows, int64_t os0, int64_t os1, int64_t os2,
-    float* __restrict__ lse_out) {
+    float* __restrict__ lse_out, StateCount sc) {
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   __shared__ float red[4];
   __shared__ __attribute__((aligned(16))) float part[256 * 4];
   __shared__ float lpart[256];
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
+  n_states = sc.of(r, n_states);
   const float* lrow = lse_states + r * l_rs;
   const float* orow = o_states + r * o_rs;
 
@@ -145,8 +162,10 @@ hipError_t launch_merge(int64_t n_rows, int64_t n_states, int64_t d_v,
                         int64_t lse_row_stride, int64_t lse_state_stride,
                         int out_dtype, void* o_out, int64_t heads,
                         int64_t t_rows, const int64_t out_strides[3],
-                        float* lse_out, hipStream_t stream) {
+                        float* lse_out, hipStream_t stream, const int32_t* kv_lens,
+                        int64_t split_size, int64_t t_k) {
   if (n_rows == 0) return hipSuccess;
+  const StateCount sc{kv_lens, split_size > 0 ? split_size : 1, t_k, heads * t_rows};
   const bool wide = d_v % 4 == 0 && o_row_stride % 4 == 0 && o_state_stride % 4 == 0 &&
                     (reinterpret_cast<uintptr_t>(o_states) & 15) == 0 && n_rows < (int64_t(1) << 31);
   if (wide) {
@@ -154,12 +173,12 @@ hipError_t launch_merge(int64_t n_rows, int64_t n_states, int64_t d_v,
       hipLaunchKernelGGL(merge_wide_kernel<float>, dim3(static_cast<unsigned>(n_rows)), dim3(256), 0, stream,
                          n_states, static_cast<int>(d_v), o_states, o_row_stride, o_state_stride, lse_states,
                          lse_row_stride, lse_state_stride, static_cast<float*>(o_out), heads, t_rows,
-                         out_strides[0], out_strides[1], out_strides[2], lse_out);
+                         out_strides[0], out_strides[1], out_strides[2], lse_out, sc);
     else
       hipLaunchKernelGGL(merge_wide_kernel<uint16_t>, dim3(static_cast<unsigned>(n_rows)), dim3(256), 0, stream,
                          n_states, static_cast<int>(d_v), o_states, o_row_stride, o_state_stride, lse_states,
                          lse_row_stride, lse_state_stride, static_cast<uint16_t*>(o_out), heads, t_rows,
-                         out_strides[0], out_strides[1], out_strides[2], lse_out);
+                         out_strides[0], out_strides[1], out_strides[2], lse_out, sc);
     return hipGetLastError();
   }
   const int64_t blocks = (n_rows + kRows - 1) / kRows;
@@ -167,12 +186,12 @@ hipError_t launch_merge(int64_t n_rows, int64_t n_states, int64_t d_v,
     hipLaunchKernelGGL(merge_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
                        n_rows, n_states, d_v, o_states, o_row_stride, o_state_stride, lse_states,
                        lse_row_stride, lse_state_stride, static_cast<float*>(o_out), heads, t_rows,
-                       out_strides[0], out_strides[1], out_strides[2], lse_out);
+                       out_strides[0], out_strides[1], out_strides[2], lse_out, sc);
   } else {
     hipLaunchKernelGGL(merge_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
                        n_rows, n_states, d_v, o_states, o_row_stride, o_state_stride, lse_states,
                        lse_row_stride, lse_state_stride, static_cast<uint16_t*>(o_out), heads, t_rows,
-                       out_strides[0], out_strides[1], out_strides[2], lse_out);
+                       out_strides[0], out_strides[1], out_strides[2], lse_out, sc);
   }
   return hipGetLastError();
 }

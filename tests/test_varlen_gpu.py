@@ -195,9 +195,14 @@ def test_kvlens_parity(case):
     lens_t = torch.tensor(lens, dtype=torch.int32, device=dd)
     m = None if wl.bias is None else wl.bias.to(dd)
     if entry == "decode":
+        # Workspace pre-filled with NaN bytes: slots of ranges past a batch's
+        # length are not written, so the merge must not read them.
+        nbytes = attn.attn_decode_workspace_bytes(wl.q, wl.k, wl.v, split_size=split, scale=wl.scale,
+                                                  causal=causal, window=w, seqlens_k=lens_t.cpu())
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=dd)
         o, lse, _ = attn.attn_decode_splitkv(wl.q.to(dd), wl.k.to(dd), wl.v.to(dd), split_size=split,
                                              scale=wl.scale, causal=causal, window=w, seqlens_k=lens_t,
-                                             bias=m)
+                                             bias=m, workspace=ws)
         n = None
         o2 = lse2 = None
     else:
