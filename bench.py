@@ -23,6 +23,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -140,6 +141,31 @@ def varlen_section(torch, attn, inputs, dev, dk, dv_, dq, dec, ws, timed):
     }
 
 
+def achievable_section(torch, dev, timed, p_tflops, d_gbs):
+    """Ceilings measured in the same session, as context for the fractions of
+    the published peaks: a library bf16 GEMM (torch.matmul, hipBLASLt) for the
+    matrix cores under a dense MFMA load, and a 1 GiB device-to-device copy
+    (reads and writes 1 GiB each) for HBM."""
+    n = 8192
+    g = torch.Generator(device="cpu").manual_seed(7)
+    a = torch.randn(n, n, generator=g).to(torch.bfloat16).to(dev)
+    b = torch.randn(n, n, generator=g).to(torch.bfloat16).to(dev)
+    c = torch.empty(n, n, dtype=torch.bfloat16, device=dev)
+    mm_ms = timed(lambda: torch.matmul(a, b, out=c))
+    mm_t = 2 * n ** 3 / (mm_ms * 1e-3) / 1e12
+    del a, b, c
+    src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    cp_ms = timed(lambda: dst.copy_(src))
+    cp_g = 2 * (1 << 30) / (cp_ms * 1e-3) / 1e9
+    del src, dst
+    return {"gemm_bf16": {"shape": "8192 x 8192 x 8192 (torch.matmul)", "ms": round(mm_ms, 4),
+                          "value": round(mm_t, 1), "unit": "TFLOP/s",
+                          "prefill_over_gemm": round(p_tflops / mm_t, 4)},
+            "copy": {"bytes": 2 * (1 << 30), "ms": round(cp_ms, 4), "value": round(cp_g, 1), "unit": "GB/s",
+                     "decode_over_copy": round(d_gbs / cp_g, 4)}}
+
+
 def recorded_traffic(key: str):
     """HBM bytes per launch of kernel `key` from the committed rocprofv3 byte
     counters (profiles/traffic.json), or None when the kernel's sources have
@@ -196,6 +222,8 @@ def main():
                     help="heads of the prefill the CPU oracle baseline times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-achievable", action="store_true",
+                    help="skip the same-session ceilings (library bf16 GEMM, device copy)")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the variable-length (packed prefill, per-batch KV length decode) measurement")
     ap.add_argument("--window", type=int, default=4096,
@@ -283,7 +311,9 @@ def main():
                                "GQA split-KV decode B=16 Hq=32 Hkv=8 Tk=32768 d=128 S=512 "
                                "(attn_decode_splitkv)",
                    "prefill_ms": round(p_avg, 4), "prefill_ms_min": round(min(pre_ms), 4),
+                   "prefill_ms_median": round(statistics.median(pre_ms), 4),
                    "decode_ms": round(d_avg, 4), "decode_ms_min": round(min(dec_ms), 4),
+                   "decode_ms_median": round(statistics.median(dec_ms), 4),
                    "wall_s": round(wall, 3)},
         "roofline": {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
@@ -375,6 +405,9 @@ def main():
     if not args.no_varlen:
         print("bench: variable-length batches", file=sys.stderr, flush=True)
         out["varlen"] = varlen_section(torch, attn, inputs, dev, dk, dv_, dq, dec, ws, timed)
+    if not args.no_achievable:
+        print("bench: achievable ceilings", file=sys.stderr, flush=True)
+        out["achievable"] = achievable_section(torch, dev, timed, p_tflops, d_gbs)
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
