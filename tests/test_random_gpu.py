@@ -1,0 +1,137 @@
+"""Seeded random problems across every option of the forward entry points,
+each compared element by element with the oracle: dtype, head sizes on the
+fast kernels (64, 128) and on the generic one, head grouping, causal or not,
+any query offset (negative, inside, past the keys), sliding windows, every
+bias broadcast with -inf entries, T_k = 0, split-KV decode with any split
+size, packed sequences and per-batch KV lengths.  Sizes stay small so the
+oracle finishes in well under a second per case."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import online_softmax_exact_amd as attn
+from online_softmax_exact_amd import inputs
+from gpu_util import assert_close, dev, ensure_built, f64
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 64
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    ensure_built()
+
+
+def draw_case(i):
+    """Case i: a dict of everything the call needs, from its own generator."""
+    r = np.random.default_rng(5000 + i)
+    c = {}
+    c["mode"] = r.choice(["fwd", "fwd", "decode", "packed", "kvlens"])
+    c["dtype"] = torch.float32 if r.random() < 0.2 else torch.bfloat16
+    fast = r.random() < 0.75
+    c["d_h"] = int(r.choice([64, 128])) if fast else int(r.choice([8, 32, 40, 96, 256]))
+    c["d_v"] = int(r.choice([64, 128])) if fast else int(r.choice([16, 24, 64, 200]))
+    c["h_kv"] = int(r.choice([1, 2, 4]))
+    c["h_q"] = c["h_kv"] * int(r.choice([1, 2, 4, 8]))
+    c["causal"] = bool(r.random() < 0.7)
+    c["window"] = 0 if r.random() < 0.6 else int(r.integers(1, 400))
+    c["bias"] = str(r.choice(["none", "none", "keys", "rows", "dense", "shared"]))
+    c["masked_frac"] = float(r.choice([0.0, 0.05, 0.3]))
+    if c["mode"] == "fwd":
+        c["b"] = int(r.integers(1, 4))
+        c["t_q"] = int(r.integers(1, 300))
+        c["t_k"] = int(r.choice([0, int(r.integers(1, 700))]) if r.random() < 0.1 else r.integers(1, 700))
+        c["q_offset"] = int(r.integers(-60, c["t_k"] + 60))
+    elif c["mode"] == "decode":
+        c["b"] = int(r.integers(1, 5))
+        c["t_q"] = int(r.integers(1, 6))
+        c["t_k"] = int(r.integers(1, 3000))
+        c["q_offset"] = c["t_k"] - c["t_q"] if r.random() < 0.7 else int(r.integers(-10, c["t_k"] + 10))
+        c["split"] = int(r.choice([1, 7, 64, 256, 512, 1000, 5000]))
+    elif c["mode"] == "packed":
+        n = int(r.integers(1, 6))
+        c["lq"] = [int(x) for x in r.integers(0, 260, n)]
+        c["lk"] = [max(0, int(x)) for x in (np.array(c["lq"]) + r.integers(-40, 300, n))]
+        c["bias"] = str(r.choice(["none", "packed", "keys"]))
+        c["q_offset"] = int(r.choice([0, 0, 0, 5, -3]))
+        c["max_q"] = int(r.choice([max(c["lq"]), 0, 100]))
+    else:  # kvlens
+        c["b"] = int(r.integers(1, 5))
+        c["t_q"] = int(r.integers(1, 200)) if r.random() < 0.5 else int(r.integers(1, 6))
+        c["t_k"] = int(r.integers(1, 2000))
+        c["lens"] = [int(x) for x in r.integers(0, c["t_k"] + 1, c["b"])]
+        c["q_offset"] = 0
+        c["decode"] = bool(r.random() < 0.5)
+        c["split"] = int(r.choice([64, 333, 512]))
+        if c["decode"]:
+            c["bias"] = "none"
+    if c["mode"] == "decode" and c["dtype"] == torch.bfloat16 and c["bias"] != "none":
+        c["bias"] = "none" if r.random() < 0.5 else c["bias"]   # half of them on the fast kernel
+    return c
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_parity(i):
+    c = draw_case(i)
+    print("case", i, c, flush=True)
+    dd = dev()
+    if c["mode"] == "packed":
+        q, k, v, m, cu_q, cu_k = inputs.make_packed(c["lq"], c["lk"], c["h_q"], c["h_kv"], c["d_h"], c["d_v"],
+                                                    dtype=c["dtype"], seed=i, bias=c["bias"],
+                                                    masked_frac=c["masked_frac"])
+        scale = inputs.default_scale(c["d_h"])
+        if q.shape[2] == 0:
+            pytest.skip("no rows drawn")
+        o, lse, n = attn.attn_fwd(q.to(dd), k.to(dd), v.to(dd), scale=scale, causal=c["causal"],
+                                  q_offset=c["q_offset"], bias=None if m is None else m.to(dd),
+                                  window=c["window"], return_n_legal=True, cu_seqlens_q=cu_q.to(dd),
+                                  cu_seqlens_k=cu_k.to(dd), max_seqlen_q=c["max_q"])
+        torch.cuda.synchronize()
+        o_ref, l_ref, n_ref = oracle.attention_varlen(
+            f64(q), f64(k), f64(v), cu_q.tolist(), cu_k.tolist(), scale=scale, causal=c["causal"],
+            q_offset=c["q_offset"], bias=None if m is None else f64(m), window=c["window"])
+        assert_close(o, lse, o_ref, l_ref, c["dtype"], what=str(c))
+        assert np.array_equal(n.cpu().numpy(), n_ref), "n_legal differs"
+        return
+
+    wl = inputs.make_random(c["b"], c["h_q"], c["h_kv"], c["t_q"], c["t_k"], c["d_h"], c["d_v"],
+                            dtype=c["dtype"], seed=i, causal=c["causal"], q_offset=c["q_offset"],
+                            bias=c["bias"], masked_frac=c["masked_frac"])
+    q, k, v = wl.q.to(dd), wl.k.to(dd), wl.v.to(dd)
+    m = None if wl.bias is None else wl.bias.to(dd)
+    b64 = None if wl.bias is None else f64(wl.bias)
+    if c["mode"] == "kvlens":
+        lens_t = torch.tensor(c["lens"], dtype=torch.int32, device=dd)
+        if c["decode"]:
+            o, lse, _ = attn.attn_decode_splitkv(q, k, v, split_size=c["split"], scale=wl.scale,
+                                                 causal=c["causal"], q_offset=0, window=c["window"],
+                                                 seqlens_k=lens_t)
+            n = None
+        else:
+            o, lse, n = attn.attn_fwd(q, k, v, scale=wl.scale, causal=c["causal"], window=c["window"], bias=m,
+                                      seqlens_k=lens_t, return_n_legal=True)
+        torch.cuda.synchronize()
+        o_ref, l_ref, n_ref = oracle.attention_kvlens(f64(wl.q), f64(wl.k), f64(wl.v), c["lens"], scale=wl.scale,
+                                                      causal=c["causal"], bias=b64, window=c["window"])
+    elif c["mode"] == "decode":
+        o, lse, _ = attn.attn_decode_splitkv(q, k, v, split_size=c["split"], scale=wl.scale, causal=c["causal"],
+                                             q_offset=c["q_offset"], bias=m, window=c["window"])
+        n = None
+        torch.cuda.synchronize()
+        o_ref, l_ref, n_ref = oracle.attention(f64(wl.q), f64(wl.k), f64(wl.v), scale=wl.scale, causal=c["causal"],
+                                               q_offset=c["q_offset"], bias=b64, window=c["window"])
+    else:
+        o, lse, n = attn.attn_fwd(q, k, v, scale=wl.scale, causal=c["causal"], q_offset=c["q_offset"], bias=m,
+                                  window=c["window"], return_n_legal=True)
+        o2, lse2 = attn.attn_fwd(q, k, v, scale=wl.scale, causal=c["causal"], q_offset=c["q_offset"], bias=m,
+                                 window=c["window"])
+        torch.cuda.synchronize()
+        o_ref, l_ref, n_ref = oracle.attention(f64(wl.q), f64(wl.k), f64(wl.v), scale=wl.scale, causal=c["causal"],
+                                               q_offset=c["q_offset"], bias=b64, window=c["window"])
+        assert_close(o2, lse2, o_ref, l_ref, c["dtype"], what=str(c) + " (no counts)")
+    assert_close(o, lse, o_ref, l_ref, c["dtype"], what=str(c))
+    if n is not None:
+        assert np.array_equal(n.cpu().numpy(), n_ref), "n_legal differs"
