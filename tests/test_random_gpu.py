@@ -135,3 +135,58 @@ def test_random_parity(i):
     assert_close(o, lse, o_ref, l_ref, c["dtype"], what=str(c))
     if n is not None:
         assert np.array_equal(n.cpu().numpy(), n_ref), "n_legal differs"
+
+
+N_BWD = 24
+BWD_TOL = {torch.float32: dict(max=1e-5, mean=1e-6), torch.bfloat16: dict(max=2e-2, mean=2e-3)}
+
+
+def draw_bwd_case(i):
+    r = np.random.default_rng(7000 + i)
+    fast = r.random() < 0.7
+    c = dict(dtype=torch.float32 if r.random() < 0.25 else torch.bfloat16,
+             d_h=int(r.choice([64, 128])) if fast else int(r.choice([16, 40, 96])),
+             d_v=int(r.choice([64, 128])) if fast else int(r.choice([24, 64, 80])),
+             h_kv=int(r.choice([1, 2])), b=int(r.integers(1, 3)),
+             t_q=int(r.integers(1, 260)), t_k=int(r.integers(1, 400)),
+             causal=bool(r.random() < 0.7), window=0 if r.random() < 0.6 else int(r.integers(1, 300)),
+             bias=str(r.choice(["none", "none", "none", "keys", "dense"])),
+             masked_frac=float(r.choice([0.0, 0.1])))
+    c["h_q"] = c["h_kv"] * int(r.choice([1, 2, 4]))
+    c["q_offset"] = int(r.integers(-30, c["t_k"] + 30))
+    return c
+
+
+@pytest.mark.parametrize("i", range(N_BWD))
+def test_random_backward_parity(i):
+    """attn_bwd on random problems (MFMA kernels for bf16 with d in {64, 128}
+    and no bias, the generic ones otherwise), relative to each gradient's
+    largest entry, with exact zeros where nothing contributes."""
+    c = draw_bwd_case(i)
+    print("case", i, c, flush=True)
+    wl = inputs.make_random(c["b"], c["h_q"], c["h_kv"], c["t_q"], c["t_k"], c["d_h"], c["d_v"],
+                            dtype=c["dtype"], seed=100 + i, causal=c["causal"], q_offset=c["q_offset"],
+                            bias=c["bias"], masked_frac=c["masked_frac"])
+    g = torch.randn((c["b"], c["h_q"], c["t_q"], c["d_v"]), generator=torch.Generator().manual_seed(i)).to(c["dtype"])
+    dd = dev()
+    q, k, v = wl.q.to(dd), wl.k.to(dd), wl.v.to(dd)
+    m = None if wl.bias is None else wl.bias.to(dd)
+    kw = dict(scale=wl.scale, causal=c["causal"], q_offset=c["q_offset"], bias=m, window=c["window"])
+    o, lse = attn.attn_fwd(q, k, v, **kw)
+    dq, dk, dv = attn.attn_bwd(q, k, v, o, lse, g.to(dd), **kw)
+    torch.cuda.synchronize()
+    b64 = None if wl.bias is None else f64(wl.bias)
+    ref = oracle.attention_backward(f64(wl.q), f64(wl.k), f64(wl.v), f64(g), scale=wl.scale, causal=c["causal"],
+                                    q_offset=c["q_offset"], bias=b64, window=c["window"])
+    _, l_ref, _ = oracle.attention(f64(wl.q), f64(wl.k), f64(wl.v), scale=wl.scale, causal=c["causal"],
+                                   q_offset=c["q_offset"], bias=b64, window=c["window"])
+    assert np.all(f64(dq)[np.isneginf(l_ref)] == 0), "dQ of a row without a legal key"
+    dead_keys = np.all(ref[2] == 0, axis=-1)
+    assert np.all(f64(dk)[dead_keys] == 0) and np.all(f64(dv)[dead_keys] == 0), "gradient of an unseen key"
+    tol = BWD_TOL[c["dtype"]]
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        g64 = f64(got)
+        assert not np.isnan(g64).any(), name
+        scale = max(float(np.abs(want).max()), 1e-30)
+        err = np.abs(g64 - want) / scale
+        assert err.max() <= tol["max"] and err.mean() <= tol["mean"], f"{name}: {err.max():.2e} / {err.mean():.2e}"
