@@ -190,7 +190,8 @@ def make_random(batch: int, heads_q: int, heads_kv: int, t_q: int, t_k: int,
 
 def varlen_lengths(n: int, max_len: int, seed: int):
     """n sequence lengths uniform in [1, max_len]: the first draw of
-    ``padded_bias``'s generator, so workload 5's seed gives its own lengths."""
+    ``padded_bias``'s generator, so the padded variable-length batch's seed gives
+    its own lengths."""
     gen = torch.Generator("cpu").manual_seed(derive_seed(seed, 4, 0))
     return [int(x) for x in torch.randint(1, max_len + 1, (n,), generator=gen)]
 

@@ -45,9 +45,9 @@ def check_sampled(wl, o, lse, rows, dtype):
     return n_ref
 
 
-def test_config1_fp32_full():
+def test_fp32_causal_1x1x128_d64():
     wl = inputs.make_config(1)
-    print("config 1", wl.name, flush=True)
+    print("workload", wl.name, flush=True)
     q, k, v, _ = to_dev(wl)
     o, lse, n = attn.attn_fwd(q, k, v, scale=wl.scale, causal=True, q_offset=0,
                               return_n_legal=True)
@@ -57,9 +57,9 @@ def test_config1_fp32_full():
     assert np.array_equal(n.cpu().numpy(), n_ref)
 
 
-def test_config2_causal_prefill():
+def test_causal_prefill_1x32x8192_d128():
     wl = inputs.make_config(2)
-    print("config 2", wl.name, flush=True)
+    print("workload", wl.name, flush=True)
     q, k, v, _ = to_dev(wl)
     o, lse, n = attn.attn_fwd(q, k, v, scale=wl.scale, causal=True, q_offset=0,
                               return_n_legal=True)
@@ -72,9 +72,9 @@ def test_config2_causal_prefill():
     check_sampled(wl, o, lse, rows, torch.bfloat16)
 
 
-def test_config3_gqa_decode():
+def test_gqa_decode_16x32x8_tk32768_split512():
     wl = inputs.make_config(3)
-    print("config 3", wl.name, flush=True)
+    print("workload", wl.name, flush=True)
     q, k, v, _ = to_dev(wl)
     o, lse, ws = attn.attn_decode_splitkv(q, k, v, split_size=wl.split_size, scale=wl.scale,
                                           causal=True, q_offset=wl.q_offset)
@@ -94,9 +94,9 @@ def test_config3_gqa_decode():
                      o_ref[0, 0], l_ref[0, 0], torch.bfloat16, what=f"partial {b},{h},{s}")
 
 
-def test_config4_verify():
+def test_verify_32x32_tq5_tk4096():
     wl = inputs.make_config(4)
-    print("config 4", wl.name, flush=True)
+    print("workload", wl.name, flush=True)
     q, k, v, _ = to_dev(wl)
     o, lse, n = attn.attn_fwd(q, k, v, scale=wl.scale, causal=True, q_offset=wl.q_offset,
                               return_n_legal=True)
@@ -111,9 +111,9 @@ def test_config4_verify():
     check_sampled(wl, o2, lse2, rows, torch.bfloat16)
 
 
-def test_config5_padded_bias():
+def test_padded_varlen_bias_8x16x4096_d64x128():
     wl = inputs.make_config(5)
-    print("config 5", wl.name, "lengths", wl.extras["lengths"], flush=True)
+    print("workload", wl.name, "lengths", wl.extras["lengths"], flush=True)
     q, k, v, m = to_dev(wl)
     o, lse, n = attn.attn_fwd(q, k, v, scale=wl.scale, causal=True, q_offset=0, bias=m,
                               return_n_legal=True)
