@@ -42,6 +42,12 @@ constexpr int kThreads = 64 * kW;
 constexpr int kRowsW = 32;              // rows (dQ) or keys (dK/dV) per wavefront
 constexpr int kBr = kRowsW * kW;        // per workgroup
 constexpr int kBc = 64;                 // streamed tile rows
+#ifndef BWD_PIPE
+#define BWD_PIPE 1     // dV: software-pipelined path for units whose two blocks are fully legal
+#endif
+#ifndef BWD_SCHED
+#define BWD_SCHED 0    // VALU instructions placed after each MFMA in that path (0: compiler's order)
+#endif
 
 struct BArgs {
   const uint16_t* q;
@@ -433,6 +439,72 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a) {
   dma_barrier();
 
   const int last_key = key0 + kRowsW - 1;
+  // Block q of a unit (rows r0 .. r0 + 31): does it hold a legal (row, key)
+  // pair of this wave, and are all its pairs legal?
+  auto block_flags = [&](int r0, bool& any, bool& full) {
+    const int64_t pf = a.q_offset + r0, pl = a.q_offset + r0 + 31;
+    any = key0 < a.t_k && r0 < a.t_q;
+    if (a.causal && pl < key0) any = false;
+    if (a.window > 0 && pf - a.window + 1 > last_key) any = false;
+    full = last_key < a.t_k && r0 + 31 < a.t_q;
+    if (a.causal && pf < last_key) full = false;
+    if (a.window > 0 && pl - a.window + 1 > key0) full = false;
+  };
+  // S of block q (register r holds row 32 q + 8 (r / 4) + 4 h + (r % 4) of
+  // the tile for this lane's key).
+  auto scores = [&](const char* qt_, int q, f32x16& sacc) {
+    sacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+      const u32x4 qop = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          row_chunk<C::H_RB>(qt_, 32 * q + lr, s, h));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qop), as_bf16x8(kreg[s]), sacc, 0, 0, 0);
+    }
+  };
+  // acc^T += A^T W for block q, A the tile at `at` read transposed, W packed.
+  auto accumulate = [&](const char* at, int q, const unsigned* pk) {
+#pragma unroll
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
+      const u32x4 bop = {pk[4 * kk2], pk[4 * kk2 + 1], pk[4 * kk2 + 2], pk[4 * kk2 + 3]};
+#pragma unroll
+      for (int mo = 0; mo < MOUT; ++mo) {
+        u32x2 lo, hi;
+        if (DK) {
+          lo = tr_read(tr_addr<C::H_RB>(at, 32 * q, kk2, mo, 0, lane));
+          hi = tr_read(tr_addr<C::H_RB>(at, 32 * q, kk2, mo, 1, lane));
+        } else {
+          lo = tr_read(tr_addr<C::V_RB>(at, 32 * q, kk2, mo, 0, lane));
+          hi = tr_read(tr_addr<C::V_RB>(at, 32 * q, kk2, mo, 1, lane));
+        }
+        const u32x4 aop = {lo[0], lo[1], hi[0], hi[1]};
+        acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bop), acc[mo], 0, 0, 0);
+      }
+    }
+  };
+  // P of a fully legal block, packed to bf16 (dV only).
+  auto probs_full = [&](const float* st_, int q, const f32x16& sacc, unsigned* pk) {
+    f32x4 l4[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      l4[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+          (const __attribute__((address_space(3))) char*)(st_) + (32 * q + 8 * g + 4 * h) * 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 2 * i;
+      const float p0 = fast_exp2(fmaf(sacc[r], a.scale_log2, -l4[r >> 2][r & 3] * kLog2e));
+      const float p1 = fast_exp2(fmaf(sacc[r + 1], a.scale_log2, -l4[(r + 1) >> 2][(r + 1) & 3] * kLog2e));
+      pk[i] = pack_bf16(p0, p1);
+    }
+  };
+  // One MFMA then BWD_SCHED VALU instructions, n times.
+  auto interleave = [&](int n) {
+    if (BWD_SCHED > 0) {
+      for (int i = 0; i < n; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, BWD_SCHED, 0);
+      }
+    }
+  };
   for (int u = 0; u < n_units; ++u) {
     int hq, i0;
     unit(u, hq, i0);
@@ -440,19 +512,30 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a) {
     const char* qt_ = qring + slot * C::H_BYTES;
     const char* gt_ = gring + slot * C::V_BYTES;
     const float* st_ = sring + slot * 128;
+    bool any_b[2], full_b[2];
+    block_flags(i0, any_b[0], full_b[0]);
+    block_flags(i0 + 32, any_b[1], full_b[1]);
+    if (!DK && BWD_PIPE && full_b[0] && full_b[1]) {
+      // Both blocks fully legal: S of both blocks first, then block 0's
+      // weights under block 1's score MFMAs and block 1's weights under
+      // block 0's accumulation MFMAs (no dependence between them).
+      f32x16 s0, s1;
+      unsigned pk0[8], pk1[8];
+      scores(qt_, 0, s0);
+      if (BWD_SCHED > 0) __builtin_amdgcn_sched_barrier(0);
+      scores(qt_, 1, s1);
+      probs_full(st_, 0, s0, pk0);
+      interleave(C::KS);
+      accumulate(gt_, 0, pk0);
+      probs_full(st_, 1, s1, pk1);
+      interleave(2 * MOUT);
+      accumulate(gt_, 1, pk1);
+    } else {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int r0 = i0 + 32 * q;                 // first row of the block
-      const int64_t pf = a.q_offset + r0, pl = a.q_offset + r0 + 31;
-      // Any legal (row, key) pair in the block for this wave?
-      bool any = key0 < a.t_k && r0 < a.t_q;
-      if (a.causal && pl < key0) any = false;
-      if (a.window > 0 && pf - a.window + 1 > last_key) any = false;
+      const bool any = any_b[q], full = full_b[q];
       if (!any) continue;
-      // All pairs legal?
-      bool full = last_key < a.t_k && r0 + 31 < a.t_q;
-      if (a.causal && pf < last_key) full = false;
-      if (a.window > 0 && pl - a.window + 1 > key0) full = false;
 
       // S = Q K^T (and dP = dO V^T): register r holds row
       // r0 + 8 (r / 4) + 4 h + (r % 4) of this lane's key.
@@ -502,24 +585,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a) {
         pk[i] = pack_bf16(w2[0], w2[1]);
       }
       // dV^T += dO^T P or dK^T += Q^T dS (A = transposed reads of the tile).
-      const char* at = DK ? qt_ : gt_;
-#pragma unroll
-      for (int kk2 = 0; kk2 < 2; ++kk2) {
-        const u32x4 bop = {pk[4 * kk2], pk[4 * kk2 + 1], pk[4 * kk2 + 2], pk[4 * kk2 + 3]};
-#pragma unroll
-        for (int mo = 0; mo < MOUT; ++mo) {
-          u32x2 lo, hi;
-          if (DK) {
-            lo = tr_read(tr_addr<C::H_RB>(at, 32 * q, kk2, mo, 0, lane));
-            hi = tr_read(tr_addr<C::H_RB>(at, 32 * q, kk2, mo, 1, lane));
-          } else {
-            lo = tr_read(tr_addr<C::V_RB>(at, 32 * q, kk2, mo, 0, lane));
-            hi = tr_read(tr_addr<C::V_RB>(at, 32 * q, kk2, mo, 1, lane));
-          }
-          const u32x4 aop = {lo[0], lo[1], hi[0], hi[1]};
-          acc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bop), acc[mo], 0, 0, 0);
-        }
-      }
+      accumulate(DK ? qt_ : gt_, q, pk);
+    }
     }
     // End of unit u: this wave's copies of unit u + 1 are done, every wave is
     // done with slot u & 1; copy unit u + 2 into it.
