@@ -15,7 +15,8 @@ window (``--window``, keys j >= pos - W + 1) and reported under
 ``sliding_window``, the prefill's backward (``attn_bwd``, upstream
 gradient N(0,1)) under ``backward``, and unpadded variable-length batches
 (packed prefill against the padded batch, decode over per-batch KV lengths)
-under ``varlen``, each with its own algorithmic counts.
+under ``varlen``, the multi-query verify and the padded batch with its dense
+bias under ``workloads``, each with its own algorithmic counts.
 """
 
 from __future__ import annotations
@@ -141,6 +142,57 @@ def varlen_section(torch, attn, inputs, dev, dk, dv_, dq, dec, ws, timed):
     }
 
 
+def padded_counts(lengths, masked_rows, heads: int, t: int, d_h: int, d_v: int):
+    """Padded causal batch with a dense bias: row i of sequence b has
+    min(i + 1, L_b) legal keys (keys past L_b are padding, masked by the bias)
+    unless it is one of the two wholly masked rows.  Bytes: Q, K, V, O, LSE
+    once, plus the bias entries in the causally visible region once (the bias
+    is shared by the heads)."""
+    pairs = 0
+    for L, rows in zip(lengths, masked_rows):
+        per = sum(min(i + 1, L) for i in range(t)) - sum(min(r + 1, L) for r in rows)
+        pairs += heads * per
+    b = len(lengths)
+    bytes_ = b * heads * t * (2 * d_h + 2 * d_v) * 2 + b * heads * t * 4 + b * t * (t + 1) // 2 * 4
+    return 2 * (d_h + d_v) * pairs, bytes_
+
+
+def workloads_section(torch, attn, inputs, dev, timed):
+    """The multi-query verify (32 x 32 heads, 5 queries at the end of 4096
+    keys) against HBM, and the padded variable-length batch with its dense
+    bias (8 x 16 heads, T = 4096, d_h = 64, d_v = 128) against both ceilings."""
+    out = {}
+    wl = inputs.make_config(4)
+    q, k, v = (t.to(dev) for t in (wl.q, wl.k, wl.v))
+    o = torch.empty(q.shape[:3] + (v.shape[3],), dtype=q.dtype, device=dev)
+    lse = torch.empty(q.shape[:3], device=dev)
+    ms = timed(lambda: attn.attn_fwd(q, k, v, scale=wl.scale, causal=True, q_offset=wl.q_offset, out=o, lse=lse))
+    by, fl = decode_counts(32, 32, 32, 5, 4096, 128, 128)
+    gbs = by / (ms * 1e-3) / 1e9
+    out["verify"] = {"workload": "multi-query verify B=32 H=32 T_q=5 at positions 4091..4095, T_k=4096, d=128 "
+                                 "(attn_fwd)", "ms": round(ms, 4), "value": round(gbs, 1), "unit": "GB/s",
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "per_launch_bytes": by,
+                                  "per_launch_flops": fl}}
+    del q, k, v, o, lse, wl
+    wl = inputs.make_config(5)
+    q, k, v, m = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.bias))
+    o = torch.empty(q.shape[:3] + (v.shape[3],), dtype=q.dtype, device=dev)
+    lse = torch.empty(q.shape[:3], device=dev)
+    ms = timed(lambda: attn.attn_fwd(q, k, v, scale=wl.scale, causal=True, bias=m, out=o, lse=lse))
+    fl, by = padded_counts(wl.extras["lengths"], wl.extras["masked_rows"], 16, 4096, 64, 128)
+    tf = fl / (ms * 1e-3) / 1e12
+    gbs = by / (ms * 1e-3) / 1e9
+    out["padded_bias"] = {"workload": "padded variable-length batch B=8 H=16 T=4096 d_h=64 d_v=128, dense fp32 bias "
+                                      "[8,1,4096,4096] with -inf padding and 2 masked rows per sequence (attn_fwd)",
+                          "ms": round(ms, 4), "value": round(tf, 2), "unit": "TFLOP/s",
+                          "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                                       "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                                       "per_launch_flops": fl, "per_launch_bytes": by,
+                                       "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}}
+    return out
+
+
 def achievable_section(torch, dev, timed, p_tflops, d_gbs):
     """Ceilings measured in the same session, as context for the fractions of
     the published peaks: a library bf16 GEMM (torch.matmul, hipBLASLt) for the
@@ -222,6 +274,8 @@ def main():
                     help="heads of the prefill the CPU oracle baseline times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the multi-query verify and padded-bias measurements")
     ap.add_argument("--no-achievable", action="store_true",
                     help="skip the same-session ceilings (library bf16 GEMM, device copy)")
     ap.add_argument("--no-varlen", action="store_true",
@@ -405,6 +459,9 @@ def main():
     if not args.no_varlen:
         print("bench: variable-length batches", file=sys.stderr, flush=True)
         out["varlen"] = varlen_section(torch, attn, inputs, dev, dk, dv_, dq, dec, ws, timed)
+    if not args.no_workloads:
+        print("bench: verify and padded-bias workloads", file=sys.stderr, flush=True)
+        out["workloads"] = workloads_section(torch, attn, inputs, dev, timed)
     if not args.no_achievable:
         print("bench: achievable ceilings", file=sys.stderr, flush=True)
         out["achievable"] = achievable_section(torch, dev, timed, p_tflops, d_gbs)

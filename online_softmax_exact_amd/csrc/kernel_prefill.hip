@@ -211,7 +211,6 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     const int tf = (pos_w_first + 1) / kBc;   // pos_w_first >= -1
     if (tf < t_full) t_full = tf;
   }
-  if (BIAS) t_full = 0;
   if (t_full > n_w) t_full = n_w;
 
   const uint16_t* kbase = a.k + b * a.ks[0] + kvh * a.ks[1];
@@ -353,10 +352,53 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     m2 = m_new;
   };
 
-  // Softmax of a block with every key legal for every row and every row
-  // already holding statistics: branch-free (tile max, new reference, weights,
-  // sums, bf16 packing), so it can run under independent MFMAs.
-  auto fast_q = [&](const f32x16& sv, unsigned* pk, float& m_new, float& alpha) {
+  // The 16 bias values of block q of tile t this lane's row meets (16-byte
+  // loads of the 4 consecutive keys each register group holds).
+  auto load_bias = [&](int t, int q, float* mb) {
+    const auto rs = make_rsrc(bias_w + t * kBc, bias_w_bytes - static_cast<int64_t>(t) * kBc * 4);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 x = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, bias_off + 128 * q + 32 * g, 0, 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mb[4 * g + e] = x[e];
+    }
+  };
+
+  // Softmax of a block whose keys are all causally visible (and inside the
+  // window) for every row, every row already holding statistics:
+  // branch-free (tile max, new reference, weights, sums, bf16 packing), so
+  // it can run under independent MFMAs.  With a bias, z = scale dot + M in
+  // base-2 units; a -inf entry gives z = -inf and weight 0 by arithmetic
+  // alone, and a block whose keys are all -inf for a row leaves its
+  // reference unchanged (its maximum is -inf), as the valid-flag rule asks.
+  auto fast_q = [&](int t, int q, const f32x16& sv, unsigned* pk, float& m_new, float& alpha) {
+    if (BIAS) {
+      float mb[16], z[16];
+      load_bias(t, q, mb);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        z[r] = fmaf(mb[r], kLog2e, sv[r] * a.scale_log2);
+        if (COUNT) count += static_cast<int>(mb[r] != -INFINITY);
+      }
+      float mx = fmaxf(z[0], z[1]);
+#pragma unroll
+      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, z[r]);
+      const float tmax = max_xor32(mx);
+      m_new = tmax > m2 + kRescale ? tmax : m2;
+      alpha = fast_exp2(m2 - m_new);
+      float ps0 = 0.0f, ps1 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p0 = fast_exp2(z[2 * i] - m_new);
+        const float p1 = fast_exp2(z[2 * i + 1] - m_new);
+        pk[i] = pack_bf16(p0, p1);
+        ps0 += p0;
+        ps1 += p1;
+      }
+      l_lane = fmaf(l_lane, alpha, ps0 + ps1);
+      return;
+    }
     float mx = fmaxf(sv[0], sv[1]);
 #pragma unroll
     for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sv[r]);
@@ -388,17 +430,7 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     if (!row_ok) lim = -1;   // rows past T_q: nothing legal, no bias read
     const int first = lo_row - kb;   // keys below the window are not legal
     float mb[16];
-    if (BIAS) {
-      // 16-byte loads of the 4 consecutive keys each register group holds.
-      const auto rs = make_rsrc(bias_w + t * kBc, bias_w_bytes - static_cast<int64_t>(t) * kBc * 4);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 x = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, bias_off + 128 * q + 32 * g, 0, 0));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mb[4 * g + e] = x[e];
-      }
-    }
+    if (BIAS) load_bias(t, q, mb);
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -490,7 +522,7 @@ __global__ __launch_bounds__(kThreads, PREFILL_WAVES_PER_SIMD) void prefill_kern
     for (int q = 0; q < kNQ; ++q) {
       if (q + 1 < kNQ) scores_q(slot, q + 1, sv[(q + 1) & 1]);
       if (q > 0) pv_q(slot, q - 1, pk[(q - 1) & 1]);
-      fast_q(sv[q & 1], pk[q & 1], mn, al);
+      fast_q(t, q, sv[q & 1], pk[q & 1], mn, al);
       if (PREFILL_PIN) {
         // Keep the block's weights ahead of the rescale branch, so they are
         // scheduled under the MFMAs issued before it rather than sunk past it.
