@@ -72,8 +72,14 @@ using namespace pf;
 struct ShapeStd {
   static constexpr int kWaves = PREFILL_WAVES, kNQ = PREFILL_BLOCKS, kSched = PREFILL_SCHED;
 };
+#ifndef PREFILL_BIG_BLOCKS
+#define PREFILL_BIG_BLOCKS 4
+#endif
+#ifndef PREFILL_BIG_SCHED
+#define PREFILL_BIG_SCHED 5
+#endif
 struct ShapeBig {
-  static constexpr int kWaves = 8, kNQ = 4, kSched = 4;
+  static constexpr int kWaves = 8, kNQ = PREFILL_BIG_BLOCKS, kSched = PREFILL_BIG_SCHED;
 };
 
 template <int DH, int DV, class S>
