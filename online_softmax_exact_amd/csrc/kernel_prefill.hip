@@ -34,6 +34,8 @@
 //   stay below 2^8.
 // * Scores live in the base-2 domain: p = exp2(dot * scale * log2(e) - m2) on
 //   v_exp_f32; LSE is converted back to natural-log units at the end.
+#include <type_traits>
+
 #include "attn_internal.h"
 #include "kernels.h"
 #include "prefill_common.h"
@@ -57,6 +59,9 @@ using namespace pf;
 #endif
 #ifndef PREFILL_PIN
 #define PREFILL_PIN 1                  // 1: full-tile weights computed before the rescale branch
+#endif
+#ifndef PREFILL_FIRST_FAST
+#define PREFILL_FIRST_FAST 1           // 1: a wave's first tile, if fully visible, on the pipelined path
 #endif
 #ifndef PREFILL_WAVES_PER_SIMD
 #define PREFILL_WAVES_PER_SIMD 2       // resident waves per SIMD the kernel is built for
@@ -527,14 +532,36 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
   // tiles on the fast path, the rest general (diagonal / masked / skipped).
   int t = t_begin;
   while (t < t_lo_full && t < n_tiles) general_step(t++);
-  if (t < n_tiles) general_step(t++);
   // Software pipeline over the 32-key blocks of a full tile: block q's
   // softmax (VALU) runs under the score MFMAs of block q + 1 and the P V
   // MFMAs of block q - 1, which are independent of it.
-  auto fast_step = [&](int t, int slot) {
+  // Block 0 of a wave's first tile when that tile is fully visible and no row
+  // has statistics yet (no bias, so every score is legal and finite): the
+  // block maximum is the reference, nothing to rescale.
+  auto fast_q_first = [&](const f32x16& sv, unsigned* pk, float& m_new) {
+    float mx = fmaxf(sv[0], sv[1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sv[r]);
+    m_new = max_xor32(mx) * a.scale_log2;
+    const float nm = -m_new;
+    float ps0 = 0.0f, ps1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p0 = fast_exp2(fmaf(sv[2 * i], a.scale_log2, nm));
+      const float p1 = fast_exp2(fmaf(sv[2 * i + 1], a.scale_log2, nm));
+      pk[i] = pack_bf16(p0, p1);
+      ps0 += p0;
+      ps1 += p1;
+    }
+    l_lane = ps0 + ps1;
+    if (COUNT) count += 16;
+  };
+  // FIRST: the wave's first statistics come from block 0 of this tile.
+  auto fast_step = [&](int t, int slot, auto first) {
+    constexpr bool FIRST = decltype(first)::value;
     f32x16 sv[2];
     unsigned pk[2][8];
-    float mn, al;
+    float mn, al = 1.0f;
     scores_q(slot, 0, sv[0]);
     // Nothing of this tile can overlap block 0's score MFMAs.
     if (kSched > 0) __builtin_amdgcn_sched_barrier(0);
@@ -542,7 +569,8 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
     for (int q = 0; q < kNQ; ++q) {
       if (q + 1 < kNQ) scores_q(slot, q + 1, sv[(q + 1) & 1]);
       if (q > 0) pv_q(slot, q - 1, pk[(q - 1) & 1]);
-      fast_q(t, q, sv[q & 1], pk[q & 1], mn, al);
+      if (FIRST && q == 0) fast_q_first(sv[q & 1], pk[q & 1], mn);
+      else fast_q(t, q, sv[q & 1], pk[q & 1], mn, al);
       if (PREFILL_PIN) {
         // Keep the block's weights ahead of the rescale branch, so they are
         // scheduled under the MFMAs issued before it rather than sunk past it.
@@ -560,19 +588,34 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
           __builtin_amdgcn_sched_group_barrier(0x002, kSched, 0);
         }
       }
-      rescale(mn, al);
+      if (FIRST && q == 0) {
+        m2 = mn;
+        has = true;
+      } else {
+        rescale(mn, al);
+      }
     }
     pv_q(slot, kNQ - 1, pk[(kNQ - 1) & 1]);
     advance(t);
   };
+  const std::false_type later{};
+  // The first tile: pipelined when it is fully visible and no row has
+  // statistics yet (no bias); otherwise general (first statistics, masks).
+  if (!BIAS && PREFILL_FIRST_FAST && t < t_full && __ballot(has) == 0) {
+    if ((t & 1) == 0) fast_step(t, 0, std::true_type{});
+    else fast_step(t, 1, std::true_type{});
+    ++t;
+  } else if (t < n_tiles) {
+    general_step(t++);
+  }
   // Tile t lives in slot t & 1; the slot is an immediate in each copy.
   if (t < t_full && __ballot(!has) == 0) {
-    if ((t & 1) == 0) fast_step(t++, 0);
+    if ((t & 1) == 0) fast_step(t++, 0, later);
     for (; t + 1 < t_full; t += 2) {
-      fast_step(t, 1);
-      fast_step(t + 1, 0);
+      fast_step(t, 1, later);
+      fast_step(t + 1, 0, later);
     }
-    if (t < t_full) fast_step(t++, 1);
+    if (t < t_full) fast_step(t++, 1, later);
   }
   for (; t < n_tiles; ++t) general_step(t);
 
