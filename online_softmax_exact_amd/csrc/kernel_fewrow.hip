@@ -75,6 +75,8 @@ struct FArgs {
   float scale_log2;
   int32_t causal;
   const int32_t* kv_lens;     // per-batch KV lengths (device), NULL = T_k for every batch
+  const float* bias;          // fp32 additive bias, contiguous along keys (BIAS instances)
+  int64_t bs[3];              // its strides over (b, hq, i), in elements
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -89,7 +91,7 @@ __device__ __forceinline__ u32x2 tr_read(const lds_char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-template <int DH, int DV, bool SPLIT, bool VAR>
+template <int DH, int DV, bool SPLIT, bool VAR, bool BIAS>
 __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
   using C = FCfg<DH, DV>;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
@@ -224,10 +226,22 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
     }
   };
 
+  // This lane's bias row (BIAS): keys [0, T_k) of (b, hq, qi); 16-byte
+  // loads of the 4 consecutive keys each register group holds.  Rows past
+  // the group's rows read an empty range (zeros; they are never legal).
+  const float* brow = BIAS ? a.bias + b * a.bs[0] + hq * a.bs[1] + static_cast<int64_t>(qi) * a.bs[2] : nullptr;
+
   if (n_tiles > 0) load(0, kreg, vreg);
 
   for (int t = 0; t < n_tiles; ++t) {
     const int64_t kb = wlo + static_cast<int64_t>(t) * kTile;
+    f32x4 mb[BIAS ? 4 : 1];
+    if (BIAS) {
+      const auto rs = make_rsrc(brow + kb, row_ok ? (a.t_k - kb) * 4 : 0);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        mb[g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (8 * g + 4 * h) * 4, 0, 0));
+    }
     // V tile -> this wave's LDS buffer (read back transposed below).
 #pragma unroll
     for (int i = 0; i < C::V_PER_LANE; ++i) {
@@ -253,7 +267,9 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = 8 * (r >> 2) + 4 * h + (r & 3);
-      const float z = (j <= lim && j >= first) ? sacc[r] * a.scale_log2 : -INFINITY;
+      float z = sacc[r] * a.scale_log2;
+      if (BIAS) z = fmaf(mb[r >> 2][r & 3], kLog2e, z);   // -inf entries mask their key
+      z = (j <= lim && j >= first) ? z : -INFINITY;
       sacc[r] = z;
       mx = fmaxf(mx, z);
     }
@@ -365,15 +381,21 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
   }
 }
 
-template <int DH, int DV, bool SPLIT>
-hipError_t launch_f(const FArgs& a, int64_t blocks, hipStream_t stream) {
-  if (a.kv_lens != nullptr)
-    hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT, true>), dim3(static_cast<unsigned>(blocks)),
+template <int DH, int DV, bool SPLIT, bool VAR>
+hipError_t launch_fb(const FArgs& a, int64_t blocks, hipStream_t stream) {
+  if (a.bias != nullptr)
+    hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT, VAR, true>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT, false>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT, VAR, false>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int DH, int DV, bool SPLIT>
+hipError_t launch_f(const FArgs& a, int64_t blocks, hipStream_t stream) {
+  return a.kv_lens != nullptr ? launch_fb<DH, DV, SPLIT, true>(a, blocks, stream)
+                              : launch_fb<DH, DV, SPLIT, false>(a, blocks, stream);
 }
 
 template <bool SPLIT>
@@ -388,7 +410,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 bool eligible(const Problem& pb, int dtype, const void* q, const void* k, const void* v,
               const void* o) {
-  if (dtype != ATTN_BF16 || pb.bias != nullptr || pb.cu_q != nullptr) return false;
+  if (dtype != ATTN_BF16 || pb.cu_q != nullptr) return false;
+  // A bias must be contiguous along keys with 16-byte aligned rows.
+  if (pb.bias != nullptr &&
+      (pb.bs[3] != 1 || ((pb.bs[0] | pb.bs[1] | pb.bs[2]) & 3) != 0 ||
+       (reinterpret_cast<uintptr_t>(pb.bias) & 15) != 0))
+    return false;
   if (!((pb.d_h == 64 || pb.d_h == 128) && (pb.d_v == 64 || pb.d_v == 128))) return false;
   if (!(pb.scale_log2 > 0.0f)) return false;
   if (pb.t_q >= (int64_t(1) << 30) || pb.t_k >= (int64_t(1) << 30)) return false;
@@ -435,6 +462,8 @@ FArgs make_args(const Problem& pb, const void* q, const void* k, const void* v) 
   a.scale_log2 = pb.scale_log2;
   a.causal = pb.causal;
   a.kv_lens = pb.kv_lens;
+  a.bias = pb.bias;
+  for (int i = 0; i < 3; ++i) a.bs[i] = pb.bs[i];
   a.batch = static_cast<int32_t>(pb.batch);
   return a;
 }

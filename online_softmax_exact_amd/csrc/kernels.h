@@ -21,7 +21,7 @@ bool launch_prefill_mfma(const Problem& pb, int dtype, const void* q, const void
                          const void* v, void* o, float* lse, int32_t* n_legal,
                          hipStream_t stream, int* status);
 
-// Few-row kernel (bf16, d_h and d_v in {64, 128}, no bias): attn_fwd when
+// Few-row kernel (bf16, d_h and d_v in {64, 128}, bias contiguous along keys): attn_fwd when
 // H_q/H_kv * T_q <= 32, and the split-KV decode partials.
 bool launch_fewrow_fwd(const Problem& pb, int dtype, const void* q, const void* k,
                        const void* v, void* o, float* lse, int32_t* n_legal,

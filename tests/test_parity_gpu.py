@@ -44,6 +44,10 @@ FWD_CASES = [
     (torch.bfloat16, 1, 32, 1, 1, 1000, 64, 64, True, 999, "none", 0.0),
     (torch.bfloat16, 2, 4, 4, 3, 200, 128, 64, True, -1, "none", 0.0),
     (torch.bfloat16, 2, 2, 2, 7, 70, 64, 128, False, 0, "none", 0.0),
+    # few rows with a bias (the call without n_legal takes the few-row kernel)
+    (torch.bfloat16, 2, 8, 2, 4, 300, 128, 128, True, 296, "keys", 0.1),
+    (torch.bfloat16, 1, 16, 4, 2, 516, 64, 64, True, 514, "dense", 0.2),
+    (torch.bfloat16, 2, 4, 4, 3, 200, 128, 64, False, 0, "shared", 0.3),
 ]
 
 
@@ -159,6 +163,12 @@ DECODE_CASES = [
     (torch.bfloat16, 1, 8, 1, 5, 700, 128, 128, 128, None, "none"),   # 40 rows: 2 row groups
     (torch.bfloat16, 2, 16, 2, 1, 3000, 128, 64, 1000, None, "none"),
     (torch.bfloat16, 1, 2, 1, 2, 5, 64, 64, 3, None, "none"),
+    # a bias contiguous along keys with 16-byte aligned rows: the few-row kernel
+    (torch.bfloat16, 2, 8, 2, 1, 2000, 128, 128, 512, None, "keys"),
+    (torch.bfloat16, 2, 4, 4, 5, 780, 128, 128, 100, None, "dense"),
+    (torch.bfloat16, 1, 8, 2, 3, 1024, 64, 128, 256, None, "shared"),
+    (torch.bfloat16, 2, 16, 4, 1, 4096, 128, 64, 512, None, "keys"),
+    (torch.bfloat16, 1, 4, 2, 2, 301, 64, 64, 64, None, "keys"),      # rows not 16-byte aligned: generic
 ]
 
 

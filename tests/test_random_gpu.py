@@ -66,8 +66,6 @@ def draw_case(i):
         c["q_offset"] = 0
         c["decode"] = bool(r.random() < 0.5)
         c["split"] = int(r.choice([64, 333, 512]))
-        if c["decode"]:
-            c["bias"] = "none"
     if c["mode"] == "decode" and c["dtype"] == torch.bfloat16 and c["bias"] != "none":
         c["bias"] = "none" if r.random() < 0.5 else c["bias"]   # half of them on the fast kernel
     return c
@@ -108,7 +106,7 @@ def test_random_parity(i):
         if c["decode"]:
             o, lse, _ = attn.attn_decode_splitkv(q, k, v, split_size=c["split"], scale=wl.scale,
                                                  causal=c["causal"], q_offset=0, window=c["window"],
-                                                 seqlens_k=lens_t)
+                                                 seqlens_k=lens_t, bias=m)
             n = None
         else:
             o, lse, n = attn.attn_fwd(q, k, v, scale=wl.scale, causal=c["causal"], window=c["window"], bias=m,
