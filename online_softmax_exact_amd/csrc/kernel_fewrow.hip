@@ -75,8 +75,14 @@ struct FArgs {
   float scale_log2;
   int32_t causal;
   const int32_t* kv_lens;     // per-batch KV lengths (device), NULL = T_k for every batch
-  const float* bias;          // fp32 additive bias, contiguous along keys (BIAS instances)
-  int64_t bs[3];              // its strides over (b, hq, i), in elements
+};
+
+// The bias of the bias instances: fp32, contiguous along keys, strides over
+// (b, hq, i) in elements.  A separate argument, so the kernels without a
+// bias keep their own (smaller) argument block.
+struct FBias {
+  const float* bias;
+  int64_t bs[3];
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -91,8 +97,14 @@ __device__ __forceinline__ u32x2 tr_read(const lds_char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-template <int DH, int DV, bool SPLIT, bool VAR, bool BIAS>
-__global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
+template <class T>
+__device__ __forceinline__ const T& first_of(const T& t) { return t; }
+
+// Bias instances take one more argument (an FBias); the others keep the
+// argument block of the kernel without a bias.
+template <int DH, int DV, bool SPLIT, bool VAR, class... Bias>
+__global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bias_arg) {
+  constexpr bool BIAS = sizeof...(Bias) > 0;
   using C = FCfg<DH, DV>;
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
 
@@ -229,7 +241,11 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
   // This lane's bias row (BIAS): keys [0, T_k) of (b, hq, qi); 16-byte
   // loads of the 4 consecutive keys each register group holds.  Rows past
   // the group's rows read an empty range (zeros; they are never legal).
-  const float* brow = BIAS ? a.bias + b * a.bs[0] + hq * a.bs[1] + static_cast<int64_t>(qi) * a.bs[2] : nullptr;
+  const float* brow = nullptr;
+  if constexpr (BIAS) {
+    const FBias& fb = first_of(bias_arg...);
+    brow = fb.bias + b * fb.bs[0] + hq * fb.bs[1] + static_cast<int64_t>(qi) * fb.bs[2];
+  }
 
   if (n_tiles > 0) load(0, kreg, vreg);
 
@@ -267,9 +283,11 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = 8 * (r >> 2) + 4 * h + (r & 3);
-      float z = sacc[r] * a.scale_log2;
-      if (BIAS) z = fmaf(mb[r >> 2][r & 3], kLog2e, z);   // -inf entries mask their key
-      z = (j <= lim && j >= first) ? z : -INFINITY;
+      float z;
+      if (BIAS)   // -inf entries mask their key
+        z = (j <= lim && j >= first) ? fmaf(mb[r >> 2][r & 3], kLog2e, sacc[r] * a.scale_log2) : -INFINITY;
+      else
+        z = (j <= lim && j >= first) ? sacc[r] * a.scale_log2 : -INFINITY;
       sacc[r] = z;
       mx = fmaxf(mx, z);
     }
@@ -382,28 +400,35 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a) {
 }
 
 template <int DH, int DV, bool SPLIT, bool VAR>
-hipError_t launch_fb(const FArgs& a, int64_t blocks, hipStream_t stream) {
-  if (a.bias != nullptr)
-    hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT, VAR, true>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(kThreads), 0, stream, a);
+hipError_t launch_fb(const FArgs& a, const FBias& fb, int64_t blocks, hipStream_t stream) {
+  if (fb.bias != nullptr)
+    hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT, VAR, FBias>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, stream, a, fb);
   else
-    hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT, VAR, false>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT, VAR>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int DH, int DV, bool SPLIT>
-hipError_t launch_f(const FArgs& a, int64_t blocks, hipStream_t stream) {
-  return a.kv_lens != nullptr ? launch_fb<DH, DV, SPLIT, true>(a, blocks, stream)
-                              : launch_fb<DH, DV, SPLIT, false>(a, blocks, stream);
+hipError_t launch_f(const FArgs& a, const FBias& fb, int64_t blocks, hipStream_t stream) {
+  return a.kv_lens != nullptr ? launch_fb<DH, DV, SPLIT, true>(a, fb, blocks, stream)
+                              : launch_fb<DH, DV, SPLIT, false>(a, fb, blocks, stream);
 }
 
 template <bool SPLIT>
-hipError_t launch_split(const FArgs& a, int64_t blocks, int d_h, int d_v, hipStream_t s) {
-  if (d_h == 128 && d_v == 128) return launch_f<128, 128, SPLIT>(a, blocks, s);
-  if (d_h == 64 && d_v == 128) return launch_f<64, 128, SPLIT>(a, blocks, s);
-  if (d_h == 128 && d_v == 64) return launch_f<128, 64, SPLIT>(a, blocks, s);
-  return launch_f<64, 64, SPLIT>(a, blocks, s);
+hipError_t launch_split(const FArgs& a, const FBias& fb, int64_t blocks, int d_h, int d_v, hipStream_t s) {
+  if (d_h == 128 && d_v == 128) return launch_f<128, 128, SPLIT>(a, fb, blocks, s);
+  if (d_h == 64 && d_v == 128) return launch_f<64, 128, SPLIT>(a, fb, blocks, s);
+  if (d_h == 128 && d_v == 64) return launch_f<128, 64, SPLIT>(a, fb, blocks, s);
+  return launch_f<64, 64, SPLIT>(a, fb, blocks, s);
+}
+
+FBias make_bias(const Problem& pb) {
+  FBias fb{};
+  fb.bias = pb.bias;
+  for (int i = 0; i < 3; ++i) fb.bs[i] = pb.bs[i];
+  return fb;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -462,8 +487,6 @@ FArgs make_args(const Problem& pb, const void* q, const void* k, const void* v) 
   a.scale_log2 = pb.scale_log2;
   a.causal = pb.causal;
   a.kv_lens = pb.kv_lens;
-  a.bias = pb.bias;
-  for (int i = 0; i < 3; ++i) a.bs[i] = pb.bs[i];
   a.batch = static_cast<int32_t>(pb.batch);
   return a;
 }
@@ -486,7 +509,7 @@ bool launch_fewrow_fwd(const Problem& pb, int dtype, const void* q, const void* 
   a.split0 = 0;
   a.n_active = 1;
   const int64_t blocks = pb.batch * pb.heads_kv * a.n_rg;
-  const hipError_t e = launch_split<false>(a, blocks, static_cast<int>(pb.d_h),
+  const hipError_t e = launch_split<false>(a, make_bias(pb), blocks, static_cast<int>(pb.d_h),
                                            static_cast<int>(pb.d_v), stream);
   *status = e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
   return true;
@@ -525,7 +548,8 @@ bool launch_fewrow_partials(const Problem& pb, int dtype, const void* q, const v
   if (blocks >= (int64_t(1) << 31)) return false;
   *err = hipSuccess;
   if (blocks > 0)
-    *err = launch_split<true>(a, blocks, static_cast<int>(pb.d_h), static_cast<int>(pb.d_v), stream);
+    *err = launch_split<true>(a, make_bias(pb), blocks, static_cast<int>(pb.d_h), static_cast<int>(pb.d_v),
+                              stream);
   if (*err == hipSuccess && a.n_active < L.n_splits && L.rows > 0) {
     const int64_t total = L.rows * (L.n_splits - a.n_active) * (pb.d_v + 1);
     const int64_t grid = total / 256 + 1 < 4096 ? total / 256 + 1 : 4096;
