@@ -404,6 +404,37 @@ def attention_backward(q, k, v, d_o, *, scale: float, causal: bool,
     return dq, dk, dv
 
 
+def attention_varlen_backward(q, k, v, d_o, cu_q, cu_k, *, scale: float, causal: bool,
+                              q_offset: int = 0, bias=None, window: int = 0):
+    """Gradients of ``attention_varlen`` (packed sequences, §33.4 shape
+    bucketing; backward of §33.3, eqs 33.6-33.8): each sequence's gradients
+    are ``attention_backward`` of its own rows and keys, with its rows at
+    q_offset + (L_k - L_q) + i and the bias (packed row x packed key) cut to
+    its diagonal block.  Rows and keys outside every sequence get zero.
+    Returns (dq, dk, dv) in the packed layout of q, k, v."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d_o = np.asarray(d_o, dtype=np.float64)
+    cu_q = [int(x) for x in cu_q]
+    cu_k = [int(x) for x in cu_k]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for s in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[s], cu_q[s + 1], cu_k[s], cu_k[s + 1]
+        if q1 == q0 and k1 == k0:
+            continue
+        b_s = None
+        if bias is not None:   # size-1 (broadcast) row or key dims are kept whole
+            bb = np.asarray(bias, dtype=np.float64)
+            b_s = bb[:, :, (slice(q0, q1) if bb.shape[2] != 1 else slice(None)),
+                     (slice(k0, k1) if bb.shape[3] != 1 else slice(None))]
+        g = attention_backward(q[:, :, q0:q1], k[:, :, k0:k1], v[:, :, k0:k1], d_o[:, :, q0:q1],
+                               scale=scale, causal=causal, q_offset=q_offset + (k1 - k0) - (q1 - q0),
+                               bias=b_s, window=window)
+        dq[:, :, q0:q1], dk[:, :, k0:k1], dv[:, :, k0:k1] = g
+    return dq, dk, dv
+
+
 def attention_backward_sampled(q, k, v, d_o, *, rows=(), keys=(), scale: float,
                                causal: bool, q_offset: int = 0, window: int = 0):
     """The gradients of ``attention_backward`` (eqs 33.6-33.8) at selected

@@ -754,6 +754,66 @@ def check_kvlens_equals_padded(R):
     assert np.array_equal(o, od) and np.array_equal(lse, ld)
 
 
+def check_varlen_backward(R):
+    """Packed-sequence gradients: (a) central finite differences of
+    sum(G_O * O) through the packed forward ``attention_varlen`` (rows at the
+    end of their keys, L_q > L_k with masked leading rows, an empty sequence,
+    GQA, a packed bias with -inf entries); (b) equal to the padded batch's
+    gradients on legal rows and real keys (padded keys masked by a -inf bias,
+    padded rows given zero upstream gradient); (c) rows and keys outside every
+    sequence get zero."""
+    rng = np.random.default_rng(34)
+    lq, lk = [3, 5, 0, 2], [4, 3, 2, 6]
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).tolist()
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).tolist()
+    hq, hkv, d_h, d_v = 4, 2, 3, 2
+    tq, tk = sum(lq) + 1, sum(lk) + 2          # one row and two keys outside every sequence
+    q = rng.standard_normal((1, hq, tq, d_h))
+    k = rng.standard_normal((1, hkv, tk, d_h))
+    v = rng.standard_normal((1, hkv, tk, d_v))
+    g = rng.standard_normal((1, hq, tq, d_v))
+    mb = rng.standard_normal((1, hq, tq, tk))
+    mb[rng.random(mb.shape) < 0.15] = -np.inf
+    for causal, w, bias in ((True, 0, None), (False, 0, mb), (True, 2, mb)):
+        kw = dict(scale=0.7, causal=causal, bias=bias, window=w)
+        dq, dk, dv = R.attention_varlen_backward(q, k, v, g, cu_q, cu_k, **kw)
+        # (c)
+        assert not dq[:, :, sum(lq):].any() and not dk[:, :, sum(lk):].any() and not dv[:, :, sum(lk):].any()
+
+        def loss(qq, kk, vv):
+            o, _, _ = R.attention_varlen(qq, kk, vv, cu_q, cu_k, **kw)
+            return float((o * g).sum())
+        eps = 1e-6
+        for name, x, grad in (("dq", q, dq), ("dk", k, dk), ("dv", v, dv)):
+            for idx in [tuple(rng.integers(0, n) for n in x.shape) for _ in range(12)]:
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                args_p = [xp if y is x else y for y in (q, k, v)]
+                args_m = [xm if y is x else y for y in (q, k, v)]
+                fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+                assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+        # (b) the padded batch, one sequence at a time
+        for s in range(len(lq)):
+            q0, q1, k0, k1 = cu_q[s], cu_q[s + 1], cu_k[s], cu_k[s + 1]
+            bucket = 7
+            qp = np.zeros((1, hq, bucket, d_h)); gp = np.zeros((1, hq, bucket, d_v))
+            kp = np.zeros((1, hkv, bucket, d_h)); vp = np.zeros((1, hkv, bucket, d_v))
+            bp = np.zeros((1, hq, bucket, bucket))
+            qp[:, :, bucket - (q1 - q0):] = q[:, :, q0:q1]
+            gp[:, :, bucket - (q1 - q0):] = g[:, :, q0:q1]
+            kp[:, :, :k1 - k0] = k[:, :, k0:k1]
+            vp[:, :, :k1 - k0] = v[:, :, k0:k1]
+            bp[:, :, :, k1 - k0:] = -np.inf
+            if bias is not None:
+                bp[:, :, bucket - (q1 - q0):, :k1 - k0] = bias[:, :, q0:q1, k0:k1]
+            pq, pk, pv = R.attention_backward(qp, kp, vp, gp, scale=0.7, causal=causal,
+                                              q_offset=(k1 - k0) - bucket, bias=bp, window=w)
+            np.testing.assert_allclose(dq[:, :, q0:q1], pq[:, :, bucket - (q1 - q0):], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(dk[:, :, k0:k1], pk[:, :, :k1 - k0], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(dv[:, :, k0:k1], pv[:, :, :k1 - k0], rtol=0, atol=1e-12)
+
+
 ALL_CHECKS = [
     check_example_25_1_exact, check_example_25_1_fp64, check_exercise_33_2,
     check_kv_cache_vectors, check_equal_scores_mean, check_single_and_two_keys,
@@ -765,5 +825,5 @@ ALL_CHECKS = [
     check_backward_finite_differences, check_backward_shift_direction, check_backward_identities,
     check_backward_single_key, check_backward_library_autograd, check_backward_sampled_matches_full,
     check_varlen_equals_padded, check_varlen_sequences_independent, check_varlen_key_bias_broadcast,
-    check_kvlens_equals_padded,
+    check_kvlens_equals_padded, check_varlen_backward,
 ]

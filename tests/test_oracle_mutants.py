@@ -56,6 +56,10 @@ MUTANTS = {
     "varlen_bias_rows_unshifted": ("(slice(q0, q1) if bb.shape[2] != 1", "(slice(0, q1 - q0) if bb.shape[2] != 1"),
     "kvlens_top_left": ("q_offset=q_offset + n_k - t_q, bias=b_s", "q_offset=q_offset, bias=b_s"),
     "kvlens_keeps_all_keys": ("k[b:b + 1, :, :n_k], v[b:b + 1, :, :n_k]", "k[b:b + 1], v[b:b + 1]"),
+    "varlen_bwd_top_left": ("scale=scale, causal=causal, q_offset=q_offset + (k1 - k0) - (q1 - q0),\n                               bias=b_s",
+                            "scale=scale, causal=causal, q_offset=q_offset,\n                               bias=b_s"),
+    "varlen_bwd_dk_rows": ("dq[:, :, q0:q1], dk[:, :, k0:k1], dv[:, :, k0:k1] = g",
+                           "dq[:, :, q0:q1], dk[:, :, q0:q0 + k1 - k0], dv[:, :, k0:k1] = g"),
 }
 
 
