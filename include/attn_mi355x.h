@@ -94,7 +94,7 @@ typedef struct {
    * sequence to a bucket length b(T) costs dense attention about
    * E[b(T)^2 - T^2] extra score work; these fields remove the padding).
    *
-   * Packed sequences (attn_fwd only): with cu_seqlens_q != NULL, batch must
+   * Packed sequences (attn_fwd and attn_bwd): with cu_seqlens_q != NULL, batch must
    * be 1 and Q, O (rows) and K, V (keys) hold n_seqs sequences one after the
    * other along T.  Sequence s owns query rows [cu_seqlens_q[s],
    * cu_seqlens_q[s+1]) and keys [cu_seqlens_k[s], cu_seqlens_k[s+1]); with
@@ -196,8 +196,10 @@ size_t attn_bwd_workspace_bytes(const attn_params_t* p);
  * share o_stride, d_q q_stride, d_k k_stride, d_v v_stride).  The bias (if
  * any) is a constant input and gets no gradient; rows with no legal key (LSE
  * = -inf) contribute nothing.  workspace: attn_bwd_workspace_bytes(p) bytes,
- * 256-byte aligned.  Variable-length fields (cu_seqlens_q, seqlens_k) are not
- * taken: ATTN_E_UNSUPPORTED. */
+ * 256-byte aligned.  Packed sequences (cu_seqlens_q) are taken as in
+ * attn_fwd, each sequence's gradients from its own rows and keys; rows and
+ * keys outside every sequence are not written, and n_seqs = 0 writes nothing.
+ * Per-batch KV lengths (seqlens_k) are not taken: ATTN_E_UNSUPPORTED. */
 int attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v,
              const void* o, const float* lse, const void* d_o, void* d_q, void* d_k,
              void* d_v, void* workspace, size_t workspace_bytes, void* stream);

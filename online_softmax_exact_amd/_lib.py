@@ -249,22 +249,30 @@ def attn_decode_splitkv(q, k_cache, v_cache, *, split_size, scale=None, causal=T
 
 
 def attn_bwd(q, k, v, o, lse, d_o, *, scale=None, causal=True, q_offset=0, bias=None, window=0,
+             cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
              d_q=None, d_k=None, d_v=None, workspace=None, stream=None):
     """Gradients (d_q, d_k, d_v) of attn_fwd's attention for the upstream
     gradient ``d_o``, recomputed from the forward's ``o`` and ``lse``.  Each
     gradient gets the shape, strides and dtype of its forward tensor; ``d_o``
-    must have the strides of ``o``."""
+    must have the strides of ``o``.
+
+    Packed sequences take the forward's ``cu_seqlens_q`` / ``cu_seqlens_k`` /
+    ``max_seqlen_q``; the library leaves rows and keys outside every sequence
+    unwritten, so gradients allocated here start at zero."""
     lib = load_library()
     if d_o.shape != o.shape or d_o.stride() != o.stride() or d_o.dtype != o.dtype:
         raise ValueError("d_o must have the shape, strides and dtype of o")
     if not lse.is_contiguous() or lse.shape != o.shape[:3] or lse.dtype != torch.float32:
         raise ValueError("lse must be the contiguous float32 [B, H_q, T_q] LSE of the forward")
     p = make_params(q, k, v, o, scale=scale, causal=causal, q_offset=q_offset, bias=bias,
-                    window=window)
+                    window=window, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
+                    max_seqlen_q=max_seqlen_q)
     grads = []
     for t, g in ((q, d_q), (k, d_k), (v, d_v)):
         if g is None:
             g = torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
+            if cu_seqlens_q is not None:
+                g.zero_()
         elif g.shape != t.shape or g.stride() != t.stride() or g.dtype != t.dtype:
             raise ValueError("gradients must have the shape, strides and dtype of their tensors")
         grads.append(g)

@@ -111,6 +111,33 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Packed sequences: the sequence holding packed index x of an axis whose
+// offsets are cu[0..n] (the last sequence starting at or before x, by binary
+// search over the offsets clamped to [0, T]), and its clamped extent [lo, hi)
+// (hi >= lo).  Returns false when x lies in no sequence.
+__device__ __forceinline__ bool find_seq(const int32_t* cu, int64_t n, int64_t T, int64_t x,
+                                         int64_t* s, int64_t* lo, int64_t* hi) {
+  auto c = [&](int64_t i) { const int64_t y = cu[i]; return y < 0 ? 0 : (y > T ? T : y); };
+  int64_t a = 0, b = n - 1;
+  while (a < b) {
+    const int64_t mid = (a + b + 1) / 2;
+    if (c(mid) <= x) a = mid; else b = mid - 1;
+  }
+  *s = a;
+  *lo = c(a);
+  const int64_t e = c(a + 1);
+  *hi = e > *lo ? e : *lo;
+  return x >= *lo && x < *hi;
+}
+
+// The clamped extent of sequence s of an axis with offsets cu (see find_seq).
+__device__ __forceinline__ void seq_extent(const int32_t* cu, int64_t T, int64_t s, int64_t* lo, int64_t* hi) {
+  auto c = [&](int64_t i) { const int64_t y = cu[i]; return y < 0 ? 0 : (y > T ? T : y); };
+  *lo = c(s);
+  const int64_t e = c(s + 1);
+  *hi = e > *lo ? e : *lo;
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   __device__ static float load(const float* p, int64_t i) { return p[i]; }

@@ -39,11 +39,10 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(Problem pb, const T* __
   }
 }
 
-// Legal-key range of query row i: [lo, hi).
-__device__ __forceinline__ void key_range(const Problem& pb, int64_t i, int64_t* lo, int64_t* hi) {
-  const int64_t pos = pb.q_offset + i;
+// Legal-key range [lo, hi) of a row at logical position pos over t_k keys.
+__device__ __forceinline__ void key_range(const Problem& pb, int64_t pos, int64_t t_k, int64_t* lo, int64_t* hi) {
   *lo = 0;
-  *hi = pb.t_k;
+  *hi = t_k;
   if (pb.causal && pos + 1 < *hi) *hi = pos + 1;
   if (pb.window > 0 && pos - pb.window + 1 > *lo) *lo = pos - pb.window + 1;
 }
@@ -62,10 +61,21 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(Problem pb, const T* __rest
   const int wave = threadIdx.x >> 6;
   for (int64_t base = blockIdx.x * int64_t(kWaves); base < rows; base += int64_t(gridDim.x) * kWaves) {
     const int64_t r = base + wave;
-    const bool ok = r < rows;
+    bool ok = r < rows;
     const int64_t i = ok ? r % pb.t_q : 0, bh = ok ? r / pb.t_q : 0;
     const int64_t hq = bh % pb.heads_q, b = bh / pb.heads_q;
     const int64_t kvh = hq / pb.group;
+    // This row's keys [k0, k0 + t_k) and position (packed sequences: its
+    // sequence's own, rows at the end of its keys; a row outside every
+    // sequence is not written).
+    int64_t k0 = 0, t_k = pb.t_k, pos = pb.q_offset + i;
+    if (pb.cu_q != nullptr && ok) {
+      int64_t sq, q0, q1, k1;
+      ok = find_seq(pb.cu_q, pb.n_seqs, pb.t_q, i, &sq, &q0, &q1);
+      seq_extent(pb.cu_k, pb.t_k, sq, &k0, &k1);
+      t_k = k1 - k0;
+      pos = pb.q_offset + t_k - (q1 - q0) + (i - q0);
+    }
     const T* qrow = q + b * pb.qs[0] + hq * pb.qs[1] + i * pb.qs[2];
     const T* grow = d_o + b * pb.os[0] + hq * pb.os[1] + i * pb.os[2];
     for (int d = lane; d < kMaxD; d += 64) {
@@ -78,11 +88,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(Problem pb, const T* __rest
       const float dd = ws_d[r];
       float acc[kAcc] = {0.0f, 0.0f, 0.0f, 0.0f};
       int64_t lo, hi;
-      key_range(pb, i, &lo, &hi);
+      key_range(pb, pos, t_k, &lo, &hi);
       if (l2 == -INFINITY) hi = lo;              // no legal key: G_Q = 0
-      const T* kbase = k + b * pb.ks[0] + kvh * pb.ks[1];
-      const T* vbase = v + b * pb.vs[0] + kvh * pb.vs[1];
-      const float* brow = HAS_BIAS ? pb.bias + b * pb.bs[0] + hq * pb.bs[1] + i * pb.bs[2] : nullptr;
+      const T* kbase = k + b * pb.ks[0] + kvh * pb.ks[1] + k0 * pb.ks[2];
+      const T* vbase = v + b * pb.vs[0] + kvh * pb.vs[1] + k0 * pb.vs[2];
+      const float* brow =
+          HAS_BIAS ? pb.bias + b * pb.bs[0] + hq * pb.bs[1] + i * pb.bs[2] + k0 * pb.bs[3] : nullptr;
       for (int64_t kb = lo; kb < hi; kb += 64) {
         const int64_t j = kb + lane;
         float ds = 0.0f;
@@ -140,9 +151,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(Problem pb, const T* __re
   const int wave = threadIdx.x >> 6;
   for (int64_t base = blockIdx.x * int64_t(kWaves); base < keys; base += int64_t(gridDim.x) * kWaves) {
     const int64_t r = base + wave;
-    const bool ok = r < keys;
+    bool ok = r < keys;
     const int64_t j = ok ? r % pb.t_k : 0, bh = ok ? r / pb.t_k : 0;
     const int64_t kvh = bh % pb.heads_kv, b = bh / pb.heads_kv;
+    // This key's rows [q0, q0 + t_q) and its index jl among its sequence's
+    // keys (packed sequences: its own sequence, whose rows sit at the end of
+    // its keys; a key outside every sequence is not written).
+    int64_t q0 = 0, t_q = pb.t_q, jl = j, q_off = pb.q_offset;
+    if (pb.cu_q != nullptr && ok) {
+      int64_t sk, k0, k1, q1;
+      ok = find_seq(pb.cu_k, pb.n_seqs, pb.t_k, j, &sk, &k0, &k1);
+      seq_extent(pb.cu_q, pb.t_q, sk, &q0, &q1);
+      t_q = q1 - q0;
+      jl = j - k0;
+      q_off = pb.q_offset + (k1 - k0) - t_q;
+    }
     const T* krow = k + b * pb.ks[0] + kvh * pb.ks[1] + j * pb.ks[2];
     const T* vrow = v + b * pb.vs[0] + kvh * pb.vs[1] + j * pb.vs[2];
     for (int d = lane; d < kMaxD; d += 64) {
@@ -153,16 +176,17 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(Problem pb, const T* __re
     if (ok) {
       // Rows i that see key j: q_offset + i >= j (causal) and
       // q_offset + i - W + 1 <= j (window).
-      int64_t ilo = 0, ihi = pb.t_q;
-      if (pb.causal && j - pb.q_offset > ilo) ilo = j - pb.q_offset;
-      if (pb.window > 0 && j - pb.q_offset + pb.window < ihi) ihi = j - pb.q_offset + pb.window;
+      int64_t ilo = 0, ihi = t_q;
+      if (pb.causal && jl - q_off > ilo) ilo = jl - q_off;
+      if (pb.window > 0 && jl - q_off + pb.window < ihi) ihi = jl - q_off + pb.window;
       float ak[kAcc] = {0.0f, 0.0f, 0.0f, 0.0f}, av[kAcc] = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int64_t g = 0; g < pb.group; ++g) {
         const int64_t hq = kvh * pb.group + g;
-        const T* qbase = q + b * pb.qs[0] + hq * pb.qs[1];
-        const T* gbase = d_o + b * pb.os[0] + hq * pb.os[1];
-        const int64_t rbase = (b * pb.heads_q + hq) * pb.t_q;
-        const float* bbase = HAS_BIAS ? pb.bias + b * pb.bs[0] + hq * pb.bs[1] + j * pb.bs[3] : nullptr;
+        const T* qbase = q + b * pb.qs[0] + hq * pb.qs[1] + q0 * pb.qs[2];
+        const T* gbase = d_o + b * pb.os[0] + hq * pb.os[1] + q0 * pb.os[2];
+        const int64_t rbase = (b * pb.heads_q + hq) * pb.t_q + q0;
+        const float* bbase =
+            HAS_BIAS ? pb.bias + b * pb.bs[0] + hq * pb.bs[1] + q0 * pb.bs[2] + j * pb.bs[3] : nullptr;
         for (int64_t ib = ilo; ib < ihi; ib += 64) {
           const int64_t i = ib + lane;
           float p = 0.0f, ds = 0.0f;

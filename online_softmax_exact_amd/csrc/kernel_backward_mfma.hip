@@ -65,6 +65,25 @@ struct BArgs {
   int32_t causal;
 };
 
+// Packed sequences: offsets of n_seqs sequences along T_q and T_k.  Packed
+// instances take it as one more kernel argument; the others keep the argument
+// block above (a larger block changes their code).
+//
+// Tile slots: sequence s owns slots [start_s, start_{s+1}) of the grid's
+// n_slots = floor(T / 128) + n_seqs, with start_s = floor(cu[s] / 128) + s
+// over the offsets of the tiled dimension (rows for dQ, keys for dK / dV).
+// floor((a + L) / 128) - floor(a / 128) + 1 >= ceil(L / 128), so each
+// sequence has a slot for every one of its tiles, found from the offsets
+// alone (no host copy of them, no per-sequence bound); slots outside a
+// sequence's tiles return at once.
+struct VArgs {
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t n_seqs, n_slots;
+};
+template <class T>
+__device__ __forceinline__ const T& first_of(const T& t) { return t; }
+
 template <int DH, int DV>
 struct BCfg {
   static constexpr int KS = DH / 16;     // k-steps over d_h
@@ -133,12 +152,50 @@ __device__ __forceinline__ const lds_char* tr_addr(const char* tile, int base, i
   return (const lds_char*)tile + src * RB + (((cb >> 4) ^ swz_v<RB>(src)) << 4) + (cb & 15);
 }
 
+// Tile slot -> (sequence, tile): the last s with start_s <= slot (a binary
+// search over the clamped offsets cu of the tiled dimension of size n).
+// Entries out of order (outside the contract) still give an s in range.
+__device__ __forceinline__ int slot_seq(const int32_t* cu, int n_seqs, int n, int slot, int* tile) {
+  int lo = 0, hi = n_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (clamp_len(cu[mid], n) / kBr + mid <= slot) lo = mid;
+    else hi = mid - 1;
+  }
+  *tile = slot - (clamp_len(cu[lo], n) / kBr + lo);
+  return lo;
+}
+
+// Moves the row pointers (q, d_o and, for dQ, the output) to sequence sq's
+// first row and the key pointers (k, v and, for dK / dV, the output) to its
+// first key, and makes the sizes and q_offset the sequence's own, with its
+// rows at the end of its keys.  *row_base is the packed row of the sequence's
+// row 0 (LSE and D keep the packed layout).
+template <bool OUT_ROWS>
+__device__ __forceinline__ void enter_seq(BArgs& a, const VArgs& va, int sq, int64_t out_row_stride,
+                                          int32_t* row_base) {
+  const int q0 = clamp_len(va.cu_q[sq], a.t_q);
+  const int q1 = max(q0, clamp_len(va.cu_q[sq + 1], a.t_q));
+  const int k0 = clamp_len(va.cu_k[sq], a.t_k);
+  const int k1 = max(k0, clamp_len(va.cu_k[sq + 1], a.t_k));
+  a.q += static_cast<int64_t>(q0) * a.qs[2];
+  a.d_o += static_cast<int64_t>(q0) * a.os[2];
+  a.k += static_cast<int64_t>(k0) * a.ks[2];
+  a.v += static_cast<int64_t>(k0) * a.vs[2];
+  a.out += static_cast<int64_t>(OUT_ROWS ? q0 : k0) * out_row_stride;
+  *row_base = q0;
+  a.q_offset += (k1 - k0) - (q1 - q0);
+  a.t_q = q1 - q0;
+  a.t_k = k1 - k0;
+}
+
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <int DH, int DV>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a) {
+template <int DH, int DV, class... Var>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a, Var... var) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  constexpr bool VAR = sizeof...(Var) > 0;
   using C = BCfg<DH, DV>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::H_BYTES + 2 * C::V_BYTES];
   char* const kring = smem;
@@ -150,18 +207,28 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a) {
   const int h = lane >> 5;
   const int lr = lane & 31;
 
-  // Heaviest query tiles first.
+  // Heaviest query tiles first (packed sequences: slots in descending order,
+  // so each sequence's last tile first).
   const int bid = blockIdx.x;
-  const int qt = a.n_tiles_grid - 1 - bid / a.n_units;
+  int qt = a.n_tiles_grid - 1 - bid / a.n_units;
   const int bh = bid % a.n_units;
   const int b = bh / a.heads_q;
   const int hq = bh % a.heads_q;
   const int kvh = hq / a.group;
+  int64_t ridx_base = (static_cast<int64_t>(b) * a.heads_q + hq) * a.t_q;   // LSE / D index of row 0
+  if constexpr (VAR) {
+    const VArgs& va = first_of(var...);
+    const int sq = slot_seq(va.cu_q, va.n_seqs, a.t_q, qt, &qt);
+    int32_t row_base;
+    enter_seq<true>(a, va, sq, a.qs[2], &row_base);
+    if (qt < 0 || qt * kBr >= a.t_q) return;   // whole workgroup: a slot outside the sequence's tiles
+    ridx_base += row_base;
+  }
 
   const int row0 = qt * kBr + wave * kRowsW;
   const int row = row0 + lr;
   const bool row_ok = row < a.t_q;
-  const int64_t ridx = (static_cast<int64_t>(b) * a.heads_q + hq) * a.t_q + row;
+  const int64_t ridx = ridx_base + row;
 
   // Q^T and dO^T operands of this lane's row.
   u32x4 qreg[C::KS], greg[C::MS];
@@ -339,9 +406,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a) {
 // ---------------------------------------------------------------------------
 // dK (WHICH = 1) or dV (WHICH = 0)
 // ---------------------------------------------------------------------------
-template <int DH, int DV, int WHICH>
-__global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a) {
+template <int DH, int DV, int WHICH, class... Var>
+__global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Var... var) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  constexpr bool VAR = sizeof...(Var) > 0;
   using C = BCfg<DH, DV>;
   constexpr bool DK = WHICH == 1;
   constexpr int MOUT = DK ? C::MQ : C::MV;     // 32-wide output slices
@@ -359,10 +427,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a) {
 
   // Low key tiles first (with causal masking they are seen by more rows).
   const int bid = blockIdx.x;
-  const int kt = bid / a.n_units;
+  int kt = bid / a.n_units;
   const int bh = bid % a.n_units;
   const int b = bh / a.heads_kv;
   const int kvh = bh % a.heads_kv;
+  const int32_t t_q_all = a.t_q;   // rows per head of LSE and D
+  int32_t row_base = 0;            // packed row of the sequence's row 0
+  if constexpr (VAR) {
+    const VArgs& va = first_of(var...);
+    const int sq = slot_seq(va.cu_k, va.n_seqs, a.t_k, kt, &kt);
+    enter_seq<false>(a, va, sq, DK ? a.ks[2] : a.vs[2], &row_base);
+    if (kt < 0 || kt * kBr >= a.t_k) return;   // whole workgroup: a slot outside the sequence's tiles
+  }
 
   const int key0 = kt * kBr + wave * kRowsW;   // first key of this wave
   const int key = key0 + lr;
@@ -414,7 +490,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a) {
     if (wave == 0) {
       // 64 LSEs and 64 D values of the tile's rows (4 bytes per lane; rows
       // past T_q read as 0 and are masked).
-      const int64_t r0 = (static_cast<int64_t>(b) * a.heads_q + hq) * a.t_q + i0;
+      const int64_t r0 = (static_cast<int64_t>(b) * a.heads_q + hq) * t_q_all + row_base + i0;
       const int64_t n = a.t_q - i0;
       const auto rl = make_rsrc(a.lse + r0, n * 4);
       const auto rd = make_rsrc(a.dd + r0, n * 4);
@@ -614,15 +690,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a) {
 }
 
 template <int DH, int DV, int WHICH>
-hipError_t launch_kv(const BArgs& a, int64_t blocks, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_kv_mfma_kernel<DH, DV, WHICH>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
-                     0, s, a);
+hipError_t launch_kv(const BArgs& a, const VArgs& va, int64_t blocks, hipStream_t s) {
+  if (va.cu_q != nullptr)
+    hipLaunchKernelGGL((bwd_kv_mfma_kernel<DH, DV, WHICH, VArgs>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, s, a, va);
+  else
+    hipLaunchKernelGGL((bwd_kv_mfma_kernel<DH, DV, WHICH>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                       0, s, a);
   return hipGetLastError();
 }
 
 template <int DH, int DV>
-hipError_t launch_dq(const BArgs& a, int64_t blocks, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_dq_mfma_kernel<DH, DV>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a);
+hipError_t launch_dq(const BArgs& a, const VArgs& va, int64_t blocks, hipStream_t s) {
+  if (va.cu_q != nullptr)
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<DH, DV, VArgs>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                       s, a, va);
+  else
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<DH, DV>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -644,7 +728,8 @@ bool launch_bwd_dq_mfma(const Problem& pb, int dtype, const void* q, const void*
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(d_q)) return false;
   for (int i = 0; i < 3; ++i)
     if ((pb.qs[i] | pb.ks[i] | pb.vs[i] | pb.os[i]) & 7) return false;
-  const int64_t n_qtiles = (pb.t_q + kBr - 1) / kBr;
+  const bool packed = pb.cu_q != nullptr;
+  const int64_t n_qtiles = packed ? pb.t_q / kBr + pb.n_seqs : (pb.t_q + kBr - 1) / kBr;
   const int64_t blocks = n_qtiles * pb.batch * pb.heads_q;
   if (blocks >= (int64_t(1) << 31) || pb.batch * pb.heads_q >= (int64_t(1) << 30)) return false;
   BArgs a{};
@@ -666,6 +751,7 @@ bool launch_bwd_dq_mfma(const Problem& pb, int dtype, const void* q, const void*
   a.heads_kv = static_cast<int32_t>(pb.heads_kv);
   a.group = pb.group;
   a.n_tiles_grid = static_cast<int32_t>(n_qtiles);
+  const VArgs va{pb.cu_q, pb.cu_k, static_cast<int32_t>(pb.n_seqs), static_cast<int32_t>(n_qtiles)};
   a.n_units = static_cast<int32_t>(pb.batch * pb.heads_q);
   a.scale_log2 = pb.scale_log2;
   a.causal = pb.causal;
@@ -673,10 +759,10 @@ bool launch_bwd_dq_mfma(const Problem& pb, int dtype, const void* q, const void*
     *err = hipSuccess;
     return true;
   }
-  if (pb.d_h == 128 && pb.d_v == 128) *err = launch_dq<128, 128>(a, blocks, stream);
-  else if (pb.d_h == 64 && pb.d_v == 128) *err = launch_dq<64, 128>(a, blocks, stream);
-  else if (pb.d_h == 128 && pb.d_v == 64) *err = launch_dq<128, 64>(a, blocks, stream);
-  else *err = launch_dq<64, 64>(a, blocks, stream);
+  if (pb.d_h == 128 && pb.d_v == 128) *err = launch_dq<128, 128>(a, va, blocks, stream);
+  else if (pb.d_h == 64 && pb.d_v == 128) *err = launch_dq<64, 128>(a, va, blocks, stream);
+  else if (pb.d_h == 128 && pb.d_v == 64) *err = launch_dq<128, 64>(a, va, blocks, stream);
+  else *err = launch_dq<64, 64>(a, va, blocks, stream);
   return true;
 }
 
@@ -694,7 +780,8 @@ bool launch_bwd_dkdv_mfma(const Problem& pb, int dtype, const void* q, const voi
     return false;
   for (int i = 0; i < 3; ++i)
     if ((pb.qs[i] | pb.ks[i] | pb.vs[i] | pb.os[i]) & 7) return false;
-  const int64_t n_ktiles = (pb.t_k + kBr - 1) / kBr;
+  const bool packed = pb.cu_q != nullptr;
+  const int64_t n_ktiles = packed ? pb.t_k / kBr + pb.n_seqs : (pb.t_k + kBr - 1) / kBr;
   const int64_t blocks = n_ktiles * pb.batch * pb.heads_kv;
   if (blocks >= (int64_t(1) << 31) || pb.batch * pb.heads_kv >= (int64_t(1) << 30)) return false;
   BArgs a{};
@@ -715,6 +802,7 @@ bool launch_bwd_dkdv_mfma(const Problem& pb, int dtype, const void* q, const voi
   a.heads_kv = static_cast<int32_t>(pb.heads_kv);
   a.group = pb.group;
   a.n_tiles_grid = static_cast<int32_t>(n_ktiles);
+  const VArgs va{pb.cu_q, pb.cu_k, static_cast<int32_t>(pb.n_seqs), static_cast<int32_t>(n_ktiles)};
   a.n_units = static_cast<int32_t>(pb.batch * pb.heads_kv);
   a.scale_log2 = pb.scale_log2;
   a.causal = pb.causal;
@@ -722,10 +810,10 @@ bool launch_bwd_dkdv_mfma(const Problem& pb, int dtype, const void* q, const voi
   if (blocks == 0) return true;
   for (int which = 0; which < 2 && *err == hipSuccess; ++which) {
     a.out = static_cast<uint16_t*>(which ? d_k : d_v);
-    if (pb.d_h == 128 && pb.d_v == 128) *err = which ? launch_kv<128, 128, 1>(a, blocks, stream) : launch_kv<128, 128, 0>(a, blocks, stream);
-    else if (pb.d_h == 64 && pb.d_v == 128) *err = which ? launch_kv<64, 128, 1>(a, blocks, stream) : launch_kv<64, 128, 0>(a, blocks, stream);
-    else if (pb.d_h == 128 && pb.d_v == 64) *err = which ? launch_kv<128, 64, 1>(a, blocks, stream) : launch_kv<128, 64, 0>(a, blocks, stream);
-    else *err = which ? launch_kv<64, 64, 1>(a, blocks, stream) : launch_kv<64, 64, 0>(a, blocks, stream);
+    if (pb.d_h == 128 && pb.d_v == 128) *err = which ? launch_kv<128, 128, 1>(a, va, blocks, stream) : launch_kv<128, 128, 0>(a, va, blocks, stream);
+    else if (pb.d_h == 64 && pb.d_v == 128) *err = which ? launch_kv<64, 128, 1>(a, va, blocks, stream) : launch_kv<64, 128, 0>(a, va, blocks, stream);
+    else if (pb.d_h == 128 && pb.d_v == 64) *err = which ? launch_kv<128, 64, 1>(a, va, blocks, stream) : launch_kv<128, 64, 0>(a, va, blocks, stream);
+    else *err = which ? launch_kv<64, 64, 1>(a, va, blocks, stream) : launch_kv<64, 64, 0>(a, va, blocks, stream);
   }
   return true;
 }

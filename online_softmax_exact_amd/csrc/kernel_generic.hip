@@ -42,17 +42,9 @@ __global__ __launch_bounds__(256) void generic_kernel(
     // batch's own length; rows sit at the end of their keys in both.
     int64_t k0 = 0, t_k = pb.t_k, pos = pb.q_offset + i;
     if (pb.cu_q != nullptr && row_ok) {
-      auto cq = [&](int64_t x) { const int64_t y = pb.cu_q[x]; return y < 0 ? 0 : (y > pb.t_q ? pb.t_q : y); };
-      auto ck = [&](int64_t x) { const int64_t y = pb.cu_k[x]; return y < 0 ? 0 : (y > pb.t_k ? pb.t_k : y); };
-      int64_t s_lo = 0, s_hi = pb.n_seqs - 1;   // last sequence starting at or before row i
-      while (s_lo < s_hi) {
-        const int64_t mid = (s_lo + s_hi + 1) / 2;
-        if (cq(mid) <= i) s_lo = mid; else s_hi = mid - 1;
-      }
-      const int64_t q0 = cq(s_lo), q1 = cq(s_lo + 1) > q0 ? cq(s_lo + 1) : q0;
-      k0 = ck(s_lo);
-      const int64_t k1 = ck(s_lo + 1) > k0 ? ck(s_lo + 1) : k0;
-      row_ok = i >= q0 && i < q1;
+      int64_t sq, q0, q1, k1;
+      row_ok = find_seq(pb.cu_q, pb.n_seqs, pb.t_q, i, &sq, &q0, &q1);
+      seq_extent(pb.cu_k, pb.t_k, sq, &k0, &k1);
       t_k = k1 - k0;
       pos = pb.q_offset + t_k - (q1 - q0) + (i - q0);
     } else if (pb.kv_lens != nullptr) {

@@ -191,15 +191,29 @@ def test_varlen_rejects(lib):
 
 def test_varlen_unsupported_entry_points(lib):
     # Split-KV decode takes per-batch lengths but not packed sequences; the
-    # backward takes neither.
+    # backward takes packed sequences but not per-batch lengths.
     p = packed_params()
     need = lib.attn_decode_workspace_bytes(ctypes.byref(p), 4)
     assert lib.attn_decode_splitkv(ctypes.byref(p), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need,
                                    None) == -4
-    for params in (packed_params(), good_params(seqlens_k=0x400000)):
-        need = lib.attn_bwd_workspace_bytes(ctypes.byref(params))
-        assert lib.attn_bwd(ctypes.byref(params), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                            FAKE, FAKE, need, None) == -4
+    params = good_params(seqlens_k=0x400000)
+    need = lib.attn_bwd_workspace_bytes(ctypes.byref(params))
+    assert lib.attn_bwd(ctypes.byref(params), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        FAKE, FAKE, need, None) == -4
+
+
+def test_packed_backward_host_checks(lib):
+    # Packed sequences reach the backward's kernels only through the same
+    # checks as attn_fwd; no sequence is a successful call that launches
+    # nothing (no GPU is touched here).
+    params = packed_params(n_seqs=0)
+    need = lib.attn_bwd_workspace_bytes(ctypes.byref(params))
+    assert lib.attn_bwd(ctypes.byref(params), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        FAKE, FAKE, need, None) == 0
+    for bad, code in ((packed_params(cu_seqlens_k=None), -1), (packed_params(batch=2), -2),
+                      (packed_params(seqlens_k=0x400000), -2), (packed_params(n_seqs=-1), -2)):
+        assert lib.attn_bwd(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, FAKE, need, None) == code
 
 
 def test_binding_varlen_arguments():
