@@ -109,7 +109,28 @@ def varlen_section(torch, attn, inputs, dev, dk, dv_, dq, dec, ws, timed):
     padded_ms = timed(lambda: attn.attn_fwd(qp, kp, vp, scale=scale, causal=True, bias=bias, out=op, lse=lp))
     flops, bytes_ = varlen_counts(lengths, hq, d_h, d_v)
     pt = flops / (packed_ms * 1e-3) / 1e12
-    del qp, kp, vp, op, lp
+
+    # Backward of the same packed batch, against the padded batch's backward
+    # (causal masking alone keeps real rows off padded keys, and a zero
+    # upstream gradient on padded rows adds nothing to real keys).
+    g = torch.randn(o.shape, generator=torch.Generator().manual_seed(1006)).to(q.dtype).to(dev)
+    gq, gk, gv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    wsb = torch.empty(hq * q.shape[2] * 4 + 256, dtype=torch.uint8, device=dev)
+    pbwd_ms = timed(lambda: attn.attn_bwd(q, k, v, o, lse, g, scale=scale, causal=True, cu_seqlens_q=cu_q,
+                                          cu_seqlens_k=cu_k, max_seqlen_q=max(lengths), d_q=gq, d_k=gk, d_v=gv,
+                                          workspace=wsb))
+    attn.attn_fwd(qp, kp, vp, scale=scale, causal=True, out=op, lse=lp)
+    gp = torch.zeros_like(op)
+    for b, n in enumerate(lengths):
+        s0 = int(cu_q[b])
+        gp[b, :, :n] = g[0, :, s0:s0 + n]
+    gqp, gkp, gvp = torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(vp)
+    wsp = torch.empty(8 * hq * t * 4, dtype=torch.uint8, device=dev)
+    padbwd_ms = timed(lambda: attn.attn_bwd(qp, kp, vp, op, lp, gp, scale=scale, causal=True, d_q=gqp, d_k=gkp,
+                                            d_v=gvp, workspace=wsp))
+    b_flops = flops // (2 * (d_h + d_v)) * 2 * (3 * d_h + 2 * d_v)
+    bt = b_flops / (pbwd_ms * 1e-3) / 1e12
+    del qp, kp, vp, op, lp, gp, gqp, gkp, gvp
 
     kv_lens = inputs.varlen_lengths(16, 32768, 1003)
     lens_t = torch.tensor(kv_lens, dtype=torch.int32, device=dev)
@@ -131,6 +152,16 @@ def varlen_section(torch, attn, inputs, dev, dk, dv_, dq, dec, ws, timed):
                                  "unit": "TFLOP/s", "frac": round(pt / PEAK_BF16_TFLOPS, 4),
                                  "traffic": recorded_traffic("packed_prefill"),
                                  "per_launch_flops": flops, "per_launch_bytes": bytes_}},
+        "backward": {"workload": f"backward of the packed causal prefill above (attn_bwd with cu_seqlens: "
+                                 "D, dQ, dV, dK kernels)",
+                     "ms": round(pbwd_ms, 4), "value": round(bt, 2), "unit": "TFLOP/s",
+                     "padded_ms": round(padbwd_ms, 4),
+                     "padded": "the same sequences padded to 4096 (B=8), dense causal attn_bwd",
+                     "speedup_vs_padded": round(padbwd_ms / pbwd_ms, 3),
+                     "roofline": {"bound": "mfma", "achieved": round(bt, 2), "peak": PEAK_BF16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(bt / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                                  "per_launch_flops": b_flops,
+                                  "flops_per_pair": "2 (3 d_h + 2 d_v): recomputed scores, dP, dV, dQ, dK"}},
         "decode": {"workload": "GQA split-KV decode B=16 Hq=32 Hkv=8 Tk<=32768 d=128 S=512 with per-batch "
                                f"KV lengths uniform in [1, 32768] (sum {sum(kv_lens)}; attn_decode_splitkv "
                                "with seqlens_k)",

@@ -1,10 +1,11 @@
-"""Seeded random problems across every option of the forward entry points,
-each compared element by element with the oracle: dtype, head sizes on the
-fast kernels (64, 128) and on the generic one, head grouping, causal or not,
-any query offset (negative, inside, past the keys), sliding windows, every
-bias broadcast with -inf entries, T_k = 0, split-KV decode with any split
-size, packed sequences and per-batch KV lengths.  Sizes stay small so the
-oracle finishes in well under a second per case."""
+"""Seeded random problems across every option of the entry points, each
+compared element by element with the oracle: dtype, head sizes on the fast
+kernels (64, 128) and on the generic one, head grouping, causal or not, any
+query offset (negative, inside, past the keys), sliding windows, every bias
+broadcast with -inf entries, T_k = 0, split-KV decode with any split size,
+packed sequences and per-batch KV lengths, and the backward on dense and
+packed batches.  Sizes stay small so the oracle finishes in well under a
+second per case."""
 
 import numpy as np
 import pytest
@@ -187,4 +188,65 @@ def test_random_backward_parity(i):
         assert not np.isnan(g64).any(), name
         scale = max(float(np.abs(want).max()), 1e-30)
         err = np.abs(g64 - want) / scale
+        assert err.max() <= tol["max"] and err.mean() <= tol["mean"], f"{name}: {err.max():.2e} / {err.mean():.2e}"
+
+
+N_BWD_PACKED = 16
+
+
+def draw_packed_bwd_case(i):
+    r = np.random.default_rng(9000 + i)
+    fast = r.random() < 0.7
+    n = int(r.integers(1, 6))
+    lq = [int(x) for x in r.integers(0, 300, n)]
+    c = dict(dtype=torch.float32 if r.random() < 0.2 else torch.bfloat16,
+             d_h=int(r.choice([64, 128])) if fast else int(r.choice([16, 40, 96])),
+             d_v=int(r.choice([64, 128])) if fast else int(r.choice([24, 64, 80])),
+             h_kv=int(r.choice([1, 2])), lq=lq,
+             lk=[max(0, int(x)) for x in (np.array(lq) + r.integers(-40, 300, n))],
+             causal=bool(r.random() < 0.7), window=0 if r.random() < 0.6 else int(r.integers(1, 300)),
+             bias=str(r.choice(["none", "none", "none", "packed", "keys"])),
+             masked_frac=float(r.choice([0.0, 0.1])), q_offset=int(r.choice([0, 0, 0, 5, -3])))
+    c["h_q"] = c["h_kv"] * int(r.choice([1, 2, 4]))
+    return c
+
+
+@pytest.mark.parametrize("i", range(N_BWD_PACKED))
+def test_random_packed_backward_parity(i):
+    """attn_bwd on random packed batches (empty sequences, L_q above or below
+    L_k, windows, biases, query offsets) against the oracle's packed
+    gradients, relative to each gradient's largest entry."""
+    c = draw_packed_bwd_case(i)
+    print("case", i, c, flush=True)
+    q, k, v, m, cu_q, cu_k = inputs.make_packed(c["lq"], c["lk"], c["h_q"], c["h_kv"], c["d_h"], c["d_v"],
+                                                dtype=c["dtype"], seed=200 + i, bias=c["bias"],
+                                                masked_frac=c["masked_frac"])
+    if q.shape[2] == 0:
+        pytest.skip("no rows drawn")
+    g = torch.randn((1, c["h_q"], q.shape[2], c["d_v"]), generator=torch.Generator().manual_seed(i)).to(c["dtype"])
+    dd = dev()
+    scale = inputs.default_scale(c["d_h"])
+    kw = dict(scale=scale, causal=c["causal"], q_offset=c["q_offset"], bias=None if m is None else m.to(dd),
+              window=c["window"], cu_seqlens_q=cu_q.to(dd), cu_seqlens_k=cu_k.to(dd), max_seqlen_q=max(c["lq"]))
+    qd, kd, vd = q.to(dd), k.to(dd), v.to(dd)
+    o, lse = attn.attn_fwd(qd, kd, vd, **kw)
+    dq, dk, dv = attn.attn_bwd(qd, kd, vd, o, lse, g.to(dd), **kw)
+    torch.cuda.synchronize()
+    b64 = None if m is None else f64(m)
+    ref = oracle.attention_varlen_backward(f64(q), f64(k), f64(v), f64(g), cu_q.tolist(), cu_k.tolist(),
+                                           scale=scale, causal=c["causal"], q_offset=c["q_offset"], bias=b64,
+                                           window=c["window"])
+    _, l_ref, _ = oracle.attention_varlen(f64(q), f64(k), f64(v), cu_q.tolist(), cu_k.tolist(), scale=scale,
+                                          causal=c["causal"], q_offset=c["q_offset"], bias=b64, window=c["window"])
+    # Exact zeros: rows without a legal key, and keys no row sees (dV's
+    # zeros; a row with a single legal key has dQ = 0 only up to rounding).
+    assert np.all(f64(dq)[np.isneginf(l_ref)] == 0), "dQ of a row without a legal key"
+    dead = np.all(ref[2] == 0, axis=-1)
+    assert np.all(f64(dk)[dead] == 0) and np.all(f64(dv)[dead] == 0), "gradient of an unseen key"
+    tol = BWD_TOL[c["dtype"]]
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        g64 = f64(got)
+        assert not np.isnan(g64).any(), name
+        s = max(float(np.abs(want).max()), 1e-30)
+        err = np.abs(g64 - want) / s
         assert err.max() <= tol["max"] and err.mean() <= tol["mean"], f"{name}: {err.max():.2e} / {err.mean():.2e}"
