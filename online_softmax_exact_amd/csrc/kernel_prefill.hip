@@ -63,6 +63,12 @@ using namespace pf;
 #ifndef PREFILL_FIRST_FAST
 #define PREFILL_FIRST_FAST 1           // 1: a wave's first tile, if fully visible, on the pipelined path
 #endif
+#ifndef PREFILL_BIG
+#define PREFILL_BIG 1                  // 0: the standard shape for every problem
+#endif
+#ifndef PREFILL_BIG_D64
+#define PREFILL_BIG_D64 1              // 1: the large shape also for d_h = 64, d_v = 128 (small grids)
+#endif
 #ifndef PREFILL_WAVES_PER_SIMD
 #define PREFILL_WAVES_PER_SIMD 2       // resident waves per SIMD the kernel is built for
 #endif
@@ -692,13 +698,17 @@ bool launch_prefill_mfma(const Problem& pb, int dtype, const void* q, const void
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return false;
   for (int i = 0; i < 3; ++i)
     if ((pb.qs[i] | pb.ks[i] | pb.vs[i] | pb.os[i]) & 7) return false;
-  // The large shape: d = 128, no bias, window or variable lengths, and at
-  // least one of its 256-row query tiles per CU (measured: 3-10 % faster on
-  // long causal and non-causal d = 128 problems, 2 % slower with a window,
-  // much slower on small grids).
+  // The large shape: no bias, window or variable lengths, and at least one
+  // of its 256-row query tiles per CU; d = 128 (measured: 3-10 % faster on
+  // long causal and non-causal problems, 2 % slower with a window, much
+  // slower on small grids), or d_h = 64, d_v = 128 with at most two tiles per
+  // CU (2-10 % faster there; with 1024 or more tiles -7 to +3 %).
   const bool packed = pb.cu_q != nullptr;
-  const bool big = pb.d_h == 128 && pb.d_v == 128 && pb.bias == nullptr && pb.window == 0 && !packed &&
-                   pb.kv_lens == nullptr && (pb.t_q + 255) / 256 * pb.batch * pb.heads_q >= 256;
+  const int64_t big_tiles = (pb.t_q + 255) / 256 * pb.batch * pb.heads_q;
+  const bool big_dims = (pb.d_h == 128 && pb.d_v == 128) ||
+                        (PREFILL_BIG_D64 && pb.d_h == 64 && pb.d_v == 128 && big_tiles <= 512);
+  const bool big = PREFILL_BIG && big_dims && pb.bias == nullptr && pb.window == 0 && !packed &&
+                   pb.kv_lens == nullptr && big_tiles >= 256;
   const int64_t kBr = big ? 32 * ShapeBig::kWaves : 32 * ShapeStd::kWaves;   // query rows per workgroup
   // Packed sequences: `rounds` query tiles per sequence in the grid (from the
   // caller's longest-sequence bound; longer sequences loop).
@@ -745,9 +755,14 @@ bool launch_prefill_mfma(const Problem& pb, int dtype, const void* q, const void
   const bool count = n_legal != nullptr;
   const bool var = packed || pb.kv_lens != nullptr;
   hipError_t e;
-  if (big)
+  if (big && pb.d_h == 128)
     e = count ? launch_cfg<128, 128, false, true, false, ShapeBig>(a, blocks, stream)
               : launch_cfg<128, 128, false, false, false, ShapeBig>(a, blocks, stream);
+#if PREFILL_BIG_D64
+  else if (big)
+    e = count ? launch_cfg<64, 128, false, true, false, ShapeBig>(a, blocks, stream)
+              : launch_cfg<64, 128, false, false, false, ShapeBig>(a, blocks, stream);
+#endif
   else if (pb.d_h == 128 && pb.d_v == 128) e = launch_dims<128, 128>(a, blocks, bias, count, var, stream);
   else if (pb.d_h == 64 && pb.d_v == 128) e = launch_dims<64, 128>(a, blocks, bias, count, var, stream);
   else if (pb.d_h == 128 && pb.d_v == 64) e = launch_dims<128, 64>(a, blocks, bias, count, var, stream);
