@@ -159,7 +159,8 @@ def varlen_section(torch, attn, inputs, dev, dk, dv_, dq, dec, ws, timed):
                      "padded": "the same sequences padded to 4096 (B=8), dense causal attn_bwd",
                      "speedup_vs_padded": round(padbwd_ms / pbwd_ms, 3),
                      "roofline": {"bound": "mfma", "achieved": round(bt, 2), "peak": PEAK_BF16_TFLOPS,
-                                  "unit": "TFLOP/s", "frac": round(bt / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                                  "unit": "TFLOP/s", "frac": round(bt / PEAK_BF16_TFLOPS, 4),
+                                  "traffic": backward_traffic("packed_"),
                                   "per_launch_flops": b_flops,
                                   "flops_per_pair": "2 (3 d_h + 2 d_v): recomputed scores, dP, dV, dQ, dK"}},
         "decode": {"workload": "GQA split-KV decode B=16 Hq=32 Hkv=8 Tk<=32768 d=128 S=512 with per-batch "
@@ -266,10 +267,10 @@ def recorded_traffic(key: str):
     return int(rec["traffic_bytes"]) if h.hexdigest() == rec["source_sha256"] else None
 
 
-def backward_traffic():
+def backward_traffic(prefix: str = ""):
     """HBM bytes of one attn_bwd call: its dQ, dV and dK kernels' recorded
     traffic (the D kernel reads O and dO once), or None if any is stale."""
-    parts = [recorded_traffic(k) for k in ("bwd_dq", "bwd_dv", "bwd_dk")]
+    parts = [recorded_traffic(prefix + k) for k in ("bwd_dq", "bwd_dv", "bwd_dk")]
     return None if None in parts else sum(parts)
 
 
