@@ -413,6 +413,28 @@ def main():
                                 "per_launch_flops": d_flops}},
         "cpu_baseline": None,
     }
+
+    def timed(fn, n=20):
+        """Average of n launches of fn, HIP events on the stream, after at
+        least 10 untimed launches and 0.25 s of them: after the host work
+        between sections the clock ramps up over the first tens of launches
+        (measured on the packed prefill: 0.376 ms for the first launch, 0.29
+        from about the 40th on)."""
+        t0, k = time.perf_counter(), 0
+        while k < 10 or time.perf_counter() - t0 < 0.25:
+            fn()
+            k += 1
+            if k % 10 == 0:
+                torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a_, b_ in evs:
+            a_.record(stream)
+            fn()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        return sum(a_.elapsed_time(b_) for a_, b_ in evs) / n
+
     if not args.no_backward:
         gd = torch.randn(pq.shape, generator=torch.Generator().manual_seed(4242)).to(torch.bfloat16).to(dev)
         run_prefill()                      # o and lse of the forward
@@ -423,15 +445,7 @@ def main():
             attn.attn_bwd(pq, pk, pv, po, pl, gd, scale=pre.scale, causal=True,
                           d_q=gq, d_k=gk, d_v=gv, workspace=ws_b)
 
-        for _ in range(10):
-            run_backward()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-        for a_, b_ in evs:
-            a_.record(stream)
-            run_backward()
-            b_.record(stream)
-        torch.cuda.synchronize()
-        b_ms = sum(a_.elapsed_time(b_) for a_, b_ in evs) / len(evs)
+        b_ms = timed(run_backward)
         pairs, _, _ = prefill_counts(8192, 32, 1, 128, 128)
         b_flops = 2 * (3 * 128 + 2 * 128) * pairs
         b_t = b_flops / (b_ms * 1e-3) / 1e12
@@ -443,18 +457,6 @@ def main():
                          "traffic": backward_traffic(),
                          "per_launch_flops": b_flops,
                          "flops_per_pair": "2 (3 d_h + 2 d_v): recomputed scores, dP, dV, dQ, dK"}}
-    def timed(fn, n=20):
-        """Average of n launches of fn (after 10 untimed), HIP events on the stream."""
-        for _ in range(10):
-            fn()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n)]
-        for a_, b_ in evs:
-            a_.record(stream)
-            fn()
-            b_.record(stream)
-        torch.cuda.synchronize()
-        return sum(a_.elapsed_time(b_) for a_, b_ in evs) / n
 
     if args.window > 0:
         w = args.window

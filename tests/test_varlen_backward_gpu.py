@@ -152,9 +152,11 @@ def test_single_sequence_backward_is_the_dense_call_bitwise(lq, lk, dh, dv):
 def test_packed_backward_workload_size():
     """The packed workload (8 causal sequences, lengths drawn as for the
     padded-batch workload, 16 heads, d_h 64, d_v 128): each sequence's
-    gradients equal a dense call on that sequence alone bit for bit, and rows
-    and keys sampled across sequences and heads match the oracle's sampled
-    gradients of that sequence."""
+    gradients equal a dense attn_bwd call on that sequence alone, given the
+    same forward outputs, bit for bit (the dense forward of the longest
+    sequence may pick another workgroup shape, so O and LSE come from the
+    packed call), and rows and keys sampled across sequences and heads match
+    the oracle's sampled gradients of that sequence."""
     lengths = inputs.varlen_lengths(8, 4096, 1005)
     hq, dh, dv = 16, 64, 128
     q, k, v, _, cu_q, cu_k = inputs.make_packed(lengths, lengths, hq, hq, dh, dv, seed=1005)
@@ -172,8 +174,8 @@ def test_packed_backward_workload_size():
     for s in range(len(lengths)):
         a, b = offs[s], offs[s + 1]
         sl = lambda t: t[:, :, a:b].contiguous()
-        o_s, l_s = attn.attn_fwd(sl(qd), sl(kd), sl(vd), scale=scale, causal=True)
-        ref = attn.attn_bwd(sl(qd), sl(kd), sl(vd), o_s, l_s, sl(gd), scale=scale, causal=True)
+        ref = attn.attn_bwd(sl(qd), sl(kd), sl(vd), sl(o), lse[:, :, a:b].contiguous(), sl(gd), scale=scale,
+                            causal=True)
         torch.cuda.synchronize()
         for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv_), ref):
             assert torch.equal(sl(got).view(torch.int16), want.view(torch.int16)), f"sequence {s}: {name}"
