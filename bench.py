@@ -250,10 +250,9 @@ def achievable_section(torch, dev, timed, p_tflops, d_gbs):
                      "decode_over_copy": round(d_gbs / cp_g, 4)}}
 
 
-def recorded_traffic(key: str):
-    """HBM bytes per launch of kernel `key` from the committed rocprofv3 byte
-    counters (profiles/traffic.json), or None when the kernel's sources have
-    changed since the counters were taken."""
+def _recorded(key: str):
+    """The committed rocprofv3 record of kernel `key` (profiles/traffic.json),
+    or None when the kernel's sources have changed since it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
@@ -264,7 +263,27 @@ def recorded_traffic(key: str):
     for f in rec["sources"]:
         with open(os.path.join(ROOT, "online_softmax_exact_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    return int(rec["traffic_bytes"]) if h.hexdigest() == rec["source_sha256"] else None
+    return rec if h.hexdigest() == rec["source_sha256"] else None
+
+
+def recorded_traffic(key: str):
+    """HBM bytes per launch of kernel `key` from the committed byte counters,
+    or None when stale."""
+    rec = _recorded(key)
+    return None if rec is None else int(rec["traffic_bytes"])
+
+
+def recorded_mfma(key: str):
+    """MFMA counters of kernel `key` from the committed profile (MfmaUtil in
+    percent, executed over algorithmic bf16 MFMA flops, the clock under the
+    counters), or None when stale or not recorded."""
+    rec = _recorded(key)
+    m = None if rec is None else rec.get("mfma")
+    if not m:
+        return None
+    alg = m.get("algorithmic_flops")
+    return {"mfma_util_pct": round(m["util_pct"], 1), "clock_ghz": round(m["clock_ghz"], 2),
+            "executed_over_algorithmic": round(m["executed_flops"] / alg, 4) if alg else None}
 
 
 def backward_traffic(prefix: str = ""):
@@ -404,6 +423,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic("prefill"), "kernel": "attn_fwd prefill",
+                     "counters": recorded_mfma("prefill"),
                      "per_launch_flops": p_flops, "per_launch_bytes": p_bytes},
         "decode": {"value": round(d_gbs, 1), "unit": "GB/s", "ms": round(d_avg, 4),
                    "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS,
