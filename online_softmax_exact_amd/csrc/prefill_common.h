@@ -41,6 +41,10 @@ struct Args {
   const int32_t* cu_k;
   const int32_t* kv_lens;
   int32_t n_seqs, rounds;
+  // Dense batches: 1 = batches one after the other (heads fastest, then
+  // query tiles), 0 = query tiles outermost (every batch's heaviest tiles
+  // first).
+  int32_t batch_major;
 };
 
 // x clamped to [0, n] (device-side length and offset arrays are never trusted).

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import online_softmax_exact_amd as attn
 from online_softmax_exact_amd import inputs
 from gpu_util import assert_close, ensure_built, oracle_full, to_dev
@@ -63,3 +64,30 @@ def test_large_shape_parity(case):
     assert_close(o, lse, o_ref, l_ref, torch.bfloat16, what=str(case))
     assert_close(o2, lse2, o_ref, l_ref, torch.bfloat16, what=str(case) + " (no counts)")
     assert np.array_equal(n.cpu().numpy(), n_ref), "n_legal differs"
+
+
+@pytest.mark.parametrize("case", [(9, 32, 32, 4000, 128, True), (40, 16, 8, 3000, 64, False)],
+                         ids=["B9H32-T4000-d128-c1", "B40H16/8-T3000-d64-c0"])
+def test_batch_major_order_sampled(case):
+    """Dense batches whose K/V exceeds 256 MB run batch after batch (the large
+    and the standard shape); rows sampled in every batch, at tile edges and
+    the ragged end, against the oracle row by row."""
+    b, hq, hkv, t, dh, causal = case
+    assert b * hkv * t * (dh + 128) * 2 > 256 << 20   # the order this test covers
+    print("case:", case, flush=True)
+    wl = inputs.make_random(b, hq, hkv, t, t, dh, 128, seed=zlib.crc32(repr(case).encode()) % 10_000,
+                            causal=causal)
+    q, k, v, _ = to_dev(wl)
+    o, lse, n = attn.attn_fwd(q, k, v, scale=wl.scale, causal=causal, return_n_legal=True)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(b)
+    rows = [(bb, int(h), int(i)) for bb in range(b)
+            for h, i in zip(r.integers(0, hq, 6), [0, 127, 128, 255, t - 1, int(r.integers(0, t))])]
+    ro, rl, rn = oracle.attention_rows(wl.q, wl.k, wl.v, rows, scale=wl.scale, causal=causal)
+    oc, lc, nc = o.cpu(), lse.cpu(), n.cpu()
+    got_o = np.stack([oc[x].double().numpy() for x in rows])
+    got_l = np.array([float(lc[x]) for x in rows])
+    err = np.abs(got_o - ro)
+    assert err.max() <= 1e-2 and err.mean() <= 1e-3, (err.max(), err.mean())
+    assert np.abs(got_l - rl).max() <= 1e-3
+    assert [int(nc[x]) for x in rows] == [int(x) for x in rn]
