@@ -28,6 +28,12 @@
 // Tiles are 64 rows; all rows of a tile use the XOR swizzle of the transposed
 // reads (16-byte row reads are conflict-free with it too: 16 consecutive rows
 // map chunk c to 16 distinct chunks).
+//
+// Work order: tiles outermost (dQ: heaviest causal tiles first; dK / dV: low
+// key tiles first), every (batch, head) of a tile together; dense batches
+// whose K/V exceeds the 256 MB Infinity Cache go batch after batch instead.
+// Packed sequences map grid slots to (sequence, tile) from the offsets (see
+// VArgs).
 #include "attn_internal.h"
 #include "kernels.h"
 #include "prefill_common.h"

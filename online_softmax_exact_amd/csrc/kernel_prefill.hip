@@ -1,7 +1,7 @@
 // MFMA prefill kernel for bf16 Q/K/V/O, d_h and d_v in {64, 128}.
 //
 // What it computes: for every query row, Algorithm 33.1 of "Chapter 33
-// 推理计算优化" §33.2 over key tiles of 64, i.e. exact softmax attention
+// 推理计算优化" §33.2 over key tiles of 64 (128 in the large shape), i.e. exact softmax attention
 // (eq 33.2) with the running statistics (m, l, u) of eq 33.3 merged tile by
 // tile (eqs 33.4-33.5).  Tiles that no row of a wave can see are skipped and
 // tiles that every row sees in full need no mask (§33.3, causal block
@@ -9,7 +9,9 @@
 //
 // Mapping onto CDNA4 (gfx950):
 // * A workgroup of 4 wavefronts owns 128 consecutive query rows of one
-//   (batch, head); wavefront w owns rows 32w..32w+31.
+//   (batch, head); wavefront w owns rows 32w..32w+31.  A large shape (8
+//   wavefronts, 256 rows, 128-key tiles) serves long problems without bias,
+//   window or variable lengths (see the launcher for the rule).
 // * Scores are computed transposed, S^T = K Q^T, with
 //   v_mfma_f32_32x32x16_bf16: A = a 32-key slice of the K tile (read from LDS
 //   with 16-byte reads), B = Q^T kept in registers for the whole kernel.  In

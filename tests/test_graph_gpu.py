@@ -1,7 +1,7 @@
 """The entry points under HIP graph capture: every step of the path is a
 kernel launch on the caller's stream (no device allocation, no memset, no
-host synchronisation), so a captured prefill + split-KV decode (+ merge)
-replays correctly.  Each replay runs after unrelated eager work that
+host synchronisation), so a captured prefill + split-KV decode (+ merge), and
+a captured backward, replay correctly.  Each replay runs after unrelated eager work that
 overwrites the inputs and is compared bit for bit with an eager call on the
 same inputs."""
 
@@ -67,3 +67,51 @@ def test_graph_replays_match_eager():
             ai = a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32)
             bi = b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)
             assert torch.equal(ai, bi), f"replay {rep}: {name} differs from the eager call"
+
+
+def test_graph_backward_replays_match_eager():
+    """attn_bwd (dense GQA and packed sequences) captured with its outputs and
+    workspace given: the D, dQ, dV and dK launches replay bit for bit."""
+    d = dev()
+    wl = inputs.make_random(2, 8, 2, 300, 300, 128, 128, seed=21, causal=True)
+    q, k, v = wl.q.to(d), wl.k.to(d), wl.v.to(d)
+    pq, pk, pv, _, cu_q, cu_k = inputs.make_packed([100, 257, 3], [140, 257, 3], 4, 4, 64, 128, seed=22)
+    pq, pk, pv, cu_q, cu_k = (t.to(d) for t in (pq, pk, pv, cu_q, cu_k))
+    pkw = dict(scale=inputs.default_scale(64), causal=True, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k, max_seqlen_q=257)
+    o, lse = attn.attn_fwd(q, k, v, scale=wl.scale, causal=True)
+    po, plse = attn.attn_fwd(pq, pk, pv, **pkw)
+    g, pg = torch.empty_like(o), torch.empty_like(po)
+    outs = [torch.zeros_like(t) for t in (q, k, v, pq, pk, pv)]
+    ws = torch.empty(2 * 8 * 300 * 4 + 256, dtype=torch.uint8, device=d)
+    pws = torch.empty(4 * 360 * 4 + 256, dtype=torch.uint8, device=d)
+
+    def step(stream=None):
+        attn.attn_bwd(q, k, v, o, lse, g, scale=wl.scale, causal=True, d_q=outs[0], d_k=outs[1], d_v=outs[2],
+                      workspace=ws, stream=stream)
+        attn.attn_bwd(pq, pk, pv, po, plse, pg, d_q=outs[3], d_k=outs[4], d_v=outs[5], workspace=pws,
+                      stream=stream, **pkw)
+
+    s = torch.cuda.Stream(device=d)
+    s.wait_stream(torch.cuda.current_stream(d))
+    with torch.cuda.stream(s):
+        step(s)
+    torch.cuda.current_stream(d).wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        step(s)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cpu")
+    for rep in range(4):
+        gen.manual_seed(100 + rep)
+        for t in (g, pg):
+            t.copy_(torch.randn(t.shape, generator=gen).to(t.dtype))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [x.clone() for x in outs]
+        ref = list(attn.attn_bwd(q, k, v, o, lse, g, scale=wl.scale, causal=True))
+        ref += list(attn.attn_bwd(pq, pk, pv, po, plse, pg, **pkw))
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {rep}: gradient {i} differs"
