@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill attention TFLOP/s + decode KV GB/s, as % of MI355X peak"
 PEAK_BF16_TFLOPS = 2516.6     # dense bf16 MFMA, 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3      # fp32 vector (256 CU x 2.4 GHz x 256 flop/clk)
 
 
 def prefill_counts(t: int, heads: int, batch: int, d_h: int, d_v: int):
@@ -190,10 +191,32 @@ def padded_counts(lengths, masked_rows, heads: int, t: int, d_h: int, d_v: int):
 
 
 def workloads_section(torch, attn, inputs, dev, timed):
-    """The multi-query verify (32 x 32 heads, 5 queries at the end of 4096
-    keys) against HBM, and the padded variable-length batch with its dense
-    bias (8 x 16 heads, T = 4096, d_h = 64, d_v = 128) against both ceilings."""
+    """The single-head fp32 problem (128 rows, d = 64: latency bound, timed
+    beside a one-element fill kernel as the launch floor), the
+    multi-query verify (32 x 32 heads, 5 queries at the end of 4096 keys)
+    against HBM and the matrix cores, and the padded variable-length batch with
+    its dense bias (8 x 16 heads, T = 4096, d_h = 64, d_v = 128) against both
+    ceilings."""
     out = {}
+    wl = inputs.make_config(1)
+    q, k, v = (t.to(dev) for t in (wl.q, wl.k, wl.v))
+    o = torch.empty(q.shape[:3] + (v.shape[3],), dtype=q.dtype, device=dev)
+    lse = torch.empty(q.shape[:3], device=dev)
+    ms = timed(lambda: attn.attn_fwd(q, k, v, scale=wl.scale, causal=True, out=o, lse=lse))
+    one = torch.empty(1, device=dev)
+    floor_ms = timed(lambda: one.fill_(0.0))
+    fl = 2 * (64 + 64) * (128 * 129 // 2)
+    tf = fl / (ms * 1e-3) / 1e12
+    out["fp32_single_head"] = {"workload": "fp32 causal B=1 H=1 T=128 d=64 (attn_fwd, generic kernel)",
+                               "us": round(ms * 1e3, 2), "launch_floor_us": round(floor_ms * 1e3, 2),
+                               "value": round(tf, 4), "unit": "TFLOP/s",
+                               "roofline": {"bound": "launch", "achieved": round(tf, 4), "peak": PEAK_FP32_TFLOPS,
+                                            "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_TFLOPS, 6),
+                                            "traffic": None, "per_launch_flops": fl,
+                                            "note": "2.1 MFLOP per call on 128 wavefronts (one per row): "
+                                                    "the time is the launch plus each row's chain of "
+                                                    "dependent loads over two 64-key blocks, not arithmetic"}}
+    del q, k, v, o, lse, wl
     wl = inputs.make_config(4)
     q, k, v = (t.to(dev) for t in (wl.q, wl.k, wl.v))
     o = torch.empty(q.shape[:3] + (v.shape[3],), dtype=q.dtype, device=dev)
@@ -205,7 +228,8 @@ def workloads_section(torch, attn, inputs, dev, timed):
                                  "(attn_fwd)", "ms": round(ms, 4), "value": round(gbs, 1), "unit": "GB/s",
                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                   "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "per_launch_bytes": by,
-                                  "per_launch_flops": fl}}
+                                  "per_launch_flops": fl,
+                                  "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5)}}
     del q, k, v, o, lse, wl
     wl = inputs.make_config(5)
     q, k, v, m = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.bias))

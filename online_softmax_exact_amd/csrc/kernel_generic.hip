@@ -13,6 +13,12 @@ namespace {
 constexpr int kWaves = 4;      // rows per workgroup
 constexpr int kMaxD = 256;
 constexpr int kAcc = kMaxD / 64;
+#ifndef GEN_ILP
+#define GEN_ILP 8          // independent partial sums of a score's dot product
+#endif
+#ifndef GEN_PV_UNROLL
+#define GEN_PV_UNROLL 8    // keys of the P V loop unrolled (their V loads in flight together)
+#endif
 
 template <typename T, bool HAS_BIAS, bool SPLIT, bool COUNT>
 __global__ __launch_bounds__(256) void generic_kernel(
@@ -80,8 +86,20 @@ __global__ __launch_bounds__(256) void generic_kernel(
         float z2 = 0.0f;
         if (legal) {
           const T* krow = kbase + j * pb.ks[2];
+          // GEN_ILP independent partial sums, so consecutive loads of the key
+          // row are in flight together instead of one per fma latency.
+          float dotp[GEN_ILP];
+#pragma unroll
+          for (int e = 0; e < GEN_ILP; ++e) dotp[e] = 0.0f;
+          int d = 0;
+          for (; d + GEN_ILP <= pb.d_h; d += GEN_ILP) {
+#pragma unroll
+            for (int e = 0; e < GEN_ILP; ++e) dotp[e] = fmaf(sq[wave][d + e], Elem<T>::load(krow, d + e), dotp[e]);
+          }
+          for (; d < pb.d_h; ++d) dotp[0] = fmaf(sq[wave][d], Elem<T>::load(krow, d), dotp[0]);
           float dot = 0.0f;
-          for (int d = 0; d < pb.d_h; ++d) dot = fmaf(sq[wave][d], Elem<T>::load(krow, d), dot);
+#pragma unroll
+          for (int e = 0; e < GEN_ILP; ++e) dot += dotp[e];
           z2 = dot * pb.scale_log2;
           if (HAS_BIAS) {
             const float mb = brow[j * pb.bs[3]];
@@ -106,6 +124,7 @@ __global__ __launch_bounds__(256) void generic_kernel(
         const float p = legal ? fast_exp2(z2 - m2) : 0.0f;
         l_lane += p;
         const int nj = (hi - kb) < 64 ? static_cast<int>(hi - kb) : 64;
+#pragma unroll GEN_PV_UNROLL
         for (int jj = 0; jj < nj; ++jj) {
           const float pj = __shfl(p, jj, 64);
           const T* vrow = vbase + (kb + jj) * pb.vs[2];
