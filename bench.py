@@ -311,8 +311,8 @@ def recorded_mfma(key: str):
 
 
 def backward_traffic(prefix: str = ""):
-    """HBM bytes of one attn_bwd call: its dQ, dV and dK kernels' recorded
-    traffic (the D kernel reads O and dO once), or None if any is stale."""
+    """HBM bytes of one attn_bwd call: its dQ (which also computes D), dV and
+    dK kernels' recorded traffic, or None if any is stale."""
     parts = [recorded_traffic(prefix + k) for k in ("bwd_dq", "bwd_dv", "bwd_dk")]
     return None if None in parts else sum(parts)
 

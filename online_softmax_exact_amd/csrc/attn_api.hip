@@ -170,9 +170,14 @@ int attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return ATTN_E_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* ws_d = static_cast<float*>(workspace);
-  hipError_t e = launch_bwd_rowdot(pb, p->dtype, o, d_o, ws_d, s);
-  if (e == hipSuccess && !launch_bwd_dq_mfma(pb, p->dtype, q, k, v, lse, d_o, ws_d, d_q, s, &e))
-    e = launch_bwd_dq_generic(pb, p->dtype, q, k, v, lse, d_o, ws_d, d_q, s);
+  // D = <dO, O> per row: computed by the MFMA dQ kernel for its rows, else
+  // by the row-dot kernel ahead of the generic dQ kernel.  dK / dV run after
+  // dQ on the same stream and read it.
+  hipError_t e = hipSuccess;
+  if (!launch_bwd_dq_mfma(pb, p->dtype, q, k, v, o, lse, d_o, ws_d, d_q, s, &e)) {
+    e = launch_bwd_rowdot(pb, p->dtype, o, d_o, ws_d, s);
+    if (e == hipSuccess) e = launch_bwd_dq_generic(pb, p->dtype, q, k, v, lse, d_o, ws_d, d_q, s);
+  }
   if (e == hipSuccess && !launch_bwd_dkdv_mfma(pb, p->dtype, q, k, v, lse, d_o, ws_d, d_k, d_v, s, &e))
     e = launch_bwd_dkdv_generic(pb, p->dtype, q, k, v, lse, d_o, ws_d, d_k, d_v, s);
   return hip_status(e);

@@ -61,7 +61,8 @@ struct BArgs {
   const uint16_t* v;
   const uint16_t* d_o;
   const float* lse;
-  const float* dd;          // D_i = <dO_i, O_i>, [B, H_q, T_q]
+  float* dd;                // D_i = <dO_i, O_i>, [B, H_q, T_q]: written by dQ, read by dK / dV
+  const uint16_t* o;        // forward output (dQ only: D from its rows)
   uint16_t* out;            // dQ, dK or dV
   int64_t qs[3], ks[3], vs[3], os[3];
   int64_t q_offset;
@@ -173,7 +174,7 @@ __device__ __forceinline__ int slot_seq(const int32_t* cu, int n_seqs, int n, in
   return lo;
 }
 
-// Moves the row pointers (q, d_o and, for dQ, the output) to sequence sq's
+// Moves the row pointers (q, d_o and, for dQ, o and the output) to sequence sq's
 // first row and the key pointers (k, v and, for dK / dV, the output) to its
 // first key, and makes the sizes and q_offset the sequence's own, with its
 // rows at the end of its keys.  *row_base is the packed row of the sequence's
@@ -187,6 +188,7 @@ __device__ __forceinline__ void enter_seq(BArgs& a, const VArgs& va, int sq, int
   const int k1 = max(k0, clamp_len(va.cu_k[sq + 1], a.t_k));
   a.q += static_cast<int64_t>(q0) * a.qs[2];
   a.d_o += static_cast<int64_t>(q0) * a.os[2];
+  if (OUT_ROWS) a.o += static_cast<int64_t>(q0) * a.os[2];   // dQ also reads O (for D)
   a.k += static_cast<int64_t>(k0) * a.ks[2];
   a.v += static_cast<int64_t>(k0) * a.vs[2];
   a.out += static_cast<int64_t>(OUT_ROWS ? q0 : k0) * out_row_stride;
@@ -255,7 +257,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a, Var..
       greg[s] = row_ok ? *reinterpret_cast<const u32x4*>(gp + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
   }
   const float lse2 = row_ok ? a.lse[ridx] * kLog2e : -INFINITY;
-  const float dd = row_ok ? a.dd[ridx] : 0.0f;
+  // D_i = <dO_i, O_i> (Exercise 33.4): this lane's half of the row from the
+  // dO operand already in registers and the same chunks of O, the halves
+  // joined by one exchange; stored for the dK / dV launches.
+  float dd = 0.0f;
+  {
+    const uint16_t* orow = a.o + b * a.os[0] + hq * a.os[1] + static_cast<int64_t>(row) * a.os[2];
+#pragma unroll
+    for (int s = 0; s < C::MS; ++s) {
+      const u32x4 ov = row_ok ? *reinterpret_cast<const u32x4*>(orow + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        dd = fmaf(__uint_as_float(greg[s][w] << 16), __uint_as_float(ov[w] << 16), dd);
+        dd = fmaf(__uint_as_float(greg[s][w] & 0xffff0000u), __uint_as_float(ov[w] & 0xffff0000u), dd);
+      }
+    }
+    dd += __shfl_xor(dd, 32);
+    if (h == 0 && row_ok) a.dd[ridx] = dd;
+  }
 
   const int pos_row = clamp_pos(a, a.q_offset + row);
   const int pos_w_first = clamp_pos(a, a.q_offset + row0);
@@ -742,16 +761,18 @@ int32_t batch_major(const Problem& pb) {
 
 // Takes bf16 problems without bias with d_h, d_v in {64, 128}, positive
 // scale, 16-byte aligned rows and sizes that fit 32-bit indices; launches the
-// dQ kernel (D must already be in dd).  Returns false when it does not apply.
+// dQ kernel, which also computes D from o and d_o into dd (for the dK / dV
+// launches that follow).  Returns false when it does not apply.
 bool launch_bwd_dq_mfma(const Problem& pb, int dtype, const void* q, const void* k, const void* v,
-                        const float* lse, const void* d_o, const float* dd, void* d_q,
+                        const void* o, const float* lse, const void* d_o, float* dd, void* d_q,
                         hipStream_t stream, hipError_t* err) {
   if (dtype != ATTN_BF16 || pb.bias != nullptr) return false;
   if (!((pb.d_h == 64 || pb.d_h == 128) && (pb.d_v == 64 || pb.d_v == 128))) return false;
   if (!(pb.scale_log2 > 0.0f)) return false;
   if (pb.t_q >= (int64_t(1) << 30) || pb.t_k >= (int64_t(1) << 30)) return false;
   if (pb.ks[2] >= (int64_t(1) << 24) || pb.vs[2] >= (int64_t(1) << 24)) return false;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(d_q)) return false;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(d_o) || !aligned16(d_q))
+    return false;
   for (int i = 0; i < 3; ++i)
     if ((pb.qs[i] | pb.ks[i] | pb.vs[i] | pb.os[i]) & 7) return false;
   const bool packed = pb.cu_q != nullptr;
@@ -765,6 +786,7 @@ bool launch_bwd_dq_mfma(const Problem& pb, int dtype, const void* q, const void*
   a.d_o = static_cast<const uint16_t*>(d_o);
   a.lse = lse;
   a.dd = dd;
+  a.o = static_cast<const uint16_t*>(o);
   a.out = static_cast<uint16_t*>(d_q);
   for (int i = 0; i < 3; ++i) {
     a.qs[i] = pb.qs[i]; a.ks[i] = pb.ks[i]; a.vs[i] = pb.vs[i]; a.os[i] = pb.os[i];
@@ -817,7 +839,7 @@ bool launch_bwd_dkdv_mfma(const Problem& pb, int dtype, const void* q, const voi
   a.v = static_cast<const uint16_t*>(v);
   a.d_o = static_cast<const uint16_t*>(d_o);
   a.lse = lse;
-  a.dd = dd;
+  a.dd = const_cast<float*>(dd);   // read only by the dK / dV kernels
   for (int i = 0; i < 3; ++i) {
     a.qs[i] = pb.qs[i]; a.ks[i] = pb.ks[i]; a.vs[i] = pb.vs[i]; a.os[i] = pb.os[i];
   }

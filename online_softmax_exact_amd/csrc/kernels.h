@@ -30,9 +30,10 @@ bool launch_fewrow_partials(const Problem& pb, int dtype, const void* q, const v
                             const void* v, const SplitLayout& L, float* ws_o, float* ws_lse,
                             hipStream_t stream, hipError_t* err);
 
-// MFMA backward dQ (bf16, d_h and d_v in {64, 128}, no bias); dd holds D.
+// MFMA backward dQ (bf16, d_h and d_v in {64, 128}, no bias); writes D of
+// every row it computes into dd.
 bool launch_bwd_dq_mfma(const Problem& pb, int dtype, const void* q, const void* k, const void* v,
-                        const float* lse, const void* d_o, const float* dd, void* d_q,
+                        const void* o, const float* lse, const void* d_o, float* dd, void* d_q,
                         hipStream_t stream, hipError_t* err);
 
 bool launch_bwd_dkdv_mfma(const Problem& pb, int dtype, const void* q, const void* k, const void* v,
