@@ -6,7 +6,8 @@ namespace attn {
 bool launch_fast_fwd(const Problem& pb, int dtype, const void* q, const void* k, const void* v,
                      void* o, float* lse, int32_t* n_legal, hipStream_t stream, int* status) {
   if (launch_fewrow_fwd(pb, dtype, q, k, v, o, lse, n_legal, stream, status)) return true;
-  return launch_prefill_mfma(pb, dtype, q, k, v, o, lse, n_legal, stream, status);
+  if (launch_prefill_mfma(pb, dtype, q, k, v, o, lse, n_legal, stream, status)) return true;
+  return launch_fp32_mfma(pb, dtype, q, k, v, o, lse, n_legal, stream, status);
 }
 
 bool launch_fast_decode_partials(const Problem& pb, int dtype, const void* q, const void* k,

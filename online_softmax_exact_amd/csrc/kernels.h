@@ -16,6 +16,11 @@ bool launch_fast_decode_partials(const Problem& pb, int dtype, const void* q,
                                  float* ws_o, float* ws_lse, hipStream_t stream,
                                  hipError_t* err);
 
+// MFMA prefill for fp32 (d_h and d_v in {64, 128}; no bias, window or
+// variable lengths).
+bool launch_fp32_mfma(const Problem& pb, int dtype, const void* q, const void* k, const void* v, void* o,
+                      float* lse, int32_t* n_legal, hipStream_t stream, int* status);
+
 // MFMA prefill (bf16, d_h and d_v in {64, 128}).
 bool launch_prefill_mfma(const Problem& pb, int dtype, const void* q, const void* k,
                          const void* v, void* o, float* lse, int32_t* n_legal,
