@@ -40,10 +40,10 @@ def far_empty(shape, dtype, gap=GAP):
     return buf.as_strided(shape, (gap, n * d, d, 1))
 
 
-@pytest.mark.parametrize("dtype,d,t", [(torch.bfloat16, 128, 300), (torch.float32, 40, 70)])
+@pytest.mark.parametrize("dtype,d,t", [(torch.bfloat16, 128, 300), (torch.float32, 64, 200), (torch.float32, 40, 70)])
 def test_fwd_batch_stride_over_2_31(dtype, d, t):
-    """attn_fwd (MFMA prefill for bf16, generic kernel for fp32) with Q, K, V
-    and O batches more than 2^31 elements apart."""
+    """attn_fwd (bf16 and fp32 MFMA prefills, the generic kernel for fp32 with
+    d = 40) with Q, K, V and O batches more than 2^31 elements apart."""
     wl = inputs.make_random(2, 2, 1, t, t, d, d, dtype=dtype, seed=31 + d, causal=True)
     q, k, v = far_apart(wl.q), far_apart(wl.k), far_apart(wl.v)
     o = far_empty((2, 2, t, d), dtype)
