@@ -13,10 +13,14 @@ KV GB/s (Q + K + V + O + LSE bytes once) is reported beside it.  After the
 timed steps, the same prefill and decode are timed once more with a sliding
 window (``--window``, keys j >= pos - W + 1) and reported under
 ``sliding_window``, the prefill's backward (``attn_bwd``, upstream
-gradient N(0,1)) under ``backward``, and unpadded variable-length batches
-(packed prefill against the padded batch, decode over per-batch KV lengths)
-under ``varlen``, the multi-query verify and the padded batch with its dense
-bias under ``workloads``, each with its own algorithmic counts.
+gradient N(0,1)) under ``backward``, unpadded variable-length batches
+(packed prefill and its backward against the padded batch, decode over
+per-batch KV lengths) under ``varlen``, the single-head fp32 problem, the
+multi-query verify and the padded batch with its dense bias under
+``workloads``, each with its own algorithmic counts, and a library GEMM and a
+device copy of the same session under ``achievable``.  ``roofline.traffic``
+and ``roofline.counters`` come from the committed rocprofv3 runs
+(profiles/traffic.json) and are null when the kernel's sources changed since.
 """
 
 from __future__ import annotations
