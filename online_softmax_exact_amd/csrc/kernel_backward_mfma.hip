@@ -1,11 +1,15 @@
-// MFMA backward kernels for bf16 Q/K/V/O/dO, d_h and d_v in {64, 128}, no
-// bias: gradients of the attention of attn_fwd by recomputing the
+// MFMA backward kernels for bf16 Q/K/V/O/dO, d_h and d_v in {64, 128}, with
+// or without a bias (keys contiguous): gradients of the attention of attn_fwd
+// by recomputing the
 // probabilities from the saved LSE, eqs 33.6-33.8 of "Chapter 33 推理计算优化"
 // §33.3 (block size, parallelism and backward recomputation):
 //   P_ij = e^{z_ij - LSE_i} on legal keys, dP = dO V^T,
 //   dS_ij = P_ij (dP_ij - D_i) with D_i = <dO_i, O_i> (Exercise 33.4),
 //   dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO.
-// No running maximum is needed: the saved LSE is the exact normaliser.
+// No running maximum is needed: the saved LSE is the exact normaliser.  With
+// a bias the exponent is scale dot + M - LSE (base 2); a row whose LSE is
+// -inf (no legal key; with a bias such a row can sit in a fully visible
+// block) takes +inf there, so all its weights are 0 without a mask.
 //
 // dQ kernel: the forward kernel's mapping.  A workgroup of 4 wavefronts owns
 // 128 query rows; K/V tiles of 64 keys stream HBM -> LDS (buffer_load ... lds
@@ -34,6 +38,8 @@
 // whose K/V exceeds the 256 MB Infinity Cache go batch after batch instead.
 // Packed sequences map grid slots to (sequence, tile) from the offsets (see
 // VArgs).
+#include <type_traits>
+
 #include "attn_internal.h"
 #include "kernels.h"
 #include "prefill_common.h"
@@ -89,8 +95,20 @@ struct VArgs {
   const int32_t* cu_k;
   int32_t n_seqs, n_slots;
 };
-template <class T>
-__device__ __forceinline__ const T& first_of(const T& t) { return t; }
+// Bias instances take the bias as one more trailing argument (fp32, keys
+// contiguous, any broadcast over batch, head and row).
+struct BBias {
+  const float* bias;
+  int64_t bs[3];   // element strides of b, hq, i (keys are contiguous)
+};
+// The trailing argument of type T (only called when one is present).
+template <class T, class U, class... R>
+__device__ __forceinline__ const T& pick(const U& u, const R&... r) {
+  if constexpr (std::is_same_v<T, U>) return u;
+  else return pick<T>(r...);
+}
+template <class T, class... X>
+constexpr bool has_arg = (std::is_same_v<T, X> || ...);
 
 template <int DH, int DV>
 struct BCfg {
@@ -177,11 +195,12 @@ __device__ __forceinline__ int slot_seq(const int32_t* cu, int n_seqs, int n, in
 // Moves the row pointers (q, d_o and, for dQ, o and the output) to sequence sq's
 // first row and the key pointers (k, v and, for dK / dV, the output) to its
 // first key, and makes the sizes and q_offset the sequence's own, with its
-// rows at the end of its keys.  *row_base is the packed row of the sequence's
-// row 0 (LSE and D keep the packed layout).
+// rows at the end of its keys.  *row_base and *key_base are the packed row
+// and key of the sequence's row 0 and key 0 (LSE, D and the bias keep the
+// packed layout).
 template <bool OUT_ROWS>
 __device__ __forceinline__ void enter_seq(BArgs& a, const VArgs& va, int sq, int64_t out_row_stride,
-                                          int32_t* row_base) {
+                                          int32_t* row_base, int32_t* key_base) {
   const int q0 = clamp_len(va.cu_q[sq], a.t_q);
   const int q1 = max(q0, clamp_len(va.cu_q[sq + 1], a.t_q));
   const int k0 = clamp_len(va.cu_k[sq], a.t_k);
@@ -193,6 +212,7 @@ __device__ __forceinline__ void enter_seq(BArgs& a, const VArgs& va, int sq, int
   a.v += static_cast<int64_t>(k0) * a.vs[2];
   a.out += static_cast<int64_t>(OUT_ROWS ? q0 : k0) * out_row_stride;
   *row_base = q0;
+  *key_base = k0;
   a.q_offset += (k1 - k0) - (q1 - q0);
   a.t_q = q1 - q0;
   a.t_k = k1 - k0;
@@ -201,10 +221,11 @@ __device__ __forceinline__ void enter_seq(BArgs& a, const VArgs& va, int sq, int
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <int DH, int DV, class... Var>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a, Var... var) {
+template <int DH, int DV, class... Extra>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a, Extra... ex) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr bool VAR = sizeof...(Var) > 0;
+  constexpr bool VAR = has_arg<VArgs, Extra...>;
+  constexpr bool BIAS = has_arg<BBias, Extra...>;
   using C = BCfg<DH, DV>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::H_BYTES + 2 * C::V_BYTES];
   char* const kring = smem;
@@ -230,11 +251,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a, Var..
   const int hq = bh % a.heads_q;
   const int kvh = hq / a.group;
   int64_t ridx_base = (static_cast<int64_t>(b) * a.heads_q + hq) * a.t_q;   // LSE / D index of row 0
+  int32_t row_base = 0, key_base = 0;
   if constexpr (VAR) {
-    const VArgs& va = first_of(var...);
+    const VArgs& va = pick<VArgs>(ex...);
     const int sq = slot_seq(va.cu_q, va.n_seqs, a.t_q, qt, &qt);
-    int32_t row_base;
-    enter_seq<true>(a, va, sq, a.qs[2], &row_base);
+    enter_seq<true>(a, va, sq, a.qs[2], &row_base, &key_base);
     if (qt < 0 || qt * kBr >= a.t_q) return;   // whole workgroup: a slot outside the sequence's tiles
     ridx_base += row_base;
   }
@@ -256,7 +277,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a, Var..
     for (int s = 0; s < C::MS; ++s)
       greg[s] = row_ok ? *reinterpret_cast<const u32x4*>(gp + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
   }
-  const float lse2 = row_ok ? a.lse[ridx] * kLog2e : -INFINITY;
+  float lse2 = row_ok ? a.lse[ridx] * kLog2e : -INFINITY;
+  // A row with no legal key has every weight 0; with a bias a full block can
+  // hold such a row (all its entries -inf), so its LSE acts as +inf there.
+  if (BIAS && lse2 == -INFINITY) lse2 = INFINITY;
+  // Bias rows of this wavefront (keys contiguous): 16 values per lane and
+  // block through a buffer that ends at the wavefront's last row and key.
+  const float* bias_w = nullptr;
+  int64_t bias_w_bytes = 0;
+  int bias_off = 0;
+  if constexpr (BIAS) {
+    const BBias& bb = pick<BBias>(ex...);
+    bias_w = bb.bias + b * bb.bs[0] + hq * bb.bs[1] + static_cast<int64_t>(row_base + row0) * bb.bs[2] + key_base;
+    const int rows_w = a.t_q - row0 < kRowsW ? a.t_q - row0 : kRowsW;
+    bias_w_bytes = rows_w > 0 ? (static_cast<int64_t>(rows_w - 1) * bb.bs[2] + a.t_k) * 4 : 0;
+    bias_off = row_ok ? static_cast<int>(lr * bb.bs[2] * 4) + 16 * h : 0;
+  }
   // D_i = <dO_i, O_i> (Exercise 33.4): this lane's half of the row from the
   // dO operand already in registers and the same chunks of O, the halves
   // joined by one exchange; stored for the dK / dV launches.
@@ -367,6 +403,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a, Var..
     if (a.t_k - 1 - kb < lim) lim = a.t_k - 1 - kb;
     if (!row_ok) lim = -1;
     const int first = lo_row - kb;
+    f32x4 mb[4];   // bias of the 16 keys (BIAS only)
+    if constexpr (BIAS) {
+      const auto rs = make_rsrc(bias_w + t * kBc, bias_w_bytes - static_cast<int64_t>(t) * kBc * 4);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        mb[g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, bias_off + 128 * q + 32 * g, 0, 0));
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float d2[2];
@@ -374,7 +417,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a, Var..
       for (int e = 0; e < 2; ++e) {
         const int r = 2 * i + e;
         const int j = 8 * (r >> 2) + 4 * h + (r & 3);
-        float p = fast_exp2(fmaf(sacc[r], a.scale_log2, -lse2));
+        const float zb = BIAS ? fmaf(mb[r >> 2][r & 3], kLog2e, -lse2) : -lse2;
+        float p = fast_exp2(fmaf(sacc[r], a.scale_log2, zb));
         if (mask) p = (j <= lim && j >= first) ? p : 0.0f;
         d2[e] = p * (dacc[r] - dd);                 // eq 33.7
       }
@@ -437,10 +481,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a, Var..
 // ---------------------------------------------------------------------------
 // dK (WHICH = 1) or dV (WHICH = 0)
 // ---------------------------------------------------------------------------
-template <int DH, int DV, int WHICH, class... Var>
-__global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Var... var) {
+template <int DH, int DV, int WHICH, class... Extra>
+__global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Extra... ex) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr bool VAR = sizeof...(Var) > 0;
+  constexpr bool VAR = has_arg<VArgs, Extra...>;
+  constexpr bool BIAS = has_arg<BBias, Extra...>;
   using C = BCfg<DH, DV>;
   constexpr bool DK = WHICH == 1;
   constexpr int MOUT = DK ? C::MQ : C::MV;     // 32-wide output slices
@@ -469,10 +514,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Var..
   const int kvh = bh % a.heads_kv;
   const int32_t t_q_all = a.t_q;   // rows per head of LSE and D
   int32_t row_base = 0;            // packed row of the sequence's row 0
+  int32_t key_base = 0;            // packed key of the sequence's key 0
   if constexpr (VAR) {
-    const VArgs& va = first_of(var...);
+    const VArgs& va = pick<VArgs>(ex...);
     const int sq = slot_seq(va.cu_k, va.n_seqs, a.t_k, kt, &kt);
-    enter_seq<false>(a, va, sq, DK ? a.ks[2] : a.vs[2], &row_base);
+    enter_seq<false>(a, va, sq, DK ? a.ks[2] : a.vs[2], &row_base, &key_base);
     if (kt < 0 || kt * kBr >= a.t_k) return;   // whole workgroup: a slot outside the sequence's tiles
   }
 
@@ -594,17 +640,65 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Var..
     }
   };
   // P of a fully legal block, packed to bf16 (dV only).
-  auto probs_full = [&](const float* st_, int q, const f32x16& sacc, unsigned* pk) {
+  // Bias of this lane's key for the 16 rows it holds in block q of the unit
+  // (hq, i0) (BIAS only): one dword each through a buffer that ends at the
+  // unit's last row and key.
+  auto load_bias = [&](int hq, int i0, int q, float* mb) {
+    if constexpr (BIAS) {
+      const BBias& bb = pick<BBias>(ex...);
+      const int rows_u = a.t_q - i0 < kBc ? a.t_q - i0 : kBc;
+      const auto rs = make_rsrc(bb.bias + b * bb.bs[0] + hq * bb.bs[1] +
+                                    static_cast<int64_t>(row_base + i0) * bb.bs[2] + key_base,
+                                (static_cast<int64_t>(rows_u - 1) * bb.bs[2] + a.t_k) * 4);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = 32 * q + 8 * (r >> 2) + 4 * h + (r & 3);
+        mb[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                              rs, (rr * static_cast<int>(bb.bs[2]) + key) * 4, 0, 0));
+      }
+    }
+  };
+  // One bias entry: row 32 q + 8 (r / 4) + 4 h + r % 4 of the unit, this
+  // lane's key.
+  auto bias_at = [&](int hq, int i0, int q, int r) -> float {
+    if constexpr (BIAS) {
+      const BBias& bb = pick<BBias>(ex...);
+      const int rows_u = a.t_q - i0 < kBc ? a.t_q - i0 : kBc;
+      const auto rs = make_rsrc(bb.bias + b * bb.bs[0] + hq * bb.bs[1] +
+                                    static_cast<int64_t>(row_base + i0) * bb.bs[2] + key_base,
+                                (static_cast<int64_t>(rows_u - 1) * bb.bs[2] + a.t_k) * 4);
+      const int rr = 32 * q + 8 * (r >> 2) + 4 * h + (r & 3);
+      return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rs, (rr * static_cast<int>(bb.bs[2]) + key) * 4, 0, 0));
+    } else {
+      return 0.0f;
+    }
+  };
+  // Exponent offset of a row: -LSE (base 2) plus its bias entry; a row with
+  // no legal key (LSE = -inf) gets weight 0 (with a bias a full block can
+  // hold one).
+  auto zoff = [&](float lse, float mbias) {
+    if constexpr (BIAS) {
+      const float l2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+      return fmaf(mbias, kLog2e, -l2);
+    } else {
+      return -lse * kLog2e;
+    }
+  };
+  auto probs_full = [&](const float* st_, int hq, int i0, int q, const f32x16& sacc, unsigned* pk) {
     f32x4 l4[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
       l4[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
           (const __attribute__((address_space(3))) char*)(st_) + (32 * q + 8 * g + 4 * h) * 4);
+    float mb[16];
+    load_bias(hq, i0, q, mb);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 2 * i;
-      const float p0 = fast_exp2(fmaf(sacc[r], a.scale_log2, -l4[r >> 2][r & 3] * kLog2e));
-      const float p1 = fast_exp2(fmaf(sacc[r + 1], a.scale_log2, -l4[(r + 1) >> 2][(r + 1) & 3] * kLog2e));
+      const float p0 = fast_exp2(fmaf(sacc[r], a.scale_log2, zoff(l4[r >> 2][r & 3], BIAS ? mb[r] : 0.0f)));
+      const float p1 =
+          fast_exp2(fmaf(sacc[r + 1], a.scale_log2, zoff(l4[(r + 1) >> 2][(r + 1) & 3], BIAS ? mb[r + 1] : 0.0f)));
       pk[i] = pack_bf16(p0, p1);
     }
   };
@@ -627,7 +721,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Var..
     bool any_b[2], full_b[2];
     block_flags(i0, any_b[0], full_b[0]);
     block_flags(i0 + 32, any_b[1], full_b[1]);
-    if (!DK && BWD_PIPE && full_b[0] && full_b[1]) {
+    if (!DK && BWD_PIPE && !BIAS && full_b[0] && full_b[1]) {
       // Both blocks fully legal: S of both blocks first, then block 0's
       // weights under block 1's score MFMAs and block 1's weights under
       // block 0's accumulation MFMAs (no dependence between them).
@@ -636,10 +730,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Var..
       scores(qt_, 0, s0);
       if (BWD_SCHED > 0) __builtin_amdgcn_sched_barrier(0);
       scores(qt_, 1, s1);
-      probs_full(st_, 0, s0, pk0);
+      probs_full(st_, hq, i0, 0, s0, pk0);
       interleave(C::KS);
       accumulate(gt_, 0, pk0);
-      probs_full(st_, 1, s1, pk1);
+      probs_full(st_, hq, i0, 1, s1, pk1);
       interleave(2 * MOUT);
       accumulate(gt_, 1, pk1);
     } else {
@@ -666,25 +760,46 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Var..
           dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(gop), as_bf16x8(vreg[s]), dacc, 0, 0, 0);
         }
       }
-      // LSE (and D) of the 16 rows this lane holds.
+      // LSE (and D) of the 16 rows this lane holds (with a bias, read per pair
+      // where they are used, with the pair's bias entries: fewer live
+      // registers).
       f32x4 l4[4], d4[4];
+      if constexpr (!BIAS) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        l4[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-            (const __attribute__((address_space(3))) char*)(st_) + (32 * q + 8 * g + 4 * h) * 4);
-        if (DK)
-          d4[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-              (const __attribute__((address_space(3))) char*)(st_) + 256 + (32 * q + 8 * g + 4 * h) * 4);
+        for (int g = 0; g < 4; ++g) {
+          l4[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+              (const __attribute__((address_space(3))) char*)(st_) + (32 * q + 8 * g + 4 * h) * 4);
+          if (DK)
+            d4[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+                (const __attribute__((address_space(3))) char*)(st_) + 256 + (32 * q + 8 * g + 4 * h) * 4);
+        }
       }
       unsigned pk[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         float w2[2];
+        float mb2[2], lse2p[2], dd2p[2];
+        if constexpr (BIAS) {
+          const int off = (32 * q + 8 * (i >> 1) + 4 * h + 2 * (i & 1)) * 4;
+          const f32x2 lp = *reinterpret_cast<const __attribute__((address_space(3))) f32x2*>(
+              (const __attribute__((address_space(3))) char*)(st_) + off);
+          lse2p[0] = lp[0];
+          lse2p[1] = lp[1];
+          if (DK) {
+            const f32x2 dp = *reinterpret_cast<const __attribute__((address_space(3))) f32x2*>(
+                (const __attribute__((address_space(3))) char*)(st_) + 256 + off);
+            dd2p[0] = dp[0];
+            dd2p[1] = dp[1];
+          }
+#pragma unroll
+          for (int e = 0; e < 2; ++e) mb2[e] = bias_at(hq, i0, q, 2 * i + e);
+        }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int r = 2 * i + e;
           const int row = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
-          float p = fast_exp2(fmaf(sacc[r], a.scale_log2, -l4[r >> 2][r & 3] * kLog2e));
+          const float lse_r = BIAS ? lse2p[e] : l4[r >> 2][r & 3];
+          float p = fast_exp2(fmaf(sacc[r], a.scale_log2, zoff(lse_r, BIAS ? mb2[e] : 0.0f)));
           if (!full) {
             const int64_t pos = a.q_offset + row;
             bool ok = key_ok && row < a.t_q;
@@ -692,7 +807,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Var..
             if (a.window > 0 && key < pos - a.window + 1) ok = false;
             p = ok ? p : 0.0f;
           }
-          w2[e] = DK ? p * (dacc[r] - d4[r >> 2][r & 3]) : p;   // dS (eq 33.7) or P
+          const float dd_r = BIAS ? dd2p[e] : d4[r >> 2][r & 3];
+          w2[e] = DK ? p * (dacc[r] - dd_r) : p;   // dS (eq 33.7) or P
         }
         pk[i] = pack_bf16(w2[0], w2[1]);
       }
@@ -725,25 +841,50 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Var..
 #endif
 }
 
+template <int DH, int DV, int WHICH, class... X>
+void launch_kv_x(const BArgs& a, int64_t blocks, hipStream_t s, X... x) {
+  hipLaunchKernelGGL((bwd_kv_mfma_kernel<DH, DV, WHICH, X...>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                     0, s, a, x...);
+}
+
+// Packed sequences and a bias each add one trailing kernel argument; the
+// instances without them keep the plain argument block.
 template <int DH, int DV, int WHICH>
-hipError_t launch_kv(const BArgs& a, const VArgs& va, int64_t blocks, hipStream_t s) {
-  if (va.cu_q != nullptr)
-    hipLaunchKernelGGL((bwd_kv_mfma_kernel<DH, DV, WHICH, VArgs>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(kThreads), 0, s, a, va);
-  else
-    hipLaunchKernelGGL((bwd_kv_mfma_kernel<DH, DV, WHICH>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
-                       0, s, a);
+hipError_t launch_kv(const BArgs& a, const VArgs& va, const BBias& bb, int64_t blocks, hipStream_t s) {
+  if (va.cu_q != nullptr && bb.bias != nullptr) launch_kv_x<DH, DV, WHICH>(a, blocks, s, va, bb);
+  else if (va.cu_q != nullptr) launch_kv_x<DH, DV, WHICH>(a, blocks, s, va);
+  else if (bb.bias != nullptr) launch_kv_x<DH, DV, WHICH>(a, blocks, s, bb);
+  else launch_kv_x<DH, DV, WHICH>(a, blocks, s);
   return hipGetLastError();
 }
 
+template <int DH, int DV, class... X>
+void launch_dq_x(const BArgs& a, int64_t blocks, hipStream_t s, X... x) {
+  hipLaunchKernelGGL((bwd_dq_mfma_kernel<DH, DV, X...>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s,
+                     a, x...);
+}
+
 template <int DH, int DV>
-hipError_t launch_dq(const BArgs& a, const VArgs& va, int64_t blocks, hipStream_t s) {
-  if (va.cu_q != nullptr)
-    hipLaunchKernelGGL((bwd_dq_mfma_kernel<DH, DV, VArgs>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       s, a, va);
-  else
-    hipLaunchKernelGGL((bwd_dq_mfma_kernel<DH, DV>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a);
+hipError_t launch_dq(const BArgs& a, const VArgs& va, const BBias& bb, int64_t blocks, hipStream_t s) {
+  if (va.cu_q != nullptr && bb.bias != nullptr) launch_dq_x<DH, DV>(a, blocks, s, va, bb);
+  else if (va.cu_q != nullptr) launch_dq_x<DH, DV>(a, blocks, s, va);
+  else if (bb.bias != nullptr) launch_dq_x<DH, DV>(a, blocks, s, bb);
+  else launch_dq_x<DH, DV>(a, blocks, s);
   return hipGetLastError();
+}
+
+// The bias the MFMA kernels take: keys contiguous, row offsets of a unit
+// (64 rows) and key offsets within 32 bits.
+bool bias_ok(const Problem& pb) {
+  if (pb.bias == nullptr) return true;
+  return pb.bs[3] == 1 && pb.bs[2] < (int64_t(1) << 22) && pb.t_k < (int64_t(1) << 28);
+}
+
+BBias make_bias(const Problem& pb) {
+  BBias bb{};
+  bb.bias = pb.bias;
+  for (int i = 0; i < 3; ++i) bb.bs[i] = pb.bs[i];
+  return bb;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -759,14 +900,15 @@ int32_t batch_major(const Problem& pb) {
 
 }  // namespace
 
-// Takes bf16 problems without bias with d_h, d_v in {64, 128}, positive
-// scale, 16-byte aligned rows and sizes that fit 32-bit indices; launches the
+// Takes bf16 problems with d_h, d_v in {64, 128}, positive scale, 16-byte
+// aligned rows, sizes that fit 32-bit indices and no bias or a bias the
+// kernels take (bias_ok); launches the
 // dQ kernel, which also computes D from o and d_o into dd (for the dK / dV
 // launches that follow).  Returns false when it does not apply.
 bool launch_bwd_dq_mfma(const Problem& pb, int dtype, const void* q, const void* k, const void* v,
                         const void* o, const float* lse, const void* d_o, float* dd, void* d_q,
                         hipStream_t stream, hipError_t* err) {
-  if (dtype != ATTN_BF16 || pb.bias != nullptr) return false;
+  if (dtype != ATTN_BF16 || !bias_ok(pb)) return false;
   if (!((pb.d_h == 64 || pb.d_h == 128) && (pb.d_v == 64 || pb.d_v == 128))) return false;
   if (!(pb.scale_log2 > 0.0f)) return false;
   if (pb.t_q >= (int64_t(1) << 30) || pb.t_k >= (int64_t(1) << 30)) return false;
@@ -800,6 +942,7 @@ bool launch_bwd_dq_mfma(const Problem& pb, int dtype, const void* q, const void*
   a.group = pb.group;
   a.n_tiles_grid = static_cast<int32_t>(n_qtiles);
   const VArgs va{pb.cu_q, pb.cu_k, static_cast<int32_t>(pb.n_seqs), static_cast<int32_t>(n_qtiles)};
+  const BBias bb = make_bias(pb);
   a.n_units = static_cast<int32_t>(pb.batch * pb.heads_q);
   a.scale_log2 = pb.scale_log2;
   a.causal = pb.causal;
@@ -808,10 +951,10 @@ bool launch_bwd_dq_mfma(const Problem& pb, int dtype, const void* q, const void*
     *err = hipSuccess;
     return true;
   }
-  if (pb.d_h == 128 && pb.d_v == 128) *err = launch_dq<128, 128>(a, va, blocks, stream);
-  else if (pb.d_h == 64 && pb.d_v == 128) *err = launch_dq<64, 128>(a, va, blocks, stream);
-  else if (pb.d_h == 128 && pb.d_v == 64) *err = launch_dq<128, 64>(a, va, blocks, stream);
-  else *err = launch_dq<64, 64>(a, va, blocks, stream);
+  if (pb.d_h == 128 && pb.d_v == 128) *err = launch_dq<128, 128>(a, va, bb, blocks, stream);
+  else if (pb.d_h == 64 && pb.d_v == 128) *err = launch_dq<64, 128>(a, va, bb, blocks, stream);
+  else if (pb.d_h == 128 && pb.d_v == 64) *err = launch_dq<128, 64>(a, va, bb, blocks, stream);
+  else *err = launch_dq<64, 64>(a, va, bb, blocks, stream);
   return true;
 }
 
@@ -819,7 +962,7 @@ bool launch_bwd_dq_mfma(const Problem& pb, int dtype, const void* q, const void*
 bool launch_bwd_dkdv_mfma(const Problem& pb, int dtype, const void* q, const void* k, const void* v,
                           const float* lse, const void* d_o, const float* dd, void* d_k, void* d_v,
                           hipStream_t stream, hipError_t* err) {
-  if (dtype != ATTN_BF16 || pb.bias != nullptr) return false;
+  if (dtype != ATTN_BF16 || !bias_ok(pb)) return false;
   if (!((pb.d_h == 64 || pb.d_h == 128) && (pb.d_v == 64 || pb.d_v == 128))) return false;
   if (!(pb.scale_log2 > 0.0f)) return false;
   if (pb.t_q >= (int64_t(1) << 30) || pb.t_k >= (int64_t(1) << 30)) return false;
@@ -852,6 +995,7 @@ bool launch_bwd_dkdv_mfma(const Problem& pb, int dtype, const void* q, const voi
   a.group = pb.group;
   a.n_tiles_grid = static_cast<int32_t>(n_ktiles);
   const VArgs va{pb.cu_q, pb.cu_k, static_cast<int32_t>(pb.n_seqs), static_cast<int32_t>(n_ktiles)};
+  const BBias bb = make_bias(pb);
   a.n_units = static_cast<int32_t>(pb.batch * pb.heads_kv);
   a.scale_log2 = pb.scale_log2;
   a.causal = pb.causal;
@@ -860,10 +1004,10 @@ bool launch_bwd_dkdv_mfma(const Problem& pb, int dtype, const void* q, const voi
   if (blocks == 0) return true;
   for (int which = 0; which < 2 && *err == hipSuccess; ++which) {
     a.out = static_cast<uint16_t*>(which ? d_k : d_v);
-    if (pb.d_h == 128 && pb.d_v == 128) *err = which ? launch_kv<128, 128, 1>(a, va, blocks, stream) : launch_kv<128, 128, 0>(a, va, blocks, stream);
-    else if (pb.d_h == 64 && pb.d_v == 128) *err = which ? launch_kv<64, 128, 1>(a, va, blocks, stream) : launch_kv<64, 128, 0>(a, va, blocks, stream);
-    else if (pb.d_h == 128 && pb.d_v == 64) *err = which ? launch_kv<128, 64, 1>(a, va, blocks, stream) : launch_kv<128, 64, 0>(a, va, blocks, stream);
-    else *err = which ? launch_kv<64, 64, 1>(a, va, blocks, stream) : launch_kv<64, 64, 0>(a, va, blocks, stream);
+    if (pb.d_h == 128 && pb.d_v == 128) *err = which ? launch_kv<128, 128, 1>(a, va, bb, blocks, stream) : launch_kv<128, 128, 0>(a, va, bb, blocks, stream);
+    else if (pb.d_h == 64 && pb.d_v == 128) *err = which ? launch_kv<64, 128, 1>(a, va, bb, blocks, stream) : launch_kv<64, 128, 0>(a, va, bb, blocks, stream);
+    else if (pb.d_h == 128 && pb.d_v == 64) *err = which ? launch_kv<128, 64, 1>(a, va, bb, blocks, stream) : launch_kv<128, 64, 0>(a, va, bb, blocks, stream);
+    else *err = which ? launch_kv<64, 64, 1>(a, va, bb, blocks, stream) : launch_kv<64, 64, 0>(a, va, bb, blocks, stream);
   }
   return true;
 }

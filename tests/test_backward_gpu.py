@@ -36,6 +36,13 @@ BWD_CASES = [
     (torch.bfloat16, 2, 2, 2, 257, 257, 128, 128, True, 0, "none", 0.0, 130),
     (torch.bfloat16, 1, 4, 4, 2048, 2048, 128, 128, True, 0, "none", 0.0, 0),
     (torch.bfloat16, 1, 2, 2, 5, 700, 128, 128, True, 695, "none", 0.0, 0),
+    # MFMA kernels with a bias: rows 301 floats apart (unaligned 16-byte
+    # loads), -inf entries and wholly masked rows inside fully visible blocks,
+    # a per-key bias with a window, grouped heads
+    (torch.bfloat16, 1, 4, 2, 257, 301, 128, 128, True, 44, "dense", 0.1, 0),
+    (torch.bfloat16, 2, 4, 4, 200, 200, 128, 128, True, 0, "keys", 0.3, 60),
+    (torch.bfloat16, 1, 8, 2, 300, 300, 64, 128, False, 0, "rows", 0.2, 0),
+    (torch.bfloat16, 2, 2, 1, 190, 190, 128, 64, True, 0, "shared", 0.05, 0),
 ]
 
 

@@ -158,8 +158,8 @@ def draw_bwd_case(i):
 
 @pytest.mark.parametrize("i", range(N_BWD))
 def test_random_backward_parity(i):
-    """attn_bwd on random problems (MFMA kernels for bf16 with d in {64, 128}
-    and no bias, the generic ones otherwise), relative to each gradient's
+    """attn_bwd on random problems (MFMA kernels for bf16 with d in {64, 128},
+    with or without a bias, the generic ones otherwise), relative to each gradient's
     largest entry, with exact zeros where nothing contributes."""
     c = draw_bwd_case(i)
     print("case", i, c, flush=True)

@@ -1,7 +1,7 @@
 """GPU parity of attn_bwd on packed sequences (§33.4 of "Chapter 33
 推理计算优化", shape bucketing; gradients by recomputation, eqs 33.6-33.8 of
-§33.3): the MFMA dQ / dK / dV kernels for bf16 with d in {64, 128} and no bias,
-the generic kernels otherwise.  Each case is compared element by element with
+§33.3): the MFMA dQ / dK / dV kernels for bf16 with d in {64, 128} (with or
+without a bias), the generic kernels otherwise.  Each case is compared element by element with
 the oracle's attention_varlen_backward, relative to each gradient's largest
 entry, with exact zeros where nothing contributes; rows and keys outside every
 sequence keep what the caller's buffers held.  At the packed workload's size
@@ -60,7 +60,7 @@ BWD_CASES = [
     (torch.bfloat16, 2, 2, [500, 140], [500, 400], 128, 128, True, "none", 0.0, 100, 0),
     (torch.bfloat16, 4, 1, [90, 200], [150, 200], 64, 64, True, "none", 0.0, 0, -7),
     (torch.bfloat16, 2, 2, [0, 0, 64], [0, 30, 64], 128, 128, True, "none", 0.0, 0, 0),
-    # generic kernels: a bias, fp32, odd head sizes
+    # a bias (MFMA kernels); fp32 and odd head sizes (generic kernels)
     (torch.bfloat16, 4, 2, [200, 77, 129], [200, 300, 129], 64, 128, True, "packed", 0.1, 0, 0),
     (torch.bfloat16, 2, 2, [300, 64], [300, 100], 128, 128, True, "keys", 0.05, 0, 0),
     (torch.float32, 2, 1, [70, 1, 33], [70, 5, 100], 64, 64, True, "none", 0.0, 0, 0),
