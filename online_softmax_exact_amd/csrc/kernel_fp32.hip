@@ -1,5 +1,6 @@
-// MFMA prefill for fp32 Q/K/V/O, d_h and d_v in {64, 128}, no bias, window
-// or variable lengths (the generic kernel serves the rest).
+// MFMA prefill for fp32 Q/K/V/O, d_h and d_v in {64, 128}, with or without a
+// bias and a sliding window, no variable lengths (the generic kernel serves
+// the rest).
 //
 // What it computes: for every query row, Algorithm 33.1 of "Chapter 33
 // 推理计算优化" §33.2 over key tiles of 32: exact softmax attention (eq 33.2)
@@ -45,6 +46,9 @@ struct F32Args {
   int32_t* n_legal;
   int64_t qs[3], ks[3], vs[3], os[3];
   int64_t q_offset;
+  int64_t window;           // keys j >= q_offset + i - window + 1; 0 = none
+  const float* bias;        // fp32 additive bias / mask, NULL = none
+  int64_t bs[4];            // its element strides over b, hq, i, j
   int32_t t_q, t_k, heads_q, group, n_qtiles, batch_heads;
   float scale_log2;
   int32_t causal;
@@ -55,7 +59,7 @@ __device__ __forceinline__ int clamp_pos32(const F32Args& a, int64_t p) {
   return p < -1 ? -1 : (p > a.t_k ? a.t_k : static_cast<int>(p));
 }
 
-template <int DH, int DV, bool COUNT>
+template <int DH, int DV, bool COUNT, bool BIAS>
 __global__ __launch_bounds__(kThreads, 2) void fp32_prefill_kernel(F32Args a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KP = DH + 1;   // padded K row, in floats
@@ -104,6 +108,19 @@ __global__ __launch_bounds__(kThreads, 2) void fp32_prefill_kernel(F32Args a) {
     if (tw < n_w) n_w = tw;
   }
   const int pos_row = clamp_pos32(a, a.q_offset + row);
+  // Sliding window: first key of this row, of the wavefront's first row and
+  // of the workgroup's first row (clamped to [0, T_k]); tiles before the
+  // workgroup's are never loaded, tiles before the wavefront's are skipped.
+  auto win_lo = [&](int64_t r) -> int {
+    if (a.window <= 0) return 0;
+    const int64_t lo = a.q_offset + r - a.window + 1;
+    return lo < 0 ? 0 : (lo > a.t_k ? a.t_k : static_cast<int>(lo));
+  };
+  const int lo_row = win_lo(row);
+  const int lo_w = win_lo(row0);
+  const int t_begin = win_lo(static_cast<int64_t>(qt) * kRows) / kKeys;
+  const float* brow = nullptr;   // this row's bias
+  if (BIAS && row_ok) brow = a.bias + b * a.bs[0] + hq * a.bs[1] + static_cast<int64_t>(row) * a.bs[2];
 
   const float* kbase = a.k + b * a.ks[0] + kvh * a.ks[1];
   const float* vbase = a.v + b * a.vs[0] + kvh * a.vs[1];
@@ -137,8 +154,8 @@ __global__ __launch_bounds__(kThreads, 2) void fp32_prefill_kernel(F32Args a) {
                             : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
   };
-  if (n_tiles > 0) fetch(0);
-  for (int t = 0; t < n_tiles; ++t) {
+  if (t_begin < n_tiles) fetch(t_begin);
+  for (int t = t_begin; t < n_tiles; ++t) {
     __syncthreads();   // every wave is done reading tile t - 1
 #pragma unroll
     for (int i = 0; i < KN; ++i) {
@@ -154,25 +171,33 @@ __global__ __launch_bounds__(kThreads, 2) void fp32_prefill_kernel(F32Args a) {
     __syncthreads();
     if (t + 1 < n_tiles) fetch(t + 1);
     const int key0 = t * kKeys;
-    if (t >= n_w) continue;   // wave-uniform: no row of this wavefront sees the tile
+    if (t >= n_w || key0 + kKeys <= lo_w) continue;   // wave-uniform: no row of this wavefront sees the tile
 
     f32x16 sacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < DH / 2; ++s)
       sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(k_tile[lr * KP + 2 * s + h], qreg[s], sacc, 0, 0, 0);
 
-    // Legal keys of this row in the tile: j < T_k and (not causal or j <= pos).
+    // Legal keys of this row in the tile: j < T_k, (not causal or j <= pos),
+    // inside the window, and a bias entry that is not -inf.
     int lim = a.causal ? pos_row - key0 : kKeys - 1;
     if (a.t_k - 1 - key0 < lim) lim = a.t_k - 1 - key0;
     if (!row_ok) lim = -1;
+    const int first = lo_row - key0;
     float z[16];
     float mx = -INFINITY;
     bool any = false;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = 8 * (r >> 2) + 4 * h + (r & 3);
-      const bool legal = j <= lim;
-      z[r] = legal ? sacc[r] * a.scale_log2 : -INFINITY;
+      bool legal = j <= lim && j >= first;
+      float zb = 0.0f;
+      if (BIAS) {
+        const float mb = legal ? brow[static_cast<int64_t>(key0 + j) * a.bs[3]] : -INFINITY;
+        legal = legal && mb != -INFINITY;
+        zb = mb * kLog2e;
+      }
+      z[r] = legal ? fmaf(sacc[r], a.scale_log2, zb) : -INFINITY;
       mx = fmaxf(mx, z[r]);
       any = any || legal;
       if (COUNT) count += legal ? 1 : 0;
@@ -231,14 +256,20 @@ __global__ __launch_bounds__(kThreads, 2) void fp32_prefill_kernel(F32Args a) {
 #endif
 }
 
+template <int DH, int DV, bool BIAS>
+void launch_b(const F32Args& a, int64_t blocks, bool count, hipStream_t s) {
+  if (count)
+    hipLaunchKernelGGL((fp32_prefill_kernel<DH, DV, true, BIAS>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((fp32_prefill_kernel<DH, DV, false, BIAS>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, s, a);
+}
+
 template <int DH, int DV>
 hipError_t launch_dims(const F32Args& a, int64_t blocks, bool count, hipStream_t s) {
-  if (count)
-    hipLaunchKernelGGL((fp32_prefill_kernel<DH, DV, true>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       s, a);
-  else
-    hipLaunchKernelGGL((fp32_prefill_kernel<DH, DV, false>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
-                       0, s, a);
+  if (a.bias != nullptr) launch_b<DH, DV, true>(a, blocks, count, s);
+  else launch_b<DH, DV, false>(a, blocks, count, s);
   return hipGetLastError();
 }
 
@@ -246,14 +277,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 }  // namespace
 
-// fp32 problems with d_h, d_v in {64, 128}, no bias, window or variable
-// lengths, 16-byte aligned tensors with strides a multiple of 4 floats, and
-// sizes that fit 32-bit tile indices.  Returns false when it does not
+// fp32 problems with d_h, d_v in {64, 128} (any bias and window), no
+// variable lengths, 16-byte aligned tensors with strides a multiple of 4
+// floats, and sizes that fit 32-bit tile indices.  Returns false when it does not
 // apply (the generic kernel then runs).
 bool launch_fp32_mfma(const Problem& pb, int dtype, const void* q, const void* k, const void* v, void* o,
                       float* lse, int32_t* n_legal, hipStream_t stream, int* status) {
-  if (dtype != ATTN_F32 || pb.bias != nullptr || pb.window != 0 || pb.cu_q != nullptr || pb.kv_lens != nullptr)
-    return false;
+  if (dtype != ATTN_F32 || pb.cu_q != nullptr || pb.kv_lens != nullptr) return false;
   if (!((pb.d_h == 64 || pb.d_h == 128) && (pb.d_v == 64 || pb.d_v == 128))) return false;
   if (pb.t_q >= (int64_t(1) << 30) || pb.t_k >= (int64_t(1) << 30)) return false;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return false;
@@ -273,6 +303,9 @@ bool launch_fp32_mfma(const Problem& pb, int dtype, const void* q, const void* k
     a.qs[i] = pb.qs[i]; a.ks[i] = pb.ks[i]; a.vs[i] = pb.vs[i]; a.os[i] = pb.os[i];
   }
   a.q_offset = pb.q_offset;
+  a.window = pb.window;
+  a.bias = pb.bias;
+  for (int i = 0; i < 4; ++i) a.bs[i] = pb.bs[i];
   a.t_q = static_cast<int32_t>(pb.t_q);
   a.t_k = static_cast<int32_t>(pb.t_k);
   a.heads_q = static_cast<int32_t>(pb.heads_q);

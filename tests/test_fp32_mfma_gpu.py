@@ -1,5 +1,5 @@
-"""GPU parity of the fp32 MFMA prefill (fp32 with d_h, d_v in {64, 128}, no
-bias, window or variable lengths), element by element against the oracle at
+"""GPU parity of the fp32 MFMA prefill (fp32 with d_h, d_v in {64, 128}, any
+bias and window, no variable lengths), element by element against the oracle at
 the fp32 tolerances (max |dO| 1e-5, mean 1e-6, LSE 1e-5): several 128-row
 workgroup tiles and 32-key tiles with ragged ends, causal and not, square and
 non-square alignment (offsets before, inside and past the keys), grouped
@@ -69,3 +69,32 @@ def test_fp32_mfma_strided_output_and_larger():
         torch.cuda.synchronize()
         assert_close(out, lse, o_ref, l_ref, torch.float32, what=f"row stride {width}")
         assert torch.all(buf[..., 64:] == 7.0), "wrote past the output view"
+
+
+BIAS_CASES = [
+    # (B, Hq, Hkv, Tq, Tk, dh, dv, causal, q_offset, bias, masked_frac, window)
+    (2, 4, 2, 200, 300, 64, 64, True, 100, "dense", 0.1, 0),
+    (1, 4, 4, 257, 257, 128, 128, True, 0, "keys", 0.3, 0),
+    (1, 2, 1, 150, 150, 64, 128, False, 0, "rows", 0.3, 0),   # wholly masked rows
+    (2, 2, 2, 300, 300, 128, 64, True, 0, "shared", 0.05, 40),
+    (1, 4, 2, 400, 400, 64, 64, True, 0, "none", 0.0, 1),
+    (1, 2, 2, 130, 600, 64, 64, True, 470, "none", 0.0, 200),
+]
+
+
+@pytest.mark.parametrize("case", BIAS_CASES, ids=[f"b{i}" for i in range(len(BIAS_CASES))])
+def test_fp32_mfma_bias_and_window(case):
+    """The fp32 MFMA prefill with every bias broadcast (-inf entries, wholly
+    masked rows) and sliding windows, against the oracle at fp32 tolerances."""
+    b, hq, hkv, tq, tk, dh, dv, causal, off, bias, mf, w = case
+    print("case", case, flush=True)
+    wl = inputs.make_random(b, hq, hkv, tq, tk, dh, dv, dtype=torch.float32,
+                            seed=zlib.crc32(repr(case).encode()) % 10_000, causal=causal, q_offset=off,
+                            bias=bias, masked_frac=mf)
+    q, k, v, m = to_dev(wl)
+    o, lse, n = attn.attn_fwd(q, k, v, scale=wl.scale, causal=causal, q_offset=off, bias=m, window=w,
+                              return_n_legal=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref, n_ref = oracle_full(wl, window=w)
+    assert_close(o, lse, o_ref, l_ref, torch.float32, what=str(case))
+    assert np.array_equal(n.cpu().numpy(), n_ref), "n_legal differs"
