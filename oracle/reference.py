@@ -435,6 +435,33 @@ def attention_varlen_backward(q, k, v, d_o, cu_q, cu_k, *, scale: float, causal:
     return dq, dk, dv
 
 
+def attention_kvlens_backward(q, k, v, d_o, kv_lens, *, scale: float, causal: bool,
+                              q_offset: int = 0, bias=None, window: int = 0):
+    """Gradients of ``attention_kvlens`` (per-batch KV lengths, §33.4 shape
+    bucketing; backward of §33.3, eqs 33.6-33.8): batch b's gradients are
+    ``attention_backward`` of its rows over keys [0, kv_lens[b]), with its
+    rows at q_offset + kv_lens[b] - T_q + i; keys at or past kv_lens[b] get
+    zero.  Returns (dq, dk, dv) in the layout of q, k, v."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d_o = np.asarray(d_o, dtype=np.float64)
+    t_q = q.shape[2]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(q.shape[0]):
+        n_k = int(kv_lens[b])
+        b_s = None
+        if bias is not None:   # a size-1 (broadcast) batch or key dim is kept whole
+            bb = np.asarray(bias, dtype=np.float64)
+            b_s = bb[(slice(b, b + 1) if bb.shape[0] != 1 else slice(None)), :, :,
+                     (slice(0, n_k) if bb.shape[3] != 1 else slice(None))]
+        g = attention_backward(q[b:b + 1], k[b:b + 1, :, :n_k], v[b:b + 1, :, :n_k], d_o[b:b + 1],
+                               scale=scale, causal=causal, q_offset=q_offset + n_k - t_q, bias=b_s,
+                               window=window)
+        dq[b:b + 1], dk[b:b + 1, :, :n_k], dv[b:b + 1, :, :n_k] = g
+    return dq, dk, dv
+
+
 def attention_backward_sampled(q, k, v, d_o, *, rows=(), keys=(), scale: float,
                                causal: bool, q_offset: int = 0, window: int = 0):
     """The gradients of ``attention_backward`` (eqs 33.6-33.8) at selected

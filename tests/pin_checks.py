@@ -814,6 +814,53 @@ def check_varlen_backward(R):
             np.testing.assert_allclose(dv[:, :, k0:k1], pv[:, :, :k1 - k0], rtol=0, atol=1e-12)
 
 
+def check_kvlens_backward(R):
+    """Gradients with per-batch KV lengths: (a) central finite differences of
+    sum(G_O * O) through the forward ``attention_kvlens`` (rows at the end of
+    each batch's keys, a batch with more rows than keys, an empty key set,
+    GQA, a bias with -inf entries, a window); (b) equal to the full-length
+    batch's gradients when the keys past kv_lens[b] are masked by a -inf bias
+    (the padded form); (c) keys past kv_lens[b] get zero."""
+    rng = np.random.default_rng(35)
+    b_n, hq, hkv, tq, tk, d_h, d_v = 3, 4, 2, 3, 6, 3, 2
+    lens = [6, 2, 0]
+    q = rng.standard_normal((b_n, hq, tq, d_h))
+    k = rng.standard_normal((b_n, hkv, tk, d_h))
+    v = rng.standard_normal((b_n, hkv, tk, d_v))
+    g = rng.standard_normal((b_n, hq, tq, d_v))
+    mb = rng.standard_normal((b_n, hq, tq, tk))
+    mb[rng.random(mb.shape) < 0.15] = -np.inf
+    for causal, w, bias in ((True, 0, None), (False, 0, mb), (True, 2, mb)):
+        kw = dict(scale=0.7, causal=causal, bias=bias, window=w)
+        dq, dk, dv = R.attention_kvlens_backward(q, k, v, g, lens, **kw)
+        for b, n in enumerate(lens):   # (c)
+            assert not dk[b, :, n:].any() and not dv[b, :, n:].any()
+
+        def loss(qq, kk, vv):
+            o, _, _ = R.attention_kvlens(qq, kk, vv, lens, **kw)
+            return float((o * g).sum())
+        eps = 1e-6
+        for name, x, grad in (("dq", q, dq), ("dk", k, dk), ("dv", v, dv)):
+            for idx in [tuple(rng.integers(0, n) for n in x.shape) for _ in range(12)]:
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                args_p = [xp if y is x else y for y in (q, k, v)]
+                args_m = [xm if y is x else y for y in (q, k, v)]
+                fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+                assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+        # (b) batch by batch: all T_k keys, those past the length masked, rows
+        # at positions q_offset + L_b - T_q + i
+        for b, n in enumerate(lens):
+            bp = np.zeros((1, hq, tq, tk)) if bias is None else bias[b:b + 1].copy()
+            bp[..., n:] = -np.inf
+            pq, pk, pv = R.attention_backward(q[b:b + 1], k[b:b + 1], v[b:b + 1], g[b:b + 1], scale=0.7,
+                                              causal=causal, q_offset=n - tq, bias=bp, window=w)
+            np.testing.assert_allclose(dq[b:b + 1], pq, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(dk[b:b + 1], pk, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(dv[b:b + 1], pv, rtol=0, atol=1e-12)
+
+
 ALL_CHECKS = [
     check_example_25_1_exact, check_example_25_1_fp64, check_exercise_33_2,
     check_kv_cache_vectors, check_equal_scores_mean, check_single_and_two_keys,
@@ -825,5 +872,5 @@ ALL_CHECKS = [
     check_backward_finite_differences, check_backward_shift_direction, check_backward_identities,
     check_backward_single_key, check_backward_library_autograd, check_backward_sampled_matches_full,
     check_varlen_equals_padded, check_varlen_sequences_independent, check_varlen_key_bias_broadcast,
-    check_kvlens_equals_padded, check_varlen_backward,
+    check_kvlens_equals_padded, check_varlen_backward, check_kvlens_backward,
 ]

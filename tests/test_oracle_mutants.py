@@ -60,6 +60,10 @@ MUTANTS = {
                             "scale=scale, causal=causal, q_offset=q_offset,\n                               bias=b_s"),
     "varlen_bwd_dk_rows": ("dq[:, :, q0:q1], dk[:, :, k0:k1], dv[:, :, k0:k1] = g",
                            "dq[:, :, q0:q1], dk[:, :, q0:q0 + k1 - k0], dv[:, :, k0:k1] = g"),
+    "kvlens_bwd_top_left": ("d_o[b:b + 1],\n                               scale=scale, causal=causal, q_offset=q_offset + n_k - t_q",
+                            "d_o[b:b + 1],\n                               scale=scale, causal=causal, q_offset=q_offset"),
+    "kvlens_bwd_keys_at_end": ("dq[b:b + 1], dk[b:b + 1, :, :n_k], dv[b:b + 1, :, :n_k] = g",
+                               "dq[b:b + 1], dk[b:b + 1, :, k.shape[2] - n_k:], dv[b:b + 1, :, :n_k] = g"),
 }
 
 
