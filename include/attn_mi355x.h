@@ -114,7 +114,7 @@ typedef struct {
   const int32_t* cu_seqlens_k; /* required with cu_seqlens_q */
   int64_t n_seqs;              /* >= 0 with cu_seqlens_q, else ignored */
   int64_t max_seqlen_q;        /* >= 0 with cu_seqlens_q, else ignored */
-  /* Per-batch KV lengths (attn_fwd and attn_decode_splitkv, not with
+  /* Per-batch KV lengths (attn_fwd, attn_bwd and attn_decode_splitkv, not with
    * cu_seqlens_q): batch b uses keys [0, L_b) of K and V, L_b =
    * seqlens_k[b] clamped to [0, T_k] in the kernel, and its row i sits at
    * q_offset + L_b - T_q + i.  DEVICE int32 array of B entries; NULL = every
@@ -199,7 +199,8 @@ size_t attn_bwd_workspace_bytes(const attn_params_t* p);
  * 256-byte aligned.  Packed sequences (cu_seqlens_q) are taken as in
  * attn_fwd, each sequence's gradients from its own rows and keys; rows and
  * keys outside every sequence are not written, and n_seqs = 0 writes nothing.
- * Per-batch KV lengths (seqlens_k) are not taken: ATTN_E_UNSUPPORTED. */
+ * Per-batch KV lengths (seqlens_k) are taken as in attn_fwd; the keys of
+ * batch b at or past L_b get zero gradients. */
 int attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v,
              const void* o, const float* lse, const void* d_o, void* d_q, void* d_k,
              void* d_v, void* workspace, size_t workspace_bytes, void* stream);

@@ -249,7 +249,7 @@ def attn_decode_splitkv(q, k_cache, v_cache, *, split_size, scale=None, causal=T
 
 
 def attn_bwd(q, k, v, o, lse, d_o, *, scale=None, causal=True, q_offset=0, bias=None, window=0,
-             cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
+             cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, seqlens_k=None,
              d_q=None, d_k=None, d_v=None, workspace=None, stream=None):
     """Gradients (d_q, d_k, d_v) of attn_fwd's attention for the upstream
     gradient ``d_o``, recomputed from the forward's ``o`` and ``lse``.  Each
@@ -258,7 +258,9 @@ def attn_bwd(q, k, v, o, lse, d_o, *, scale=None, causal=True, q_offset=0, bias=
 
     Packed sequences take the forward's ``cu_seqlens_q`` / ``cu_seqlens_k`` /
     ``max_seqlen_q``; the library leaves rows and keys outside every sequence
-    unwritten, so gradients allocated here start at zero."""
+    unwritten, so gradients allocated here start at zero.  Per-batch KV
+    lengths take the forward's ``seqlens_k``; keys past a batch's length get
+    zero gradients."""
     lib = load_library()
     if d_o.shape != o.shape or d_o.stride() != o.stride() or d_o.dtype != o.dtype:
         raise ValueError("d_o must have the shape, strides and dtype of o")
@@ -266,7 +268,7 @@ def attn_bwd(q, k, v, o, lse, d_o, *, scale=None, causal=True, q_offset=0, bias=
         raise ValueError("lse must be the contiguous float32 [B, H_q, T_q] LSE of the forward")
     p = make_params(q, k, v, o, scale=scale, causal=causal, q_offset=q_offset, bias=bias,
                     window=window, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
-                    max_seqlen_q=max_seqlen_q)
+                    max_seqlen_q=max_seqlen_q, seqlens_k=seqlens_k)
     grads = []
     for t, g in ((q, d_q), (k, d_k), (v, d_v)):
         if g is None:

@@ -159,7 +159,6 @@ int attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v
   int st = validate(p, &pb);
   if (st != ATTN_OK) return st;
   if ((st = check_pointers(pb, q, k, v, o, lse)) != ATTN_OK) return st;
-  if (pb.kv_lens != nullptr) return ATTN_E_UNSUPPORTED;
   if (pb.cu_q != nullptr && pb.n_seqs == 0) return ATTN_OK;
   const bool rows = numel_nonzero(pb.batch, pb.heads_q, pb.t_q, 1);
   const bool keys = numel_nonzero(pb.batch, pb.heads_kv, pb.t_k, 1);

@@ -67,7 +67,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(Problem pb, const T* __rest
     const int64_t kvh = hq / pb.group;
     // This row's keys [k0, k0 + t_k) and position (packed sequences: its
     // sequence's own, rows at the end of its keys; a row outside every
-    // sequence is not written).
+    // sequence is not written; per-batch KV lengths: the batch's first L_b
+    // keys, rows at the end of them).
     int64_t k0 = 0, t_k = pb.t_k, pos = pb.q_offset + i;
     if (pb.cu_q != nullptr && ok) {
       int64_t sq, q0, q1, k1;
@@ -75,6 +76,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(Problem pb, const T* __rest
       seq_extent(pb.cu_k, pb.t_k, sq, &k0, &k1);
       t_k = k1 - k0;
       pos = pb.q_offset + t_k - (q1 - q0) + (i - q0);
+    } else if (pb.kv_lens != nullptr && ok) {
+      const int64_t raw = pb.kv_lens[b];
+      t_k = raw < 0 ? 0 : (raw > pb.t_k ? pb.t_k : raw);
+      pos = pb.q_offset + t_k - pb.t_q + i;
     }
     const T* qrow = q + b * pb.qs[0] + hq * pb.qs[1] + i * pb.qs[2];
     const T* grow = d_o + b * pb.os[0] + hq * pb.os[1] + i * pb.os[2];
@@ -157,7 +162,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(Problem pb, const T* __re
     // This key's rows [q0, q0 + t_q) and its index jl among its sequence's
     // keys (packed sequences: its own sequence, whose rows sit at the end of
     // its keys; a key outside every sequence is not written).
+    // Per-batch KV lengths: rows at q_offset + L_b - T_q + i; a key at or
+    // past L_b is seen by no row and gets zero.
     int64_t q0 = 0, t_q = pb.t_q, jl = j, q_off = pb.q_offset;
+    bool seen = true;
     if (pb.cu_q != nullptr && ok) {
       int64_t sk, k0, k1, q1;
       ok = find_seq(pb.cu_k, pb.n_seqs, pb.t_k, j, &sk, &k0, &k1);
@@ -165,6 +173,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(Problem pb, const T* __re
       t_q = q1 - q0;
       jl = j - k0;
       q_off = pb.q_offset + (k1 - k0) - t_q;
+    } else if (pb.kv_lens != nullptr && ok) {
+      const int64_t raw = pb.kv_lens[b];
+      const int64_t len = raw < 0 ? 0 : (raw > pb.t_k ? pb.t_k : raw);
+      q_off = pb.q_offset + len - pb.t_q;
+      seen = j < len;
     }
     const T* krow = k + b * pb.ks[0] + kvh * pb.ks[1] + j * pb.ks[2];
     const T* vrow = v + b * pb.vs[0] + kvh * pb.vs[1] + j * pb.vs[2];
@@ -176,7 +189,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(Problem pb, const T* __re
     if (ok) {
       // Rows i that see key j: q_offset + i >= j (causal) and
       // q_offset + i - W + 1 <= j (window).
-      int64_t ilo = 0, ihi = t_q;
+      int64_t ilo = 0, ihi = seen ? t_q : 0;
       if (pb.causal && jl - q_off > ilo) ilo = jl - q_off;
       if (pb.window > 0 && jl - q_off + pb.window < ihi) ihi = jl - q_off + pb.window;
       float ak[kAcc] = {0.0f, 0.0f, 0.0f, 0.0f}, av[kAcc] = {0.0f, 0.0f, 0.0f, 0.0f};

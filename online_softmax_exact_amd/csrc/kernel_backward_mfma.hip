@@ -94,6 +94,9 @@ struct VArgs {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int32_t n_seqs, n_slots;
+  // Per-batch KV lengths instead (cu_q NULL): batch b uses keys [0, L_b),
+  // rows at q_offset + L_b - T_q + i; dense grid; keys past L_b get zero.
+  const int32_t* kv_lens;
 };
 // Bias instances take the bias as one more trailing argument (fp32, keys
 // contiguous, any broadcast over batch, head and row).
@@ -254,10 +257,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a, Extra
   int32_t row_base = 0, key_base = 0;
   if constexpr (VAR) {
     const VArgs& va = pick<VArgs>(ex...);
-    const int sq = slot_seq(va.cu_q, va.n_seqs, a.t_q, qt, &qt);
-    enter_seq<true>(a, va, sq, a.qs[2], &row_base, &key_base);
-    if (qt < 0 || qt * kBr >= a.t_q) return;   // whole workgroup: a slot outside the sequence's tiles
-    ridx_base += row_base;
+    if (va.cu_q != nullptr) {
+      const int sq = slot_seq(va.cu_q, va.n_seqs, a.t_q, qt, &qt);
+      enter_seq<true>(a, va, sq, a.qs[2], &row_base, &key_base);
+      if (qt < 0 || qt * kBr >= a.t_q) return;   // whole workgroup: a slot outside the sequence's tiles
+      ridx_base += row_base;
+    } else {
+      const int len = clamp_len(va.kv_lens[b], a.t_k);
+      a.q_offset += len - a.t_q;
+      a.t_k = len;
+    }
   }
 
   const int row0 = qt * kBr + wave * kRowsW;
@@ -515,11 +524,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Extra
   const int32_t t_q_all = a.t_q;   // rows per head of LSE and D
   int32_t row_base = 0;            // packed row of the sequence's row 0
   int32_t key_base = 0;            // packed key of the sequence's key 0
+  int32_t t_k_store = a.t_k;       // keys whose gradient this launch writes
   if constexpr (VAR) {
     const VArgs& va = pick<VArgs>(ex...);
-    const int sq = slot_seq(va.cu_k, va.n_seqs, a.t_k, kt, &kt);
-    enter_seq<false>(a, va, sq, DK ? a.ks[2] : a.vs[2], &row_base, &key_base);
-    if (kt < 0 || kt * kBr >= a.t_k) return;   // whole workgroup: a slot outside the sequence's tiles
+    if (va.cu_q != nullptr) {
+      const int sq = slot_seq(va.cu_k, va.n_seqs, a.t_k, kt, &kt);
+      enter_seq<false>(a, va, sq, DK ? a.ks[2] : a.vs[2], &row_base, &key_base);
+      if (kt < 0 || kt * kBr >= a.t_k) return;   // whole workgroup: a slot outside the sequence's tiles
+      t_k_store = a.t_k;
+    } else {
+      const int len = clamp_len(va.kv_lens[b], a.t_k);
+      a.q_offset += len - a.t_q;
+      a.t_k = len;   // keys [len, T_k) are seen by no row: their gradients are written as 0
+    }
   }
 
   const int key0 = kt * kBr + wave * kRowsW;   // first key of this wave
@@ -547,6 +564,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Extra
   int64_t i_lo = 0, i_hi = a.t_q;
   if (a.causal && wk0 - a.q_offset > i_lo) i_lo = wk0 - a.q_offset;
   if (a.window > 0 && wk0 + kBr - 1 - a.q_offset + a.window < i_hi) i_hi = wk0 + kBr - 1 - a.q_offset + a.window;
+  if (VAR && wk0 >= a.t_k) i_hi = 0;   // per-batch lengths: a tile past L_b sees no row
   if (i_lo > i_hi) i_lo = i_hi;
   const int qt_lo = static_cast<int>(i_lo / kBc);
   const int n_qt = i_hi > i_lo ? static_cast<int>((i_hi + kBc - 1) / kBc) - qt_lo : 0;
@@ -823,7 +841,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Extra
   }
 
   // dK = scale dS^T Q (eq 33.8) or dV = P^T dO (eq 33.6); keys no row sees get 0.
-  if (!key_ok) return;
+  if (!(VAR ? key < t_k_store : key_ok)) return;
   const float sc = DK ? a.scale_log2 * kLn2 : 1.0f;
   uint16_t* op = DK ? a.out + b * a.ks[0] + kvh * a.ks[1] + static_cast<int64_t>(key) * a.ks[2]
                     : a.out + b * a.vs[0] + kvh * a.vs[1] + static_cast<int64_t>(key) * a.vs[2];
@@ -851,8 +869,9 @@ void launch_kv_x(const BArgs& a, int64_t blocks, hipStream_t s, X... x) {
 // instances without them keep the plain argument block.
 template <int DH, int DV, int WHICH>
 hipError_t launch_kv(const BArgs& a, const VArgs& va, const BBias& bb, int64_t blocks, hipStream_t s) {
-  if (va.cu_q != nullptr && bb.bias != nullptr) launch_kv_x<DH, DV, WHICH>(a, blocks, s, va, bb);
-  else if (va.cu_q != nullptr) launch_kv_x<DH, DV, WHICH>(a, blocks, s, va);
+  const bool var = va.cu_q != nullptr || va.kv_lens != nullptr;
+  if (var && bb.bias != nullptr) launch_kv_x<DH, DV, WHICH>(a, blocks, s, va, bb);
+  else if (var) launch_kv_x<DH, DV, WHICH>(a, blocks, s, va);
   else if (bb.bias != nullptr) launch_kv_x<DH, DV, WHICH>(a, blocks, s, bb);
   else launch_kv_x<DH, DV, WHICH>(a, blocks, s);
   return hipGetLastError();
@@ -866,8 +885,9 @@ void launch_dq_x(const BArgs& a, int64_t blocks, hipStream_t s, X... x) {
 
 template <int DH, int DV>
 hipError_t launch_dq(const BArgs& a, const VArgs& va, const BBias& bb, int64_t blocks, hipStream_t s) {
-  if (va.cu_q != nullptr && bb.bias != nullptr) launch_dq_x<DH, DV>(a, blocks, s, va, bb);
-  else if (va.cu_q != nullptr) launch_dq_x<DH, DV>(a, blocks, s, va);
+  const bool var = va.cu_q != nullptr || va.kv_lens != nullptr;
+  if (var && bb.bias != nullptr) launch_dq_x<DH, DV>(a, blocks, s, va, bb);
+  else if (var) launch_dq_x<DH, DV>(a, blocks, s, va);
   else if (bb.bias != nullptr) launch_dq_x<DH, DV>(a, blocks, s, bb);
   else launch_dq_x<DH, DV>(a, blocks, s);
   return hipGetLastError();
@@ -941,7 +961,7 @@ bool launch_bwd_dq_mfma(const Problem& pb, int dtype, const void* q, const void*
   a.heads_kv = static_cast<int32_t>(pb.heads_kv);
   a.group = pb.group;
   a.n_tiles_grid = static_cast<int32_t>(n_qtiles);
-  const VArgs va{pb.cu_q, pb.cu_k, static_cast<int32_t>(pb.n_seqs), static_cast<int32_t>(n_qtiles)};
+  const VArgs va{pb.cu_q, pb.cu_k, static_cast<int32_t>(pb.n_seqs), static_cast<int32_t>(n_qtiles), pb.kv_lens};
   const BBias bb = make_bias(pb);
   a.n_units = static_cast<int32_t>(pb.batch * pb.heads_q);
   a.scale_log2 = pb.scale_log2;
@@ -994,7 +1014,7 @@ bool launch_bwd_dkdv_mfma(const Problem& pb, int dtype, const void* q, const voi
   a.heads_kv = static_cast<int32_t>(pb.heads_kv);
   a.group = pb.group;
   a.n_tiles_grid = static_cast<int32_t>(n_ktiles);
-  const VArgs va{pb.cu_q, pb.cu_k, static_cast<int32_t>(pb.n_seqs), static_cast<int32_t>(n_ktiles)};
+  const VArgs va{pb.cu_q, pb.cu_k, static_cast<int32_t>(pb.n_seqs), static_cast<int32_t>(n_ktiles), pb.kv_lens};
   const BBias bb = make_bias(pb);
   a.n_units = static_cast<int32_t>(pb.batch * pb.heads_kv);
   a.scale_log2 = pb.scale_log2;

@@ -190,16 +190,17 @@ def test_varlen_rejects(lib):
 
 
 def test_varlen_unsupported_entry_points(lib):
-    # Split-KV decode takes per-batch lengths but not packed sequences; the
-    # backward takes packed sequences but not per-batch lengths.
+    # Split-KV decode takes per-batch lengths but not packed sequences (the
+    # backward takes both; with no rows and no keys it has nothing to do).
     p = packed_params()
     need = lib.attn_decode_workspace_bytes(ctypes.byref(p), 4)
     assert lib.attn_decode_splitkv(ctypes.byref(p), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need,
                                    None) == -4
-    params = good_params(seqlens_k=0x400000)
-    need = lib.attn_bwd_workspace_bytes(ctypes.byref(params))
-    assert lib.attn_bwd(ctypes.byref(params), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                        FAKE, FAKE, need, None) == -4
+    params = good_params(seqlens_k=0x400000, batch=0)
+    assert lib.attn_bwd(ctypes.byref(params), None, None, None, None, None, None, None, None,
+                        None, None, 0, None) == 0
+    assert lib.attn_bwd(ctypes.byref(packed_params(seqlens_k=0x400000)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -2   # not with packed sequences
 
 
 def test_packed_backward_host_checks(lib):
