@@ -250,3 +250,55 @@ def test_random_packed_backward_parity(i):
         s = max(float(np.abs(want).max()), 1e-30)
         err = np.abs(g64 - want) / s
         assert err.max() <= tol["max"] and err.mean() <= tol["mean"], f"{name}: {err.max():.2e} / {err.mean():.2e}"
+
+
+N_BWD_KVLENS = 12
+
+
+@pytest.mark.parametrize("i", range(N_BWD_KVLENS))
+def test_random_kvlens_backward_parity(i):
+    """attn_bwd on random batches with per-batch KV lengths (zero lengths,
+    lengths below T_q, windows, biases) against the oracle's gradients; keys
+    past each length are written as zero."""
+    r = np.random.default_rng(11000 + i)
+    fast = r.random() < 0.7
+    dtype = torch.float32 if r.random() < 0.2 else torch.bfloat16
+    d_h = int(r.choice([64, 128])) if fast else int(r.choice([16, 40, 96]))
+    d_v = int(r.choice([64, 128])) if fast else int(r.choice([24, 64, 80]))
+    h_kv = int(r.choice([1, 2]))
+    h_q = h_kv * int(r.choice([1, 2, 4]))
+    b = int(r.integers(1, 4))
+    t_q = int(r.integers(1, 200))
+    t_k = int(r.integers(1, 600))
+    lens = [int(x) for x in r.integers(0, t_k + 1, b)]
+    causal = bool(r.random() < 0.7)
+    window = 0 if r.random() < 0.6 else int(r.integers(1, 300))
+    bias = str(r.choice(["none", "none", "keys", "dense"]))
+    print("case", i, dict(dtype=dtype, d_h=d_h, d_v=d_v, h=(h_q, h_kv), b=b, t_q=t_q, t_k=t_k, lens=lens,
+                          causal=causal, window=window, bias=bias), flush=True)
+    wl = inputs.make_random(b, h_q, h_kv, t_q, t_k, d_h, d_v, dtype=dtype, seed=300 + i, causal=causal,
+                            bias=bias, masked_frac=0.1 if bias != "none" else 0.0)
+    g = torch.randn((b, h_q, t_q, d_v), generator=torch.Generator().manual_seed(i)).to(dtype)
+    dd = dev()
+    q, k, v = wl.q.to(dd), wl.k.to(dd), wl.v.to(dd)
+    m = None if wl.bias is None else wl.bias.to(dd)
+    kw = dict(scale=wl.scale, causal=causal, bias=m, window=window,
+              seqlens_k=torch.tensor(lens, dtype=torch.int32, device=dd))
+    o, lse = attn.attn_fwd(q, k, v, **kw)
+    dq, dk, dv = attn.attn_bwd(q, k, v, o, lse, g.to(dd), **kw)
+    torch.cuda.synchronize()
+    b64 = None if wl.bias is None else f64(wl.bias)
+    ref = oracle.attention_kvlens_backward(f64(wl.q), f64(wl.k), f64(wl.v), f64(g), lens, scale=wl.scale,
+                                           causal=causal, bias=b64, window=window)
+    _, l_ref, _ = oracle.attention_kvlens(f64(wl.q), f64(wl.k), f64(wl.v), lens, scale=wl.scale, causal=causal,
+                                          bias=b64, window=window)
+    assert np.all(f64(dq)[np.isneginf(l_ref)] == 0), "dQ of a row without a legal key"
+    dead = np.all(ref[2] == 0, axis=-1)
+    assert np.all(f64(dk)[dead] == 0) and np.all(f64(dv)[dead] == 0), "gradient of an unseen key"
+    tol = BWD_TOL[dtype]
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        g64 = f64(got)
+        assert not np.isnan(g64).any(), name
+        s = max(float(np.abs(want).max()), 1e-30)
+        err = np.abs(g64 - want) / s
+        assert err.max() <= tol["max"] and err.mean() <= tol["mean"], f"{name}: {err.max():.2e} / {err.mean():.2e}"
