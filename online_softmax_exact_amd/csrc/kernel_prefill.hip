@@ -71,6 +71,12 @@ using namespace pf;
 #ifndef PREFILL_BIG_D64
 #define PREFILL_BIG_D64 1              // 1: the large shape also for d_h = 64, d_v = 128 (small grids)
 #endif
+#ifndef PREFILL_BIAS_NAT
+#define PREFILL_BIAS_NAT 1             // 1: bias scores formed in natural-log units (one VALU op fewer each)
+#endif
+#ifndef PREFILL_BIAS_PF
+#define PREFILL_BIAS_PF 1              // 1: bias of a full tile loaded at the previous tile's barrier (no counts)
+#endif
 #ifndef PREFILL_WAVES_PER_SIMD
 #define PREFILL_WAVES_PER_SIMD 2       // resident waves per SIMD the kernel is built for
 #endif
@@ -407,6 +413,18 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
     }
   };
 
+  // Bias values of the next full tile, loaded right after the barrier that
+  // ends the tile before it and ahead of that barrier's K/V copies, so they
+  // have the score MFMAs of the tile's first blocks to arrive and the next
+  // barrier (which waits for every load) never waits for them.  Counting
+  // instances keep per-block loads: they have no registers to spare.
+  constexpr bool kBiasPf = BIAS && !COUNT && PREFILL_BIAS_PF;
+  float mbp[kBiasPf ? kNQ : 1][16];
+  auto prefetch_bias = [&](int t) {
+#pragma unroll
+    for (int q = 0; q < (kBiasPf ? kNQ : 1); ++q) load_bias(t, q, mbp[q]);
+  };
+
   // Softmax of a block whose keys are all causally visible (and inside the
   // window) for every row, every row already holding statistics:
   // branch-free (tile max, new reference, weights, sums, bf16 packing), so
@@ -416,24 +434,43 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
   // reference unchanged (its maximum is -inf), as the valid-flag rule asks.
   auto fast_q = [&](int t, int q, const f32x16& sv, unsigned* pk, float& m_new, float& alpha) {
     if (BIAS) {
+      // z = scale dot + M in natural-log units (one fma); the base-2 factor
+      // goes into the exponent's fma, so a score costs two VALU operations
+      // besides its max and exp.
       float mb[16], z[16];
-      load_bias(t, q, mb);
+      if (kBiasPf) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mb[r] = mbp[q][r];
+      } else {
+        load_bias(t, q, mb);
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+#if PREFILL_BIAS_NAT
+        z[r] = fmaf(sv[r], a.scale, mb[r]);
+#else
         z[r] = fmaf(mb[r], kLog2e, sv[r] * a.scale_log2);
+#endif
         if (COUNT) count += static_cast<int>(mb[r] != -INFINITY);
       }
       float mx = fmaxf(z[0], z[1]);
 #pragma unroll
       for (int r = 2; r < 16; ++r) mx = fmaxf(mx, z[r]);
+#if PREFILL_BIAS_NAT
+      const float tmax = max_xor32(mx) * kLog2e;
+      const float zc = kLog2e;
+#else
       const float tmax = max_xor32(mx);
+      const float zc = 1.0f;
+#endif
       m_new = tmax > m2 + kRescale ? tmax : m2;
       alpha = fast_exp2(m2 - m_new);
+      const float nm = -m_new;
       float ps0 = 0.0f, ps1 = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float p0 = fast_exp2(z[2 * i] - m_new);
-        const float p1 = fast_exp2(z[2 * i + 1] - m_new);
+        const float p0 = fast_exp2(fmaf(z[2 * i], zc, nm));
+        const float p1 = fast_exp2(fmaf(z[2 * i + 1], zc, nm));
         pk[i] = pack_bf16(p0, p1);
         ps0 += p0;
         ps1 += p1;
@@ -473,21 +510,31 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
     const int first = lo_row - kb;   // keys below the window are not legal
     float mb[16];
     if (BIAS) load_bias(t, q, mb);
+    // Legal scores are kept as u with z = c u in base-2 units: u = dot and
+    // c = scale log2 e, or with a bias u = scale dot + M and c = log2 e (c > 0,
+    // so the maximum commutes with c); the weights take c in their fma.
     float mx = -INFINITY;
+#if PREFILL_BIAS_NAT
+    const float c = BIAS ? kLog2e : a.scale_log2;
+#else
+    const float c = 1.0f;
+#endif
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = 8 * (r >> 2) + 4 * h + (r & 3);
+#if PREFILL_BIAS_NAT
+      float z = BIAS ? fmaf(sv[r], a.scale, mb[r]) : sv[r];
+#else
       float z = sv[r] * a.scale_log2;
+      if (BIAS) z = fmaf(mb[r], kLog2e, z);
+#endif
       bool ok = j <= lim && j >= first;
-      if (BIAS) {
-        ok = ok && mb[r] != -INFINITY;
-        z = fmaf(mb[r], kLog2e, z);
-      }
+      if (BIAS) ok = ok && mb[r] != -INFINITY;
       if (COUNT) count += static_cast<int>(ok);
       sv[r] = ok ? z : -INFINITY;
       mx = fmaxf(mx, sv[r]);
     }
-    const float tmax = max_xor32(mx);
+    const float tmax = max_xor32(mx) * c;
     // First legal key of a row: store; later: lazy reference update.
     float m_new = m2;
     if (tmax != -INFINITY) {
@@ -503,10 +550,11 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
     rescale(m_new, alpha);
     l_lane *= alpha;
     float ps0 = 0.0f, ps1 = 0.0f;
+    const float nm2 = -m2;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float p0 = fast_exp2(sv[2 * i] - m2);
-      const float p1 = fast_exp2(sv[2 * i + 1] - m2);
+      const float p0 = fast_exp2(fmaf(sv[2 * i], c, nm2));
+      const float p1 = fast_exp2(fmaf(sv[2 * i + 1], c, nm2));
       pk[i] = pack_bf16(p0, p1);
       ps0 += p0;
       ps1 += p1;
@@ -516,8 +564,11 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
 
   // End of step t: wait for the DMA of tile t + 1 (issued one step ago),
   // barrier (every wave is done with slot t & 1), then DMA tile t + 2 into it.
+  // The first full tile always follows a general one, so every full tile's
+  // bias was prefetched here at the end of the tile before it.
   auto advance = [&](int t) {
     dma_barrier();
+    if (kBiasPf && t + 1 < t_full) prefetch_bias(t + 1);
     if (t + 2 < n_tiles) gload(t + 2);
   };
 
@@ -755,6 +806,7 @@ bool launch_prefill_mfma(const Problem& pb, int dtype, const void* q, const void
   a.n_qtiles = static_cast<int32_t>(n_qtiles);
   a.batch_heads = static_cast<int32_t>(pb.batch * pb.heads_q);
   a.scale_log2 = pb.scale_log2;
+  a.scale = pb.scale_log2 * kLn2;
   a.causal = pb.causal;
   a.cu_q = pb.cu_q;
   a.cu_k = pb.cu_k;

@@ -45,6 +45,7 @@ struct Args {
   // query tiles), 0 = query tiles outermost (every batch's heaviest tiles
   // first).
   int32_t batch_major;
+  float scale;   // scale in natural-log units (scale_log2 = scale * log2 e)
 };
 
 // x clamped to [0, n] (device-side length and offset arrays are never trusted).
@@ -75,7 +76,11 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
 // i % 4 of the 8-byte rows read by lanes 4 j + i / 4, j = 0..3.
-__device__ __forceinline__ u32x2 tr_read(const lds_char* p) {
+// The restrict qualifier gives the read alias information, as the K tile's
+// plain loads have; without it the compiler waits for every HBM -> LDS copy
+// in flight before the read, including the copy into the other ring slot
+// that the barrier protocol already keeps apart.
+__device__ __forceinline__ u32x2 tr_read(const lds_char* __restrict__ p) {
   i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4*)(p));
   return __builtin_bit_cast(u32x2, v);
