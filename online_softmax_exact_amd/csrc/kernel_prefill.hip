@@ -77,6 +77,9 @@ using namespace pf;
 #ifndef PREFILL_BIAS_PF
 #define PREFILL_BIAS_PF 1              // 1: bias of a full tile loaded at the previous tile's barrier (no counts)
 #endif
+#ifndef PREFILL_BIAS_LDS
+#define PREFILL_BIAS_LDS 1             // 1: full tiles' bias staged through LDS where it fits
+#endif
 #ifndef PREFILL_WAVES_PER_SIMD
 #define PREFILL_WAVES_PER_SIMD 2       // resident waves per SIMD the kernel is built for
 #endif
@@ -101,6 +104,18 @@ struct ShapeBig {
   static constexpr int kWaves = 8, kNQ = PREFILL_BIG_BLOCKS, kSched = PREFILL_BIG_SCHED;
 };
 
+// s_waitcnt vmcnt(n) for a count n <= N known once the caller is unrolled
+// (the instruction takes an immediate).
+template <int N>
+__device__ __forceinline__ void wait_vm_upto(int n) {
+  if constexpr (N == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (n >= N) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    else wait_vm_upto<N - 1>(n);
+  }
+}
+
 template <int DH, int DV, class S>
 struct Cfg {
   static constexpr int kBc = 32 * S::kNQ;        // keys per tile
@@ -124,8 +139,13 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
   constexpr int kBc = C::kBc;            // keys per tile
   constexpr int kBr = 32 * S::kWaves;    // query rows per workgroup
   constexpr int kSched = S::kSched;
-  // Two K slots then two V slots; tile t lives in slot t & 1.
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::K_BYTES + 2 * C::V_BYTES];
+  // Two K slots then two V slots; tile t lives in slot t & 1.  Instances with
+  // a bias (no counts) whose rings leave room for two workgroups per CU add a
+  // 4 KB bias block per wave and 32-key block (staged bias, below).
+  constexpr int kRing = 2 * C::K_BYTES + 2 * C::V_BYTES;
+  constexpr int kBiasStage = S::kWaves * kNQ * 4096;
+  constexpr bool kBiasLds = BIAS && !COUNT && PREFILL_BIAS_LDS && kRing + kBiasStage <= 81920;
+  __shared__ __attribute__((aligned(1024))) char smem[kRing + (kBiasLds ? kBiasStage : 0)];
   char* const kring = smem;
   char* const vring = smem + 2 * C::K_BYTES;
 
@@ -418,11 +438,51 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
   // have the score MFMAs of the tile's first blocks to arrive and the next
   // barrier (which waits for every load) never waits for them.  Counting
   // instances keep per-block loads: they have no registers to spare.
-  constexpr bool kBiasPf = BIAS && !COUNT && PREFILL_BIAS_PF;
+  constexpr bool kBiasPf = BIAS && !COUNT && PREFILL_BIAS_PF && !kBiasLds;
   float mbp[kBiasPf ? kNQ : 1][16];
-  auto prefetch_bias = [&](int t) {
+  // Staged bias (kBiasLds): a lane's own 16-byte loads touch 32 rows, i.e. 32
+  // cache lines, per instruction, and that line rate bounds a biased tile.
+  // Instead each wave copies its 32 rows x 32 keys (4 KB per block) with
+  // buffer_load ... lds, 8 whole rows per instruction, into its own LDS
+  // block, 16-byte chunk c of row r at chunk slot c ^ (r & 7) so the reads
+  // below are free of bank conflicts; lane l of copy i carries row
+  // 8 i + l / 8, chunk slot l % 8.
+  char* const bstage = smem + kRing + wave * (kNQ * 4096);
+  int bdma[4];
 #pragma unroll
-    for (int q = 0; q < (kBiasPf ? kNQ : 1); ++q) load_bias(t, q, mbp[q]);
+  for (int i = 0; i < 4; ++i) {
+    const int rr = 8 * i + (lane >> 3);
+    bdma[i] = kBiasLds ? static_cast<int>(rr * a.bs[2] * 4) + 16 * ((lane & 7) ^ (rr & 7)) : 0;
+  }
+  auto prefetch_bias = [&](int t) {
+    if (kBiasLds) {
+      const auto rs = make_rsrc(bias_w + t * kBc, bias_w_bytes - static_cast<int64_t>(t) * kBc * 4);
+#pragma unroll
+      for (int q = 0; q < kNQ; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void*)(bstage + q * 4096 + i * 1024), 16,
+              bdma[i] + 128 * q, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int q = 0; q < (kBiasPf ? kNQ : 1); ++q) load_bias(t, q, mbp[q]);
+    }
+  };
+  // Block q's staged values: wait until at most the 4 (kNQ - 1 - q) copies
+  // issued last are in flight, which covers block q's copies whether or not
+  // the K/V copies of tile t + 1 (issued after the bias) went out, and keeps
+  // the wait free of branches; then the 4 chunks 2 g + h of this lane's row.
+  auto staged_bias = [&](int q, float* mb) {
+    wait_vm_upto<4 * (kNQ - 1)>(4 * (kNQ - 1 - q));
+    const lds_char* rowp = (const lds_char*)bstage + q * 4096 + lr * 128;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 x = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+          rowp + (((2 * g + h) ^ (lr & 7)) << 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mb[4 * g + e] = x[e];
+    }
   };
 
   // Softmax of a block whose keys are all causally visible (and inside the
@@ -438,7 +498,9 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
       // goes into the exponent's fma, so a score costs two VALU operations
       // besides its max and exp.
       float mb[16], z[16];
-      if (kBiasPf) {
+      if constexpr (kBiasLds) {
+        staged_bias(q, mb);
+      } else if (kBiasPf) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mb[r] = mbp[q][r];
       } else {
@@ -568,7 +630,7 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
   // bias was prefetched here at the end of the tile before it.
   auto advance = [&](int t) {
     dma_barrier();
-    if (kBiasPf && t + 1 < t_full) prefetch_bias(t + 1);
+    if ((kBiasPf || kBiasLds) && t + 1 < t_full) prefetch_bias(t + 1);
     if (t + 2 < n_tiles) gload(t + 2);
   };
 

@@ -137,3 +137,9 @@ def test_padded_varlen_bias_8x16x4096_d64x128():
     extra += [(b, 3, min(wl.extras["lengths"][b], 4095)) for b in range(8)]  # first padded row
     rows = sample_rows(8, 16, 4096, 48, seed=5, extra=extra)
     check_sampled(wl, o, lse, rows, torch.bfloat16)
+    # The same call without counts (the launch configuration the benchmark
+    # times, whose full tiles stage the bias through LDS) gives the same bits.
+    o2, lse2 = attn.attn_fwd(q, k, v, scale=wl.scale, causal=True, q_offset=0, bias=m)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.view(torch.int16), o.view(torch.int16)), "O without counts differs"
+    assert torch.equal(lse2, lse), "LSE without counts differs"
