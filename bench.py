@@ -231,8 +231,8 @@ def workloads_section(torch, attn, inputs, dev, timed):
     out["verify"] = {"workload": "multi-query verify B=32 H=32 T_q=5 at positions 4091..4095, T_k=4096, d=128 "
                                  "(attn_fwd)", "ms": round(ms, 4), "value": round(gbs, 1), "unit": "GB/s",
                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                  "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "per_launch_bytes": by,
-                                  "per_launch_flops": fl,
+                                  "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": recorded_traffic("verify"),
+                                  "per_launch_bytes": by, "per_launch_flops": fl,
                                   "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 5)}}
     del q, k, v, o, lse, wl
     wl = inputs.make_config(5)
@@ -247,7 +247,8 @@ def workloads_section(torch, attn, inputs, dev, timed):
                                       "[8,1,4096,4096] with -inf padding and 2 masked rows per sequence (attn_fwd)",
                           "ms": round(ms, 4), "value": round(tf, 2), "unit": "TFLOP/s",
                           "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
-                                       "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                                       "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                       "traffic": recorded_traffic("padded_bias"), "counters": recorded_mfma("padded_bias"),
                                        "per_launch_flops": fl, "per_launch_bytes": by,
                                        "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}}
     return out
