@@ -6,7 +6,7 @@ and both must match the oracle element by element.  Cases: grouped heads,
 query rows ending inside a wavefront, several full key tiles with a ragged
 tail, causal and not, offsets, biases per head, shared by heads and shared
 by rows, a strided bias view (rows wider than T_k), -inf entries, and a
-sliding window.  The windowed case starts its rows past the first keys: a
+sliding window; packed sequences with a packed or per-key bias.  The windowed case starts its rows past the first keys: a
 bf16 row over one to three keys outputs nearly one value row, whose rounding
 alone takes most of the 1e-2 budget (there |o| reaches 2-4)."""
 
@@ -16,9 +16,10 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import online_softmax_exact_amd as attn
 from online_softmax_exact_amd import inputs
-from gpu_util import assert_close, dev, ensure_built, oracle_full, to_dev
+from gpu_util import assert_close, dev, ensure_built, f64, oracle_full, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -61,4 +62,35 @@ def test_staged_bias_parity(case):
     assert torch.equal(lse, lse_c), "staged and per-block bias give another LSE"
     o_ref, l_ref, n_ref = oracle_full(wl, window=w)
     assert np.array_equal(n.cpu().numpy(), n_ref), "n_legal differs"
+    assert_close(o, lse, o_ref, l_ref, torch.bfloat16, what=str(case))
+
+
+PACKED_CASES = [
+    # (Hq, Hkv, L_q per sequence, L_k per sequence, dh, dv, causal, bias, masked_frac, max_seqlen_q)
+    (4, 4, [200, 77, 129, 300], [200, 300, 129, 500], 64, 128, True, "packed", 0.1, 300),
+    (4, 2, [130, 257], [500, 257], 128, 64, False, "packed", 0.05, 128),   # workgroups loop over tiles
+    (2, 2, [300, 64], [300, 100], 64, 64, True, "keys", 0.05, 300),
+]
+
+
+@pytest.mark.parametrize("case", PACKED_CASES, ids=[f"p{i}" for i in range(len(PACKED_CASES))])
+def test_staged_bias_packed(case):
+    """Packed sequences with a packed (or per-key) bias through the staged
+    path, against the per-block path (bitwise) and the oracle."""
+    hq, hkv, lq, lk, dh, dv, causal, bias, mf, max_q = case
+    print("case", case, flush=True)
+    q, k, v, m, cu_q, cu_k = inputs.make_packed(lq, lk, hq, hkv, dh, dv, dtype=torch.bfloat16,
+                                                seed=zlib.crc32(repr(case).encode()) % 10_000,
+                                                bias=bias, masked_frac=mf)
+    d = dev()
+    scale = inputs.default_scale(dh)
+    kw = dict(scale=scale, causal=causal, bias=m.to(d), cu_seqlens_q=cu_q.to(d), cu_seqlens_k=cu_k.to(d),
+              max_seqlen_q=max_q)
+    o, lse = attn.attn_fwd(q.to(d), k.to(d), v.to(d), **kw)
+    o_c, lse_c, _ = attn.attn_fwd(q.to(d), k.to(d), v.to(d), return_n_legal=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_c.view(torch.int16)), "staged and per-block bias give other bits"
+    assert torch.equal(lse, lse_c), "staged and per-block bias give another LSE"
+    o_ref, l_ref, _ = oracle.attention_varlen(f64(q), f64(k), f64(v), cu_q.tolist(), cu_k.tolist(),
+                                              scale=scale, causal=causal, bias=f64(m))
     assert_close(o, lse, o_ref, l_ref, torch.bfloat16, what=str(case))
