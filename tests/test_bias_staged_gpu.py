@@ -5,10 +5,11 @@ loaded per block straight into registers): the two must give the same bits,
 and both must match the oracle element by element.  Cases: grouped heads,
 query rows ending inside a wavefront, several full key tiles with a ragged
 tail, causal and not, offsets, biases per head, shared by heads and shared
-by rows, a strided bias view (rows wider than T_k), -inf entries, and a
-sliding window; packed sequences with a packed or per-key bias.  The windowed case starts its rows past the first keys: a
-bf16 row over one to three keys outputs nearly one value row, whose rounding
-alone takes most of the 1e-2 budget (there |o| reaches 2-4)."""
+by rows, a strided bias view (rows wider than T_k), -inf entries, a sliding
+window, and packed sequences with a packed or per-key bias.  The windowed
+case starts its rows past the first keys: a bf16 row over one to three keys
+outputs nearly one value row, whose rounding alone takes most of the 1e-2
+budget (there |o| reaches 2-4)."""
 
 import zlib
 
