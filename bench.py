@@ -216,7 +216,7 @@ def workloads_section(torch, attn, inputs, dev, timed):
                                "value": round(tf, 4), "unit": "TFLOP/s",
                                "roofline": {"bound": "launch", "achieved": round(tf, 4), "peak": PEAK_FP32_TFLOPS,
                                             "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_TFLOPS, 6),
-                                            "traffic": None, "per_launch_flops": fl,
+                                            "traffic": recorded_traffic("fp32_single_head"), "per_launch_flops": fl,
                                             "note": "2.1 MFLOP per call in one workgroup: the time is "
                                                     "the launch plus the latency of its last wavefront's "
                                                     "four 32-key tiles, not arithmetic"}}
