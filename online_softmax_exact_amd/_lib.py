@@ -115,6 +115,22 @@ def _outer_strides(t: torch.Tensor, name: str):
     return tuple(int(x) for x in t.stride()[:3])
 
 
+def _same_device(device, **tensors):
+    """Every named tensor (None skipped) lives on ``device``."""
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, not on {device} with the other operands")
+
+
+def _require_gpu(q, **tensors):
+    """The kernels read and write device memory: q must be a GPU tensor and
+    every other operand must be on its device (a host pointer handed to a
+    kernel would fault)."""
+    if q.device.type != "cuda":
+        raise ValueError(f"operands must be GPU tensors (got {q.device})")
+    _same_device(q.device, **tensors)
+
+
 def _int32_vector(t, n, name, device):
     if t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] != n or not t.is_contiguous() \
             or t.device != device:
@@ -134,6 +150,7 @@ def make_params(q, k, v, o, *, scale, causal, q_offset, bias, window=0, cu_seqle
         raise ValueError("k and v must be [B, H_kv, T_k, *] with the batch of q")
     if k.shape[3] != dh:
         raise ValueError("q and k must share d_h")
+    _same_device(q.device, k=k, v=v, o=None if o.device.type == "meta" else o)
     p.q_offset = int(q_offset)
     p.q_stride[:] = _outer_strides(q, "q")
     p.k_stride[:] = _outer_strides(k, "k")
@@ -168,13 +185,20 @@ def make_params(q, k, v, o, *, scale, causal, q_offset, bias, window=0, cu_seqle
 
 
 def _outputs(q, d_v, out, lse):
+    """The output and LSE tensors: allocated here, or the caller's after
+    checking that the kernels' writes stay inside them (shape, dtype and
+    device; any outer strides of out, a contiguous LSE)."""
     b, hq, tq, _ = q.shape
     if out is None:
         out = torch.empty((b, hq, tq, d_v), dtype=q.dtype, device=q.device)
+    elif out.dtype != q.dtype or tuple(out.shape) != (b, hq, tq, d_v) or out.device != q.device:
+        raise ValueError(f"out must be a [B, H_q, T_q, d_v] = {(b, hq, tq, d_v)} {q.dtype} tensor "
+                         f"on {q.device}")
     if lse is None:
         lse = torch.empty((b, hq, tq), dtype=torch.float32, device=q.device)
-    elif not lse.is_contiguous() or lse.shape != (b, hq, tq):
-        raise ValueError("lse must be a contiguous [B, H_q, T_q] float32 tensor")
+    elif (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (b, hq, tq)
+          or lse.device != q.device):
+        raise ValueError("lse must be a contiguous [B, H_q, T_q] float32 tensor on the device of q")
     return out, lse
 
 
@@ -192,6 +216,8 @@ def attn_fwd(q, k, v, *, scale=None, causal=True, q_offset=0, bias=None, window=
     uses keys [0, L_b) and its row i sits at q_offset + L_b - T_q + i."""
     lib = load_library()
     out, lse = _outputs(q, v.shape[3], out, lse)
+    _require_gpu(q, k=k, v=v, bias=bias, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
+                 seqlens_k=seqlens_k)
     p = make_params(q, k, v, out, scale=scale, causal=causal, q_offset=q_offset, bias=bias,
                     window=window, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
                     max_seqlen_q=max_seqlen_q, seqlens_k=seqlens_k)
@@ -235,12 +261,16 @@ def attn_decode_splitkv(q, k_cache, v_cache, *, split_size, scale=None, causal=T
     ``attn_decode_workspace_bytes`` bytes; allocated here when None."""
     lib = load_library()
     out, lse = _outputs(q, v_cache.shape[3], out, lse)
+    _require_gpu(q, k_cache=k_cache, v_cache=v_cache, bias=bias, seqlens_k=seqlens_k,
+                 workspace=workspace)
     off = _decode_offset(q, k_cache, q_offset, seqlens_k)
     p = make_params(q, k_cache, v_cache, out, scale=scale, causal=causal, q_offset=off, bias=bias,
                     window=window, seqlens_k=seqlens_k)
     need = int(lib.attn_decode_workspace_bytes(ctypes.byref(p), int(split_size)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
     _check(lib.attn_decode_splitkv(ctypes.byref(p), int(split_size), _ptr(q), _ptr(k_cache),
                                    _ptr(v_cache), _ptr(out), _ptr(lse),
                                    ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
@@ -262,6 +292,9 @@ def attn_bwd(q, k, v, o, lse, d_o, *, scale=None, causal=True, q_offset=0, bias=
     lengths take the forward's ``seqlens_k``; keys past a batch's length get
     zero gradients."""
     lib = load_library()
+    _require_gpu(q, k=k, v=v, o=o, lse=lse, d_o=d_o, bias=bias, cu_seqlens_q=cu_seqlens_q,
+                 cu_seqlens_k=cu_seqlens_k, seqlens_k=seqlens_k, d_q=d_q, d_k=d_k, d_v=d_v,
+                 workspace=workspace)
     if d_o.shape != o.shape or d_o.stride() != o.stride() or d_o.dtype != o.dtype:
         raise ValueError("d_o must have the shape, strides and dtype of o")
     if not lse.is_contiguous() or lse.shape != o.shape[:3] or lse.dtype != torch.float32:
@@ -281,6 +314,8 @@ def attn_bwd(q, k, v, o, lse, d_o, *, scale=None, causal=True, q_offset=0, bias=
     need = int(lib.attn_bwd_workspace_bytes(ctypes.byref(p)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
     _check(lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o),
                         _ptr(grads[0]), _ptr(grads[1]), _ptr(grads[2]),
                         ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
@@ -317,11 +352,17 @@ def attn_merge_states(o_states, lse_states, *, out_dtype=torch.float32, out=None
     if d_v > 1 and o_states.stride(2) != 1:
         raise ValueError("o_states must have a contiguous innermost dimension")
     if out is None:
+        if out_dtype not in _DTYPES:
+            raise ValueError("out_dtype must be float32 or bfloat16")
         out = torch.empty((r, d_v), dtype=out_dtype, device=o_states.device)
     if lse_out is None:
         lse_out = torch.empty((r,), dtype=torch.float32, device=o_states.device)
-    if out.dim() != 2 or (d_v > 1 and out.stride(1) != 1) or not lse_out.is_contiguous():
-        raise ValueError("out must be [R, d_v] with a contiguous row; lse_out contiguous")
+    if out.dtype not in _DTYPES or tuple(out.shape) != (r, d_v) or (d_v > 1 and out.stride(1) != 1):
+        raise ValueError(f"out must be a float32 or bfloat16 [R, d_v] = {(r, d_v)} tensor with "
+                         "contiguous rows")
+    if lse_out.dtype != torch.float32 or lse_out.numel() != r or not lse_out.is_contiguous():
+        raise ValueError(f"lse_out must be a contiguous float32 tensor of R = {r} elements")
+    _require_gpu(o_states, lse_states=lse_states, out=out, lse_out=lse_out)
     _check(lib.attn_merge_states(r, s, d_v, _ptr(o_states), o_states.stride(0),
                                  o_states.stride(1), _ptr(lse_states), lse_states.stride(0),
                                  lse_states.stride(1), _DTYPES[out.dtype], _ptr(out),

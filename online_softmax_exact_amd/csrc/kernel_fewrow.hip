@@ -312,7 +312,13 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
         for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
     }
 
-    unsigned pk[8];
+    // Weights as two bf16 terms each, hi = bf16(p) and lo = bf16(p - hi)
+    // (p - hi is exact in fp32), so hi + lo is within 2^-16 of p and a row
+    // with only a few keys, whose output is nearly one value row, does not
+    // add a 2^-8 weight rounding to the output's own bf16 rounding.  The
+    // second product costs matrix-pipe time, which this HBM-bound kernel has
+    // to spare.
+    unsigned pk[8], pl[8];
     {
       float p[16];
       float ls = 0.0f;
@@ -323,13 +329,18 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
       }
       l_lane += ls;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pk[i] = pack_bf16(p[2 * i], p[2 * i + 1]);
+      for (int i = 0; i < 8; ++i) {
+        pk[i] = pack_bf16(p[2 * i], p[2 * i + 1]);
+        pl[i] = pack_bf16(p[2 * i] - __uint_as_float(pk[i] << 16),
+                          p[2 * i + 1] - __uint_as_float(pk[i] & 0xffff0000u));
+      }
     }
 
     asm volatile("" ::: "memory");   // keep the V stores above the transposed reads
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const u32x4 bop = {pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]};
+      const u32x4 bol = {pl[4 * kk], pl[4 * kk + 1], pl[4 * kk + 2], pl[4 * kk + 3]};
       const int src_row = 16 * kk + 4 * h + ((lane & 15) >> 2);
 #pragma unroll
       for (int mo = 0; mo < C::MO; ++mo) {
@@ -339,6 +350,7 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
         const u32x2 x1 = tr_read(p0 + 8 * C::V_STRIDE);
         const u32x4 aop = {x0[0], x0[1], x1[0], x1[1]};
         oacc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bop), oacc[mo], 0, 0, 0);
+        oacc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bol), oacc[mo], 0, 0, 0);
       }
     }
     asm volatile("" ::: "memory");   // the next tile's V stores come after these reads

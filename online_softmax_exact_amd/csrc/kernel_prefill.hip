@@ -409,6 +409,29 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
     }
   };
 
+  // The same product with each weight carried as two bf16 terms, hi + lo
+  // (hi = the weight rounded to bf16, lo = the rounded remainder, so hi + lo
+  // is within 2^-16 of the fp32 weight): both share each V^T operand read.
+  // General blocks use it: they hold every key of the rows with only a few
+  // keys, whose output is close to a single value row, where a weight
+  // rounded once to bf16 (2^-8) would add to the output's own bf16 rounding.
+  auto pv2_q = [&](int slot, int q, const unsigned* pk, const unsigned* pl) {
+#pragma unroll
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
+      const u32x4 bop = {pk[4 * kk2], pk[4 * kk2 + 1], pk[4 * kk2 + 2], pk[4 * kk2 + 3]};
+      const u32x4 bol = {pl[4 * kk2], pl[4 * kk2 + 1], pl[4 * kk2 + 2], pl[4 * kk2 + 3]};
+      const int off = slot * C::V_BYTES + (32 * q + 16 * kk2) * C::V_RB;
+#pragma unroll
+      for (int mo = 0; mo < C::MO; ++mo) {
+        const u32x2 lo = tr_read(vp[0][mo] + off);
+        const u32x2 hi = tr_read(vp[1][mo] + off);
+        const u32x4 aop = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bop), oacc[mo], 0, 0, 0);
+        oacc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bol), oacc[mo], 0, 0, 0);
+      }
+    }
+  };
+
   // Rescale O and l when a row's reference maximum moved (wave-uniform test).
   auto rescale = [&](float m_new, float alpha) {
     if (__ballot(m_new != m2) != 0) {
@@ -563,7 +586,7 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
   // General softmax of a block (masks, bias, first statistics of a row).
   // Legal iff key < T_k, causally visible, and bias != -inf; illegal scores
   // become -inf and give weight 0; a block with no legal key changes nothing.
-  auto general_q = [&](int t, int q, f32x16& sv, unsigned* pk) {
+  auto general_q = [&](int t, int q, f32x16& sv, unsigned* pk, unsigned* pl) {
     const int kb = t * kBc + 32 * q;
     int lim = a.causal ? pos_row - kb : 32;
     if (a.t_k - 1 - kb < lim) lim = a.t_k - 1 - kb;   // keys past T_k do not exist
@@ -618,6 +641,8 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
       const float p0 = fast_exp2(fmaf(sv[2 * i], c, nm2));
       const float p1 = fast_exp2(fmaf(sv[2 * i + 1], c, nm2));
       pk[i] = pack_bf16(p0, p1);
+      // Remainders p - bf16(p): exact in fp32 (bf16(p) shares p's leading bits).
+      pl[i] = pack_bf16(p0 - __uint_as_float(pk[i] << 16), p1 - __uint_as_float(pk[i] & 0xffff0000u));
       ps0 += p0;
       ps1 += p1;
     }
@@ -649,10 +674,10 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
         if (a.causal && t * kBc + 32 * q > pos_w_last) break;
         if (t * kBc + 32 * q + 31 < lo_w_first) continue;   // below every row's window
         f32x16 sv;
-        unsigned pk[8];
+        unsigned pk[8], pl[8];
         scores_q(t & 1, q, sv);
-        general_q(t, q, sv, pk);
-        pv_q(t & 1, q, pk);
+        general_q(t, q, sv, pk, pl);
+        pv2_q(t & 1, q, pk, pl);
       }
     }
     advance(t);

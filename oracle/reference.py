@@ -69,6 +69,7 @@ partitions and an independent library softmax.
 
 from __future__ import annotations
 
+import functools
 import math
 from fractions import Fraction
 from typing import Callable, List, Optional, Sequence, Tuple
@@ -630,24 +631,21 @@ def finalize(state, d_v: int, arith: Arith = FP64):
 def blocked_single_query(z: Sequence, values: Sequence[Sequence],
                          legal: Sequence[bool], blocks: Sequence[Sequence[int]],
                          arith: Arith = FP64):
-    """Algorithm 33.1 for one query: keys read block by block.
+    """One query's result computed from per-block statistics (eqs 33.3-33.5).
 
-    Start with "no legal key yet"; for each block compute its scores' legal
-    subset, skip it if empty, store it if it is the first non-empty block,
-    otherwise merge (eqs 33.4-33.5); at the end return u/ℓ or the fully masked
-    row's defined output.  ``blocks`` lists key indices; together they must
-    partition the keys.
+    ``blocks`` lists key indices and must partition the keys.  Each block is
+    summarised by its statistics (m, ℓ, u) over its legal keys (eq 33.3), or
+    by "empty" when it has none; the summaries are folded left to right with
+    the merge rule (eqs 33.4-33.5), where an empty summary is the identity
+    (§33.2 valid flags); the folded state gives u/ℓ and m + ln ℓ, or the
+    defined output of a row with no legal key.  The merge is associative and
+    commutative in exact arithmetic, so any partition and order must give the
+    same result as the materialised definition.
     """
     d_v = len(values[0]) if len(values) else 0
-    state = None
-    for blk in blocks:
-        zb = [z[j] for j in blk]
-        vb = [values[j] for j in blk]
-        lb = [legal[j] for j in blk]
-        st = block_stats(zb, vb, lb, arith)
-        if st is None:
-            continue
-        state = st if state is None else merge_stats(state, st, arith)
+    summaries = (block_stats([z[j] for j in blk], [values[j] for j in blk],
+                             [legal[j] for j in blk], arith) for blk in blocks)
+    state = functools.reduce(lambda acc, st: merge_stats(acc, st, arith), summaries, None)
     return finalize(state, d_v, arith)
 
 
@@ -682,7 +680,12 @@ def merge_partials(o_parts: np.ndarray, lse_parts: np.ndarray):
 
 
 def set_partitions(items: List[int]):
-    """Every set partition of ``items`` (Bell-number many), as lists of blocks."""
+    """Every set partition of ``items`` exactly once, as lists of blocks.
+
+    A partition of [x] + rest is a partition of rest with x either added to
+    one of its blocks or put in a block of its own; distinct choices give
+    distinct partitions, so there are Bell(n) of them.
+    """
     if not items:
         yield []
         return

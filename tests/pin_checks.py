@@ -223,14 +223,33 @@ def check_partitions_exact(R):
     num = [sum(masses[j] * vals[j][d] for j in range(6) if legal[j]) for d in range(2)]
     den = sum(masses[j] for j in range(6) if legal[j])
     want = [x / den for x in num]
-    count = 0
+    seen = set()
     for part in R.set_partitions(list(range(6))):
+        seen.add(tuple(sorted(tuple(sorted(b)) for b in part)))
         for order in itertools.islice(itertools.permutations(part), 24):
             o, lse = R.blocked_single_query(z, vals, legal, list(order), R.EXACT)
             assert o == want, (order, o, want)
             assert lse == R.LogOf(den)
-            count += 1
-    assert count > 203  # Bell(6) partitions, several orders each
+    assert len(seen) == 203  # Bell(6): every partition of the 6 keys was merged
+
+
+def check_set_partitions(R):
+    """The partition generator behind the brute force yields every set
+    partition exactly once: Bell numbers 1, 1, 2, 5, 15, 52, 203, 877 for
+    n = 0..7 (OEIS A000110), each yield a true partition (non-empty disjoint
+    blocks covering the items), no partition twice."""
+    bell = [1, 1, 2, 5, 15, 52, 203, 877]
+    for n, want in enumerate(bell):
+        items = list(range(n))
+        seen = set()
+        for part in R.set_partitions(items):
+            assert all(len(b) > 0 for b in part), part
+            flat = sorted(x for b in part for x in b)
+            assert flat == items, part
+            canon = tuple(sorted(tuple(sorted(b)) for b in part))
+            assert canon not in seen, ("repeated", part)
+            seen.add(canon)
+        assert len(seen) == want, (n, len(seen), want)
 
 
 def check_partitions_fp64(R):
@@ -864,7 +883,7 @@ def check_kvlens_backward(R):
 ALL_CHECKS = [
     check_example_25_1_exact, check_example_25_1_fp64, check_exercise_33_2,
     check_kv_cache_vectors, check_equal_scores_mean, check_single_and_two_keys,
-    check_invariants, check_partitions_exact, check_partitions_fp64,
+    check_invariants, check_set_partitions, check_partitions_exact, check_partitions_fp64,
     check_masked_blocks_and_rows, check_alignment, check_gqa_mapping,
     check_split_merge, check_rows_match_full, check_library_softmax,
     check_bias_broadcast, check_window_counts, check_window_single_key,

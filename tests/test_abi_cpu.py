@@ -250,3 +250,44 @@ def test_binding_varlen_arguments():
     with pytest.raises(ValueError):
         _lib.make_params(q2, kv2, kv2, q2, scale=None, causal=True, q_offset=0, bias=None,
                          seqlens_k=lens[:1])
+
+
+def test_binding_rejects_bad_outputs_and_devices():
+    # Caller-supplied outputs must hold every write the kernels make, and no
+    # host tensor may reach a kernel: each bad argument raises before a launch.
+    import torch
+    q = torch.zeros(1, 2, 10, 64, dtype=torch.bfloat16)
+    kv = torch.zeros(1, 2, 12, 64, dtype=torch.bfloat16)
+    good_o = torch.zeros(1, 2, 10, 64, dtype=torch.bfloat16)
+    good_l = torch.zeros(1, 2, 10)
+    assert _lib._outputs(q, 64, good_o, good_l) == (good_o, good_l)
+    for bad_o, bad_l in ((good_o.float(), None),                                    # out dtype
+                         (torch.zeros(1, 2, 9, 64, dtype=torch.bfloat16), None),     # out rows
+                         (torch.zeros(1, 2, 10, 32, dtype=torch.bfloat16), None),    # out d_v
+                         (None, good_l.double()),                                    # lse dtype
+                         (None, torch.zeros(1, 2, 9)),                               # lse shape
+                         (None, torch.zeros(1, 10, 2).transpose(1, 2)),              # lse strides
+                         (good_o.to("meta"), None), (None, good_l.to("meta"))):     # device
+        with pytest.raises(ValueError):
+            _lib._outputs(q, 64, bad_o, bad_l)
+    # Operands on different devices.
+    with pytest.raises(ValueError):
+        _lib.make_params(q, kv.to("meta"), kv, q, scale=None, causal=True, q_offset=0, bias=None)
+    # Host tensors never reach the library.
+    with pytest.raises(ValueError, match="GPU tensors"):
+        _lib.attn_fwd(q, kv, kv)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        _lib.attn_decode_splitkv(q, kv, kv, split_size=4)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        _lib.attn_bwd(q, kv, kv, good_o, good_l, good_o)
+    # The merge checks its outputs' shapes and dtypes, then the device.
+    st = torch.zeros(5, 3, 16)
+    ls = torch.zeros(5, 3)
+    for kw in (dict(out=torch.zeros(4, 16)), dict(out=torch.zeros(5, 8)),
+               dict(out=torch.zeros(5, 16, dtype=torch.float64)),
+               dict(lse_out=torch.zeros(4)), dict(lse_out=torch.zeros(5, dtype=torch.float64)),
+               dict(out_dtype=torch.float16)):
+        with pytest.raises(ValueError):
+            _lib.attn_merge_states(st, ls, **kw)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        _lib.attn_merge_states(st, ls)

@@ -6,10 +6,9 @@ and both must match the oracle element by element.  Cases: grouped heads,
 query rows ending inside a wavefront, several full key tiles with a ragged
 tail, causal and not, offsets, biases per head, shared by heads and shared
 by rows, a strided bias view (rows wider than T_k), -inf entries, a sliding
-window, and packed sequences with a packed or per-key bias.  The windowed
-case starts its rows past the first keys: a bf16 row over one to three keys
-outputs nearly one value row, whose rounding alone takes most of the 1e-2
-budget (there |o| reaches 2-4)."""
+window (also a three-key window from position 0, so that every row's output
+is nearly one value row), and packed sequences with a packed or per-key
+bias."""
 
 import zlib
 
@@ -38,6 +37,7 @@ CASES = [
     (1, 2, 2, 100, 1000, 64, 128, True, 900, "keys", 0.1, 0, 0),
     (1, 2, 2, 190, 333, 64, 128, True, 143, "shared", 0.05, 0, 40),   # bias rows 373 floats apart
     (2, 4, 4, 385, 435, 64, 128, True, 50, "shared", 0.1, 100, 0),
+    (2, 4, 4, 385, 435, 64, 128, True, 0, "shared", 0.1, 3, 0),
     (1, 8, 2, 31, 600, 128, 64, False, 0, "dense", 0.0, 0, 0),          # one partial wavefront of rows
 ]
 

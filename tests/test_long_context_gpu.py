@@ -13,7 +13,7 @@ import torch
 import oracle
 import online_softmax_exact_amd as attn
 from online_softmax_exact_amd import inputs
-from gpu_util import TOL, dev, ensure_built, f64
+from gpu_util import TOL, dev, ensure_built, f64, o_max_allowed
 
 pytestmark = pytest.mark.gpu
 
@@ -29,7 +29,7 @@ def _check_rows(o, lse, rows, ro, rl, what):
     err = np.abs(got_o - ro)
     tol = TOL[torch.bfloat16]
     print(what, "max", float(err.max()), "mean", float(err.mean()), flush=True)
-    assert err.max() <= tol["o_max"] and err.mean() <= tol["o_mean"], what
+    assert np.all(err <= o_max_allowed(ro, torch.bfloat16)) and err.mean() <= tol["o_mean"], what
     dead = np.isneginf(rl)
     assert np.array_equal(np.isneginf(got_l), dead), what + ": masked-row flags"
     assert np.all(got_o[dead] == 0), what + ": masked row not zero"

@@ -30,8 +30,10 @@ MUTANTS = {
     "merge_keeps_first_max": ("m = m_a if not arith.gt(m_b, m_a) else m_b", "m = m_a"),
     "stats_first_key_max": ("        if arith.gt(z[j], m):\n            m = z[j]", "        pass"),
     "masked_row_nan": ("live = n_legal > 0", "live = n_legal >= 0"),
-    "empty_block_not_skipped": ("        if st is None:\n            continue\n        state = st if",
-                                "        if st is None:\n            st = (0.0, 0.0, [0.0] * d_v)\n        state = st if"),
+    "empty_block_not_skipped": ("    if not idx:\n        return None",
+                                "    if not idx:\n        return (0.0, 0.0, [0.0] * len(values[0]))"),
+    "partitions_no_singleton": ("        yield [[first]] + part\n", "\n"),
+    "partitions_first_block_only": ("        for i in range(len(part)):", "        for i in [0] * len(part):"),
     "split_range_inclusive": ("legal = legal & (j >= lo) & (j < hi)", "legal = legal & (j >= lo) & (j <= hi)"),
     "rows_offset_ignored": ("pos = q_offset + i", "pos = i"),
     "window_off_by_one": ("legal = legal & (j >= q_offset + i - window + 1)",
