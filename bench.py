@@ -323,24 +323,38 @@ def backward_traffic(prefix: str = ""):
 
 
 def cpu_baseline(wl, heads: int):
-    """The fp64 oracle as it stands, on `heads` heads of the prefill workload."""
-    import numpy as np
+    """The fp64 oracle as it stands, on `heads` heads of the prefill workload:
+    one oracle call per head on a thread pool of the CPUs this process may
+    run on (numpy releases the GIL in its products and ufuncs), BLAS pinned
+    to one thread per worker, and no more workers than the host memory holds
+    (each materialises three T x T fp64 matrices)."""
+    import concurrent.futures as cf
+
     import oracle
+    from threadpoolctl import threadpool_limits
+
+    t = wl.q.shape[2]
+    cpus = len(os.sched_getaffinity(0))
+    per_worker = 3 * t * t * 8 + 4 * t * wl.q.shape[3] * 8
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = 1
-    q = wl.q[:, :heads].double().numpy()
-    k = wl.k[:, :heads].double().numpy()
-    v = wl.v[:, :heads].double().numpy()
+        avail = os.sysconf("SC_AVPHYS_PAGES") * os.sysconf("SC_PAGE_SIZE")
+    except (ValueError, OSError):  # pragma: no cover
+        avail = per_worker * cpus
+    workers = max(1, min(cpus, heads, int(0.5 * avail // per_worker)))
+
+    def one(h):
+        with threadpool_limits(limits=1):
+            oracle.attention(wl.q[:, h:h + 1].double().numpy(), wl.k[:, h:h + 1].double().numpy(),
+                             wl.v[:, h:h + 1].double().numpy(), scale=wl.scale, causal=True, q_offset=0)
+
     t0 = time.perf_counter()
-    oracle.attention(q, k, v, scale=wl.scale, causal=True, q_offset=0)
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one, range(heads)))
     dt = time.perf_counter() - t0
-    t = q.shape[2]
-    _, flops, _ = prefill_counts(t, heads, 1, q.shape[3], v.shape[3])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{heads} of 32 heads of the causal prefill (T=8192, d=128), fp64 numpy, "
+    _, flops, _ = prefill_counts(t, heads, 1, wl.q.shape[3], wl.v.shape[3])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(workers), "kind": "oracle",
+            "sample": f"{heads} of 32 heads of the causal prefill (T=8192, d=128), fp64 numpy, one "
+                      f"oracle call per head on {workers} threads ({cpus} CPUs available), "
                       f"{dt:.1f} s wall"}
 
 
@@ -349,7 +363,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=60,
-                    help="untimed steps; ~60 brings the GPU clock to its steady state")
+                    help="untimed steps at least; warm-up goes on until --warmup-s has passed too")
+    ap.add_argument("--warmup-s", type=float, default=1.0,
+                    help="seconds of untimed steps at least (the clock ramps over the first ~0.5 s "
+                         "of load)")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="heads of the prefill the CPU oracle baseline times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -403,10 +420,18 @@ def main():
                                  lse=dl)
 
     print("bench: timing", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    # Warm-up: at least --warmup steps and at least --warmup-s seconds, so the
+    # timed steps see the steady-state clock (it ramps over the first tens of
+    # launches after idle; a few steps alone leave the early ones slow).
+    warmed, t_w = 0, time.perf_counter()
+    while warmed < args.warmup or time.perf_counter() - t_w < args.warmup_s:
         run_prefill()
         run_decode()
+        warmed += 1
+        if warmed % 10 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t_w
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t_start = time.perf_counter()
     for e in ev:
@@ -448,7 +473,8 @@ def main():
                    "prefill_ms_median": round(statistics.median(pre_ms), 4),
                    "decode_ms": round(d_avg, 4), "decode_ms_min": round(min(dec_ms), 4),
                    "decode_ms_median": round(statistics.median(dec_ms), 4),
-                   "wall_s": round(wall, 3)},
+                   "wall_s": round(wall, 3), "warmup_steps_run": warmed,
+                   "warmup_s": round(warm_s, 3)},
         "roofline": {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic("prefill"), "kernel": "attn_fwd prefill",
