@@ -20,7 +20,8 @@
  * ---------------------------------------
  * - Tensor pointers are DEVICE pointers owned by the caller.  The library
  *   allocates no device memory and keeps no mutable global state, so calls on
- *   different streams may run concurrently.
+ *   different streams may run concurrently; the one exception is the fixed
+ *   per-GPU workspace of attn_decode_splitkv_noalloc (see there).
  * - Layout is [B, H, T, D] with the innermost (D) dimension contiguous; the
  *   three outer strides are given in ELEMENTS, must be >= 0, and may be 0 to
  *   broadcast.  LSE and n_legal are contiguous [B, H_q, T_q].
@@ -46,7 +47,12 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
+
+/* Size of the per-GPU decode workspace that attn_decode_splitkv_noalloc uses
+ * (32 MiB: the GQA decode of batch 16, 32 query heads, 64 ranges and d_v 128
+ * needs 16.9 MB). */
+#define ATTN_DECODE_SCRATCH_BYTES (32u << 20)
 
 typedef enum {
   ATTN_OK = 0,
@@ -57,7 +63,9 @@ typedef enum {
                               variable-length field the entry point does not take */
   ATTN_E_STRIDE = -5,      /* a negative stride */
   ATTN_E_WORKSPACE = -6,   /* decode workspace missing or too small */
-  ATTN_E_HIP = -7          /* the HIP runtime refused a launch */
+  ATTN_E_HIP = -7,         /* the HIP runtime refused a launch */
+  ATTN_E_SCRATCH = -8      /* attn_decode_splitkv_noalloc: the problem needs more than
+                              ATTN_DECODE_SCRATCH_BYTES of workspace */
 } attn_status_t;
 
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
@@ -125,6 +133,13 @@ typedef struct {
 /* sizeof(attn_params_t), so that bindings can check their mirror of it. */
 size_t attn_params_sizeof(void);
 int attn_abi_version(void);
+/* A one-line description of an attn_status_t.  Every entry point reports
+ * input it cannot honour with one of these codes instead of proceeding: the
+ * consistency conditions of §33.3 ("interface, backends and correctness
+ * conditions": mask polarity, causal alignment, head grouping, scale,
+ * strides) and the rejection of inconsistent caches by the cached forward of
+ * "Generation and Caching with the Same Model".  Unknown codes give
+ * "unknown status"; the string is static. */
 const char* attn_strerror(int status);
 
 /* Exact attention over all query rows (prefill, non-square causal, verify).
@@ -139,9 +154,13 @@ int attn_fwd(const attn_params_t* p, const void* q, const void* k,
              void* stream);
 
 /* Bytes of device workspace that attn_decode_splitkv needs for this problem
- * and split size: fp32 partial outputs [B, H_q, T_q, S, d_v] followed by fp32
- * partial LSEs [B, H_q, T_q, S] (each array 256-byte aligned), where
- * S = ceil(T_k / split_size) (at least 1).  Returns 0 on invalid arguments. */
+ * and split size: one stored partial per query row and key range, the
+ * range's (o_s, lse_s), which stands for its statistics (m, l, u) =
+ * (lse_s, 1, o_s) in the merge of eqs 33.4-33.5 (§33.2; the merge holds for
+ * any reference maximum).  Layout: fp32 partial outputs [B, H_q, T_q, S, d_v]
+ * followed by fp32 partial LSEs [B, H_q, T_q, S] (each array 256-byte
+ * aligned), where S = ceil(T_k / split_size) (at least 1).  Returns 0 on
+ * invalid arguments. */
 size_t attn_decode_workspace_bytes(const attn_params_t* p, int64_t split_size);
 
 /* Split-KV attention for few query rows over a long KV cache (decode).
@@ -162,6 +181,25 @@ int attn_decode_splitkv(const attn_params_t* p, int64_t split_size,
                         const void* v_cache, void* o, float* lse,
                         void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* attn_decode_splitkv without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation).  Same problem, split size, inputs, outputs and results
+ * (the same kernels) as attn_decode_splitkv; the partials go to a fixed
+ * array of ATTN_DECODE_SCRATCH_BYTES in device memory that the library holds
+ * on every GPU it runs on until the process ends (its address on the current
+ * device is looked up on the first call there).  The call runs on the
+ * current device, which must be the device of the tensors and the stream.
+ * Returns ATTN_E_SCRATCH, before touching the device, when
+ * attn_decode_workspace_bytes(p, split_size) exceeds
+ * ATTN_DECODE_SCRATCH_BYTES.  Allocates nothing.  Every call on a GPU shares
+ * that GPU's array: calls that overlap on one GPU (on different streams, or
+ * from several threads) race and their results are undefined; calls ordered
+ * on one stream are safe, since each call writes every partial it reads. */
+int attn_decode_splitkv_noalloc(const attn_params_t* p, int64_t split_size,
+                                const void* q, const void* k_cache,
+                                const void* v_cache, void* o, float* lse,
+                                void* stream);
 
 /* Merge n_states partial results per row (eqs 33.4-33.5 of §33.2).
  * Row r, state s: o_states[r*o_row_stride + s*o_state_stride + d] (fp32, d <

@@ -24,8 +24,9 @@ ATTN_E_HIP = -7
 _DTYPES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
 
 EXPORTED = ("attn_params_sizeof", "attn_abi_version", "attn_strerror", "attn_fwd",
-            "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_merge_states",
-            "attn_bwd_workspace_bytes", "attn_bwd")
+            "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_decode_splitkv_noalloc",
+            "attn_merge_states", "attn_bwd_workspace_bytes", "attn_bwd")
+DECODE_SCRATCH_BYTES = 32 << 20   # ATTN_DECODE_SCRATCH_BYTES
 
 
 class Params(ctypes.Structure):
@@ -71,6 +72,8 @@ def load_library(path: Optional[str] = None):
     lib.attn_decode_workspace_bytes.argtypes = [pp, i64]
     lib.attn_decode_splitkv.restype = ctypes.c_int
     lib.attn_decode_splitkv.argtypes = [pp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.attn_decode_splitkv_noalloc.restype = ctypes.c_int
+    lib.attn_decode_splitkv_noalloc.argtypes = [pp, i64, vp, vp, vp, vp, vp, vp]
     lib.attn_merge_states.restype = ctypes.c_int
     lib.attn_merge_states.argtypes = [i64, i64, i64, vp, i64, i64, vp, i64, i64,
                                       ctypes.c_int32, vp, i64, vp, vp]
@@ -276,6 +279,27 @@ def attn_decode_splitkv(q, k_cache, v_cache, *, split_size, scale=None, causal=T
                                    ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                    _stream(q.device, stream)))
     return out, lse, workspace
+
+
+def attn_decode_splitkv_noalloc(q, k_cache, v_cache, *, split_size, scale=None, causal=True,
+                                q_offset=None, bias=None, window=0, seqlens_k=None, out=None,
+                                lse=None, stream=None):
+    """attn_decode_splitkv with the library's fixed per-GPU workspace instead
+    of a caller's (the C entry point allocates nothing; outputs are allocated
+    here when not given).  Returns (o, lse).  Problems whose workspace would
+    exceed DECODE_SCRATCH_BYTES raise ValueError; calls that overlap on one
+    GPU race on that workspace."""
+    lib = load_library()
+    out, lse = _outputs(q, v_cache.shape[3], out, lse)
+    _require_gpu(q, k_cache=k_cache, v_cache=v_cache, bias=bias, seqlens_k=seqlens_k)
+    off = _decode_offset(q, k_cache, q_offset, seqlens_k)
+    p = make_params(q, k_cache, v_cache, out, scale=scale, causal=causal, q_offset=off, bias=bias,
+                    window=window, seqlens_k=seqlens_k)
+    with torch.cuda.device(q.device):   # the library works on the current device
+        _check(lib.attn_decode_splitkv_noalloc(ctypes.byref(p), int(split_size), _ptr(q),
+                                               _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
+                                               _stream(q.device, stream)))
+    return out, lse
 
 
 def attn_bwd(q, k, v, o, lse, d_o, *, scale=None, causal=True, q_offset=0, bias=None, window=0,

@@ -8,8 +8,18 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "attn_internal.h"
 #include "kernels.h"
+
+// Decode workspace of attn_decode_splitkv_noalloc, for callers that cannot
+// allocate device memory: one array per GPU, held until the process ends.
+// Host code never passes its name to a kernel (on the host the name is only
+// a stand-in for the device variable); it uses the per-device address that
+// hipGetSymbolAddress returns.
+static __device__ __align__(256) char scratch[ATTN_DECODE_SCRATCH_BYTES];
 
 namespace attn {
 
@@ -107,6 +117,50 @@ int check_pointers(const Problem& pb, const void* q, const void* k, const void* 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E_HIP; }
 
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device (with it current) and kept: each GPU holds its own
+// copy of the array at its own address.
+constexpr int kMaxDevices = 64;
+std::atomic<char*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_of_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_E_HIP;
+  char* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (ptr == nullptr) {
+      void* addr = nullptr;
+      if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr)
+        return ATTN_E_HIP;
+      ptr = static_cast<char*>(addr);
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return ATTN_OK;
+}
+
+// Split-KV partials into the workspace `ws` (layout L), then their merge
+// into o / lse.  Shared by both decode entry points.
+int decode_into(const Problem& pb, int dtype, int64_t split_size, const void* q,
+                const void* k_cache, const void* v_cache, void* o, float* lse, char* ws,
+                const SplitLayout& L, hipStream_t s) {
+  float* ws_o = reinterpret_cast<float*>(ws);
+  float* ws_l = reinterpret_cast<float*>(ws + L.lse_offset);
+  hipError_t e = hipSuccess;
+  if (!launch_fast_decode_partials(pb, dtype, q, k_cache, v_cache, L, ws_o, ws_l, s, &e))
+    e = launch_generic(pb, dtype, q, k_cache, v_cache, nullptr, nullptr, nullptr,
+                       split_size, ws_o, ws_l, s);
+  if (e != hipSuccess) return ATTN_E_HIP;
+  const int64_t out_strides[3] = {pb.os[0], pb.os[1], pb.os[2]};
+  return hip_status(launch_merge(L.rows, L.n_splits, pb.d_v, ws_o, L.n_splits * pb.d_v, pb.d_v,
+                                 ws_l, L.n_splits, 1, dtype, o, pb.heads_q, pb.t_q,
+                                 out_strides, lse, s, pb.kv_lens, split_size, pb.t_k));
+}
+
 }  // namespace
 }  // namespace attn
 
@@ -128,6 +182,7 @@ const char* attn_strerror(int status) {
     case ATTN_E_STRIDE: return "negative stride";
     case ATTN_E_WORKSPACE: return "decode workspace missing or too small";
     case ATTN_E_HIP: return "HIP runtime error at launch";
+    case ATTN_E_SCRATCH: return "decode needs more workspace than the no-allocation entry point holds (ATTN_DECODE_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -201,18 +256,28 @@ int attn_decode_splitkv(const attn_params_t* p, int64_t split_size, const void* 
   const SplitLayout L = split_layout(pb, split_size);
   if (workspace == nullptr || workspace_bytes < L.total) return ATTN_E_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return ATTN_E_WORKSPACE;
-  float* ws_o = static_cast<float*>(workspace);
-  float* ws_l = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse_offset);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
-  if (!launch_fast_decode_partials(pb, p->dtype, q, k_cache, v_cache, L, ws_o, ws_l, s, &e))
-    e = launch_generic(pb, p->dtype, q, k_cache, v_cache, nullptr, nullptr, nullptr,
-                       split_size, ws_o, ws_l, s);
-  if (e != hipSuccess) return ATTN_E_HIP;
-  const int64_t out_strides[3] = {pb.os[0], pb.os[1], pb.os[2]};
-  return hip_status(launch_merge(L.rows, L.n_splits, pb.d_v, ws_o, L.n_splits * pb.d_v, pb.d_v,
-                                 ws_l, L.n_splits, 1, p->dtype, o, pb.heads_q, pb.t_q,
-                                 out_strides, lse, s, pb.kv_lens, split_size, pb.t_k));
+  return decode_into(pb, p->dtype, split_size, q, k_cache, v_cache, o, lse,
+                     static_cast<char*>(workspace), L, static_cast<hipStream_t>(stream));
+}
+
+int attn_decode_splitkv_noalloc(const attn_params_t* p, int64_t split_size, const void* q,
+                                const void* k_cache, const void* v_cache, void* o, float* lse,
+                                void* stream) {
+  Problem pb;
+  int st = validate(p, &pb);
+  if (st != ATTN_OK) return st;
+  if (split_size < 1) return ATTN_E_SHAPE;
+  if ((st = check_pointers(pb, q, k_cache, v_cache, o, lse)) != ATTN_OK) return st;
+  if (pb.cu_q != nullptr) return ATTN_E_UNSUPPORTED;
+  if (pb.batch == 0 || pb.t_q == 0) return ATTN_OK;
+  const SplitLayout L = split_layout(pb, split_size);
+  if (L.total > static_cast<size_t>(ATTN_DECODE_SCRATCH_BYTES)) return ATTN_E_SCRATCH;
+  // Every partial the merge reads is written by this call's partial kernels
+  // first, so nothing left in the array by an earlier call is read.
+  char* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != ATTN_OK) return st;
+  return decode_into(pb, p->dtype, split_size, q, k_cache, v_cache, o, lse, ws, L,
+                     static_cast<hipStream_t>(stream));
 }
 
 int attn_merge_states(int64_t n_rows, int64_t n_states, int64_t d_v, const float* o_states,

@@ -37,12 +37,12 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_params_layout(lib):
-    assert lib.attn_abi_version() == 3
+    assert lib.attn_abi_version() == 4
     assert lib.attn_params_sizeof() == ctypes.sizeof(_lib.Params) == 256
 
 
 def test_strerror(lib):
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert lib.attn_strerror(code)
     assert b"unknown" in lib.attn_strerror(-99)
 
@@ -291,3 +291,28 @@ def test_binding_rejects_bad_outputs_and_devices():
             _lib.attn_merge_states(st, ls, **kw)
     with pytest.raises(ValueError, match="GPU tensors"):
         _lib.attn_merge_states(st, ls)
+
+
+def test_decode_noalloc_validation(lib):
+    # The entry point without a workspace validates like attn_decode_splitkv
+    # and rejects a problem whose workspace exceeds its fixed array before it
+    # touches the device.
+    p = good_params(t_q=1, t_k=1 << 20)
+    need = lib.attn_decode_workspace_bytes(ctypes.byref(p), 64)
+    assert need > _lib.DECODE_SCRATCH_BYTES
+    assert lib.attn_decode_splitkv_noalloc(ctypes.byref(p), 64, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           None) == -8
+    assert b"no-allocation" in lib.attn_strerror(-8)
+    p = good_params()
+    assert lib.attn_decode_splitkv_noalloc(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           None) == -2
+    assert lib.attn_decode_splitkv_noalloc(None, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert lib.attn_decode_splitkv_noalloc(ctypes.byref(p), 4, None, FAKE, FAKE, FAKE, FAKE,
+                                           None) == -1
+    bad = good_params(heads_q=3)
+    assert lib.attn_decode_splitkv_noalloc(ctypes.byref(bad), 4, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           None) == -2
+    # Nothing to do: no rows.
+    empty = good_params(t_q=0)
+    assert lib.attn_decode_splitkv_noalloc(ctypes.byref(empty), 4, None, None, None, None, None,
+                                           None) == 0
