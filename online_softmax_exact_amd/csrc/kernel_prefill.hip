@@ -467,26 +467,34 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
   // cache lines, per instruction, and that line rate bounds a biased tile.
   // Instead each wave copies its 32 rows x 32 keys (4 KB per block) with
   // buffer_load ... lds, 8 whole rows per instruction, into its own LDS
-  // block, 16-byte chunk c of row r at chunk slot c ^ (r & 7) so the reads
-  // below are free of bank conflicts; lane l of copy i carries row
-  // 8 i + l / 8, chunk slot l % 8.
+  // block, 16-byte chunk c of row r at chunk slot c ^ bswz(r); lane l of
+  // copy i carries row 8 i + l / 8, chunk slot l % 8.  A 16-byte read serves
+  // 16 lanes (16 rows of one chunk) per cycle, and with 128-byte rows rows r
+  // and r + 8 share banks unless their slots differ: with bswz(r) =
+  // (r >> 1) & 7 the 16 rows of a read cover all 64 banks once (r & 7 left
+  // two-way conflicts).
+  auto bswz = [](int r) { return (r >> 1) & 7; };
   char* const bstage = smem + kRing + wave * (kNQ * 4096);
   int bdma[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rr = 8 * i + (lane >> 3);
-    bdma[i] = kBiasLds ? static_cast<int>(rr * a.bs[2] * 4) + 16 * ((lane & 7) ^ (rr & 7)) : 0;
+    bdma[i] = kBiasLds ? static_cast<int>(rr * a.bs[2] * 4) + 16 * ((lane & 7) ^ bswz(rr)) : 0;
   }
+  // Copies of block q of tile t's bias into the wave's staging block q (four
+  // instructions).
+  auto stage_block = [&](int t, int q) {
+    const auto rs = make_rsrc(bias_w + t * kBc, bias_w_bytes - static_cast<int64_t>(t) * kBc * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(bstage + q * 4096 + i * 1024), 16,
+          bdma[i] + 128 * q, 0, 0, 0);
+  };
   auto prefetch_bias = [&](int t) {
     if (kBiasLds) {
-      const auto rs = make_rsrc(bias_w + t * kBc, bias_w_bytes - static_cast<int64_t>(t) * kBc * 4);
 #pragma unroll
-      for (int q = 0; q < kNQ; ++q)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rs, (__attribute__((address_space(3))) void*)(bstage + q * 4096 + i * 1024), 16,
-              bdma[i] + 128 * q, 0, 0, 0);
+      for (int q = 0; q < kNQ; ++q) stage_block(t, q);
     } else {
 #pragma unroll
       for (int q = 0; q < (kBiasPf ? kNQ : 1); ++q) load_bias(t, q, mbp[q]);
@@ -496,39 +504,52 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
   // issued last are in flight, which covers block q's copies whether or not
   // the K/V copies of tile t + 1 (issued after the bias) went out, and keeps
   // the wait free of branches; then the 4 chunks 2 g + h of this lane's row.
+  // Byte offsets in a staging block of this lane's row and chunks 2 g + h.
+  int bread[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) bread[g] = lr * 128 + (((2 * g + h) ^ bswz(lr)) << 4);
   auto staged_bias = [&](int q, float* mb) {
     wait_vm_upto<4 * (kNQ - 1)>(4 * (kNQ - 1 - q));
-    const lds_char* rowp = (const lds_char*)bstage + q * 4096 + lr * 128;
+    const lds_char* blk = (const lds_char*)bstage + q * 4096;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f32x4 x = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-          rowp + (((2 * g + h) ^ (lr & 7)) << 4));
+      const f32x4 x = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(blk + bread[g]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) mb[4 * g + e] = x[e];
     }
   };
 
   // Softmax of a block whose keys are all causally visible (and inside the
-  // window) for every row, every row already holding statistics:
-  // branch-free (tile max, new reference, weights, sums, bf16 packing), so
-  // it can run under independent MFMAs.  With a bias, z = scale dot + M in
-  // base-2 units; a -inf entry gives z = -inf and weight 0 by arithmetic
-  // alone, and a block whose keys are all -inf for a row leaves its
-  // reference unchanged (its maximum is -inf), as the valid-flag rule asks.
-  auto fast_q = [&](int t, int q, const f32x16& sv, unsigned* pk, float& m_new, float& alpha) {
-    if (BIAS) {
-      // z = scale dot + M in natural-log units (one fma); the base-2 factor
-      // goes into the exponent's fma, so a score costs two VALU operations
-      // besides its max and exp.
-      float mb[16], z[16];
-      if constexpr (kBiasLds) {
-        staged_bias(q, mb);
-      } else if (kBiasPf) {
+  // window) for every row, every row already holding statistics.  The
+  // weights are taken against the row's current reference m2 without
+  // forming the block maximum: the merge rule holds for any reference, so
+  // only their size matters.  A lane whose 16 weights sum past kSumMax (a
+  // weight above 2^16, or an overflow to inf) flags the block; the caller
+  // then runs redo_q (rare: the reference only lags behind scores more than
+  // 16 base-2 units above it).  Branch-free otherwise (weights, sums, bf16
+  // packing), so it runs under independent MFMAs.  With a bias, z = scale dot
+  // + M in natural-log units (one fma), the base-2 factor riding in the
+  // exponent's fma; a -inf entry gives weight 0 by arithmetic alone, and a
+  // block whose keys are all -inf for a row adds nothing (the valid-flag
+  // rule).  l_prev receives l before the block.
+  auto block_bias = [&](int t, int q, float* mb) {
+    if constexpr (kBiasLds) {
+      staged_bias(q, mb);
+    } else if (kBiasPf) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mb[r] = mbp[q][r];
-      } else {
-        load_bias(t, q, mb);
-      }
+      for (int r = 0; r < 16; ++r) mb[r] = mbp[q][r];
+    } else {
+      load_bias(t, q, mb);
+    }
+  };
+  // Weights of block q against reference m2 into pk; returns this lane's sum
+  // (and, with `counting`, adds the block's legal keys to count).
+  auto block_weights = [&](int t, int q, const f32x16& sv, unsigned* pk, bool counting) -> float {
+    float ps0 = 0.0f, ps1 = 0.0f;
+    const float nm = -m2;
+    if (BIAS) {
+      float mb[16], z[16];
+      block_bias(t, q, mb);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
 #if PREFILL_BIAS_NAT
@@ -536,22 +557,13 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
 #else
         z[r] = fmaf(mb[r], kLog2e, sv[r] * a.scale_log2);
 #endif
-        if (COUNT) count += static_cast<int>(mb[r] != -INFINITY);
+        if (COUNT && counting) count += static_cast<int>(mb[r] != -INFINITY);
       }
-      float mx = fmaxf(z[0], z[1]);
-#pragma unroll
-      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, z[r]);
 #if PREFILL_BIAS_NAT
-      const float tmax = max_xor32(mx) * kLog2e;
       const float zc = kLog2e;
 #else
-      const float tmax = max_xor32(mx);
       const float zc = 1.0f;
 #endif
-      m_new = tmax > m2 + kRescale ? tmax : m2;
-      alpha = fast_exp2(m2 - m_new);
-      const float nm = -m_new;
-      float ps0 = 0.0f, ps1 = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float p0 = fast_exp2(fmaf(z[2 * i], zc, nm));
@@ -560,27 +572,49 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
         ps0 += p0;
         ps1 += p1;
       }
-      l_lane = fmaf(l_lane, alpha, ps0 + ps1);
-      return;
-    }
-    float mx = fmaxf(sv[0], sv[1]);
+    } else {
 #pragma unroll
-    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sv[r]);
-    const float tmax = max_xor32(mx) * a.scale_log2;
-    m_new = tmax > m2 + kRescale ? tmax : m2;
-    alpha = fast_exp2(m2 - m_new);
-    const float nm = -m_new;
-    float ps0 = 0.0f, ps1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p0 = fast_exp2(fmaf(sv[2 * i], a.scale_log2, nm));
-      const float p1 = fast_exp2(fmaf(sv[2 * i + 1], a.scale_log2, nm));
-      pk[i] = pack_bf16(p0, p1);
-      ps0 += p0;
-      ps1 += p1;
+      for (int i = 0; i < 8; ++i) {
+        const float p0 = fast_exp2(fmaf(sv[2 * i], a.scale_log2, nm));
+        const float p1 = fast_exp2(fmaf(sv[2 * i + 1], a.scale_log2, nm));
+        pk[i] = pack_bf16(p0, p1);
+        ps0 += p0;
+        ps1 += p1;
+      }
+      if (COUNT && counting) count += 16;
     }
-    l_lane = fmaf(l_lane, alpha, ps0 + ps1);
-    if (COUNT) count += 16;
+    return ps0 + ps1;
+  };
+  auto fast_q = [&](int t, int q, const f32x16& sv, unsigned* pk, bool& need, float& l_prev) {
+    const float blk = block_weights(t, q, sv, pk, true);
+    need = !(blk <= kSumMax);
+    l_prev = l_lane;
+    l_lane += blk;
+  };
+  // The rare path of a flagged block (wave-uniform): the block maximum of
+  // every row, the reference moved up where it is exceeded, O and l rescaled
+  // by e^(m_old - m_new) (eqs 33.4-33.5), the block's weights recomputed.
+  auto redo_q = [&](int t, int q, const f32x16& sv, unsigned* pk, float l_prev) {
+    float mx = -INFINITY;
+    if (BIAS) {
+      float mb[16];
+      block_bias(t, q, mb);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaf(sv[r], a.scale, mb[r]));
+      mx = max_xor32(mx) * kLog2e;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[r]);
+      mx = max_xor32(mx) * a.scale_log2;
+    }
+    const float m_new = mx > m2 ? mx : m2;
+    const float alpha = fast_exp2(m2 - m_new);
+#pragma unroll
+    for (int i = 0; i < C::MO; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+    m2 = m_new;
+    l_lane = fmaf(l_prev, alpha, block_weights(t, q, sv, pk, false));
   };
 
   // General softmax of a block (masks, bias, first statistics of a row).
@@ -716,7 +750,8 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
     constexpr bool FIRST = decltype(first)::value;
     f32x16 sv[2];
     unsigned pk[2][8];
-    float mn, al = 1.0f;
+    float mn = 0.0f, lp = 0.0f;
+    bool need = false;
     scores_q(slot, 0, sv[0]);
     // Nothing of this tile can overlap block 0's score MFMAs.
     if (kSched > 0) __builtin_amdgcn_sched_barrier(0);
@@ -725,7 +760,7 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
       if (q + 1 < kNQ) scores_q(slot, q + 1, sv[(q + 1) & 1]);
       if (q > 0) pv_q(slot, q - 1, pk[(q - 1) & 1]);
       if (FIRST && q == 0) fast_q_first(sv[q & 1], pk[q & 1], mn);
-      else fast_q(t, q, sv[q & 1], pk[q & 1], mn, al);
+      else fast_q(t, q, sv[q & 1], pk[q & 1], need, lp);
       if (PREFILL_PIN) {
         // Keep the block's weights ahead of the rescale branch, so they are
         // scheduled under the MFMAs issued before it rather than sunk past it.
@@ -746,8 +781,8 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
       if (FIRST && q == 0) {
         m2 = mn;
         has = true;
-      } else {
-        rescale(mn, al);
+      } else if (__ballot(need) != 0) {
+        redo_q(t, q, sv[q & 1], pk[q & 1], lp);
       }
     }
     pv_q(slot, kNQ - 1, pk[(kNQ - 1) & 1]);

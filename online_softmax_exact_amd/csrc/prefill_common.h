@@ -17,6 +17,9 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr float kRescale = 8.0f;   // lazy-rescale threshold, base-2 units
+// Full tiles: largest sum of a lane's 16 weights (each below 2^16 then) taken
+// against the lagging reference before the reference must move.
+constexpr float kSumMax = 65536.0f;
 
 // Kernel arguments (after host-side validation; positions and sizes fit 32
 // bits, strides are in elements).
