@@ -17,8 +17,10 @@ gradient N(0,1)) under ``backward``, unpadded variable-length batches
 (packed prefill and its backward against the padded batch, decode over
 per-batch KV lengths) under ``varlen``, the single-head fp32 problem, the
 multi-query verify and the padded batch with its dense bias under
-``workloads``, each with its own algorithmic counts, and a library GEMM and a
-device copy of the same session under ``achievable``.  ``roofline.traffic``
+``workloads``, each with its own algorithmic counts, a library GEMM and a
+device copy of the same session under ``achievable``, and the unit rates of
+the part (HBM stream, exp, LDS reads, MFMA; libattn_probes.so) under
+``ceilings``.  ``roofline.traffic``
 and ``roofline.counters`` come from the committed rocprofv3 runs
 (profiles/traffic.json) and are null when the kernel's sources changed since.
 """
@@ -279,6 +281,61 @@ def achievable_section(torch, dev, timed, p_tflops, d_gbs):
                      "decode_over_copy": round(d_gbs / cp_g, 4)}}
 
 
+def ceilings_section(torch, dev, stream):
+    """Unit rates measured on the part itself (libattn_probes.so): an HBM
+    streaming read of 2 GiB, the v_exp_f32 rate, the LDS read rate with
+    16-byte and with transposed 8-byte reads, and the bf16 MFMA rate of
+    independent v_mfma_f32_32x32x16_bf16 chains.  The cost model bounds a
+    kernel by its work over the rate of the unit doing it, so these are the
+    ceilings its fractions are read against (next to the published peaks)."""
+    from online_softmax_exact_amd import _probes
+
+    blocks = 2048                                    # 8 workgroups of 4 waves per CU
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+
+    def run(fn, n=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a_, b_ in evs:
+            a_.record(stream)
+            fn()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a_.elapsed_time(b_) for a_, b_ in evs)
+        return ts[len(ts) // 2] * 1e-3               # seconds, median
+
+    src = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
+    t_rd = run(lambda: _probes.stream_read(src, out, blocks, stream))
+    del src
+    iters_exp = 2048
+    t_exp = run(lambda: _probes.exp_rate(out, blocks, iters_exp, stream))
+    iters_lds = 64
+    t_lds = run(lambda: _probes.lds_read(out, blocks, iters_lds, False, stream))
+    t_tr = run(lambda: _probes.lds_read(out, blocks, iters_lds, True, stream))
+    iters_mfma = 256
+    t_mf = run(lambda: _probes.mfma_rate(out, blocks, iters_mfma, stream))
+    cus, nominal_ghz = 256, 2.4
+    rd = (2 << 30) / t_rd / 1e9
+    ex = blocks * 256 * 8 * iters_exp / t_exp
+    lds = blocks * 4 * 65536 * iters_lds / t_lds
+    ldt = blocks * 4 * 32768 * iters_lds / t_tr
+    mf = blocks * 4 * 4 * iters_mfma * 32768 / t_mf / 1e12
+    return {
+        "hbm_stream_read": {"bytes": 2 << 30, "ms": round(t_rd * 1e3, 4), "value": round(rd, 1), "unit": "GB/s",
+                            "frac_of_peak": round(rd / PEAK_HBM_GBS, 4)},
+        "exp_f32": {"value": round(ex / 1e9, 1), "unit": "G exp/s (8 independent chains of exp2 and a multiply)",
+                    "per_cu_per_nominal_clock": round(ex / cus / (nominal_ghz * 1e9), 2)},
+        "lds_read_b128": {"value": round(lds / 1e12, 2), "unit": "TB/s",
+                          "bytes_per_cu_per_nominal_clock": round(lds / cus / (nominal_ghz * 1e9), 1)},
+        "lds_read_tr_b64": {"value": round(ldt / 1e12, 2), "unit": "TB/s",
+                            "bytes_per_cu_per_nominal_clock": round(ldt / cus / (nominal_ghz * 1e9), 1)},
+        "mfma_bf16": {"value": round(mf, 1), "unit": "TFLOP/s", "frac_of_peak": round(mf / PEAK_BF16_TFLOPS, 4),
+                      "note": "independent 32x32x16 bf16 MFMA chains, no memory traffic"},
+    }
+
+
 def _recorded(key: str):
     """The committed rocprofv3 record of kernel `key` (profiles/traffic.json),
     or None when the kernel's sources have changed since it was taken."""
@@ -375,6 +432,8 @@ def main():
                     help="skip the multi-query verify and padded-bias measurements")
     ap.add_argument("--no-achievable", action="store_true",
                     help="skip the same-session ceilings (library bf16 GEMM, device copy)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the unit microbenchmarks (HBM stream, exp, LDS, MFMA rates)")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the variable-length (packed prefill, per-batch KV length decode) measurement")
     ap.add_argument("--window", type=int, default=4096,
@@ -574,6 +633,9 @@ def main():
     if not args.no_achievable:
         print("bench: achievable ceilings", file=sys.stderr, flush=True)
         out["achievable"] = achievable_section(torch, dev, timed, p_tflops, d_gbs)
+    if not args.no_ceilings:
+        print("bench: unit microbenchmarks", file=sys.stderr, flush=True)
+        out["ceilings"] = ceilings_section(torch, dev, stream)
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)

@@ -17,7 +17,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libattn_mi355x.so")
+# Another build of the same library (for instance the host-sanitized one of
+# build.build_sanitized) can be named by ATTN_MI355X_LIBRARY.
+LIB_PATH = os.environ.get("ATTN_MI355X_LIBRARY") or os.path.join(_HERE, "libattn_mi355x.so")
 
 ATTN_F32, ATTN_BF16 = 0, 1
 ATTN_E_HIP = -7

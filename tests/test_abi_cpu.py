@@ -316,3 +316,22 @@ def test_decode_noalloc_validation(lib):
     empty = good_params(t_q=0)
     assert lib.attn_decode_splitkv_noalloc(ctypes.byref(empty), 4, None, None, None, None, None,
                                            None) == 0
+
+
+def test_probe_library_exports_its_header():
+    from online_softmax_exact_amd import _probes
+    header = os.path.join(ROOT, "include", "attn_probes.h")
+    text = re.sub(r"/\*.*?\*/", "", open(header, encoding="utf-8").read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(attn_probe_[a-z_0-9]+)\s*\(", text)))
+    assert set(names) == set(_probes.EXPORTED)
+    if not os.path.exists(_probes.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    plib = _probes.load_library()
+    for n in names:
+        assert hasattr(plib, n), n
+    # Invalid arguments are rejected before any launch (no GPU needed).
+    assert plib.attn_probe_exp(None, 1, 1, None) == -2
+    assert plib.attn_probe_mfma(ctypes.c_void_p(0x100000), 0, 1, None) == -2
+    assert plib.attn_probe_lds_read(None, 1, 1, 0, None) == -2
+    assert plib.attn_probe_stream_read(ctypes.c_void_p(0x100001), 64, ctypes.c_void_p(0x100000), 1, None) == -2
