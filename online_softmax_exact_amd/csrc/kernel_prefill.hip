@@ -98,7 +98,7 @@ struct ShapeStd {
 #define PREFILL_BIG_BLOCKS 4
 #endif
 #ifndef PREFILL_BIG_SCHED
-#define PREFILL_BIG_SCHED 5
+#define PREFILL_BIG_SCHED 3
 #endif
 struct ShapeBig {
   static constexpr int kWaves = 8, kNQ = PREFILL_BIG_BLOCKS, kSched = PREFILL_BIG_SCHED;
