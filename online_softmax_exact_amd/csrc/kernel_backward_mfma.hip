@@ -57,6 +57,9 @@ constexpr int kBc = 64;                 // streamed tile rows
 #ifndef BWD_PIPE
 #define BWD_PIPE 1     // dV: software-pipelined path for units whose two blocks are fully legal
 #endif
+#ifndef BWD_FUSED
+#define BWD_FUSED 1    // dense batches without a bias: dK and dV in one launch
+#endif
 #ifndef BWD_SCHED
 #define BWD_SCHED 0    // VALU instructions placed after each MFMA in that path (0: compiler's order)
 #endif
@@ -859,6 +862,268 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Extra
 #endif
 }
 
+// ---------------------------------------------------------------------------
+// dK and dV in one pass (dense batches without a bias)
+// ---------------------------------------------------------------------------
+// The workgroup's 128 keys as in the dK / dV kernels (wavefront w owns keys
+// 32 w .. 32 w + 31, K^T resident as the B operand of S = Q K^T), but each
+// streamed block of 32 query rows serves both gradients: S = Q K^T and
+// dP = dO V^T are computed once, then dV^T += dO^T P and dK^T += Q^T dS.  So a
+// (row, key) pair costs 4 products here and 3 in the dQ kernel, 7 in all
+// instead of the 8 of separate dV and dK launches (each of which recomputes
+// S).  Two accumulator sets leave no registers for V^T, so the workgroup's
+// 128 V rows are copied into LDS once and read as the B operand of dP
+// (16-byte row reads); Q / dO stream in 32-row tiles to keep the two rings
+// and the V rows within 80 KB (two workgroups per CU).
+constexpr int kBf = 32;   // rows per streamed tile
+
+template <int DH, int DV>
+struct FusedCfg {
+  static constexpr int KS = DH / 16;
+  static constexpr int MS = DV / 16;
+  static constexpr int MQ = DH / 32;
+  static constexpr int MV = DV / 32;
+  static constexpr int H_RB = DH * 2;
+  static constexpr int V_RB = DV * 2;
+  static constexpr int H_BYTES = kBf * H_RB;
+  static constexpr int V_BYTES = kBf * V_RB;
+  static constexpr int H_DMA = H_BYTES / 1024 / kW;   // 1 KB copies per wavefront per tile
+  static constexpr int V_DMA = V_BYTES / 1024 / kW;
+  static constexpr int VS_BYTES = kBr * V_RB;         // the workgroup's V rows
+  static constexpr int VS_DMA = VS_BYTES / 1024 / kW;
+};
+
+template <int DH, int DV>
+__global__ __launch_bounds__(kThreads, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16_t* d_v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using C = FusedCfg<DH, DV>;
+  // Q ring, dO ring (two slots each), per slot 64 LSEs and 64 D values, then
+  // the V rows of the workgroup's keys.
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::H_BYTES + 2 * C::V_BYTES + 1024 + C::VS_BYTES];
+  char* const qring = smem;
+  char* const gring = smem + 2 * C::H_BYTES;
+  float* const sring = reinterpret_cast<float*>(smem + 2 * C::H_BYTES + 2 * C::V_BYTES);
+  char* const vstage = smem + 2 * C::H_BYTES + 2 * C::V_BYTES + 1024;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int lr = lane & 31;
+
+  // Low key tiles first (with causal masking they are seen by more rows).
+  const int bid = blockIdx.x;
+  int kt = bid / a.n_units;
+  int bh = bid % a.n_units;
+  if (a.batch_major) {
+    const int i2 = bid / a.heads_kv;
+    kt = i2 % a.n_tiles_grid;
+    bh = (i2 / a.n_tiles_grid) * a.heads_kv + bid % a.heads_kv;
+  }
+  const int b = bh / a.heads_kv;
+  const int kvh = bh % a.heads_kv;
+
+  const int key0 = kt * kBr + wave * kRowsW;   // first key of this wave
+  const int key = key0 + lr;
+  const bool key_ok = key < a.t_k;
+
+  // K^T operand of this lane's key.
+  u32x4 kreg[C::KS];
+  {
+    const uint16_t* kp = a.k + b * a.ks[0] + kvh * a.ks[1] + static_cast<int64_t>(key) * a.ks[2];
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s)
+      kreg[s] = key_ok ? *reinterpret_cast<const u32x4*>(kp + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
+  }
+
+  // Query rows that can see a key of the workgroup.
+  const int64_t wk0 = static_cast<int64_t>(kt) * kBr;
+  int64_t i_lo = 0, i_hi = a.t_q;
+  if (a.causal && wk0 - a.q_offset > i_lo) i_lo = wk0 - a.q_offset;
+  if (a.window > 0 && wk0 + kBr - 1 - a.q_offset + a.window < i_hi) i_hi = wk0 + kBr - 1 - a.q_offset + a.window;
+  if (i_lo > i_hi) i_lo = i_hi;
+  const int qt_lo = static_cast<int>(i_lo / kBf);
+  const int n_qt = i_hi > i_lo ? static_cast<int>((i_hi + kBf - 1) / kBf) - qt_lo : 0;
+  const int n_units = n_qt * a.group;          // (query head of the group, 32-row tile)
+
+  const int q_row_bytes = static_cast<int>(a.qs[2]) * 2;
+  const int g_row_bytes = static_cast<int>(a.os[2]) * 2;
+  const int v_row_bytes = static_cast<int>(a.vs[2]) * 2;
+  int qoff[C::H_DMA], goff[C::V_DMA];
+  dma_offsets<C::H_RB, C::H_DMA>(wave, lane, q_row_bytes, qoff);
+  dma_offsets<C::V_RB, C::V_DMA>(wave, lane, g_row_bytes, goff);
+  auto unit = [&](int u, int& hq, int& i0) {
+    hq = kvh * a.group + u / n_qt;
+    i0 = (qt_lo + u % n_qt) * kBf;
+  };
+  auto gload = [&](int u) {
+    int hq, i0;
+    unit(u, hq, i0);
+    const int slot = u & 1;
+    dma_tile<C::H_RB, C::H_DMA>(a.q + b * a.qs[0] + hq * a.qs[1], i0, a.t_q, q_row_bytes,
+                                qring + slot * C::H_BYTES, wave, qoff);
+    dma_tile<C::V_RB, C::V_DMA>(a.d_o + b * a.os[0] + hq * a.os[1], i0, a.t_q, g_row_bytes,
+                                gring + slot * C::V_BYTES, wave, goff);
+    if (wave == 0) {
+      // LSEs and D values of the tile's rows, 4 bytes per lane (rows past
+      // T_q read as 0 and are masked; the upper 32 are not used).
+      const int64_t r0 = (static_cast<int64_t>(b) * a.heads_q + hq) * a.t_q + i0;
+      const int64_t n = a.t_q - i0;
+      const auto rl = make_rsrc(a.lse + r0, n * 4);
+      const auto rd = make_rsrc(a.dd + r0, n * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rl, (__attribute__((address_space(3))) void*)(sring + slot * 128), 4, lane * 4, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rd, (__attribute__((address_space(3))) void*)(sring + slot * 128 + 64), 4, lane * 4, 0, 0, 0);
+    }
+  };
+
+  f32x16 acck[C::MQ], accv[C::MV];
+#pragma unroll
+  for (int i = 0; i < C::MQ; ++i) acck[i] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < C::MV; ++i) accv[i] = f32x16{};
+
+  auto dma_barrier = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  // The workgroup's V rows (rows past T_k arrive as zeros), then the first
+  // two units.
+  {
+    int vsoff[C::VS_DMA];
+    dma_offsets<C::V_RB, C::VS_DMA>(wave, lane, v_row_bytes, vsoff);
+    dma_tile<C::V_RB, C::VS_DMA>(a.v + b * a.vs[0] + kvh * a.vs[1], wk0, a.t_k, v_row_bytes, vstage, wave,
+                                 vsoff);
+  }
+  if (n_units > 0) gload(0);
+  if (n_units > 1) gload(1);
+  dma_barrier();
+
+  const int last_key = key0 + kRowsW - 1;
+  for (int u = 0; u < n_units; ++u) {
+    int hq, i0;
+    unit(u, hq, i0);
+    const int slot = u & 1;
+    const char* qt_ = qring + slot * C::H_BYTES;
+    const char* gt_ = gring + slot * C::V_BYTES;
+    const float* st_ = sring + slot * 128;
+    // Does the block hold a legal (row, key) pair of this wave, and are all
+    // its pairs legal?
+    const int64_t pf = a.q_offset + i0, pl = a.q_offset + i0 + 31;
+    bool any = key0 < a.t_k && i0 < a.t_q;
+    if (a.causal && pl < key0) any = false;
+    if (a.window > 0 && pf - a.window + 1 > last_key) any = false;
+    bool full = last_key < a.t_k && i0 + 31 < a.t_q;
+    if (a.causal && pf < last_key) full = false;
+    if (a.window > 0 && pl - a.window + 1 > key0) full = false;
+    if (any) {
+      // S = Q K^T and dP = dO V^T: register r holds row i0 + 8 (r / 4) +
+      // 4 h + (r % 4) for this lane's key.
+      f32x16 sacc = f32x16{}, dacc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) {
+        const u32x4 qop = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            row_chunk<C::H_RB>(qt_, lr, s, h));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qop), as_bf16x8(kreg[s]), sacc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int s = 0; s < C::MS; ++s) {
+        const u32x4 gop = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            row_chunk<C::V_RB>(gt_, lr, s, h));
+        const u32x4 vop = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            row_chunk<C::V_RB>(vstage, wave * kRowsW + lr, s, h));
+        dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(gop), as_bf16x8(vop), dacc, 0, 0, 0);
+      }
+      // P (eq 33.6's weights) and dS = P (dP - D) (eq 33.7), packed to bf16.
+      unsigned pk[8], pd[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int off = (8 * (i >> 1) + 4 * h + 2 * (i & 1)) * 4;
+        const f32x2 lp = *reinterpret_cast<const __attribute__((address_space(3))) f32x2*>(
+            (const __attribute__((address_space(3))) char*)(st_) + off);
+        const f32x2 dp = *reinterpret_cast<const __attribute__((address_space(3))) f32x2*>(
+            (const __attribute__((address_space(3))) char*)(st_) + 256 + off);
+        float w[2], ds[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * i + e;
+          float p = fast_exp2(fmaf(sacc[r], a.scale_log2, -lp[e] * kLog2e));
+          if (!full) {
+            const int row = i0 + 8 * (r >> 2) + 4 * h + (r & 3);
+            const int64_t pos = a.q_offset + row;
+            bool ok = key_ok && row < a.t_q;
+            if (a.causal && key > pos) ok = false;
+            if (a.window > 0 && key < pos - a.window + 1) ok = false;
+            p = ok ? p : 0.0f;
+          }
+          w[e] = p;
+          ds[e] = p * (dacc[r] - dp[e]);
+        }
+        pk[i] = pack_bf16(w[0], w[1]);
+        pd[i] = pack_bf16(ds[0], ds[1]);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS (A = transposed reads of the tiles).
+#pragma unroll
+      for (int kk2 = 0; kk2 < 2; ++kk2) {
+        const u32x4 bp = {pk[4 * kk2], pk[4 * kk2 + 1], pk[4 * kk2 + 2], pk[4 * kk2 + 3]};
+        const u32x4 bd = {pd[4 * kk2], pd[4 * kk2 + 1], pd[4 * kk2 + 2], pd[4 * kk2 + 3]};
+#pragma unroll
+        for (int mo = 0; mo < C::MV; ++mo) {
+          const u32x2 lo = tr_read(tr_addr<C::V_RB>(gt_, 0, kk2, mo, 0, lane));
+          const u32x2 hi = tr_read(tr_addr<C::V_RB>(gt_, 0, kk2, mo, 1, lane));
+          const u32x4 aop = {lo[0], lo[1], hi[0], hi[1]};
+          accv[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bp), accv[mo], 0, 0, 0);
+        }
+#pragma unroll
+        for (int mo = 0; mo < C::MQ; ++mo) {
+          const u32x2 lo = tr_read(tr_addr<C::H_RB>(qt_, 0, kk2, mo, 0, lane));
+          const u32x2 hi = tr_read(tr_addr<C::H_RB>(qt_, 0, kk2, mo, 1, lane));
+          const u32x4 aop = {lo[0], lo[1], hi[0], hi[1]};
+          acck[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bd), acck[mo], 0, 0, 0);
+        }
+      }
+    }
+    // Unit u done: this wave's copies of unit u + 1 have landed, every wave is
+    // done with slot u & 1, which takes unit u + 2.
+    dma_barrier();
+    if (u + 2 < n_units) gload(u + 2);
+  }
+
+  // dK = scale dS^T Q (eq 33.8) and dV = P^T dO (eq 33.6); keys no row sees get 0.
+  if (!key_ok) return;
+  const float sc = a.scale_log2 * kLn2;
+  uint16_t* kp = a.out + b * a.ks[0] + kvh * a.ks[1] + static_cast<int64_t>(key) * a.ks[2];
+  uint16_t* vp = d_v + b * a.vs[0] + kvh * a.vs[1] + static_cast<int64_t>(key) * a.vs[2];
+#pragma unroll
+  for (int mo = 0; mo < C::MQ; ++mo)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack_bf16(acck[mo][4 * g] * sc, acck[mo][4 * g + 1] * sc);
+      w[1] = pack_bf16(acck[mo][4 * g + 2] * sc, acck[mo][4 * g + 3] * sc);
+      *reinterpret_cast<u32x2*>(kp + 32 * mo + 8 * g + 4 * h) = w;
+    }
+#pragma unroll
+  for (int mo = 0; mo < C::MV; ++mo)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack_bf16(accv[mo][4 * g], accv[mo][4 * g + 1]);
+      w[1] = pack_bf16(accv[mo][4 * g + 2], accv[mo][4 * g + 3]);
+      *reinterpret_cast<u32x2*>(vp + 32 * mo + 8 * g + 4 * h) = w;
+    }
+#endif
+}
+
+template <int DH, int DV>
+hipError_t launch_kvf(const BArgs& a, uint16_t* d_v, int64_t blocks, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_kvf_mfma_kernel<DH, DV>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a,
+                     d_v);
+  return hipGetLastError();
+}
+
 template <int DH, int DV, int WHICH, class... X>
 void launch_kv_x(const BArgs& a, int64_t blocks, hipStream_t s, X... x) {
   hipLaunchKernelGGL((bwd_kv_mfma_kernel<DH, DV, WHICH, X...>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
@@ -1022,6 +1287,16 @@ bool launch_bwd_dkdv_mfma(const Problem& pb, int dtype, const void* q, const voi
   a.batch_major = batch_major(pb);
   *err = hipSuccess;
   if (blocks == 0) return true;
+  // Dense batches without a bias: one launch for both gradients.
+  if (BWD_FUSED && !packed && pb.kv_lens == nullptr && pb.bias == nullptr) {
+    a.out = static_cast<uint16_t*>(d_k);
+    uint16_t* dv = static_cast<uint16_t*>(d_v);
+    if (pb.d_h == 128 && pb.d_v == 128) *err = launch_kvf<128, 128>(a, dv, blocks, stream);
+    else if (pb.d_h == 64 && pb.d_v == 128) *err = launch_kvf<64, 128>(a, dv, blocks, stream);
+    else if (pb.d_h == 128 && pb.d_v == 64) *err = launch_kvf<128, 64>(a, dv, blocks, stream);
+    else *err = launch_kvf<64, 64>(a, dv, blocks, stream);
+    return true;
+  }
   for (int which = 0; which < 2 && *err == hipSuccess; ++which) {
     a.out = static_cast<uint16_t*>(which ? d_k : d_v);
     if (pb.d_h == 128 && pb.d_v == 128) *err = which ? launch_kv<128, 128, 1>(a, va, bb, blocks, stream) : launch_kv<128, 128, 0>(a, va, bb, blocks, stream);
