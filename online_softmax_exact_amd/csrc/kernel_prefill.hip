@@ -50,6 +50,9 @@ using namespace pf;
 #ifndef PREFILL_BLOCKS
 #define PREFILL_BLOCKS 2               // 32-key blocks per key tile (one barrier per tile)
 #endif
+#ifndef PREFILL_BIAS_XCD
+#define PREFILL_BIAS_XCD 1             // head-shared bias: heads of a query tile on one XCD (see the work order)
+#endif
 #ifndef PREFILL_XCD_MAP
 #define PREFILL_XCD_MAP 0              // 1: keep one head per XCD at a time (see the work order)
 #endif
@@ -79,6 +82,9 @@ using namespace pf;
 #endif
 #ifndef PREFILL_BIAS_LDS
 #define PREFILL_BIAS_LDS 1             // 1: full tiles' bias staged through LDS where it fits
+#endif
+#ifndef PREFILL_BIAS_EARLY
+#define PREFILL_BIAS_EARLY 1           // 1: a staged block's next-tile bias copied as soon as it is read
 #endif
 #ifndef PREFILL_WAVES_PER_SIMD
 #define PREFILL_WAVES_PER_SIMD 2       // resident waves per SIMD the kernel is built for
@@ -144,7 +150,9 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
   // 4 KB bias block per wave and 32-key block (staged bias, below).
   constexpr int kRing = 2 * C::K_BYTES + 2 * C::V_BYTES;
   constexpr int kBiasStage = S::kWaves * kNQ * 4096;
-  constexpr bool kBiasLds = BIAS && !COUNT && PREFILL_BIAS_LDS && kRing + kBiasStage <= 81920;
+  constexpr int kLdsShare = 163840 * S::kWaves / (4 * PREFILL_WAVES_PER_SIMD);   // LDS per workgroup
+  constexpr bool kBiasLds = BIAS && !COUNT && PREFILL_BIAS_LDS && kRing + kBiasStage <= kLdsShare;
+  constexpr bool kBiasEarly = kBiasLds && PREFILL_BIAS_EARLY;
   __shared__ __attribute__((aligned(1024))) char smem[kRing + (kBiasLds ? kBiasStage : 0)];
   char* const kring = smem;
   char* const vring = smem + 2 * C::K_BYTES;
@@ -172,6 +180,24 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
     const int i2 = bid / a.heads_q;
     idx = i2 % a.n_qtiles;
     bh = (i2 / a.n_qtiles) * a.heads_q + bid % a.heads_q;
+  } else if (!VAR && a.xcd_heads) {
+    // The default order in groups g = (tile, batch) of heads_q workgroups.
+    // XCD x (= bid mod 8) receives ids x, x + 8, ...: here it runs groups x,
+    // x + 8, ... one after the other, so the heads that read the same bias
+    // rows run at the same time behind one L2, and every XCD still sees the
+    // tiles heaviest first.  Ids past the last whole round of 8 groups keep
+    // the default order.
+    const int rounds8 = a.n_qtiles * (a.batch_heads / a.heads_q) / 8;
+    if (bid < rounds8 * 8 * a.heads_q) {
+      const int local = bid >> 3;
+      const int g = (local / a.heads_q) * 8 + (bid & 7);
+      const int nb = a.batch_heads / a.heads_q;
+      idx = g / nb;
+      bh = (g % nb) * a.heads_q + local % a.heads_q;
+    } else {
+      idx = bid / a.batch_heads;
+      bh = bid % a.batch_heads;
+    }
   } else {
     idx = bid / a.batch_heads;
     bh = bid % a.batch_heads;
@@ -500,16 +526,23 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
       for (int q = 0; q < (kBiasPf ? kNQ : 1); ++q) load_bias(t, q, mbp[q]);
     }
   };
-  // Block q's staged values: wait until at most the 4 (kNQ - 1 - q) copies
-  // issued last are in flight, which covers block q's copies whether or not
-  // the K/V copies of tile t + 1 (issued after the bias) went out, and keeps
-  // the wait free of branches; then the 4 chunks 2 g + h of this lane's row.
-  // Byte offsets in a staging block of this lane's row and chunks 2 g + h.
+  // Block q's staged values of tile t: the copies issued after them are the
+  // 4 (kNQ - 1 - q) of the later blocks, unless tile t is the last the K/V
+  // copies of tile t + 1, and (kBiasEarly, tile t + 1 full) the 4 q copies of
+  // tile t + 1's blocks before q, so waiting until at most that many are in
+  // flight waits for block q's copies alone; then the 4 chunks 2 g + h of
+  // this lane's row.  Byte offsets in a staging block of this lane's row and
+  // chunks 2 g + h:
   int bread[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) bread[g] = lr * 128 + (((2 * g + h) ^ bswz(lr)) << 4);
-  auto staged_bias = [&](int q, float* mb) {
-    wait_vm_upto<4 * (kNQ - 1)>(4 * (kNQ - 1 - q));
+  auto staged_bias = [&](int t, int q, float* mb) {
+    constexpr int kKV = C::K_DMA + C::V_DMA, kMax = 4 * (kNQ - 1) + kKV;
+    const bool kv = t + 1 < n_tiles, nb = kBiasEarly && t + 1 < t_full;
+    if (kv && nb) wait_vm_upto<kMax>(4 * (kNQ - 1 - q) + kKV + 4 * q);
+    else if (kv) wait_vm_upto<kMax>(4 * (kNQ - 1 - q) + kKV);
+    else if (nb) wait_vm_upto<kMax>(4 * (kNQ - 1 - q) + 4 * q);
+    else wait_vm_upto<kMax>(4 * (kNQ - 1 - q));
     const lds_char* blk = (const lds_char*)bstage + q * 4096;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -534,7 +567,7 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
   // rule).  l_prev receives l before the block.
   auto block_bias = [&](int t, int q, float* mb) {
     if constexpr (kBiasLds) {
-      staged_bias(q, mb);
+      staged_bias(t, q, mb);
     } else if (kBiasPf) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mb[r] = mbp[q][r];
@@ -687,9 +720,17 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
   // barrier (every wave is done with slot t & 1), then DMA tile t + 2 into it.
   // The first full tile always follows a general one, so every full tile's
   // bias was prefetched here at the end of the tile before it.
-  auto advance = [&](int t) {
-    dma_barrier();
-    if ((kBiasPf || kBiasLds) && t + 1 < t_full) prefetch_bias(t + 1);
+  // A full tile with kBiasEarly has already issued the copies of tile
+  // t + 1's bias (the newest 4 kNQ), so it waits for the older K/V copies
+  // only: the barrier then leaves them in flight (this wave's own LDS blocks,
+  // which no other wave touches).
+  auto advance = [&](int t, bool fast) {
+    if (kBiasEarly && fast && t + 1 < t_full) {
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(4 * kNQ) : "memory");
+    } else {
+      dma_barrier();
+      if ((kBiasPf || kBiasLds) && t + 1 < t_full) prefetch_bias(t + 1);
+    }
     if (t + 2 < n_tiles) gload(t + 2);
   };
 
@@ -714,7 +755,7 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
         pv2_q(t & 1, q, pk, pl);
       }
     }
-    advance(t);
+    advance(t, false);
   };
   // General tiles up to the wave's first tile inside every row's window, then
   // one more (it gives every row its first statistics), the run of full
@@ -784,9 +825,12 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
       } else if (__ballot(need) != 0) {
         redo_q(t, q, sv[q & 1], pk[q & 1], lp);
       }
+      // Block q's staged bias is read (the redo included): its LDS block
+      // takes tile t + 1's block q now, a tile ahead of its use.
+      if (kBiasEarly && t + 1 < t_full) stage_block(t + 1, q);
     }
     pv_q(slot, kNQ - 1, pk[(kNQ - 1) & 1]);
-    advance(t);
+    advance(t, true);
   };
   const std::false_type later{};
   // The first tile: pipelined when it is fully visible and no row has
@@ -943,6 +987,14 @@ bool launch_prefill_mfma(const Problem& pb, int dtype, const void* q, const void
   const int64_t kv_bytes = pb.batch * pb.heads_kv * pb.t_k * (pb.d_h + pb.d_v) * 2;
   a.batch_major = !packed && pb.kv_lens == nullptr && pb.bias == nullptr && pb.batch > 1 &&
                   kv_bytes > (int64_t(256) << 20);
+  // A bias shared by the heads is read by every head of a query tile: in the
+  // default order those heads sit on all 8 XCDs and each XCD fetches the same
+  // bias rows past its L2; grouped by XCD they run together on one.  Measured
+  // on d_h = 64, d_v = 128 causal batches of 2048-4096 rows: 4 to 16 batches
+  // of 8-32 heads 2-19 % faster, 2 batches of 32 heads 0-5 % slower (there
+  // the default order's fixed heads per XCD keep more K/V in its caches).
+  a.xcd_heads = PREFILL_BIAS_XCD && !packed && pb.kv_lens == nullptr && pb.bias != nullptr &&
+                pb.bs[1] == 0 && pb.bs[2] != 0 && pb.heads_q > 1 && pb.batch >= 4;
 
   const bool bias = pb.bias != nullptr;
   const bool count = n_legal != nullptr;

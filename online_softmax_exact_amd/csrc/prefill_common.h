@@ -48,6 +48,9 @@ struct Args {
   // query tiles), 0 = query tiles outermost (every batch's heaviest tiles
   // first).
   int32_t batch_major;
+  // Dense batches: 1 = the heads of a (query tile, batch) pair run together
+  // on one XCD (the default order otherwise).
+  int32_t xcd_heads;
   float scale;   // scale in natural-log units (scale_log2 = scale * log2 e)
 };
 

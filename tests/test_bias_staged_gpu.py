@@ -4,7 +4,8 @@ full tile's bias through LDS (calls without legal-key counts, d_h/d_v of
 loaded per block straight into registers): the two must give the same bits,
 and both must match the oracle element by element.  Cases: grouped heads,
 query rows ending inside a wavefront, several full key tiles with a ragged
-tail, causal and not, offsets, biases per head, shared by heads and shared
+tail, causal and not, offsets, biases per head, shared by heads (also over
+4 or more batches, whose workgroups run in the XCD-grouped order) and shared
 by rows, a strided bias view (rows wider than T_k), -inf entries, a sliding
 window (also a three-key window from position 0, so that every row's output
 is nearly one value row), and packed sequences with a packed or per-key
@@ -39,6 +40,11 @@ CASES = [
     (2, 4, 4, 385, 435, 64, 128, True, 50, "shared", 0.1, 100, 0),
     (2, 4, 4, 385, 435, 64, 128, True, 0, "shared", 0.1, 3, 0),
     (1, 8, 2, 31, 600, 128, 64, False, 0, "dense", 0.0, 0, 0),          # one partial wavefront of rows
+    # Head-shared bias over 4 or more batches: workgroups grouped by XCD,
+    # 15 (tile, batch) groups (one whole round of 8, the rest in the default
+    # order) and 24 (three whole rounds).
+    (5, 3, 3, 300, 420, 64, 128, True, 0, "shared", 0.1, 0, 0),
+    (4, 2, 1, 700, 700, 64, 128, True, 0, "shared", 0.05, 0, 0),
 ]
 
 
