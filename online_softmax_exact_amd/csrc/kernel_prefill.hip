@@ -83,6 +83,9 @@ using namespace pf;
 #ifndef PREFILL_BIAS_LDS
 #define PREFILL_BIAS_LDS 1             // 1: full tiles' bias staged through LDS where it fits
 #endif
+#ifndef PREFILL_BIAS_SKIP
+#define PREFILL_BIAS_SKIP 1            // 1: a full tile whose staged bias is all -inf for the wave is skipped
+#endif
 #ifndef PREFILL_BIAS_EARLY
 #define PREFILL_BIAS_EARLY 1           // 1: a staged block's next-tile bias copied as soon as it is read
 #endif
@@ -536,13 +539,16 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
   int bread[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) bread[g] = lr * 128 + (((2 * g + h) ^ bswz(lr)) << 4);
-  auto staged_bias = [&](int t, int q, float* mb) {
+  auto staged_wait = [&](int t, int q) {
     constexpr int kKV = C::K_DMA + C::V_DMA, kMax = 4 * (kNQ - 1) + kKV;
     const bool kv = t + 1 < n_tiles, nb = kBiasEarly && t + 1 < t_full;
     if (kv && nb) wait_vm_upto<kMax>(4 * (kNQ - 1 - q) + kKV + 4 * q);
     else if (kv) wait_vm_upto<kMax>(4 * (kNQ - 1 - q) + kKV);
     else if (nb) wait_vm_upto<kMax>(4 * (kNQ - 1 - q) + 4 * q);
     else wait_vm_upto<kMax>(4 * (kNQ - 1 - q));
+  };
+  auto staged_bias = [&](int t, int q, float* mb) {
+    staged_wait(t, q);
     const lds_char* blk = (const lds_char*)bstage + q * 4096;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -550,6 +556,30 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
 #pragma unroll
       for (int e = 0; e < 4; ++e) mb[4 * g + e] = x[e];
     }
+  };
+
+  // A full tile whose staged bias is -inf for every row and key of the wave
+  // (keys past a padded sequence's end, say) gives every weight 0 and
+  // changes no statistic (the valid-flag rule), so the wave may skip its
+  // products and softmax.  The test costs a live tile one read and compare:
+  // only when every lane's first entry is -inf are all entries read (compared
+  // as bits, so a NaN counts as live and reaches the output as it would).
+  auto dead_tile = [&](int t) -> bool {
+    staged_wait(t, 0);
+    const lds_char* b0 = (const lds_char*)bstage;
+    const unsigned f = *reinterpret_cast<const __attribute__((address_space(3))) unsigned*>(b0 + bread[0]);
+    if (__ballot(f != 0xff800000u) != 0) return false;
+    staged_wait(t, kNQ - 1);
+    bool live = false;
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x4 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(b0 + q * 4096 + bread[g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) live |= x[e] != 0xff800000u;
+      }
+    return __ballot(live) == 0;
   };
 
   // Softmax of a block whose keys are all causally visible (and inside the
@@ -793,43 +823,49 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
     unsigned pk[2][8];
     float mn = 0.0f, lp = 0.0f;
     bool need = false;
-    scores_q(slot, 0, sv[0]);
-    // Nothing of this tile can overlap block 0's score MFMAs.
-    if (kSched > 0) __builtin_amdgcn_sched_barrier(0);
+    // Dead tiles skip the products and the softmax but keep the copies.
+    const bool dead = kBiasLds && PREFILL_BIAS_SKIP && dead_tile(t);
+    if (!dead) {
+      scores_q(slot, 0, sv[0]);
+      // Nothing of this tile can overlap block 0's score MFMAs.
+      if (kSched > 0) __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int q = 0; q < kNQ; ++q) {
-      if (q + 1 < kNQ) scores_q(slot, q + 1, sv[(q + 1) & 1]);
-      if (q > 0) pv_q(slot, q - 1, pk[(q - 1) & 1]);
-      if (FIRST && q == 0) fast_q_first(sv[q & 1], pk[q & 1], mn);
-      else fast_q(t, q, sv[q & 1], pk[q & 1], need, lp);
-      if (PREFILL_PIN) {
-        // Keep the block's weights ahead of the rescale branch, so they are
-        // scheduled under the MFMAs issued before it rather than sunk past it.
-        const unsigned* w = pk[q & 1];
-        asm volatile("" ::"v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]),
-                     "v"(w[7]), "v"(l_lane));
-      }
-      if (kSched > 0) {
-        // One MFMA, then kSched VALU instructions of the softmax, so
-        // the in-order issue never waits on the matrix pipe with VALU work
-        // behind it.
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, kSched, 0);
+      if (!dead) {
+        if (q + 1 < kNQ) scores_q(slot, q + 1, sv[(q + 1) & 1]);
+        if (q > 0) pv_q(slot, q - 1, pk[(q - 1) & 1]);
+        if (FIRST && q == 0) fast_q_first(sv[q & 1], pk[q & 1], mn);
+        else fast_q(t, q, sv[q & 1], pk[q & 1], need, lp);
+        if (PREFILL_PIN) {
+          // Keep the block's weights ahead of the rescale branch, so they are
+          // scheduled under the MFMAs issued before it rather than sunk past it.
+          const unsigned* w = pk[q & 1];
+          asm volatile("" ::"v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]),
+                       "v"(w[7]), "v"(l_lane));
         }
-      }
-      if (FIRST && q == 0) {
-        m2 = mn;
-        has = true;
-      } else if (__ballot(need) != 0) {
-        redo_q(t, q, sv[q & 1], pk[q & 1], lp);
+        if (kSched > 0) {
+          // One MFMA, then kSched VALU instructions of the softmax, so
+          // the in-order issue never waits on the matrix pipe with VALU work
+          // behind it.
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, kSched, 0);
+          }
+        }
+        if (FIRST && q == 0) {
+          m2 = mn;
+          has = true;
+        } else if (__ballot(need) != 0) {
+          redo_q(t, q, sv[q & 1], pk[q & 1], lp);
+        }
       }
       // Block q's staged bias is read (the redo included): its LDS block
       // takes tile t + 1's block q now, a tile ahead of its use.
       if (kBiasEarly && t + 1 < t_full) stage_block(t + 1, q);
     }
-    pv_q(slot, kNQ - 1, pk[(kNQ - 1) & 1]);
+    if (!dead) pv_q(slot, kNQ - 1, pk[(kNQ - 1) & 1]);
     advance(t, true);
   };
   const std::false_type later{};

@@ -72,6 +72,40 @@ def test_staged_bias_parity(case):
     assert_close(o, lse, o_ref, l_ref, torch.bfloat16, what=str(case))
 
 
+PADDED_CASES = [
+    # (B, Hq, Hkv, Tq, Tk, dh, dv, causal, q_offset)
+    (4, 4, 4, 700, 700, 64, 128, True, 0),
+    (2, 4, 2, 600, 900, 64, 64, True, 300),
+    (3, 2, 2, 500, 800, 128, 64, False, 0),
+]
+
+
+@pytest.mark.parametrize("case", PADDED_CASES, ids=[f"pad{i}" for i in range(len(PADDED_CASES))])
+def test_staged_bias_padded_keys(case):
+    """Head-shared bias of a padded batch (keys past each sequence's length
+    -inf, two rows -inf throughout): full tiles whose staged bias is -inf for
+    every row of a wavefront are skipped, which adds exactly nothing, so the
+    call gives the bits of the per-block instance (which computes them) and
+    matches the oracle."""
+    b, hq, hkv, tq, tk, dh, dv, causal, off = case
+    print("case", case, flush=True)
+    seed = zlib.crc32(repr(case).encode()) % 10_000
+    wl = inputs.make_random(b, hq, hkv, tq, tk, dh, dv, dtype=torch.bfloat16, seed=seed, causal=causal,
+                            q_offset=off)
+    wl.bias, lengths, _ = inputs.padded_bias(b, tq, tk, seed)
+    assert min(lengths) + 64 < tk   # at least one whole tile of padded keys
+    q, k, v, m = to_dev(wl)
+    o, lse = attn.attn_fwd(q, k, v, scale=wl.scale, causal=causal, q_offset=off, bias=m)
+    o_c, lse_c, n = attn.attn_fwd(q, k, v, scale=wl.scale, causal=causal, q_offset=off, bias=m,
+                                  return_n_legal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_c.view(torch.int16)), "skipping dead tiles changed bits"
+    assert torch.equal(lse, lse_c), "skipping dead tiles changed the LSE"
+    o_ref, l_ref, n_ref = oracle_full(wl)
+    assert np.array_equal(n.cpu().numpy(), n_ref), "n_legal differs"
+    assert_close(o, lse, o_ref, l_ref, torch.bfloat16, what=str(case))
+
+
 PACKED_CASES = [
     # (Hq, Hkv, L_q per sequence, L_k per sequence, dh, dv, causal, bias, masked_frac, max_seqlen_q)
     (4, 4, [200, 77, 129, 300], [200, 300, 129, 500], 64, 128, True, "packed", 0.1, 300),
