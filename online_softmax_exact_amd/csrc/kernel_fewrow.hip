@@ -55,6 +55,9 @@ struct FCfg {
   static constexpr int MERGE_O = kWaves * kRows * DV * 4;
   static constexpr int MERGE = MERGE_O + 2 * kWaves * kRows * 4;
   static constexpr int SMEM = MERGE > kWaves * VBUF ? MERGE : kWaves * VBUF;
+  // Bias instances: two 4 KB staging blocks per wave after the V buffers.
+  static constexpr int BSTAGE = kWaves * VBUF;
+  static constexpr int SMEM_B = MERGE > BSTAGE + kWaves * 8192 ? MERGE : BSTAGE + kWaves * 8192;
 };
 
 struct FArgs {
@@ -83,6 +86,7 @@ struct FArgs {
 struct FBias {
   const float* bias;
   int64_t bs[3];
+  int64_t extent;   // elements from `bias` to one past its last element
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -106,7 +110,7 @@ template <int DH, int DV, bool SPLIT, bool VAR, class... Bias>
 __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bias_arg) {
   constexpr bool BIAS = sizeof...(Bias) > 0;
   using C = FCfg<DH, DV>;
-  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+  __shared__ __attribute__((aligned(16))) char smem[BIAS ? C::SMEM_B : C::SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -218,46 +222,85 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
   for (int i = 0; i < C::MO; ++i) oacc[i] = f32x16{};
 
   // Plain global loads (measured faster here than buffer loads); rows past
-  // the wave's range end are not read and give zeros.
+  // the wave's range end give zeros.  Bias instances issue every load (rows
+  // past the end read key 0 and are then zeroed): the wait for the staged
+  // bias below counts the loads issued after it.
   u32x4 kreg[C::KS], vreg[C::V_PER_LANE];
   auto ld = [](const uint16_t* p) -> u32x4 { return *reinterpret_cast<const u32x4*>(p); };
   auto load = [&](int t, u32x4* kr, u32x4* vr) {
     const int64_t kb = wlo + static_cast<int64_t>(t) * kTile;
     const int64_t key = kb + lr;
     const bool kok = key < whi;
-    const uint16_t* kp = kbase + key * a.ks[2] + 8 * h;
+    const uint16_t* kp = kbase + (BIAS && !kok ? 0 : key) * a.ks[2] + 8 * h;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      kr[ks] = kok ? ld(kp + 16 * ks) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < C::KS; ++ks) {
+      if (BIAS) {
+        const u32x4 x = ld(kp + 16 * ks);
+        kr[ks] = kok ? x : u32x4{0, 0, 0, 0};
+      } else {
+        kr[ks] = kok ? ld(kp + 16 * ks) : u32x4{0, 0, 0, 0};
+      }
+    }
 #pragma unroll
     for (int i = 0; i < C::V_PER_LANE; ++i) {
       const int c = lane + 64 * i;
       const int r = c / (DV / 8), col = c % (DV / 8);
       const bool vok = kb + r < whi;
-      vr[i] = vok ? ld(vbase + (kb + r) * a.vs[2] + col * 8) : u32x4{0, 0, 0, 0};
+      if (BIAS) {
+        const u32x4 x = ld(vbase + (vok ? kb + r : 0) * a.vs[2] + col * 8);
+        vr[i] = vok ? x : u32x4{0, 0, 0, 0};
+      } else {
+        vr[i] = vok ? ld(vbase + (kb + r) * a.vs[2] + col * 8) : u32x4{0, 0, 0, 0};
+      }
     }
   };
 
-  // This lane's bias row (BIAS): keys [0, T_k) of (b, hq, qi); 16-byte
-  // loads of the 4 consecutive keys each register group holds.  Rows past
-  // the group's rows read an empty range (zeros; they are never legal).
-  const float* brow = nullptr;
+  // Bias (BIAS): each wave copies its 32 rows x 32 keys of tile t (4 KB)
+  // into staging block t & 1 with buffer_load ... lds, 8 rows (128 bytes
+  // each) per instruction, one tile ahead, from the base of the workgroup's
+  // first row (b, kvh * group, row 0) plus the tile's first key; lane l of
+  // copy i carries row 8 i + l / 8, chunk slot l % 8, which holds the row's
+  // chunk (l % 8) ^ bswz(row), so a 16-byte read of 16 rows' same chunk
+  // covers all 64 banks.  Rows past the group's rows copy row 0 (never
+  // legal).  The descriptor's size ends at the bias's last element, so keys
+  // past it read zeros.
+  const float* bias_w = nullptr;
+  int64_t bias_left = 0;   // elements from bias_w to the end of the bias
+  int bdma[4];
+  char* const bstage = smem + C::BSTAGE + wave * 8192;
+  auto bswz = [](int r) { return (r >> 1) & 7; };
   if constexpr (BIAS) {
     const FBias& fb = first_of(bias_arg...);
-    brow = fb.bias + b * fb.bs[0] + hq * fb.bs[1] + static_cast<int64_t>(qi) * fb.bs[2];
+    const int64_t off0 = b * fb.bs[0] + static_cast<int64_t>(kvh) * a.group * fb.bs[1];
+    bias_w = fb.bias + off0;
+    bias_left = fb.extent - off0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 8 * i + (lane >> 3);
+      const int nn = rg * kRows + row;
+      const int64_t roff = nn < a.rows ? (nn / a.t_q) * fb.bs[1] + static_cast<int64_t>(nn % a.t_q) * fb.bs[2] : 0;
+      bdma[i] = static_cast<int>(roff * 4) + 16 * ((lane & 7) ^ bswz(row));
+    }
   }
+  auto stage_bias = [&](int t) {
+    const int64_t kb = wlo + static_cast<int64_t>(t) * kTile;
+    const auto rs = make_rsrc(bias_w + kb, (bias_left - kb) * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(bstage + (t & 1) * 4096 + i * 1024), 16, bdma[i], 0, 0, 0);
+  };
+  int bread[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) bread[g] = lr * 128 + (((2 * g + h) ^ bswz(lr)) << 4);
 
-  if (n_tiles > 0) load(0, kreg, vreg);
+  if (n_tiles > 0) {
+    load(0, kreg, vreg);
+    if (BIAS) stage_bias(0);
+  }
 
   for (int t = 0; t < n_tiles; ++t) {
     const int64_t kb = wlo + static_cast<int64_t>(t) * kTile;
-    f32x4 mb[BIAS ? 4 : 1];
-    if (BIAS) {
-      const auto rs = make_rsrc(brow + kb, row_ok ? (a.t_k - kb) * 4 : 0);
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        mb[g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (8 * g + 4 * h) * 4, 0, 0));
-    }
     // V tile -> this wave's LDS buffer (read back transposed below).
 #pragma unroll
     for (int i = 0; i < C::V_PER_LANE; ++i) {
@@ -269,7 +312,27 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[ks]), as_bf16x8(qreg[ks]), sacc, 0, 0, 0);
-    if (t + 1 < n_tiles) load(t + 1, kreg, vreg);
+    if (t + 1 < n_tiles) {
+      load(t + 1, kreg, vreg);
+      if (BIAS) stage_bias(t + 1);
+    }
+    f32x4 mb[BIAS ? 4 : 1];
+    if (BIAS) {
+      // Tile t's copies are older than the KS + V_PER_LANE loads and 4
+      // copies of tile t + 1 issued above (all of them unconditional), so at
+      // most that many in flight means they have landed.
+      asm volatile("" ::: "memory");
+      if (t + 1 < n_tiles) {
+        constexpr int kYounger = C::KS + C::V_PER_LANE + 4;
+        static_assert(kYounger < 64, "vmcnt holds 6 bits");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kYounger) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      const lds_char* blk = (const lds_char*)bstage + (t & 1) * 4096;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) mb[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(blk + bread[g]);
+    }
 
     // Register r holds key kb + 8 (r / 4) + 4 h + (r % 4) of this lane's row.
     int64_t lim64 = whi - 1 - kb;
@@ -440,6 +503,7 @@ FBias make_bias(const Problem& pb) {
   FBias fb{};
   fb.bias = pb.bias;
   for (int i = 0; i < 3; ++i) fb.bs[i] = pb.bs[i];
+  fb.extent = (pb.batch - 1) * pb.bs[0] + (pb.heads_q - 1) * pb.bs[1] + (pb.t_q - 1) * pb.bs[2] + pb.t_k;
   return fb;
 }
 
@@ -448,10 +512,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 bool eligible(const Problem& pb, int dtype, const void* q, const void* k, const void* v,
               const void* o) {
   if (dtype != ATTN_BF16 || pb.cu_q != nullptr) return false;
-  // A bias must be contiguous along keys with 16-byte aligned rows.
+  // A bias must be contiguous along keys with 16-byte aligned rows, and a
+  // row group's rows must start within 2^29 - 32 elements of its first row
+  // (the staging copies address them with 31-bit byte offsets).
   if (pb.bias != nullptr &&
       (pb.bs[3] != 1 || ((pb.bs[0] | pb.bs[1] | pb.bs[2]) & 3) != 0 ||
-       (reinterpret_cast<uintptr_t>(pb.bias) & 15) != 0))
+       (reinterpret_cast<uintptr_t>(pb.bias) & 15) != 0 ||
+       (pb.group - 1) * pb.bs[1] + (pb.t_q - 1) * pb.bs[2] >= (int64_t(1) << 29) - 32))
     return false;
   if (!((pb.d_h == 64 || pb.d_h == 128) && (pb.d_v == 64 || pb.d_v == 128))) return false;
   if (!(pb.scale_log2 > 0.0f)) return false;

@@ -176,6 +176,9 @@ KV_CASES = [
     ("decode", torch.bfloat16, 4, 8, 8, 1, 3000, 64, 64, True, [3000, 1500, 7, 0], 600, "none", 256),
     ("decode", torch.bfloat16, 3, 8, 2, 5, 2048, 128, 128, True, [2048, 4, 1000], 0, "none", 300),
     ("decode", torch.float32, 3, 4, 2, 2, 700, 64, 64, True, [700, 1, 300], 0, "none", 128),
+    # with a bias (the few-row kernel stages it through LDS)
+    ("decode", torch.bfloat16, 3, 8, 2, 2, 3000, 128, 128, True, [3000, 17, 1500], 0, "dense", 512),
+    ("decode", torch.bfloat16, 4, 16, 4, 1, 2048, 64, 128, True, [2048, 1, 777, 0], 0, "keys", 256),
     ("fwd", torch.bfloat16, 4, 16, 4, 4, 2000, 128, 128, True, [2000, 3, 1000, 0], 0, "none", None),
     ("fwd", torch.bfloat16, 3, 4, 2, 300, 1000, 128, 128, True, [1000, 300, 100], 0, "none", None),
     ("fwd", torch.bfloat16, 2, 4, 4, 200, 600, 64, 128, True, [600, 250], 0, "dense", None),
