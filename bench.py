@@ -167,7 +167,7 @@ def varlen_section(torch, attn, inputs, dev, dk, dv_, dq, dec, ws, timed):
                      "speedup_vs_padded": round(padbwd_ms / pbwd_ms, 3),
                      "roofline": {"bound": "mfma", "achieved": round(bt, 2), "peak": PEAK_BF16_TFLOPS,
                                   "unit": "TFLOP/s", "frac": round(bt / PEAK_BF16_TFLOPS, 4),
-                                  "traffic": backward_traffic("packed_"),
+                                  "traffic": backward_traffic(packed=True),
                                   "per_launch_flops": b_flops,
                                   "flops_per_pair": "2 (3 d_h + 2 d_v): recomputed scores, dP, dV, dQ, dK"}},
         "decode": {"workload": "GQA split-KV decode B=16 Hq=32 Hkv=8 Tk<=32768 d=128 S=512 with per-batch "
@@ -372,10 +372,12 @@ def recorded_mfma(key: str):
             "executed_over_algorithmic": round(m["executed_flops"] / alg, 4) if alg else None}
 
 
-def backward_traffic(prefix: str = ""):
-    """HBM bytes of one attn_bwd call: its dQ (which also computes D), dV and
-    dK kernels' recorded traffic, or None if any is stale."""
-    parts = [recorded_traffic(prefix + k) for k in ("bwd_dq", "bwd_dv", "bwd_dk")]
+def backward_traffic(packed: bool = False):
+    """HBM bytes of one attn_bwd call: its kernels' recorded traffic, or None
+    if any is stale.  Dense batches run the dQ kernel (which also computes D)
+    and the fused dK/dV kernel; packed sequences the dQ, dV and dK kernels."""
+    keys = ("packed_bwd_dq", "packed_bwd_dv", "packed_bwd_dk") if packed else ("bwd_dq", "bwd_kvf")
+    parts = [recorded_traffic(k) for k in keys]
     return None if None in parts else sum(parts)
 
 
@@ -584,7 +586,7 @@ def main():
         b_flops = 2 * (3 * 128 + 2 * 128) * pairs
         b_t = b_flops / (b_ms * 1e-3) / 1e12
         out["backward"] = {
-            "workload": "causal backward B=1 H=32 T=8192 d=128 (attn_bwd: D, dQ, dV, dK kernels)",
+            "workload": "causal backward B=1 H=32 T=8192 d=128 (attn_bwd: a dQ kernel that also forms D, then one fused dK/dV kernel)",
             "ms": round(b_ms, 4), "value": round(b_t, 2), "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "achieved": round(b_t, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(b_t / PEAK_BF16_TFLOPS, 4),
