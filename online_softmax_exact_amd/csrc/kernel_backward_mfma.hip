@@ -795,10 +795,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Extra
                 (const __attribute__((address_space(3))) char*)(st_) + 256 + (32 * q + 8 * g + 4 * h) * 4);
         }
       }
-      unsigned pk[8];
+      // Straight-line over the 16 pairs (no branch per score); a partly legal
+      // block then zeroes its illegal pairs.
+      float wv[16];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float w2[2];
         float mb2[2], lse2p[2], dd2p[2];
         if constexpr (BIAS) {
           const int off = (32 * q + 8 * (i >> 1) + 4 * h + 2 * (i & 1)) * 4;
@@ -818,21 +819,26 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Extra
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int r = 2 * i + e;
-          const int row = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
           const float lse_r = BIAS ? lse2p[e] : l4[r >> 2][r & 3];
-          float p = fast_exp2(fmaf(sacc[r], a.scale_log2, zoff(lse_r, BIAS ? mb2[e] : 0.0f)));
-          if (!full) {
-            const int64_t pos = a.q_offset + row;
-            bool ok = key_ok && row < a.t_q;
-            if (a.causal && key > pos) ok = false;
-            if (a.window > 0 && key < pos - a.window + 1) ok = false;
-            p = ok ? p : 0.0f;
-          }
+          const float p = fast_exp2(fmaf(sacc[r], a.scale_log2, zoff(lse_r, BIAS ? mb2[e] : 0.0f)));
           const float dd_r = BIAS ? dd2p[e] : d4[r >> 2][r & 3];
-          w2[e] = DK ? p * (dacc[r] - dd_r) : p;   // dS (eq 33.7) or P
+          wv[r] = DK ? p * (dacc[r] - dd_r) : p;   // dS (eq 33.7) or P
         }
-        pk[i] = pack_bf16(w2[0], w2[1]);
       }
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int64_t pos = a.q_offset + row;
+          bool ok = key_ok && row < a.t_q;
+          ok = ok && !(a.causal && key > pos);
+          ok = ok && !(a.window > 0 && key < pos - a.window + 1);
+          wv[r] = ok ? wv[r] : 0.0f;
+        }
+      }
+      unsigned pk[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pk[i] = pack_bf16(wv[2 * i], wv[2 * i + 1]);
       // dV^T += dO^T P or dK^T += Q^T dS (A = transposed reads of the tile).
       accumulate(DK ? qt_ : gt_, q, pk);
     }
@@ -873,11 +879,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Extra
 // instead of the 8 of separate dV and dK launches (each of which recomputes
 // S).  Two accumulator sets leave no registers for V^T, so the workgroup's
 // 128 V rows are copied into LDS once and read as the B operand of dP
-// (16-byte row reads); Q / dO stream in 32-row tiles to keep the two rings
-// and the V rows within 80 KB (two workgroups per CU).
+// (16-byte row reads); Q / dO stream in 32-row tiles through rings of NS
+// slots.  Two shapes: W = 4 wavefronts (128 keys) with two slots, which keeps
+// the rings and the V rows within 80 KB (two workgroups per CU); and, for
+// d_h = d_v = 128, W = 8 (256 keys, one workgroup per CU) with four slots, so
+// each streamed tile serves twice the keys and is copied three units ahead.
 constexpr int kBf = 32;   // rows per streamed tile
 
-template <int DH, int DV>
+#ifndef BWD_FUSED_W8
+#define BWD_FUSED_W8 0    // 1: the fused d 128 kernel as 8 wavefronts with a 4-slot ring (measured slower)
+#endif
+
+template <int DH, int DV, int W>
 struct FusedCfg {
   static constexpr int KS = DH / 16;
   static constexpr int MS = DV / 16;
@@ -887,23 +900,26 @@ struct FusedCfg {
   static constexpr int V_RB = DV * 2;
   static constexpr int H_BYTES = kBf * H_RB;
   static constexpr int V_BYTES = kBf * V_RB;
-  static constexpr int H_DMA = H_BYTES / 1024 / kW;   // 1 KB copies per wavefront per tile
-  static constexpr int V_DMA = V_BYTES / 1024 / kW;
-  static constexpr int VS_BYTES = kBr * V_RB;         // the workgroup's V rows
-  static constexpr int VS_DMA = VS_BYTES / 1024 / kW;
+  static constexpr int H_DMA = H_BYTES / 1024 / W;   // 1 KB copies per wavefront per tile
+  static constexpr int V_DMA = V_BYTES / 1024 / W;
+  static constexpr int KEYS = kRowsW * W;            // keys per workgroup
+  static constexpr int VS_BYTES = KEYS * V_RB;       // the workgroup's V rows
+  static constexpr int VS_DMA = VS_BYTES / 1024 / W;
+  static_assert(H_DMA >= 1 && V_DMA >= 1 && H_BYTES % (1024 * W) == 0 && V_BYTES % (1024 * W) == 0,
+                "each wavefront copies whole 1 KB blocks of a tile");
 };
 
-template <int DH, int DV>
-__global__ __launch_bounds__(kThreads, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16_t* d_v) {
+template <int DH, int DV, int W, int NS>
+__global__ __launch_bounds__(64 * W, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16_t* d_v) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using C = FusedCfg<DH, DV>;
-  // Q ring, dO ring (two slots each), per slot 64 LSEs and 64 D values, then
-  // the V rows of the workgroup's keys.
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::H_BYTES + 2 * C::V_BYTES + 1024 + C::VS_BYTES];
+  using C = FusedCfg<DH, DV, W>;
+  // Q ring, dO ring (NS slots each), the V rows of the workgroup's keys, then
+  // per slot 64 LSEs and 64 D values.
+  __shared__ __attribute__((aligned(1024))) char smem[NS * (C::H_BYTES + C::V_BYTES) + C::VS_BYTES + NS * 512];
   char* const qring = smem;
-  char* const gring = smem + 2 * C::H_BYTES;
-  float* const sring = reinterpret_cast<float*>(smem + 2 * C::H_BYTES + 2 * C::V_BYTES);
-  char* const vstage = smem + 2 * C::H_BYTES + 2 * C::V_BYTES + 1024;
+  char* const gring = smem + NS * C::H_BYTES;
+  char* const vstage = smem + NS * (C::H_BYTES + C::V_BYTES);
+  float* const sring = reinterpret_cast<float*>(smem + NS * (C::H_BYTES + C::V_BYTES) + C::VS_BYTES);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -923,7 +939,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kvf_mfma_kernel(BArgs a, uint
   const int b = bh / a.heads_kv;
   const int kvh = bh % a.heads_kv;
 
-  const int key0 = kt * kBr + wave * kRowsW;   // first key of this wave
+  const int key0 = kt * C::KEYS + wave * kRowsW;   // first key of this wave
   const int key = key0 + lr;
   const bool key_ok = key < a.t_k;
 
@@ -937,10 +953,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kvf_mfma_kernel(BArgs a, uint
   }
 
   // Query rows that can see a key of the workgroup.
-  const int64_t wk0 = static_cast<int64_t>(kt) * kBr;
+  const int64_t wk0 = static_cast<int64_t>(kt) * C::KEYS;
   int64_t i_lo = 0, i_hi = a.t_q;
   if (a.causal && wk0 - a.q_offset > i_lo) i_lo = wk0 - a.q_offset;
-  if (a.window > 0 && wk0 + kBr - 1 - a.q_offset + a.window < i_hi) i_hi = wk0 + kBr - 1 - a.q_offset + a.window;
+  if (a.window > 0 && wk0 + C::KEYS - 1 - a.q_offset + a.window < i_hi) i_hi = wk0 + C::KEYS - 1 - a.q_offset + a.window;
   if (i_lo > i_hi) i_lo = i_hi;
   const int qt_lo = static_cast<int>(i_lo / kBf);
   const int n_qt = i_hi > i_lo ? static_cast<int>((i_hi + kBf - 1) / kBf) - qt_lo : 0;
@@ -959,7 +975,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kvf_mfma_kernel(BArgs a, uint
   auto gload = [&](int u) {
     int hq, i0;
     unit(u, hq, i0);
-    const int slot = u & 1;
+    const int slot = u % NS;
     dma_tile<C::H_RB, C::H_DMA>(a.q + b * a.qs[0] + hq * a.qs[1], i0, a.t_q, q_row_bytes,
                                 qring + slot * C::H_BYTES, wave, qoff);
     dma_tile<C::V_RB, C::V_DMA>(a.d_o + b * a.os[0] + hq * a.os[1], i0, a.t_q, g_row_bytes,
@@ -984,9 +1000,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kvf_mfma_kernel(BArgs a, uint
 #pragma unroll
   for (int i = 0; i < C::MV; ++i) accv[i] = f32x16{};
 
-  auto dma_barrier = [&]() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  // Wait until this wave's copies of unit u have landed (the copies of the
+  // units after it, issued later, may still be in flight: in-order
+  // completion), then the workgroup barrier; a bare s_barrier, since the
+  // fence __syncthreads adds would also wait for those later copies.
+  constexpr int kOps = C::H_DMA + C::V_DMA;   // copies per unit and wavefront (+2 on wavefront 0)
+  const int ops = kOps + (wave == 0 ? 2 : 0);
+  // `last` = the last unit whose copies were issued.
+  auto unit_barrier = [&](int u, int last) {
+    int later = (last < n_units - 1 ? last : n_units - 1) - u;   // units issued after u
+    if (later < 0) later = 0;
+    wait_vm_upto<(NS - 1) * (kOps + 2)>(later * ops);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
   // The workgroup's V rows (rows past T_k arrive as zeros), then the first
@@ -997,15 +1022,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kvf_mfma_kernel(BArgs a, uint
     dma_tile<C::V_RB, C::VS_DMA>(a.v + b * a.vs[0] + kvh * a.vs[1], wk0, a.t_k, v_row_bytes, vstage, wave,
                                  vsoff);
   }
-  if (n_units > 0) gload(0);
-  if (n_units > 1) gload(1);
-  dma_barrier();
+#pragma unroll
+  for (int u = 0; u < NS; ++u)
+    if (u < n_units) gload(u);
+  unit_barrier(0, NS - 1);
 
   const int last_key = key0 + kRowsW - 1;
   for (int u = 0; u < n_units; ++u) {
     int hq, i0;
     unit(u, hq, i0);
-    const int slot = u & 1;
+    const int slot = u % NS;
     const char* qt_ = qring + slot * C::H_BYTES;
     const char* gt_ = gring + slot * C::V_BYTES;
     const float* st_ = sring + slot * 128;
@@ -1037,7 +1063,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kvf_mfma_kernel(BArgs a, uint
         dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(gop), as_bf16x8(vop), dacc, 0, 0, 0);
       }
       // P (eq 33.6's weights) and dS = P (dP - D) (eq 33.7), packed to bf16.
-      unsigned pk[8], pd[8];
+      // Straight-line (no branch per score, so the LDS reads of LSE and D are
+      // scheduled ahead of their use); a partly legal block then zeroes its
+      // illegal pairs.
+      __builtin_amdgcn_sched_barrier(0);   // the products above stay above
+      float w[16], dsv[16];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int off = (8 * (i >> 1) + 4 * h + 2 * (i & 1)) * 4;
@@ -1045,25 +1075,32 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kvf_mfma_kernel(BArgs a, uint
             (const __attribute__((address_space(3))) char*)(st_) + off);
         const f32x2 dp = *reinterpret_cast<const __attribute__((address_space(3))) f32x2*>(
             (const __attribute__((address_space(3))) char*)(st_) + 256 + off);
-        float w[2], ds[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int r = 2 * i + e;
-          float p = fast_exp2(fmaf(sacc[r], a.scale_log2, -lp[e] * kLog2e));
-          if (!full) {
-            const int row = i0 + 8 * (r >> 2) + 4 * h + (r & 3);
-            const int64_t pos = a.q_offset + row;
-            bool ok = key_ok && row < a.t_q;
-            if (a.causal && key > pos) ok = false;
-            if (a.window > 0 && key < pos - a.window + 1) ok = false;
-            p = ok ? p : 0.0f;
-          }
-          w[e] = p;
-          ds[e] = p * (dacc[r] - dp[e]);
+          w[r] = fast_exp2(fmaf(sacc[r], a.scale_log2, -lp[e] * kLog2e));
+          dsv[r] = w[r] * (dacc[r] - dp[e]);
         }
-        pk[i] = pack_bf16(w[0], w[1]);
-        pd[i] = pack_bf16(ds[0], ds[1]);
       }
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int64_t pos = a.q_offset + row;
+          bool ok = key_ok && row < a.t_q;
+          ok = ok && !(a.causal && key > pos);
+          ok = ok && !(a.window > 0 && key < pos - a.window + 1);
+          w[r] = ok ? w[r] : 0.0f;
+          dsv[r] = ok ? dsv[r] : 0.0f;
+        }
+      }
+      unsigned pk[8], pd[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pk[i] = pack_bf16(w[2 * i], w[2 * i + 1]);
+        pd[i] = pack_bf16(dsv[2 * i], dsv[2 * i + 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       // dV^T += dO^T P and dK^T += Q^T dS (A = transposed reads of the tiles).
 #pragma unroll
       for (int kk2 = 0; kk2 < 2; ++kk2) {
@@ -1085,10 +1122,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kvf_mfma_kernel(BArgs a, uint
         }
       }
     }
-    // Unit u done: this wave's copies of unit u + 1 have landed, every wave is
-    // done with slot u & 1, which takes unit u + 2.
-    dma_barrier();
-    if (u + 2 < n_units) gload(u + 2);
+    // Unit u done: unit u + 1's copies have landed, every wave is done with
+    // slot u % NS, which takes unit u + NS.
+    if (u + 1 < n_units) unit_barrier(u + 1, u + NS - 1);
+    if (u + NS < n_units) gload(u + NS);
   }
 
   // dK = scale dS^T Q (eq 33.8) and dV = P^T dO (eq 33.6); keys no row sees get 0.
@@ -1117,10 +1154,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kvf_mfma_kernel(BArgs a, uint
 #endif
 }
 
-template <int DH, int DV>
+template <int DH, int DV, int W, int NS>
 hipError_t launch_kvf(const BArgs& a, uint16_t* d_v, int64_t blocks, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_kvf_mfma_kernel<DH, DV>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a,
-                     d_v);
+  hipLaunchKernelGGL((bwd_kvf_mfma_kernel<DH, DV, W, NS>), dim3(static_cast<unsigned>(blocks)), dim3(64 * W), 0,
+                     s, a, d_v);
   return hipGetLastError();
 }
 
@@ -1291,10 +1328,20 @@ bool launch_bwd_dkdv_mfma(const Problem& pb, int dtype, const void* q, const voi
   if (BWD_FUSED && !packed && pb.kv_lens == nullptr && pb.bias == nullptr) {
     a.out = static_cast<uint16_t*>(d_k);
     uint16_t* dv = static_cast<uint16_t*>(d_v);
-    if (pb.d_h == 128 && pb.d_v == 128) *err = launch_kvf<128, 128>(a, dv, blocks, stream);
-    else if (pb.d_h == 64 && pb.d_v == 128) *err = launch_kvf<64, 128>(a, dv, blocks, stream);
-    else if (pb.d_h == 128 && pb.d_v == 64) *err = launch_kvf<128, 64>(a, dv, blocks, stream);
-    else *err = launch_kvf<64, 64>(a, dv, blocks, stream);
+    if (BWD_FUSED_W8 && pb.d_h == 128 && pb.d_v == 128) {
+      // 256 keys per workgroup.
+      const int64_t n8 = (pb.t_k + 2 * kBr - 1) / (2 * kBr);
+      a.n_tiles_grid = static_cast<int32_t>(n8);
+      *err = launch_kvf<128, 128, 8, 4>(a, dv, n8 * pb.batch * pb.heads_kv, stream);
+    } else if (pb.d_h == 128 && pb.d_v == 128) {
+      *err = launch_kvf<128, 128, kW, 2>(a, dv, blocks, stream);
+    } else if (pb.d_h == 64 && pb.d_v == 128) {
+      *err = launch_kvf<64, 128, kW, 2>(a, dv, blocks, stream);
+    } else if (pb.d_h == 128 && pb.d_v == 64) {
+      *err = launch_kvf<128, 64, kW, 2>(a, dv, blocks, stream);
+    } else {
+      *err = launch_kvf<64, 64, kW, 2>(a, dv, blocks, stream);
+    }
     return true;
   }
   for (int which = 0; which < 2 && *err == hipSuccess; ++which) {

@@ -113,18 +113,6 @@ struct ShapeBig {
   static constexpr int kWaves = 8, kNQ = PREFILL_BIG_BLOCKS, kSched = PREFILL_BIG_SCHED;
 };
 
-// s_waitcnt vmcnt(n) for a count n <= N known once the caller is unrolled
-// (the instruction takes an immediate).
-template <int N>
-__device__ __forceinline__ void wait_vm_upto(int n) {
-  if constexpr (N == 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  } else {
-    if (n >= N) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-    else wait_vm_upto<N - 1>(n);
-  }
-}
-
 template <int DH, int DV, class S>
 struct Cfg {
   static constexpr int kBc = 32 * S::kNQ;        // keys per tile

@@ -54,6 +54,19 @@ struct Args {
   float scale;   // scale in natural-log units (scale_log2 = scale * log2 e)
 };
 
+// s_waitcnt vmcnt(n) for a count n <= N known once the caller is unrolled
+// (the instruction takes an immediate; a runtime n becomes a chain of
+// compares that waits at the largest immediate not above it).
+template <int N>
+__device__ __forceinline__ void wait_vm_upto(int n) {
+  if constexpr (N == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (n >= N) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    else wait_vm_upto<N - 1>(n);
+  }
+}
+
 // x clamped to [0, n] (device-side length and offset arrays are never trusted).
 __device__ __forceinline__ int clamp_len(int x, int n) { return x < 0 ? 0 : (x > n ? n : x); }
 
