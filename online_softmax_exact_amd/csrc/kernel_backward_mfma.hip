@@ -886,6 +886,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Extra
 // each streamed tile serves twice the keys and is copied three units ahead.
 constexpr int kBf = 32;   // rows per streamed tile
 
+#ifndef BWD_FUSED_VAR
+#define BWD_FUSED_VAR 1   // 1: packed sequences and per-batch KV lengths also take the fused launch
+#endif
 #ifndef BWD_FUSED_W8
 #define BWD_FUSED_W8 0    // 1: the fused d 128 kernel as 8 wavefronts with a 4-slot ring (measured slower)
 #endif
@@ -909,10 +912,12 @@ struct FusedCfg {
                 "each wavefront copies whole 1 KB blocks of a tile");
 };
 
-template <int DH, int DV, int W, int NS>
-__global__ __launch_bounds__(64 * W, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16_t* d_v) {
+template <int DH, int DV, int W, int NS, class... Extra>
+__global__ __launch_bounds__(64 * W, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16_t* d_v, Extra... ex) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  constexpr bool VAR = has_arg<VArgs, Extra...>;
   using C = FusedCfg<DH, DV, W>;
+  static_assert(!VAR || C::KEYS == kBr, "packed slots are counted in 128-key tiles");
   // Q ring, dO ring (NS slots each), the V rows of the workgroup's keys, then
   // per slot 64 LSEs and 64 D values.
   __shared__ __attribute__((aligned(1024))) char smem[NS * (C::H_BYTES + C::V_BYTES) + C::VS_BYTES + NS * 512];
@@ -931,13 +936,35 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16
   const int bid = blockIdx.x;
   int kt = bid / a.n_units;
   int bh = bid % a.n_units;
-  if (a.batch_major) {
+  if (!VAR && a.batch_major) {
     const int i2 = bid / a.heads_kv;
     kt = i2 % a.n_tiles_grid;
     bh = (i2 / a.n_tiles_grid) * a.heads_kv + bid % a.heads_kv;
   }
   const int b = bh / a.heads_kv;
   const int kvh = bh % a.heads_kv;
+  // Variable-length batches, as in the separate dK / dV launches: a packed
+  // slot enters its sequence (sizes, pointers and q_offset its own; LSE and
+  // D keep the packed rows); per-batch KV lengths cut T_k (keys past it see
+  // no row and get 0).
+  const int32_t t_q_all = a.t_q;   // rows per head of LSE and D
+  int32_t row_base = 0;            // packed row of the sequence's row 0
+  int32_t t_k_store = a.t_k;       // keys whose gradients this launch writes
+  if constexpr (VAR) {
+    const VArgs& va = pick<VArgs>(ex...);
+    if (va.cu_q != nullptr) {
+      int32_t key_base = 0;
+      const int sq = slot_seq(va.cu_k, va.n_seqs, a.t_k, kt, &kt);
+      enter_seq<false>(a, va, sq, a.ks[2], &row_base, &key_base);
+      d_v += static_cast<int64_t>(key_base) * a.vs[2];
+      if (kt < 0 || kt * C::KEYS >= a.t_k) return;   // whole workgroup: a slot outside the sequence's tiles
+      t_k_store = a.t_k;
+    } else {
+      const int len = clamp_len(va.kv_lens[b], a.t_k);
+      a.q_offset += len - a.t_q;
+      a.t_k = len;
+    }
+  }
 
   const int key0 = kt * C::KEYS + wave * kRowsW;   // first key of this wave
   const int key = key0 + lr;
@@ -957,6 +984,7 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16
   int64_t i_lo = 0, i_hi = a.t_q;
   if (a.causal && wk0 - a.q_offset > i_lo) i_lo = wk0 - a.q_offset;
   if (a.window > 0 && wk0 + C::KEYS - 1 - a.q_offset + a.window < i_hi) i_hi = wk0 + C::KEYS - 1 - a.q_offset + a.window;
+  if (VAR && wk0 >= a.t_k) i_hi = 0;   // per-batch lengths: a tile past L_b sees no row
   if (i_lo > i_hi) i_lo = i_hi;
   const int qt_lo = static_cast<int>(i_lo / kBf);
   const int n_qt = i_hi > i_lo ? static_cast<int>((i_hi + kBf - 1) / kBf) - qt_lo : 0;
@@ -983,7 +1011,7 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16
     if (wave == 0) {
       // LSEs and D values of the tile's rows, 4 bytes per lane (rows past
       // T_q read as 0 and are masked; the upper 32 are not used).
-      const int64_t r0 = (static_cast<int64_t>(b) * a.heads_q + hq) * a.t_q + i0;
+      const int64_t r0 = (static_cast<int64_t>(b) * a.heads_q + hq) * t_q_all + row_base + i0;
       const int64_t n = a.t_q - i0;
       const auto rl = make_rsrc(a.lse + r0, n * 4);
       const auto rd = make_rsrc(a.dd + r0, n * 4);
@@ -1129,7 +1157,7 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16
   }
 
   // dK = scale dS^T Q (eq 33.8) and dV = P^T dO (eq 33.6); keys no row sees get 0.
-  if (!key_ok) return;
+  if (!(VAR ? key < t_k_store : key_ok)) return;
   const float sc = a.scale_log2 * kLn2;
   uint16_t* kp = a.out + b * a.ks[0] + kvh * a.ks[1] + static_cast<int64_t>(key) * a.ks[2];
   uint16_t* vp = d_v + b * a.vs[0] + kvh * a.vs[1] + static_cast<int64_t>(key) * a.vs[2];
@@ -1154,11 +1182,17 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16
 #endif
 }
 
-template <int DH, int DV, int W, int NS>
-hipError_t launch_kvf(const BArgs& a, uint16_t* d_v, int64_t blocks, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_kvf_mfma_kernel<DH, DV, W, NS>), dim3(static_cast<unsigned>(blocks)), dim3(64 * W), 0,
-                     s, a, d_v);
+template <int DH, int DV, int W, int NS, class... X>
+hipError_t launch_kvf(const BArgs& a, uint16_t* d_v, int64_t blocks, hipStream_t s, X... x) {
+  hipLaunchKernelGGL((bwd_kvf_mfma_kernel<DH, DV, W, NS, X...>), dim3(static_cast<unsigned>(blocks)), dim3(64 * W),
+                     0, s, a, d_v, x...);
   return hipGetLastError();
+}
+
+// The fused launch without or with variable lengths.
+template <int DH, int DV>
+hipError_t launch_kvf_var(const BArgs& a, const VArgs& va, bool var, uint16_t* d_v, int64_t blocks, hipStream_t s) {
+  return var ? launch_kvf<DH, DV, kW, 2>(a, d_v, blocks, s, va) : launch_kvf<DH, DV, kW, 2>(a, d_v, blocks, s);
 }
 
 template <int DH, int DV, int WHICH, class... X>
@@ -1324,23 +1358,25 @@ bool launch_bwd_dkdv_mfma(const Problem& pb, int dtype, const void* q, const voi
   a.batch_major = batch_major(pb);
   *err = hipSuccess;
   if (blocks == 0) return true;
-  // Dense batches without a bias: one launch for both gradients.
-  if (BWD_FUSED && !packed && pb.kv_lens == nullptr && pb.bias == nullptr) {
+  // Without a bias: one launch for both gradients (dense batches, packed
+  // sequences and per-batch KV lengths).
+  const bool var = packed || pb.kv_lens != nullptr;
+  if (BWD_FUSED && pb.bias == nullptr && (BWD_FUSED_VAR || !var)) {
     a.out = static_cast<uint16_t*>(d_k);
     uint16_t* dv = static_cast<uint16_t*>(d_v);
-    if (BWD_FUSED_W8 && pb.d_h == 128 && pb.d_v == 128) {
+    if (BWD_FUSED_W8 && !var && pb.d_h == 128 && pb.d_v == 128) {
       // 256 keys per workgroup.
       const int64_t n8 = (pb.t_k + 2 * kBr - 1) / (2 * kBr);
       a.n_tiles_grid = static_cast<int32_t>(n8);
       *err = launch_kvf<128, 128, 8, 4>(a, dv, n8 * pb.batch * pb.heads_kv, stream);
     } else if (pb.d_h == 128 && pb.d_v == 128) {
-      *err = launch_kvf<128, 128, kW, 2>(a, dv, blocks, stream);
+      *err = launch_kvf_var<128, 128>(a, va, var, dv, blocks, stream);
     } else if (pb.d_h == 64 && pb.d_v == 128) {
-      *err = launch_kvf<64, 128, kW, 2>(a, dv, blocks, stream);
+      *err = launch_kvf_var<64, 128>(a, va, var, dv, blocks, stream);
     } else if (pb.d_h == 128 && pb.d_v == 64) {
-      *err = launch_kvf<128, 64, kW, 2>(a, dv, blocks, stream);
+      *err = launch_kvf_var<128, 64>(a, va, var, dv, blocks, stream);
     } else {
-      *err = launch_kvf<64, 64, kW, 2>(a, dv, blocks, stream);
+      *err = launch_kvf_var<64, 64>(a, va, var, dv, blocks, stream);
     }
     return true;
   }
