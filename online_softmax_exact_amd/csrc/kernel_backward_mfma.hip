@@ -996,14 +996,18 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16
   int qoff[C::H_DMA], goff[C::V_DMA];
   dma_offsets<C::H_RB, C::H_DMA>(wave, lane, q_row_bytes, qoff);
   dma_offsets<C::V_RB, C::V_DMA>(wave, lane, g_row_bytes, goff);
-  auto unit = [&](int u, int& hq, int& i0) {
-    hq = kvh * a.group + u / n_qt;
-    i0 = (qt_lo + u % n_qt) * kBf;
-  };
-  auto gload = [&](int u) {
-    int hq, i0;
-    unit(u, hq, i0);
-    const int slot = u % NS;
+  // Units in order: (head of the group g, row tile qt), qt fastest.  The next
+  // unit to copy is tracked incrementally (no division per unit).
+  int l_u = 0, l_g = 0, l_qt = 0;
+  auto gload_next = [&]() {
+    const int hq = kvh * a.group + l_g;
+    const int i0 = (qt_lo + l_qt) * kBf;
+    const int slot = l_u % NS;
+    ++l_u;
+    if (++l_qt == n_qt) {
+      l_qt = 0;
+      ++l_g;
+    }
     dma_tile<C::H_RB, C::H_DMA>(a.q + b * a.qs[0] + hq * a.qs[1], i0, a.t_q, q_row_bytes,
                                 qring + slot * C::H_BYTES, wave, qoff);
     dma_tile<C::V_RB, C::V_DMA>(a.d_o + b * a.os[0] + hq * a.os[1], i0, a.t_q, g_row_bytes,
@@ -1052,13 +1056,14 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16
   }
 #pragma unroll
   for (int u = 0; u < NS; ++u)
-    if (u < n_units) gload(u);
+    if (u < n_units) gload_next();
   unit_barrier(0, NS - 1);
 
   const int last_key = key0 + kRowsW - 1;
+  int c_qt = 0;   // row tile of unit u
   for (int u = 0; u < n_units; ++u) {
-    int hq, i0;
-    unit(u, hq, i0);
+    const int i0 = (qt_lo + c_qt) * kBf;
+    if (++c_qt == n_qt) c_qt = 0;
     const int slot = u % NS;
     const char* qt_ = qring + slot * C::H_BYTES;
     const char* gt_ = gring + slot * C::V_BYTES;
@@ -1153,7 +1158,7 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16
     // Unit u done: unit u + 1's copies have landed, every wave is done with
     // slot u % NS, which takes unit u + NS.
     if (u + 1 < n_units) unit_barrier(u + 1, u + NS - 1);
-    if (u + NS < n_units) gload(u + NS);
+    if (u + NS < n_units) gload_next();
   }
 
   // dK = scale dS^T Q (eq 33.8) and dV = P^T dO (eq 33.6); keys no row sees get 0.
