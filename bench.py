@@ -374,9 +374,9 @@ def recorded_mfma(key: str):
 
 def backward_traffic(packed: bool = False):
     """HBM bytes of one attn_bwd call: its kernels' recorded traffic, or None
-    if any is stale.  Dense batches run the dQ kernel (which also computes D)
-    and the fused dK/dV kernel; packed sequences the dQ, dV and dK kernels."""
-    keys = ("packed_bwd_dq", "packed_bwd_dv", "packed_bwd_dk") if packed else ("bwd_dq", "bwd_kvf")
+    if any is stale: the dQ kernel (which also computes D) and the fused
+    dK/dV kernel, for dense batches and packed sequences alike."""
+    keys = ("packed_bwd_dq", "packed_bwd_kvf") if packed else ("bwd_dq", "bwd_kvf")
     parts = [recorded_traffic(k) for k in keys]
     return None if None in parts else sum(parts)
 
