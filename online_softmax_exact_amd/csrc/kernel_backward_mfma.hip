@@ -869,7 +869,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Extra
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV in one pass (dense batches without a bias)
+// dK and dV in one pass (calls without a bias: dense batches, packed
+// sequences, per-batch KV lengths)
 // ---------------------------------------------------------------------------
 // The workgroup's 128 keys as in the dK / dV kernels (wavefront w owns keys
 // 32 w .. 32 w + 31, K^T resident as the B operand of S = Q K^T), but each
@@ -880,10 +881,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Extra
 // S).  Two accumulator sets leave no registers for V^T, so the workgroup's
 // 128 V rows are copied into LDS once and read as the B operand of dP
 // (16-byte row reads); Q / dO stream in 32-row tiles through rings of NS
-// slots.  Two shapes: W = 4 wavefronts (128 keys) with two slots, which keeps
-// the rings and the V rows within 80 KB (two workgroups per CU); and, for
-// d_h = d_v = 128, W = 8 (256 keys, one workgroup per CU) with four slots, so
-// each streamed tile serves twice the keys and is copied three units ahead.
+// slots.  The shape used: W = 4 wavefronts (128 keys) with two slots, which
+// keeps the rings and the V rows within 80 KB (two workgroups per CU).  The
+// template also builds, for d_h = d_v = 128, W = 8 (256 keys, one workgroup
+// per CU) with four slots, each streamed tile serving twice the keys and
+// copied three units ahead (BWD_FUSED_W8; measured slower, off).
 constexpr int kBf = 32;   // rows per streamed tile
 
 #ifndef BWD_FUSED_VAR
