@@ -172,10 +172,13 @@ size_t attn_decode_workspace_bytes(const attn_params_t* p, int64_t split_size);
  * Same outputs and conventions as attn_fwd (no n_legal).  split_size >= 1.
  * workspace must hold attn_decode_workspace_bytes(p, split_size) bytes
  * (256-byte aligned); its contents after the call are the partials in the
- * layout above, except that with seqlens_k the slots of ranges at or past
- * L_b hold no key of the batch and are not written (the merge reads only the
- * first ceil(L_b / split_size) partials of a row of batch b).  cu_seqlens_q
- * is not taken (ATTN_E_UNSUPPORTED). */
+ * layout above for the ranges some row may see; the others hold no legal key
+ * of any row and are neither written nor read: without seqlens_k, ranges at
+ * or past the last causal position q_offset + T_q (causal) and ranges wholly
+ * before the first window start q_offset - window + 1 (window > 0); with
+ * seqlens_k, ranges at or past L_b (the merge reads only the first
+ * ceil(L_b / split_size) partials of a row of batch b).  cu_seqlens_q is not
+ * taken (ATTN_E_UNSUPPORTED). */
 int attn_decode_splitkv(const attn_params_t* p, int64_t split_size,
                         const void* q, const void* k_cache,
                         const void* v_cache, void* o, float* lse,

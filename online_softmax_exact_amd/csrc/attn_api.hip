@@ -33,6 +33,21 @@ SplitLayout split_layout(const Problem& pb, int64_t split_size) {
   L.lse_offset = (o_bytes + 255) & ~static_cast<size_t>(255);
   L.total = L.lse_offset + ((static_cast<size_t>(L.rows) * L.n_splits * sizeof(float) + 255) &
                             ~static_cast<size_t>(255));
+  L.s0 = 0;
+  L.s1 = L.n_splits;
+  if (pb.kv_lens == nullptr) {
+    int64_t k_lo = 0, k_hi = pb.t_k;
+    if (pb.causal && pb.q_offset + pb.t_q < k_hi) k_hi = pb.q_offset + pb.t_q;
+    if (pb.window > 0 && pb.q_offset - pb.window + 1 > k_lo) k_lo = pb.q_offset - pb.window + 1;
+    if (k_hi > k_lo) {
+      L.s0 = k_lo / split_size;
+      L.s1 = (k_hi - 1) / split_size + 1;
+      if (L.s1 > L.n_splits) L.s1 = L.n_splits;
+      if (L.s0 > L.s1) L.s0 = L.s1;
+    } else {
+      L.s0 = L.s1 = 0;
+    }
+  }
   return L;
 }
 
@@ -155,9 +170,11 @@ int decode_into(const Problem& pb, int dtype, int64_t split_size, const void* q,
     e = launch_generic(pb, dtype, q, k_cache, v_cache, nullptr, nullptr, nullptr,
                        split_size, ws_o, ws_l, s);
   if (e != hipSuccess) return ATTN_E_HIP;
+  // The merge reads the splits some row can see (a row with none gets the
+  // defined (+0, -inf)).
   const int64_t out_strides[3] = {pb.os[0], pb.os[1], pb.os[2]};
-  return hip_status(launch_merge(L.rows, L.n_splits, pb.d_v, ws_o, L.n_splits * pb.d_v, pb.d_v,
-                                 ws_l, L.n_splits, 1, dtype, o, pb.heads_q, pb.t_q,
+  return hip_status(launch_merge(L.rows, L.s1 - L.s0, pb.d_v, ws_o + L.s0 * pb.d_v, L.n_splits * pb.d_v,
+                                 pb.d_v, ws_l + L.s0, L.n_splits, 1, dtype, o, pb.heads_q, pb.t_q,
                                  out_strides, lse, s, pb.kv_lens, split_size, pb.t_k));
 }
 

@@ -37,8 +37,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // Workspace layout of split-KV decode: fp32 o partials [rows, S, d_v], then
 // fp32 lse partials [rows, S], where rows = B * H_q * T_q in (b, hq, i) order.
+// Splits [s0, s1) hold every key some row may see: keys below the last
+// causal position + 1 and at or past the first window start.  The others are
+// neither computed nor merged (with per-batch KV lengths, which the host does
+// not read, every split is in the range).
 struct SplitLayout {
   int64_t rows, n_splits, split_size;
+  int64_t s0, s1;
   size_t o_bytes, lse_offset, total;
 };
 SplitLayout split_layout(const Problem& pb, int64_t split_size);

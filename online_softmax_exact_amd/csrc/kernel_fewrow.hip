@@ -561,22 +561,6 @@ bool eligible(const Problem& pb, int dtype, const void* q, const void* k, const 
   return true;
 }
 
-// Partials (o_s, lse_s) = (0, -inf) of the splits in [0, s0) and [s1, n_splits),
-// which hold no key any row may see.
-__global__ __launch_bounds__(256) void empty_partials_kernel(float* ws_o, float* ws_lse, int64_t rows,
-                                                             int64_t n_splits, int64_t s0, int64_t s1,
-                                                             int64_t d_v) {
-  const int64_t n_inactive = n_splits - (s1 - s0);
-  const int64_t total = rows * n_inactive * (d_v + 1);
-  for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < total; e += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t c = e % (d_v + 1), rest = e / (d_v + 1);
-    const int64_t j = rest % n_inactive, r = rest / n_inactive;
-    const int64_t sp = j < s0 ? j : j + (s1 - s0);
-    if (c < d_v) ws_o[(r * n_splits + sp) * d_v + c] = 0.0f;
-    else ws_lse[r * n_splits + sp] = -INFINITY;
-  }
-}
-
 FArgs make_args(const Problem& pb, const void* q, const void* k, const void* v) {
   FArgs a{};
   a.q = static_cast<const uint16_t*>(q);
@@ -635,38 +619,17 @@ bool launch_fewrow_partials(const Problem& pb, int dtype, const void* q, const v
   a.ws_lse = ws_lse;
   a.split_size = L.split_size;
   a.n_splits = static_cast<int32_t>(L.n_splits);
-  // Splits any row may see: keys [k_lo, k_hi) with k_hi = last position + 1
-  // (causal) and k_lo = first window start; the others are filled as empty
-  // partials without running the attention kernel on them.
-  int64_t k_lo = 0, k_hi = pb.t_k;
-  if (pb.causal && pb.q_offset + pb.t_q < k_hi) k_hi = pb.q_offset + pb.t_q;
-  if (pb.window > 0 && pb.q_offset - pb.window + 1 > k_lo) k_lo = pb.q_offset - pb.window + 1;
-  int64_t s0 = 0, s1 = 0;
-  if (pb.kv_lens != nullptr) {
-    // Positions depend on lengths the host does not read: every split runs
-    // (one past a batch's length only writes its empty partial).
-    s1 = L.n_splits;
-  } else if (k_hi > k_lo) {
-    s0 = k_lo / L.split_size;
-    s1 = (k_hi - 1) / L.split_size + 1;
-    if (s1 > L.n_splits) s1 = L.n_splits;
-    if (s0 > s1) s0 = s1;
-  }
-  a.split0 = static_cast<int32_t>(s0);
-  a.n_active = static_cast<int32_t>(s1 - s0);
+  // Only the splits some row may see run (L.s0, L.s1); the merge reads no
+  // other.  With per-batch lengths every split is launched, and one at or
+  // past its batch's length returns at once.
+  a.split0 = static_cast<int32_t>(L.s0);
+  a.n_active = static_cast<int32_t>(L.s1 - L.s0);
   const int64_t blocks = pb.batch * pb.heads_kv * a.n_rg * a.n_active;
   if (blocks >= (int64_t(1) << 31)) return false;
   *err = hipSuccess;
   if (blocks > 0)
     *err = launch_split<true>(a, make_bias(pb), blocks, static_cast<int>(pb.d_h), static_cast<int>(pb.d_v),
                               stream);
-  if (*err == hipSuccess && a.n_active < L.n_splits && L.rows > 0) {
-    const int64_t total = L.rows * (L.n_splits - a.n_active) * (pb.d_v + 1);
-    const int64_t grid = total / 256 + 1 < 4096 ? total / 256 + 1 : 4096;
-    hipLaunchKernelGGL(empty_partials_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, ws_o,
-                       ws_lse, L.rows, L.n_splits, s0, s1, pb.d_v);
-    *err = hipGetLastError();
-  }
   return true;
 }
 

@@ -91,6 +91,21 @@ def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
     return dict(o_max=float(np.abs(og - o_ref).max()) if og.size else 0.0)
 
 
+def visible_splits(t_q, t_k, q_offset, split_size, window=0, causal=True):
+    """Key ranges [s0, s1) of a split-KV decode that hold a key some row may
+    see (below the last causal position + 1, at or past the first window
+    start): the ranges whose partials the decode writes and merges."""
+    n = max(1, -(-t_k // split_size))
+    k_lo, k_hi = 0, t_k
+    if causal:
+        k_hi = min(k_hi, q_offset + t_q)
+    if window > 0:
+        k_lo = max(k_lo, q_offset - window + 1)
+    if k_hi <= k_lo:
+        return 0, 0
+    return k_lo // split_size, min(n, (k_hi - 1) // split_size + 1)
+
+
 def host_workers():
     """Threads for the CPU oracle: the CPUs this process may run on."""
     return max(1, len(os.sched_getaffinity(0)))

@@ -12,7 +12,7 @@ import torch
 import oracle
 import online_softmax_exact_amd as attn
 from online_softmax_exact_amd import inputs
-from gpu_util import assert_close, dev, ensure_built, f64, oracle_full, to_dev
+from gpu_util import assert_close, dev, ensure_built, f64, oracle_full, to_dev, visible_splits
 
 pytestmark = pytest.mark.gpu
 
@@ -189,9 +189,13 @@ def test_decode_parity(case):
     op_ref, lp_ref = oracle.split_partials(f64(wl.q), f64(wl.k), f64(wl.v), scale=wl.scale,
                                            causal=True, q_offset=off, split_size=split,
                                            bias=None if wl.bias is None else f64(wl.bias))
+    # Ranges past every row's last position are neither written nor merged:
+    # the oracle's partials there are all empty.
     o_parts, l_parts = attn.split_workspace_views(ws, q, v, split)
-    assert_close(f64(o_parts), f64(l_parts), op_ref, lp_ref,
-                 torch.float32 if dt == torch.float32 else torch.bfloat16, what="partials")
+    s0, s1 = visible_splits(tq, tk, off, split)
+    assert bool(np.isneginf(lp_ref[..., :s0]).all()) and bool(np.isneginf(lp_ref[..., s1:]).all())
+    assert_close(f64(o_parts[..., s0:s1, :]), f64(l_parts[..., s0:s1]), op_ref[..., s0:s1, :],
+                 lp_ref[..., s0:s1], torch.float32 if dt == torch.float32 else torch.bfloat16, what="partials")
 
 
 def test_incremental_equals_full():
