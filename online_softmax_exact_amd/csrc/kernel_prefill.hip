@@ -50,9 +50,6 @@ using namespace pf;
 #ifndef PREFILL_BLOCKS
 #define PREFILL_BLOCKS 2               // 32-key blocks per key tile (one barrier per tile)
 #endif
-#ifndef PREFILL_XCD_ROT
-#define PREFILL_XCD_ROT 2              // head groups on XCDs: batch rotates every this many query tiles
-#endif
 #ifndef PREFILL_BIAS_XCD
 #define PREFILL_BIAS_XCD 1             // head-shared bias: heads of a query tile on one XCD (see the work order)
 #endif
@@ -184,8 +181,7 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
     const int rounds8 = a.n_qtiles * (a.batch_heads / a.heads_q) / 8;
     if (bid < rounds8 * 8 * a.heads_q) {
       const int local = bid >> 3;
-      const int k = local / a.heads_q;
-      const int g = k * 8 + (PREFILL_XCD_ROT > 0 ? ((bid & 7) + k / (PREFILL_XCD_ROT > 0 ? PREFILL_XCD_ROT : 1)) & 7 : (bid & 7));
+      const int g = (local / a.heads_q) * 8 + (bid & 7);
       const int nb = a.batch_heads / a.heads_q;
       idx = g / nb;
       bh = (g % nb) * a.heads_q + local % a.heads_q;
