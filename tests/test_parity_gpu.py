@@ -158,6 +158,7 @@ DECODE_CASES = [
     (torch.bfloat16, 1, 8, 1, 3, 300, 64, 128, 1, None, "none"),
     (torch.bfloat16, 1, 4, 2, 2, 513, 128, 128, 4096, None, "none"),
     (torch.bfloat16, 2, 4, 2, 4, 640, 128, 128, 64, 100, "none"),   # many splits beyond pos
+    (torch.bfloat16, 1, 4, 2, 3, 300, 128, 128, 64, -8, "none"),    # no key visible: no split runs
     (torch.float32, 1, 2, 1, 1, 1000, 64, 64, 96, None, "keys"),
     (torch.bfloat16, 1, 4, 4, 2, 400, 64, 128, 128, None, "dense"),
     (torch.bfloat16, 1, 8, 1, 5, 700, 128, 128, 128, None, "none"),   # 40 rows: 2 row groups
