@@ -130,8 +130,10 @@ typedef struct {
   const int32_t* seqlens_k;
 } attn_params_t;
 
-/* sizeof(attn_params_t), so that bindings can check their mirror of it. */
+/* sizeof(attn_params_t), so that bindings can check their mirror of it.
+ * (Binding plumbing: no passage of the pages defines it.) */
 size_t attn_params_sizeof(void);
+/* ATTN_ABI_VERSION as built into the library, for the same check. */
 int attn_abi_version(void);
 /* A one-line description of an attn_status_t.  Every entry point reports
  * input it cannot honour with one of these codes instead of proceeding: the
