@@ -456,7 +456,9 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
   float* mo_area = reinterpret_cast<float*>(smem);
   float* m_area = mo_area + kWaves * kRows * DV;
   float* l_area = m_area + kWaves * kRows;
-  {
+  // Only the group's rows are stored (decode: G of the 32 lanes' rows).
+  const int rows_here = a.rows - rg * kRows < kRows ? a.rows - rg * kRows : kRows;
+  if (lr < rows_here) {
     float* dst = mo_area + (wave * kRows + lr) * DV;
 #pragma unroll
     for (int mo = 0; mo < C::MO; ++mo)
@@ -471,7 +473,6 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
     }
   }
   __syncthreads();
-  const int rows_here = a.rows - rg * kRows < kRows ? a.rows - rg * kRows : kRows;
   for (int e = tid; e < rows_here * DV; e += kThreads) {
     const int rr = e / DV, d = e % DV;
     float M = -INFINITY;
