@@ -58,7 +58,11 @@ struct FCfg {
   static constexpr int V_STRIDE = DV * 2 + 64;         // bytes per V row in LDS
   static constexpr int VBUF = kTile * V_STRIDE;        // one wave's V tile
   static constexpr int V_PER_LANE = kTile * DV / 8 / 64;
-  static constexpr int MERGE_O = kWaves * kRows * DV * 4;
+  // Wave states in LDS for the end-of-range merge: rows DV + 8 floats apart,
+  // so row r starts 8 r banks on and a 16-byte store of up to 8 rows (both
+  // lane halves) touches every bank at most once.
+  static constexpr int MO_STRIDE = DV + 8;
+  static constexpr int MERGE_O = kWaves * kRows * MO_STRIDE * 4;
   static constexpr int MERGE = MERGE_O + 2 * kWaves * kRows * 4;
   static constexpr int SMEM = MERGE > kWaves * VBUF ? MERGE : kWaves * VBUF;
   // Bias instances: two 4 KB staging blocks per wave after the V buffers.
@@ -454,12 +458,12 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
   const float l_row = l_lane + __shfl_xor(l_lane, 32, 64);
   __syncthreads();                         // V buffers are free now
   float* mo_area = reinterpret_cast<float*>(smem);
-  float* m_area = mo_area + kWaves * kRows * DV;
+  float* m_area = mo_area + kWaves * kRows * C::MO_STRIDE;
   float* l_area = m_area + kWaves * kRows;
   // Only the group's rows are stored (decode: G of the 32 lanes' rows).
   const int rows_here = a.rows - rg * kRows < kRows ? a.rows - rg * kRows : kRows;
   if (lr < rows_here) {
-    float* dst = mo_area + (wave * kRows + lr) * DV;
+    float* dst = mo_area + (wave * kRows + lr) * C::MO_STRIDE;
 #pragma unroll
     for (int mo = 0; mo < C::MO; ++mo)
 #pragma unroll
@@ -485,7 +489,7 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
         const float mw = m_area[w * kRows + rr];
         if (mw == -INFINITY) continue;       // this wave saw no legal key
         const float c = fast_exp2(mw - M);
-        num = fmaf(c, mo_area[(w * kRows + rr) * DV + d], num);
+        num = fmaf(c, mo_area[(w * kRows + rr) * C::MO_STRIDE + d], num);
         den = fmaf(c, l_area[w * kRows + rr], den);
       }
     }
