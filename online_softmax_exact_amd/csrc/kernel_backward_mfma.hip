@@ -891,6 +891,9 @@ constexpr int kBf = 32;   // rows per streamed tile
 #ifndef BWD_FUSED_VAR
 #define BWD_FUSED_VAR 1   // 1: packed sequences and per-batch KV lengths also take the fused launch
 #endif
+#ifndef BWD_READ_AHEAD
+#define BWD_READ_AHEAD 1  // 1: fused dK/dV products read their A operand a step ahead
+#endif
 #ifndef BWD_FUSED_W8
 #define BWD_FUSED_W8 0    // 1: the fused d 128 kernel as 8 wavefronts with a 4-slot ring (measured slower)
 #endif
@@ -1137,23 +1140,67 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16
       }
       __builtin_amdgcn_sched_barrier(0);
       // dV^T += dO^T P and dK^T += Q^T dS (A = transposed reads of the tiles).
+      // Step i = (kk2, then the MV dV slices, then the MQ dK slices); with
+      // kAhead the A operand of step i + 1 is read before the product of
+      // step i, so each product waits only for reads issued a step earlier
+      // instead of for its own.  Not at d_h = d_v = 128, which has no
+      // registers for it (4 more spilled, 6 % slower).
+      constexpr bool kAhead = BWD_READ_AHEAD && DH + DV < 256;
+      if constexpr (kAhead) {
+        constexpr int kSteps = 2 * (C::MV + C::MQ);
+        auto a_op = [&](int i) -> u32x4 {
+          const int kk2 = i / (C::MV + C::MQ), j = i % (C::MV + C::MQ);
+          const bool dv = j < C::MV;
+          const int mo = dv ? j : j - C::MV;
+          const lds_char* p0 = dv ? tr_addr<C::V_RB>(gt_, 0, kk2, mo, 0, lane) : tr_addr<C::H_RB>(qt_, 0, kk2, mo, 0, lane);
+          const lds_char* p1 = dv ? tr_addr<C::V_RB>(gt_, 0, kk2, mo, 1, lane) : tr_addr<C::H_RB>(qt_, 0, kk2, mo, 1, lane);
+          const u32x2 lo = tr_read(p0);
+          const u32x2 hi = tr_read(p1);
+          return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+        u32x4 cur = a_op(0);
 #pragma unroll
-      for (int kk2 = 0; kk2 < 2; ++kk2) {
-        const u32x4 bp = {pk[4 * kk2], pk[4 * kk2 + 1], pk[4 * kk2 + 2], pk[4 * kk2 + 3]};
-        const u32x4 bd = {pd[4 * kk2], pd[4 * kk2 + 1], pd[4 * kk2 + 2], pd[4 * kk2 + 3]};
-#pragma unroll
-        for (int mo = 0; mo < C::MV; ++mo) {
-          const u32x2 lo = tr_read(tr_addr<C::V_RB>(gt_, 0, kk2, mo, 0, lane));
-          const u32x2 hi = tr_read(tr_addr<C::V_RB>(gt_, 0, kk2, mo, 1, lane));
-          const u32x4 aop = {lo[0], lo[1], hi[0], hi[1]};
-          accv[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bp), accv[mo], 0, 0, 0);
+        for (int i = 0; i < kSteps; ++i) {
+          u32x4 nxt = cur;
+          if (i + 1 < kSteps) nxt = a_op(i + 1);
+          const int kk2 = i / (C::MV + C::MQ), j = i % (C::MV + C::MQ);
+          if (j < C::MV) {
+            const u32x4 bp = {pk[4 * kk2], pk[4 * kk2 + 1], pk[4 * kk2 + 2], pk[4 * kk2 + 3]};
+            accv[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), as_bf16x8(bp), accv[j], 0, 0, 0);
+          } else {
+            const u32x4 bd = {pd[4 * kk2], pd[4 * kk2 + 1], pd[4 * kk2 + 2], pd[4 * kk2 + 3]};
+            acck[j - C::MV] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), as_bf16x8(bd), acck[j - C::MV], 0, 0, 0);
+          }
+          cur = nxt;
         }
+        // Keep that order: the first operand's two reads, then per step the
+        // next operand's two reads and the step's product.
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-        for (int mo = 0; mo < C::MQ; ++mo) {
-          const u32x2 lo = tr_read(tr_addr<C::H_RB>(qt_, 0, kk2, mo, 0, lane));
-          const u32x2 hi = tr_read(tr_addr<C::H_RB>(qt_, 0, kk2, mo, 1, lane));
-          const u32x4 aop = {lo[0], lo[1], hi[0], hi[1]};
-          acck[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bd), acck[mo], 0, 0, 0);
+        for (int i = 0; i < kSteps; ++i) {
+          if (i + 1 < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      } else {
+#pragma unroll
+        for (int kk2 = 0; kk2 < 2; ++kk2) {
+          const u32x4 bp = {pk[4 * kk2], pk[4 * kk2 + 1], pk[4 * kk2 + 2], pk[4 * kk2 + 3]};
+          const u32x4 bd = {pd[4 * kk2], pd[4 * kk2 + 1], pd[4 * kk2 + 2], pd[4 * kk2 + 3]};
+#pragma unroll
+          for (int mo = 0; mo < C::MV; ++mo) {
+            const u32x2 lo = tr_read(tr_addr<C::V_RB>(gt_, 0, kk2, mo, 0, lane));
+            const u32x2 hi = tr_read(tr_addr<C::V_RB>(gt_, 0, kk2, mo, 1, lane));
+            const u32x4 aop = {lo[0], lo[1], hi[0], hi[1]};
+            accv[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bp), accv[mo], 0, 0, 0);
+          }
+#pragma unroll
+          for (int mo = 0; mo < C::MQ; ++mo) {
+            const u32x2 lo = tr_read(tr_addr<C::H_RB>(qt_, 0, kk2, mo, 0, lane));
+            const u32x2 hi = tr_read(tr_addr<C::H_RB>(qt_, 0, kk2, mo, 1, lane));
+            const u32x4 aop = {lo[0], lo[1], hi[0], hi[1]};
+            acck[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bd), acck[mo], 0, 0, 0);
+          }
         }
       }
     }
