@@ -60,6 +60,9 @@ constexpr int kBc = 64;                 // streamed tile rows
 #ifndef BWD_FUSED
 #define BWD_FUSED 1    // dense batches without a bias: dK and dV in one launch
 #endif
+#ifndef BWD_READ_AHEAD
+#define BWD_READ_AHEAD 1  // 1: MFMA products read their LDS operand a step ahead (where registers allow)
+#endif
 #ifndef BWD_SCHED
 #define BWD_SCHED 0    // VALU instructions placed after each MFMA in that path (0: compiler's order)
 #endif
@@ -233,6 +236,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a, Extra
   constexpr bool VAR = has_arg<VArgs, Extra...>;
   constexpr bool BIAS = has_arg<BBias, Extra...>;
   using C = BCfg<DH, DV>;
+  // Products read their LDS operand a step ahead (BWD_READ_AHEAD), so each
+  // waits for a read issued a product earlier rather than for its own: at
+  // d_h = d_v = 128 without a bias (backward B1 H32 T8192 1.87 -> 1.82 ms;
+  // its extra registers spill outside the tile loop only).  With a bias the
+  // spills land inside the loop, and at d_h = 64 it measured no gain.
+  constexpr bool kDqAhead = BWD_READ_AHEAD && DH == 128 && DV == 128 && !BIAS;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::H_BYTES + 2 * C::V_BYTES];
   char* const kring = smem;
   char* const vring = smem + 2 * C::H_BYTES;
@@ -379,23 +388,76 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a, Extra
     const char* vt = vring + slot * C::V_BYTES;
     sacc = f32x16{};
     dacc = f32x16{};
+    if constexpr (kDqAhead) {
+      // Step i < KS: S with K chunk i; then dP with V chunk i - KS.  The A
+      // operand of step i + 1 is read before the product of step i.
+      constexpr int kSteps = C::KS + C::MS;
+      auto a_op = [&](int i) -> u32x4 {
+        const lds_char* p = i < C::KS ? row_chunk<C::H_RB>(kt, 32 * q + lr, i, h)
+                                      : row_chunk<C::V_RB>(vt, 32 * q + lr, i - C::KS, h);
+        return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
+      };
+      u32x4 cur = a_op(0);
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      const u32x4 kop = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-          row_chunk<C::H_RB>(kt, 32 * q + lr, s, h));
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop), as_bf16x8(qreg[s]), sacc, 0, 0, 0);
-    }
+      for (int i = 0; i < kSteps; ++i) {
+        u32x4 nxt = cur;
+        if (i + 1 < kSteps) nxt = a_op(i + 1);
+        if (i < C::KS)
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), as_bf16x8(qreg[i]), sacc, 0, 0, 0);
+        else
+          dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), as_bf16x8(greg[i - C::KS]), dacc, 0, 0, 0);
+        cur = nxt;
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-    for (int s = 0; s < C::MS; ++s) {
-      const u32x4 vop = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-          row_chunk<C::V_RB>(vt, 32 * q + lr, s, h));
-      dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop), as_bf16x8(greg[s]), dacc, 0, 0, 0);
+      for (int i = 0; i < kSteps; ++i) {
+        if (i + 1 < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) {
+        const u32x4 kop = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            row_chunk<C::H_RB>(kt, 32 * q + lr, s, h));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kop), as_bf16x8(qreg[s]), sacc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int s = 0; s < C::MS; ++s) {
+        const u32x4 vop = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            row_chunk<C::V_RB>(vt, 32 * q + lr, s, h));
+        dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop), as_bf16x8(greg[s]), dacc, 0, 0, 0);
+      }
     }
   };
   // dQ^T += K^T dS^T for block q (B operand of step kk2: keys
   // 32 q + 16 kk2 + 4 h + (0..3) and + 8 + (0..3), where the reads fetch K).
   auto dq_acc = [&](int slot, int q, const unsigned* pk) {
     const char* kt = kring + slot * C::H_BYTES;
+    if constexpr (kDqAhead) {
+      constexpr int kSteps = 2 * C::MQ;
+      auto a_op = [&](int i) -> u32x4 {
+        const u32x2 lo = tr_read(tr_addr<C::H_RB>(kt, 32 * q, i / C::MQ, i % C::MQ, 0, lane));
+        const u32x2 hi = tr_read(tr_addr<C::H_RB>(kt, 32 * q, i / C::MQ, i % C::MQ, 1, lane));
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
+      u32x4 cur = a_op(0);
+#pragma unroll
+      for (int i = 0; i < kSteps; ++i) {
+        u32x4 nxt = cur;
+        if (i + 1 < kSteps) nxt = a_op(i + 1);
+        const int kk2 = i / C::MQ, mo = i % C::MQ;
+        const u32x4 bop = {pk[4 * kk2], pk[4 * kk2 + 1], pk[4 * kk2 + 2], pk[4 * kk2 + 3]};
+        qacc[mo] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), as_bf16x8(bop), qacc[mo], 0, 0, 0);
+        cur = nxt;
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < kSteps; ++i) {
+        if (i + 1 < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int kk2 = 0; kk2 < 2; ++kk2) {
       const u32x4 bop = {pk[4 * kk2], pk[4 * kk2 + 1], pk[4 * kk2 + 2], pk[4 * kk2 + 3]};
@@ -890,9 +952,6 @@ constexpr int kBf = 32;   // rows per streamed tile
 
 #ifndef BWD_FUSED_VAR
 #define BWD_FUSED_VAR 1   // 1: packed sequences and per-batch KV lengths also take the fused launch
-#endif
-#ifndef BWD_READ_AHEAD
-#define BWD_READ_AHEAD 1  // 1: fused dK/dV products read their A operand a step ahead
 #endif
 #ifndef BWD_FUSED_W8
 #define BWD_FUSED_W8 0    // 1: the fused d 128 kernel as 8 wavefronts with a 4-slot ring (measured slower)
