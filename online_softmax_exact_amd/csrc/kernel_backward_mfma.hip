@@ -1061,32 +1061,91 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16
   dma_offsets<C::H_RB, C::H_DMA>(wave, lane, q_row_bytes, qoff);
   dma_offsets<C::V_RB, C::V_DMA>(wave, lane, g_row_bytes, goff);
   // Units in order: (head of the group g, row tile qt), qt fastest.  The next
-  // unit to copy is tracked incrementally (no division per unit).
+  // unit to copy is tracked incrementally: its Q / dO tile addresses, the
+  // bytes left to the end of the head's rows and its first LSE / D index
+  // advance by one row tile per unit and move to the next head's first tile
+  // when qt wraps (additions only; no 64-bit products per unit).  At
+  // d_h = d_v = 128 that scalar state costs the kernel registers it does not
+  // have (a further spill, 3 % slower there), so it recomputes each unit's
+  // addresses from the head and row tile instead.
+  constexpr bool kIncr = DH + DV < 256;
   int l_u = 0, l_g = 0, l_qt = 0;
+  const int64_t i_first = static_cast<int64_t>(qt_lo) * kBf;
+  const char* q_head = reinterpret_cast<const char*>(a.q + b * a.qs[0] + static_cast<int64_t>(kvh) * a.group * a.qs[1]);
+  const char* g_head = reinterpret_cast<const char*>(a.d_o + b * a.os[0] + static_cast<int64_t>(kvh) * a.group * a.os[1]);
+  const char* q_next = q_head + i_first * q_row_bytes;
+  const char* g_next = g_head + i_first * g_row_bytes;
+  int64_t rows_left = a.t_q - i_first;   // rows from the next unit's first row to T_q
+  int64_t q_left = rows_left * q_row_bytes, g_left = rows_left * g_row_bytes;
+  int64_t r_next = (static_cast<int64_t>(b) * a.heads_q + static_cast<int64_t>(kvh) * a.group) * t_q_all + row_base +
+                   i_first;
   auto gload_next = [&]() {
-    const int hq = kvh * a.group + l_g;
-    const int i0 = (qt_lo + l_qt) * kBf;
+    if constexpr (!kIncr) {
+      const int hq = kvh * a.group + l_g;
+      const int i0 = (qt_lo + l_qt) * kBf;
+      const int slot = l_u % NS;
+      ++l_u;
+      if (++l_qt == n_qt) {
+        l_qt = 0;
+        ++l_g;
+      }
+      dma_tile<C::H_RB, C::H_DMA>(a.q + b * a.qs[0] + hq * a.qs[1], i0, a.t_q, q_row_bytes,
+                                  qring + slot * C::H_BYTES, wave, qoff);
+      dma_tile<C::V_RB, C::V_DMA>(a.d_o + b * a.os[0] + hq * a.os[1], i0, a.t_q, g_row_bytes,
+                                  gring + slot * C::V_BYTES, wave, goff);
+      if (wave == 0) {
+        const int64_t r0 = (static_cast<int64_t>(b) * a.heads_q + hq) * t_q_all + row_base + i0;
+        const int64_t n = a.t_q - i0;
+        const auto rl = make_rsrc(a.lse + r0, n * 4);
+        const auto rd = make_rsrc(a.dd + r0, n * 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rl, (__attribute__((address_space(3))) void*)(sring + slot * 128), 4, lane * 4, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rd, (__attribute__((address_space(3))) void*)(sring + slot * 128 + 64), 4, lane * 4, 0, 0, 0);
+      }
+      return;
+    }
     const int slot = l_u % NS;
     ++l_u;
-    if (++l_qt == n_qt) {
-      l_qt = 0;
-      ++l_g;
-    }
-    dma_tile<C::H_RB, C::H_DMA>(a.q + b * a.qs[0] + hq * a.qs[1], i0, a.t_q, q_row_bytes,
-                                qring + slot * C::H_BYTES, wave, qoff);
-    dma_tile<C::V_RB, C::V_DMA>(a.d_o + b * a.os[0] + hq * a.os[1], i0, a.t_q, g_row_bytes,
-                                gring + slot * C::V_BYTES, wave, goff);
+    const auto rq = make_rsrc(q_next, q_left);
+    const auto rg = make_rsrc(g_next, g_left);
+#pragma unroll
+    for (int j = 0; j < C::H_DMA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rq, (__attribute__((address_space(3))) void*)(qring + slot * C::H_BYTES + (wave * C::H_DMA + j) * 1024),
+          16, qoff[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < C::V_DMA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rg, (__attribute__((address_space(3))) void*)(gring + slot * C::V_BYTES + (wave * C::V_DMA + j) * 1024),
+          16, goff[j], 0, 0, 0);
     if (wave == 0) {
       // LSEs and D values of the tile's rows, 4 bytes per lane (rows past
       // T_q read as 0 and are masked; the upper 32 are not used).
-      const int64_t r0 = (static_cast<int64_t>(b) * a.heads_q + hq) * t_q_all + row_base + i0;
-      const int64_t n = a.t_q - i0;
-      const auto rl = make_rsrc(a.lse + r0, n * 4);
-      const auto rd = make_rsrc(a.dd + r0, n * 4);
+      const auto rl = make_rsrc(a.lse + r_next, rows_left * 4);
+      const auto rd = make_rsrc(a.dd + r_next, rows_left * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rl, (__attribute__((address_space(3))) void*)(sring + slot * 128), 4, lane * 4, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rd, (__attribute__((address_space(3))) void*)(sring + slot * 128 + 64), 4, lane * 4, 0, 0, 0);
+    }
+    if (++l_qt == n_qt) {   // next head of the group, from its first row tile
+      l_qt = 0;
+      q_head += a.qs[1] * 2;
+      g_head += a.os[1] * 2;
+      q_next = q_head + i_first * q_row_bytes;
+      g_next = g_head + i_first * g_row_bytes;
+      rows_left = a.t_q - i_first;
+      q_left = rows_left * q_row_bytes;
+      g_left = rows_left * g_row_bytes;
+      r_next += t_q_all - static_cast<int64_t>(n_qt - 1) * kBf;
+    } else {
+      q_next += kBf * q_row_bytes;
+      g_next += kBf * g_row_bytes;
+      rows_left -= kBf;
+      q_left -= kBf * q_row_bytes;
+      g_left -= kBf * g_row_bytes;
+      r_next += kBf;
     }
   };
 
