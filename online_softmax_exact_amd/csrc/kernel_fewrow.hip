@@ -43,6 +43,12 @@ constexpr int kTile = 32;         // keys per tile
 #ifndef FEWROW_INTERLEAVE
 #define FEWROW_INTERLEAVE 1       // 1: a long range's tiles go round-robin to the waves
 #endif
+#ifndef FEWROW_PAIR
+#define FEWROW_PAIR 1             // 1: split mode takes two consecutive splits per workgroup
+#endif
+#ifndef FEWROW_PAIR_RR
+#define FEWROW_PAIR_RR 1          // 1: a pair's split deals its tiles round-robin to its two waves
+#endif
 #ifndef FEWROW_NT
 #define FEWROW_NT 1               // 1: K/V loads marked non-temporal
 #endif
@@ -84,6 +90,7 @@ struct FArgs {
   int64_t split_size;       // keys per work item
   int32_t t_q, t_k, heads_q, heads_kv, group, rows, n_rg, n_splits;
   int32_t split0, n_active;   // the grid covers splits [split0, split0 + n_active)
+  int32_t pair;               // split mode: each workgroup takes two consecutive splits, two waves each
   int32_t batch;
   float scale_log2;
   int32_t causal;
@@ -116,9 +123,10 @@ __device__ __forceinline__ const T& first_of(const T& t) { return t; }
 
 // Bias instances take one more argument (an FBias); the others keep the
 // argument block of the kernel without a bias.
-template <int DH, int DV, bool SPLIT, bool VAR, class... Bias>
+template <int DH, int DV, bool SPLIT, bool VAR, bool PAIR, class... Bias>
 __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bias_arg) {
   constexpr bool BIAS = sizeof...(Bias) > 0;
+  static_assert(!PAIR || (SPLIT && !BIAS), "pairs of splits: split mode without a bias");
   using C = FCfg<DH, DV>;
   __shared__ __attribute__((aligned(16))) char smem[BIAS ? C::SMEM_B : C::SMEM];
 
@@ -136,17 +144,30 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
   // KV heads: KV head x of every batch) with all their splits, split fastest:
   // the same work on every XCD whatever the lengths, and the workgroups on
   // one XCD stream different offsets of their K/V rows.
+  // PAIR (split mode, no bias): a work item is two consecutive splits, waves
+  // 0-1 on the first and 2-3 on the second: half the workgroups, so half the
+  // per-workgroup start and end latency per key.
   const int64_t n_groups = static_cast<int64_t>(a.n_rg) * a.heads_kv * a.batch;
+  constexpr bool pair = PAIR;
+  const int n_items = pair ? (a.n_active + 1) / 2 : a.n_active;
   int64_t g;
-  int s;
+  int item;
   if (VAR && n_groups % 8 == 0) {
     const int64_t x = blockIdx.x % 8, j = blockIdx.x / 8;
-    g = (j / a.n_active) * 8 + x;
-    s = a.split0 + static_cast<int>(j % a.n_active);
+    g = (j / n_items) * 8 + x;
+    item = static_cast<int>(j % n_items);
   } else {
-    g = blockIdx.x / a.n_active;
-    s = a.split0 + static_cast<int>(blockIdx.x % a.n_active);
+    g = blockIdx.x / n_items;
+    item = static_cast<int>(blockIdx.x % n_items);
   }
+  const int s_first = a.split0 + (pair ? 2 * item : item);
+  constexpr int kW = pair ? 2 : kWaves;             // waves per split
+  const int half = pair ? wave >> 1 : 0;            // which split of the item this wave takes
+  const int wi = pair ? wave & 1 : wave;            // the wave's index within its split
+  const int s = s_first + half;
+  // A split past the grid's range (the second of an odd count) computes and
+  // writes nothing.
+  bool s_live = !pair || s < a.split0 + a.n_active;
   const int kvh = static_cast<int>(g % a.heads_kv);
   const int rg = static_cast<int>((g / a.heads_kv) % a.n_rg);
   const int b = static_cast<int>(g / a.heads_kv / a.n_rg);
@@ -157,7 +178,8 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
     const int lk = raw < 0 ? 0 : (raw > a.t_k ? a.t_k : raw);
     // A range at or past L_b holds no key of this batch: nothing to write
     // (the merge reads only the first ceil(L_b / split_size) partials).
-    if (SPLIT && static_cast<int64_t>(s) * a.split_size >= lk) return;
+    if (SPLIT && static_cast<int64_t>(s_first) * a.split_size >= lk) return;
+    if (pair && static_cast<int64_t>(s) * a.split_size >= lk) s_live = false;
     a.q_offset += lk - a.t_q;
     a.t_k = lk;
   }
@@ -181,10 +203,13 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
     const int64_t first = a.q_offset - a.window + 1;   // smallest window start of any row
     if (first > lo) lo = first;
   }
+  if (pair && !s_live) hi = lo;
   // A work item with no key any of its rows may see (a split wholly past the
   // last position or before the first window, or T_k = 0) only writes its
-  // empty result: O = +0 and LSE = -inf (the valid-flag rule of §33.2).
-  if (hi <= lo) {
+  // empty result: O = +0 and LSE = -inf (the valid-flag rule of §33.2).  A
+  // pair goes on (its waves of an empty split compute nothing, and the merge
+  // writes that split's empty result).
+  if (hi <= lo && !pair) {
     const int rows_here = a.rows - rg * kRows < kRows ? a.rows - rg * kRows : kRows;
     for (int e = tid; e < rows_here * DV; e += kThreads) {
       const int rr = e / DV, d = e % DV;
@@ -221,14 +246,14 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
   const int64_t all_tiles = (len + kTile - 1) / kTile;
   int64_t wlo, whi, tstep;
   int n_tiles;
-  if (FEWROW_INTERLEAVE && all_tiles > 4 * kWaves) {
-    wlo = lo + static_cast<int64_t>(wave) * kTile;
+  if (FEWROW_INTERLEAVE && (all_tiles > 4 * kWaves || (pair && FEWROW_PAIR_RR))) {
+    wlo = lo + static_cast<int64_t>(wi) * kTile;
     whi = hi;
-    tstep = kWaves * kTile;
-    n_tiles = all_tiles > wave ? static_cast<int>((all_tiles - wave + kWaves - 1) / kWaves) : 0;
+    tstep = kW * kTile;
+    n_tiles = all_tiles > wi ? static_cast<int>((all_tiles - wi + kW - 1) / kW) : 0;
   } else {
-    const int64_t part = ((len + kWaves - 1) / kWaves + kTile - 1) / kTile * kTile;
-    wlo = lo + wave * part;
+    const int64_t part = ((len + kW - 1) / kW + kTile - 1) / kTile * kTile;
+    wlo = lo + wi * part;
     whi = wlo + part < hi ? wlo + part : hi;
     if (whi < wlo) whi = wlo;
     tstep = kTile;
@@ -477,15 +502,25 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
     }
   }
   __syncthreads();
-  for (int e = tid; e < rows_here * DV; e += kThreads) {
-    const int rr = e / DV, d = e % DV;
+  // Each split's kW wave states merge into its partial; with a pair the
+  // second split is written only if it lies in the grid's range and (per-batch
+  // lengths) before L_b.
+  constexpr int n_half = pair ? 2 : 1;
+  for (int e = tid; e < n_half * rows_here * DV; e += kThreads) {
+    const int hf = pair ? e / (rows_here * DV) : 0;
+    const int e2 = e - hf * rows_here * DV;
+    const int rr = e2 / DV, d = e2 % DV;
+    const int w0 = hf * kW;
+    const int sp = s_first + hf;
+    if (pair && !(sp < a.split0 + a.n_active && static_cast<int64_t>(sp) * a.split_size < a.t_k)) continue;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m_area[w * kRows + rr]);
+    for (int i = 0; i < kW; ++i) M = fmaxf(M, m_area[(w0 + i) * kRows + rr]);
     float num = 0.0f, den = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int i = 0; i < kW; ++i) {
+        const int w = w0 + i;
         const float mw = m_area[w * kRows + rr];
         if (mw == -INFINITY) continue;       // this wave saw no legal key
         const float c = fast_exp2(mw - M);
@@ -500,8 +535,8 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
     const bool live = M != -INFINITY;
     const float val = live ? num / den : 0.0f;
     if (SPLIT) {
-      a.ws_o[(ridx * a.n_splits + s) * DV + d] = val;
-      if (d == 0) a.ws_lse[ridx * a.n_splits + s] = live ? (M + fast_log2(den)) * kLn2 : -INFINITY;
+      a.ws_o[(ridx * a.n_splits + sp) * DV + d] = val;
+      if (d == 0) a.ws_lse[ridx * a.n_splits + sp] = live ? (M + fast_log2(den)) * kLn2 : -INFINITY;
     } else {
       uint16_t* op = a.o + b * a.os[0] + ghq * a.os[1] + static_cast<int64_t>(gi) * a.os[2];
       op[d] = f32_to_bf16(val);
@@ -513,10 +548,13 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
 template <int DH, int DV, bool SPLIT, bool VAR>
 hipError_t launch_fb(const FArgs& a, const FBias& fb, int64_t blocks, hipStream_t stream) {
   if (fb.bias != nullptr)
-    hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT, VAR, FBias>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT, VAR, false, FBias>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kThreads), 0, stream, a, fb);
+  else if (SPLIT && a.pair)
+    hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT, VAR, SPLIT>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT, VAR>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((fewrow_kernel<DH, DV, SPLIT, VAR, false>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -629,7 +667,15 @@ bool launch_fewrow_partials(const Problem& pb, int dtype, const void* q, const v
   // past its batch's length returns at once.
   a.split0 = static_cast<int32_t>(L.s0);
   a.n_active = static_cast<int32_t>(L.s1 - L.s0);
-  const int64_t blocks = pb.batch * pb.heads_kv * a.n_rg * a.n_active;
+  // Two splits per workgroup (two waves each; no bias) when the grid holds at
+  // most 4 work items per CU (1024): there the per-workgroup start and end
+  // latency is what the split costs (windowed decode, 1024 items: 56 -> 50
+  // us).  Larger grids stream better one split per workgroup (decode, 8192
+  // items: 341 -> 354 us with pairs; 2048 items: 121 -> 134 us).
+  const int64_t singles = pb.batch * pb.heads_kv * a.n_rg * a.n_active;
+  a.pair = FEWROW_PAIR && a.n_active >= 2 && pb.bias == nullptr && singles <= 1024;
+  const int64_t items = a.pair ? (a.n_active + 1) / 2 : a.n_active;
+  const int64_t blocks = pb.batch * pb.heads_kv * a.n_rg * items;
   if (blocks >= (int64_t(1) << 31)) return false;
   *err = hipSuccess;
   if (blocks > 0)
