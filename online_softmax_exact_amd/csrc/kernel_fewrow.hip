@@ -506,10 +506,10 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
   // second split is written only if it lies in the grid's range and (per-batch
   // lengths) before L_b.
   constexpr int n_half = pair ? 2 : 1;
-  for (int e = tid; e < n_half * rows_here * DV; e += kThreads) {
-    const int hf = pair ? e / (rows_here * DV) : 0;
-    const int e2 = e - hf * rows_here * DV;
-    const int rr = e2 / DV, d = e2 % DV;
+#pragma unroll
+  for (int hf = 0; hf < n_half; ++hf)
+  for (int e = tid; e < rows_here * DV; e += kThreads) {
+    const int rr = e / DV, d = e % DV;
     const int w0 = hf * kW;
     const int sp = s_first + hf;
     if (pair && !(sp < a.split0 + a.n_active && static_cast<int64_t>(sp) * a.split_size < a.t_k)) continue;
@@ -668,12 +668,13 @@ bool launch_fewrow_partials(const Problem& pb, int dtype, const void* q, const v
   a.split0 = static_cast<int32_t>(L.s0);
   a.n_active = static_cast<int32_t>(L.s1 - L.s0);
   // Two splits per workgroup (two waves each; no bias) when the grid holds at
-  // most 4 work items per CU (1024): there the per-workgroup start and end
-  // latency is what the split costs (windowed decode, 1024 items: 56 -> 50
-  // us).  Larger grids stream better one split per workgroup (decode, 8192
-  // items: 341 -> 354 us with pairs; 2048 items: 121 -> 134 us).
+  // most 8 work items per CU (2048): there the per-workgroup start and end
+  // latency is what the split costs (windowed decode, 1024 items: 56.8 ->
+  // 49.4 us; 32-row decode groups, 2048 items: 121 -> 116 us).  The decode
+  // workload's grid (8192 items of 4 rows) streams better one split per
+  // workgroup (343 -> 353 us with pairs).
   const int64_t singles = pb.batch * pb.heads_kv * a.n_rg * a.n_active;
-  a.pair = FEWROW_PAIR && a.n_active >= 2 && pb.bias == nullptr && singles <= 1024;
+  a.pair = FEWROW_PAIR && a.n_active >= 2 && pb.bias == nullptr && singles <= 2048;
   const int64_t items = a.pair ? (a.n_active + 1) / 2 : a.n_active;
   const int64_t blocks = pb.batch * pb.heads_kv * a.n_rg * items;
   if (blocks >= (int64_t(1) << 31)) return false;
