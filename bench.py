@@ -213,15 +213,16 @@ def workloads_section(torch, attn, inputs, dev, timed):
     floor_ms = timed(lambda: one.fill_(0.0))
     fl = 2 * (64 + 64) * (128 * 129 // 2)
     tf = fl / (ms * 1e-3) / 1e12
-    out["fp32_single_head"] = {"workload": "fp32 causal B=1 H=1 T=128 d=64 (attn_fwd, fp32 MFMA kernel)",
+    out["fp32_single_head"] = {"workload": "fp32 causal B=1 H=1 T=128 d=64 (attn_fwd, fp32 MFMA key-split kernel)",
                                "us": round(ms * 1e3, 2), "launch_floor_us": round(floor_ms * 1e3, 2),
                                "value": round(tf, 4), "unit": "TFLOP/s",
                                "roofline": {"bound": "launch", "achieved": round(tf, 4), "peak": PEAK_FP32_TFLOPS,
                                             "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_TFLOPS, 6),
                                             "traffic": recorded_traffic("fp32_single_head"), "per_launch_flops": fl,
-                                            "note": "2.1 MFLOP per call in one workgroup: the time is "
-                                                    "the launch plus the latency of its last wavefront's "
-                                                    "four 32-key tiles, not arithmetic"}}
+                                            "note": "2.1 MFLOP per call in four workgroups of 32 rows "
+                                                    "whose wavefronts take one 32-key tile each: the time "
+                                                    "is the launch plus one tile's dependent MFMA chain "
+                                                    "and the merge, not arithmetic"}}
     del q, k, v, o, lse, wl
     wl = inputs.make_config(4)
     q, k, v = (t.to(dev) for t in (wl.q, wl.k, wl.v))

@@ -23,6 +23,10 @@
 //   and A = V[that key][32 mo + l % 32] comes from the LDS tile.
 // * K rows in LDS are padded by one float so the 32 rows of a column read hit
 //   32 different banks; V rows are read along columns, which is conflict-free.
+// * Grids of fewer than FP32_SPLIT_BELOW such workgroups (the single-head
+//   workload has one) take fp32_split_kernel instead: one workgroup per 32
+//   rows whose wavefronts split the rows' key tiles and merge their states,
+//   so the serial chain is a quarter of the tiles.
 #include "attn_internal.h"
 #include "kernels.h"
 
@@ -36,6 +40,9 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;   // query rows per workgroup
 constexpr int kKeys = 32;            // keys per tile
+#ifndef FP32_SPLIT_BELOW
+#define FP32_SPLIT_BELOW 64          // grids below this many 128-row workgroups take fp32_split_kernel
+#endif
 
 struct F32Args {
   const float* q;
@@ -52,6 +59,7 @@ struct F32Args {
   int32_t t_q, t_k, heads_q, group, n_qtiles, batch_heads;
   float scale_log2;
   int32_t causal;
+  int32_t split;            // 1: fp32_split_kernel (one workgroup per 32 rows, keys split over waves)
 };
 
 // Logical position clamped to [-1, T_k]: every value >= T_k - 1 sees all keys.
@@ -256,8 +264,247 @@ __global__ __launch_bounds__(kThreads, 2) void fp32_prefill_kernel(F32Args a) {
 #endif
 }
 
+// Small grids (fewer workgroups than fp32_prefill_kernel would fill the CUs
+// with): one workgroup per 32 query rows, whose 4 wavefronts split the
+// rows' visible key tiles into 4 contiguous parts.  Each wavefront streams
+// its part through its own LDS tiles (no barriers), keeps its own (m, l, u)
+// per row and stores them at the end; the 4 states of a row are merged by
+// eqs 33.4-33.5 (a part with no legal key contributes nothing).  The
+// critical path is then a quarter of the row block's tiles instead of all
+// the tiles of a 128-row block's last wavefront.
+template <int DH, int DV, bool COUNT, bool BIAS>
+__global__ __launch_bounds__(kThreads, 1) void fp32_split_kernel(F32Args a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int KP = DH + 1;            // padded K row, in floats
+  constexpr int MO = DV / 32;
+  constexpr int K_FL = kKeys * KP;      // a multiple of 4 floats: the V tile after it stays 16-byte aligned
+  constexpr int TILE_FL = K_FL + kKeys * DV;
+  constexpr int MERGE_FL = kWaves * 32 * DV + 3 * kWaves * 32;
+  constexpr int SMEM_FL = kWaves * TILE_FL > MERGE_FL ? kWaves * TILE_FL : MERGE_FL;
+  static_assert(K_FL % 4 == 0, "V tile alignment");
+  __shared__ __attribute__((aligned(16))) float smem[SMEM_FL];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int lr = lane & 31;
+
+  // Heaviest (latest, when causal) row blocks first.
+  const int n_rb = (a.t_q + 31) / 32;
+  const int bid = blockIdx.x;
+  const int rb = n_rb - 1 - bid / a.batch_heads;
+  const int bh = bid % a.batch_heads;
+  const int b = bh / a.heads_q;
+  const int hq = bh % a.heads_q;
+  const int kvh = hq / a.group;
+
+  const int row0 = rb * 32;
+  const int row = row0 + lr;
+  const bool row_ok = row < a.t_q;
+
+  float qreg[DH / 2];
+  {
+    const float* qp = a.q + b * a.qs[0] + hq * a.qs[1] + static_cast<int64_t>(row) * a.qs[2];
+#pragma unroll
+    for (int s = 0; s < DH / 2; ++s) qreg[s] = row_ok ? qp[2 * s + h] : 0.0f;
+  }
+
+  auto win_lo = [&](int64_t r) -> int {
+    if (a.window <= 0) return 0;
+    const int64_t lo = a.q_offset + r - a.window + 1;
+    return lo < 0 ? 0 : (lo > a.t_k ? a.t_k : static_cast<int>(lo));
+  };
+  // Key tiles some row of the block may see: [t0, t1), cut into 4 parts.
+  const int last_row = row0 + 31 < a.t_q ? row0 + 31 : a.t_q - 1;
+  const int pos_last = clamp_pos32(a, a.q_offset + last_row);
+  const int k_end = a.causal ? (pos_last + 1 < a.t_k ? pos_last + 1 : a.t_k) : a.t_k;
+  const int t0 = win_lo(row0) / kKeys;
+  int t1 = (k_end + kKeys - 1) / kKeys;
+  if (t1 < t0) t1 = t0;
+  const int part = (t1 - t0 + kWaves - 1) / kWaves;
+  const int tw0 = t0 + wave * part < t1 ? t0 + wave * part : t1;
+  const int tw1 = tw0 + part < t1 ? tw0 + part : t1;
+
+  const int pos_row = clamp_pos32(a, a.q_offset + row);
+  const int lo_row = win_lo(row);
+  const float* brow = nullptr;
+  if (BIAS && row_ok) brow = a.bias + b * a.bs[0] + hq * a.bs[1] + static_cast<int64_t>(row) * a.bs[2];
+  const float* kbase = a.k + b * a.ks[0] + kvh * a.ks[1];
+  const float* vbase = a.v + b * a.vs[0] + kvh * a.vs[1];
+  float* const k_tile = smem + wave * TILE_FL;
+  float* const v_tile = k_tile + K_FL;
+
+  bool has = false;
+  float m2 = 0.0f;
+  float l_lane = 0.0f;
+  int32_t count = 0;
+  f32x16 oacc[MO];
+#pragma unroll
+  for (int i = 0; i < MO; ++i) oacc[i] = f32x16{};
+
+  // This wavefront's copies of tile t: lane l moves 16-byte chunks
+  // c = l + 64 i; keys past T_k read as zero.
+  constexpr int KN = kKeys * DH / 4 / 64;
+  constexpr int VN = kKeys * DV / 4 / 64;
+  f32x4 kpre[KN], vpre[VN];
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const int c = lane + 64 * i, key = t * kKeys + c / (DH / 4), d = 4 * (c % (DH / 4));
+      kpre[i] = key < a.t_k ? *reinterpret_cast<const f32x4*>(kbase + static_cast<int64_t>(key) * a.ks[2] + d)
+                            : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int i = 0; i < VN; ++i) {
+      const int c = lane + 64 * i, key = t * kKeys + c / (DV / 4), d = 4 * (c % (DV / 4));
+      vpre[i] = key < a.t_k ? *reinterpret_cast<const f32x4*>(vbase + static_cast<int64_t>(key) * a.vs[2] + d)
+                            : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  };
+  if (tw0 < tw1) fetch(tw0);
+  for (int t = tw0; t < tw1; ++t) {
+    // The previous tile's operand reads were issued before these stores (LDS
+    // operations of a wavefront run in order).
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const int c = lane + 64 * i, kk = c / (DH / 4), d = 4 * (c % (DH / 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) k_tile[kk * KP + d + e] = kpre[i][e];
+    }
+#pragma unroll
+    for (int i = 0; i < VN; ++i) {
+      const int c = lane + 64 * i, kk = c / (DV / 4), d = 4 * (c % (DV / 4));
+      *reinterpret_cast<f32x4*>(v_tile + kk * DV + d) = vpre[i];
+    }
+    asm volatile("" ::: "memory");
+    if (t + 1 < tw1) fetch(t + 1);
+    const int key0 = t * kKeys;
+
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < DH / 2; ++s)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(k_tile[lr * KP + 2 * s + h], qreg[s], sacc, 0, 0, 0);
+
+    int lim = a.causal ? pos_row - key0 : kKeys - 1;
+    if (a.t_k - 1 - key0 < lim) lim = a.t_k - 1 - key0;
+    if (!row_ok) lim = -1;
+    const int first = lo_row - key0;
+    float z[16];
+    float mx = -INFINITY;
+    bool any = false;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = 8 * (r >> 2) + 4 * h + (r & 3);
+      bool legal = j <= lim && j >= first;
+      float zb = 0.0f;
+      if (BIAS) {
+        const float mb = legal ? brow[static_cast<int64_t>(key0 + j) * a.bs[3]] : -INFINITY;
+        legal = legal && mb != -INFINITY;
+        zb = mb * kLog2e;
+      }
+      z[r] = legal ? fmaf(sacc[r], a.scale_log2, zb) : -INFINITY;
+      mx = fmaxf(mx, z[r]);
+      any = any || legal;
+      if (COUNT) count += legal ? 1 : 0;
+    }
+    const float tmax = fmaxf(mx, __shfl_xor(mx, 32));
+    const int any_partner = __shfl_xor(static_cast<int>(any), 32);
+    const bool any_row = any || any_partner != 0;
+    const float m_new = any_row ? (has ? fmaxf(m2, tmax) : tmax) : m2;
+    const float alpha = (has && any_row) ? fast_exp2(m2 - m_new) : 1.0f;
+    l_lane *= alpha;
+#pragma unroll
+    for (int i = 0; i < MO; ++i) oacc[i] *= alpha;
+    if (any_row) {
+      m2 = m_new;
+      has = true;
+    }
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = z[r] == -INFINITY ? 0.0f : fast_exp2(z[r] - m2);
+      l_lane += p[r];
+    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int key = 8 * (s >> 2) + 4 * h + (s & 3);
+#pragma unroll
+      for (int mo = 0; mo < MO; ++mo)
+        oacc[mo] = __builtin_amdgcn_mfma_f32_32x32x2f32(v_tile[key * DV + 32 * mo + lr], p[s], oacc[mo], 0, 0, 0);
+    }
+  }
+
+  // ---- merge the four wavefront states of each row ----
+  const float l_row = l_lane + __shfl_xor(l_lane, 32);
+  if (COUNT) count += __shfl_xor(count, 32);
+  __syncthreads();                             // every wavefront is done with its tiles
+  float* const mo_area = smem;                 // [wave][row][DV]
+  float* const m_area = smem + kWaves * 32 * DV;
+  float* const l_area = m_area + kWaves * 32;
+  int32_t* const c_area = reinterpret_cast<int32_t*>(l_area + kWaves * 32);
+  {
+    float* dst = mo_area + (wave * 32 + lr) * DV;
+#pragma unroll
+    for (int mo = 0; mo < MO; ++mo)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = {oacc[mo][4 * g], oacc[mo][4 * g + 1], oacc[mo][4 * g + 2], oacc[mo][4 * g + 3]};
+        *reinterpret_cast<f32x4*>(dst + 32 * mo + 8 * g + 4 * h) = x;
+      }
+    if (h == 0) {
+      m_area[wave * 32 + lr] = has ? m2 : -INFINITY;
+      l_area[wave * 32 + lr] = l_row;
+      c_area[wave * 32 + lr] = count;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < 32 * DV; e += kThreads) {
+    const int r = e / DV, d = e % DV;
+    const int orow = row0 + r;
+    if (orow >= a.t_q) break;                  // e grows with r: no later row exists
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m_area[w * 32 + r]);
+    float num = 0.0f, den = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = m_area[w * 32 + r];
+        if (mw == -INFINITY) continue;           // this part held no legal key of the row
+        const float c = fast_exp2(mw - M);
+        num = fmaf(c, mo_area[(w * 32 + r) * DV + d], num);
+        den = fmaf(c, l_area[w * 32 + r], den);
+      }
+    }
+    const bool live = M != -INFINITY;
+    a.o[b * a.os[0] + hq * a.os[1] + static_cast<int64_t>(orow) * a.os[2] + d] = live ? num / den : 0.0f;
+    if (d == 0) {
+      const int64_t ridx = (static_cast<int64_t>(b) * a.heads_q + hq) * a.t_q + orow;
+      a.lse[ridx] = live ? (M + fast_log2(den)) * kLn2 : -INFINITY;
+      if (COUNT) {
+        int32_t n = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) n += c_area[w * 32 + r];
+        a.n_legal[ridx] = n;
+      }
+    }
+  }
+#endif
+}
+
 template <int DH, int DV, bool BIAS>
 void launch_b(const F32Args& a, int64_t blocks, bool count, hipStream_t s) {
+  if (a.split) {
+    if (count)
+      hipLaunchKernelGGL((fp32_split_kernel<DH, DV, true, BIAS>), dim3(static_cast<unsigned>(blocks)),
+                         dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((fp32_split_kernel<DH, DV, false, BIAS>), dim3(static_cast<unsigned>(blocks)),
+                         dim3(kThreads), 0, s, a);
+    return;
+  }
   if (count)
     hipLaunchKernelGGL((fp32_prefill_kernel<DH, DV, true, BIAS>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kThreads), 0, s, a);
@@ -290,8 +537,12 @@ bool launch_fp32_mfma(const Problem& pb, int dtype, const void* q, const void* k
   for (int i = 0; i < 3; ++i)
     if ((pb.qs[i] | pb.ks[i] | pb.vs[i] | pb.os[i]) & 3) return false;
   const int64_t n_qtiles = (pb.t_q + kRows - 1) / kRows;
-  const int64_t blocks = n_qtiles * pb.batch * pb.heads_q;
+  int64_t blocks = n_qtiles * pb.batch * pb.heads_q;
   if (blocks >= (int64_t(1) << 31) || pb.batch * pb.heads_q >= (int64_t(1) << 30)) return false;
+  // Fewer workgroups than FP32_SPLIT_BELOW: one per 32 rows, keys split over
+  // its wavefronts (4x the workgroups, a quarter of the serial tiles each).
+  const bool split = blocks < FP32_SPLIT_BELOW;
+  if (split) blocks = (pb.t_q + 31) / 32 * pb.batch * pb.heads_q;
   F32Args a;
   a.q = static_cast<const float*>(q);
   a.k = static_cast<const float*>(k);
@@ -314,6 +565,7 @@ bool launch_fp32_mfma(const Problem& pb, int dtype, const void* q, const void* k
   a.batch_heads = static_cast<int32_t>(pb.batch * pb.heads_q);
   a.scale_log2 = pb.scale_log2;
   a.causal = pb.causal;
+  a.split = split;
   const bool count = n_legal != nullptr;
   hipError_t e;
   if (pb.d_h == 128 && pb.d_v == 128) e = launch_dims<128, 128>(a, blocks, count, stream);

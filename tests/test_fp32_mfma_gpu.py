@@ -4,7 +4,10 @@ the fp32 tolerances (max |dO| 1e-5, mean 1e-6, LSE 1e-5): several 128-row
 workgroup tiles and 32-key tiles with ragged ends, causal and not, square and
 non-square alignment (offsets before, inside and past the keys), grouped
 heads, T_k = 0 and wholly masked rows, n_legal counts, and a strided output
-view."""
+view.  Grids of fewer than 64 128-row workgroups run the key-split kernel
+(one workgroup per 32 rows, keys split over its wavefronts, states merged in
+LDS): CASES and BIAS_CASES take it; GRID_CASES are sized to take the 128-row
+kernel with the same options."""
 
 import zlib
 
@@ -97,4 +100,49 @@ def test_fp32_mfma_bias_and_window(case):
     torch.cuda.synchronize()
     o_ref, l_ref, n_ref = oracle_full(wl, window=w)
     assert_close(o, lse, o_ref, l_ref, torch.float32, what=str(case))
+    assert np.array_equal(n.cpu().numpy(), n_ref), "n_legal differs"
+
+
+def _standard_grid(b, hq, tq):
+    return b * hq * -(-tq // 128) >= 64
+
+
+GRID_CASES = [
+    # (B, Hq, Hkv, Tq, Tk, dh, dv, causal, q_offset, bias, masked_frac, window)
+    (4, 8, 2, 300, 300, 128, 128, True, 0, "none", 0.0, 0),
+    (8, 8, 8, 150, 90, 64, 64, True, -70, "none", 0.0, 0),
+    (16, 4, 4, 129, 31, 64, 128, True, 0, "none", 0.0, 0),
+    (64, 1, 1, 64, 0, 64, 64, True, 0, "none", 0.0, 0),
+    (8, 8, 2, 100, 700, 128, 64, False, 0, "none", 0.0, 0),
+    (8, 8, 4, 200, 300, 64, 64, True, 100, "dense", 0.1, 0),
+    (8, 8, 8, 130, 130, 128, 128, True, 0, "shared", 0.05, 40),
+]
+
+
+def test_case_lists_take_their_kernels():
+    """CASES and BIAS_CASES are small grids (key-split kernel), GRID_CASES
+    large ones (128-row kernel)."""
+    for c in CASES + BIAS_CASES:
+        assert not _standard_grid(c[0], c[1], c[3]), c
+    for c in GRID_CASES:
+        assert _standard_grid(c[0], c[1], c[3]), c
+
+
+@pytest.mark.parametrize("case", GRID_CASES, ids=[f"g{i}" for i in range(len(GRID_CASES))])
+def test_fp32_mfma_standard_grid(case):
+    """The 128-row fp32 kernel (grids of 64 workgroups or more) on the options
+    the small-grid cases above give the key-split kernel."""
+    b, hq, hkv, tq, tk, dh, dv, causal, off, bias, mf, w = case
+    print("case", case, flush=True)
+    wl = inputs.make_random(b, hq, hkv, tq, tk, dh, dv, dtype=torch.float32,
+                            seed=zlib.crc32(repr(case).encode()) % 10_000, causal=causal, q_offset=off,
+                            bias=bias, masked_frac=mf)
+    q, k, v, m = to_dev(wl)
+    o, lse, n = attn.attn_fwd(q, k, v, scale=wl.scale, causal=causal, q_offset=off, bias=m, window=w,
+                              return_n_legal=True)
+    o2, lse2 = attn.attn_fwd(q, k, v, scale=wl.scale, causal=causal, q_offset=off, bias=m, window=w)
+    torch.cuda.synchronize()
+    o_ref, l_ref, n_ref = oracle_full(wl, window=w)
+    assert_close(o, lse, o_ref, l_ref, torch.float32, what=str(case))
+    assert_close(o2, lse2, o_ref, l_ref, torch.float32, what=str(case) + " (no counts)")
     assert np.array_equal(n.cpu().numpy(), n_ref), "n_legal differs"
