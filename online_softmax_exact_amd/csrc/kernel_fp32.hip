@@ -303,11 +303,17 @@ __global__ __launch_bounds__(kThreads, 1) void fp32_split_kernel(F32Args a) {
   const int row = row0 + lr;
   const bool row_ok = row < a.t_q;
 
+  // Q^T operand of step s: Q[row][2 s + h], from 16-byte loads of a valid
+  // row (rows past T_q read row 0 and are zeroed: no branch per load).
   float qreg[DH / 2];
   {
-    const float* qp = a.q + b * a.qs[0] + hq * a.qs[1] + static_cast<int64_t>(row) * a.qs[2];
+    const float* qp = a.q + b * a.qs[0] + hq * a.qs[1] + static_cast<int64_t>(row_ok ? row : 0) * a.qs[2];
 #pragma unroll
-    for (int s = 0; s < DH / 2; ++s) qreg[s] = row_ok ? qp[2 * s + h] : 0.0f;
+    for (int c = 0; c < DH / 4; ++c) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(qp + 4 * c);
+      qreg[2 * c] = row_ok ? (h ? x[1] : x[0]) : 0.0f;
+      qreg[2 * c + 1] = row_ok ? (h ? x[3] : x[2]) : 0.0f;
+    }
   }
 
   auto win_lo = [&](int64_t r) -> int {
@@ -348,18 +354,20 @@ __global__ __launch_bounds__(kThreads, 1) void fp32_split_kernel(F32Args a) {
   constexpr int KN = kKeys * DH / 4 / 64;
   constexpr int VN = kKeys * DV / 4 / 64;
   f32x4 kpre[KN], vpre[VN];
+  // Keys past T_k read key 0 (a tile holds at least one key below T_k) and
+  // are zeroed, so every load is issued without a branch.
   auto fetch = [&](int t) {
 #pragma unroll
     for (int i = 0; i < KN; ++i) {
       const int c = lane + 64 * i, key = t * kKeys + c / (DH / 4), d = 4 * (c % (DH / 4));
-      kpre[i] = key < a.t_k ? *reinterpret_cast<const f32x4*>(kbase + static_cast<int64_t>(key) * a.ks[2] + d)
-                            : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      const f32x4 x = *reinterpret_cast<const f32x4*>(kbase + static_cast<int64_t>(key < a.t_k ? key : 0) * a.ks[2] + d);
+      kpre[i] = key < a.t_k ? x : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 #pragma unroll
     for (int i = 0; i < VN; ++i) {
       const int c = lane + 64 * i, key = t * kKeys + c / (DV / 4), d = 4 * (c % (DV / 4));
-      vpre[i] = key < a.t_k ? *reinterpret_cast<const f32x4*>(vbase + static_cast<int64_t>(key) * a.vs[2] + d)
-                            : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      const f32x4 x = *reinterpret_cast<const f32x4*>(vbase + static_cast<int64_t>(key < a.t_k ? key : 0) * a.vs[2] + d);
+      vpre[i] = key < a.t_k ? x : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
   };
   if (tw0 < tw1) fetch(tw0);
@@ -382,10 +390,15 @@ __global__ __launch_bounds__(kThreads, 1) void fp32_split_kernel(F32Args a) {
     if (t + 1 < tw1) fetch(t + 1);
     const int key0 = t * kKeys;
 
+    // Every K operand is read before the products, so the chain of products
+    // waits for LDS once.
+    float kop[DH / 2];
+#pragma unroll
+    for (int s = 0; s < DH / 2; ++s) kop[s] = k_tile[lr * KP + 2 * s + h];
     f32x16 sacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < DH / 2; ++s)
-      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(k_tile[lr * KP + 2 * s + h], qreg[s], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kop[s], qreg[s], sacc, 0, 0, 0);
 
     int lim = a.causal ? pos_row - key0 : kKeys - 1;
     if (a.t_k - 1 - key0 < lim) lim = a.t_k - 1 - key0;
@@ -427,13 +440,16 @@ __global__ __launch_bounds__(kThreads, 1) void fp32_split_kernel(F32Args a) {
       p[r] = z[r] == -INFINITY ? 0.0f : fast_exp2(z[r] - m2);
       l_lane += p[r];
     }
+    float vop[16][MO];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const int key = 8 * (s >> 2) + 4 * h + (s & 3);
+    for (int s = 0; s < 16; ++s)
+#pragma unroll
+      for (int mo = 0; mo < MO; ++mo) vop[s][mo] = v_tile[(8 * (s >> 2) + 4 * h + (s & 3)) * DV + 32 * mo + lr];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
 #pragma unroll
       for (int mo = 0; mo < MO; ++mo)
-        oacc[mo] = __builtin_amdgcn_mfma_f32_32x32x2f32(v_tile[key * DV + 32 * mo + lr], p[s], oacc[mo], 0, 0, 0);
-    }
+        oacc[mo] = __builtin_amdgcn_mfma_f32_32x32x2f32(vop[s][mo], p[s], oacc[mo], 0, 0, 0);
   }
 
   // ---- merge the four wavefront states of each row ----
