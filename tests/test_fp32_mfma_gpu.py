@@ -146,3 +146,20 @@ def test_fp32_mfma_standard_grid(case):
     assert_close(o, lse, o_ref, l_ref, torch.float32, what=str(case))
     assert_close(o2, lse2, o_ref, l_ref, torch.float32, what=str(case) + " (no counts)")
     assert np.array_equal(n.cpu().numpy(), n_ref), "n_legal differs"
+
+
+def test_fp32_split_kernel_strided_output():
+    """The key-split kernel (a small grid) writing into an output view whose
+    rows are 80 floats apart: matches the oracle and leaves the rest of each
+    row untouched."""
+    wl = inputs.make_random(1, 2, 1, 100, 300, 64, 64, dtype=torch.float32, seed=43, causal=True,
+                            q_offset=150)
+    assert not _standard_grid(1, 2, 100)
+    q, k, v, _ = to_dev(wl)
+    o_ref, l_ref, _ = oracle_full(wl)
+    buf = torch.full((1, 2, 100, 80), 7.0, device=dev())
+    out = buf[..., :64]
+    _, lse = attn.attn_fwd(q, k, v, scale=wl.scale, causal=True, q_offset=150, out=out)
+    torch.cuda.synchronize()
+    assert_close(out, lse, o_ref, l_ref, torch.float32, what="split kernel, row stride 80")
+    assert torch.all(buf[..., 64:] == 7.0), "wrote past the output view"
