@@ -6,8 +6,11 @@ attention ABI of ``include/attn_mi355x.h``) and ``libattn_probes.so`` (the
 unit microbenchmarks of ``include/attn_probes.h``) next to this file.
 ``build_sanitized()`` links a copy of the attention library whose host code
 in ``attn_api.hip`` (argument validation, kernel choice) carries AddressSanitizer
-and UndefinedBehaviorSanitizer checks, for the CPU tests of the ABI.  Always
-rebuilds when called.
+and UndefinedBehaviorSanitizer checks, for the CPU tests of the ABI.
+``build()`` also links ``libattn_mi355x_poison.so``, every kernel
+compiled with ``-DATTN_DEBUG_POISON=1`` (LDS filled with NaN bytes at kernel
+entry and ahead of every HBM -> LDS copy), which the GPU tests run beside
+the normal build.  Always rebuilds when called.
 """
 
 from __future__ import annotations
@@ -24,6 +27,8 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn_mi355x.so")
 PROBES_LIB = os.path.join(PKG, "libattn_probes.so")
 SANITIZED_LIB = os.path.join(OUT_DIR, "sanitized", "libattn_mi355x.so")
+POISON_LIB = os.path.join(PKG, "libattn_mi355x_poison.so")
+POISON = ["-DATTN_DEBUG_POISON=1"]
 PROBES_SRC = "probes.hip"
 # Sanitizers on the host pass only (device code is built as usual).
 HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
@@ -74,12 +79,17 @@ def _link(objs, lib: str, verbose: bool, extra=()) -> str:
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
+    poison_dir = os.path.join(OUT_DIR, "poison")
     os.makedirs(OUT_DIR, exist_ok=True)
+    os.makedirs(poison_dir, exist_ok=True)
     srcs = sources() + [os.path.join(CSRC, PROBES_SRC)]
-    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    _link(objs[:-1], LIB, verbose)
-    _link(objs[-1:], PROBES_LIB, verbose)
+    jobs_list = [(s, (), OUT_DIR) for s in srcs] + [(s, POISON, poison_dir) for s in sources()]
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(jobs_list)))) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1], j[2]), jobs_list))
+    n = len(srcs)
+    _link(objs[:n - 1], LIB, verbose)
+    _link(objs[n - 1:n], PROBES_LIB, verbose)
+    _link(objs[n:], POISON_LIB, verbose)
     return LIB
 
 

@@ -143,6 +143,47 @@ __device__ __forceinline__ void seq_extent(const int32_t* cu, int64_t T, int64_t
   *hi = e > *lo ? e : *lo;
 }
 
+// LDS poisoning (debug builds compiled with -DATTN_DEBUG_POISON=1): every
+// kernel fills its LDS with all-one bytes when it starts, and every HBM -> LDS
+// copy first fills the bytes it is about to write, so a read of LDS that no
+// write of this launch (or of the current copy into a reused slot) reached
+// sees a NaN (fp32 and bf16 alike) instead of zeros or an older tile.  Such a
+// build gives the normal build's outputs bit for bit exactly when no such
+// read happens; the GPU tests compare the two.
+#ifndef ATTN_DEBUG_POISON
+#define ATTN_DEBUG_POISON 0
+#endif
+
+// Whole-workgroup fill of [p, p + bytes) (4-byte aligned), then a barrier.
+// Call at kernel entry, before any early return, from every thread.
+__device__ __forceinline__ void debug_poison_lds(void* p, int bytes) {
+  if (ATTN_DEBUG_POISON) {
+    uint32_t* w = static_cast<uint32_t*>(p);
+    for (int i = static_cast<int>(threadIdx.x); i < bytes / 4; i += static_cast<int>(blockDim.x)) w[i] = ~0u;
+    __syncthreads();
+  }
+}
+
+// One HBM -> LDS copy of BYTES (4 or 16) per lane: lane l's bytes land at
+// dst + BYTES * l.  Poisoning builds fill those bytes first and wait for the
+// fill, so the copy's data lands after it.
+template <int BYTES>
+__device__ __forceinline__ void lds_copy(__amdgpu_buffer_rsrc_t rs, __attribute__((address_space(3))) void* dst,
+                                         int voffset) {
+  static_assert(BYTES == 4 || BYTES == 16, "4- or 16-byte copies");
+  if (ATTN_DEBUG_POISON) {
+    __attribute__((address_space(3))) uint32_t* d =
+        reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(dst) + (BYTES / 4) * (threadIdx.x & 63);
+#pragma unroll
+    for (int e = 0; e < BYTES / 4; ++e) d[e] = ~0u;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+  if constexpr (BYTES == 4)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, voffset, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voffset, 0, 0, 0);
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   __device__ static float load(const float* p, int64_t i) { return p[i]; }

@@ -57,6 +57,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(Problem pb, const T* __rest
                                                      int64_t rows) {
   __shared__ float sq[kWaves][kMaxD];
   __shared__ float sg[kWaves][kMaxD];
+  debug_poison_lds(sq, sizeof(sq));
+  debug_poison_lds(sg, sizeof(sg));
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   for (int64_t base = blockIdx.x * int64_t(kWaves); base < rows; base += int64_t(gridDim.x) * kWaves) {
@@ -152,6 +154,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(Problem pb, const T* __re
                                                        T* __restrict__ d_v, int64_t keys) {
   __shared__ float sk[kWaves][kMaxD];
   __shared__ float sv[kWaves][kMaxD];
+  debug_poison_lds(sk, sizeof(sk));
+  debug_poison_lds(sv, sizeof(sv));
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   for (int64_t base = blockIdx.x * int64_t(kWaves); base < keys; base += int64_t(gridDim.x) * kWaves) {

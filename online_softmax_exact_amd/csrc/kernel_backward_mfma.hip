@@ -164,8 +164,7 @@ __device__ __forceinline__ void dma_tile(const void* base, int64_t first_row, in
                             (n_rows - first_row) * row_bytes);
 #pragma unroll
   for (int j = 0; j < N; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (__attribute__((address_space(3))) void*)(slot + (wave * N + j) * 1024), 16, off[j], 0, 0, 0);
+    lds_copy<16>(rs, (__attribute__((address_space(3))) void*)(slot + (wave * N + j) * 1024), off[j]);
 }
 
 // Address of the 16-byte chunk holding elements 16 s + 8 h .. + 7 of row r of
@@ -243,6 +242,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma_kernel(BArgs a, Extra
   // spills land inside the loop, and at d_h = 64 it measured no gain.
   constexpr bool kDqAhead = BWD_READ_AHEAD && DH == 128 && DV == 128 && !BIAS;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::H_BYTES + 2 * C::V_BYTES];
+  debug_poison_lds(smem, sizeof(smem));
   char* const kring = smem;
   char* const vring = smem + 2 * C::H_BYTES;
 
@@ -565,6 +565,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Extra
   constexpr int MOUT = DK ? C::MQ : C::MV;     // 32-wide output slices
   // Q ring, dO ring (two slots each), then per slot 64 LSEs and 64 D values.
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::H_BYTES + 2 * C::V_BYTES + 1024];
+  debug_poison_lds(smem, sizeof(smem));
   char* const qring = smem;
   char* const gring = smem + 2 * C::H_BYTES;
   float* const sring = reinterpret_cast<float*>(smem + 2 * C::H_BYTES + 2 * C::V_BYTES);
@@ -659,10 +660,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kv_mfma_kernel(BArgs a, Extra
       const int64_t n = a.t_q - i0;
       const auto rl = make_rsrc(a.lse + r0, n * 4);
       const auto rd = make_rsrc(a.dd + r0, n * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rl, (__attribute__((address_space(3))) void*)(sring + slot * 128), 4, lane * 4, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rd, (__attribute__((address_space(3))) void*)(sring + slot * 128 + 64), 4, lane * 4, 0, 0, 0);
+      lds_copy<4>(rl, (__attribute__((address_space(3))) void*)(sring + slot * 128), lane * 4);
+      lds_copy<4>(rd, (__attribute__((address_space(3))) void*)(sring + slot * 128 + 64), lane * 4);
     }
   };
 
@@ -985,6 +984,7 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16
   // Q ring, dO ring (NS slots each), the V rows of the workgroup's keys, then
   // per slot 64 LSEs and 64 D values.
   __shared__ __attribute__((aligned(1024))) char smem[NS * (C::H_BYTES + C::V_BYTES) + C::VS_BYTES + NS * 512];
+  debug_poison_lds(smem, sizeof(smem));
   char* const qring = smem;
   char* const gring = smem + NS * C::H_BYTES;
   char* const vstage = smem + NS * (C::H_BYTES + C::V_BYTES);
@@ -1098,10 +1098,8 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16
         const int64_t n = a.t_q - i0;
         const auto rl = make_rsrc(a.lse + r0, n * 4);
         const auto rd = make_rsrc(a.dd + r0, n * 4);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rl, (__attribute__((address_space(3))) void*)(sring + slot * 128), 4, lane * 4, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rd, (__attribute__((address_space(3))) void*)(sring + slot * 128 + 64), 4, lane * 4, 0, 0, 0);
+        lds_copy<4>(rl, (__attribute__((address_space(3))) void*)(sring + slot * 128), lane * 4);
+        lds_copy<4>(rd, (__attribute__((address_space(3))) void*)(sring + slot * 128 + 64), lane * 4);
       }
       return;
     }
@@ -1111,23 +1109,17 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_kvf_mfma_kernel(BArgs a, uint16
     const auto rg = make_rsrc(g_next, g_left);
 #pragma unroll
     for (int j = 0; j < C::H_DMA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rq, (__attribute__((address_space(3))) void*)(qring + slot * C::H_BYTES + (wave * C::H_DMA + j) * 1024),
-          16, qoff[j], 0, 0, 0);
+      lds_copy<16>(rq, (__attribute__((address_space(3))) void*)(qring + slot * C::H_BYTES + (wave * C::H_DMA + j) * 1024), qoff[j]);
 #pragma unroll
     for (int j = 0; j < C::V_DMA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rg, (__attribute__((address_space(3))) void*)(gring + slot * C::V_BYTES + (wave * C::V_DMA + j) * 1024),
-          16, goff[j], 0, 0, 0);
+      lds_copy<16>(rg, (__attribute__((address_space(3))) void*)(gring + slot * C::V_BYTES + (wave * C::V_DMA + j) * 1024), goff[j]);
     if (wave == 0) {
       // LSEs and D values of the tile's rows, 4 bytes per lane (rows past
       // T_q read as 0 and are masked; the upper 32 are not used).
       const auto rl = make_rsrc(a.lse + r_next, rows_left * 4);
       const auto rd = make_rsrc(a.dd + r_next, rows_left * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rl, (__attribute__((address_space(3))) void*)(sring + slot * 128), 4, lane * 4, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rd, (__attribute__((address_space(3))) void*)(sring + slot * 128 + 64), 4, lane * 4, 0, 0, 0);
+      lds_copy<4>(rl, (__attribute__((address_space(3))) void*)(sring + slot * 128), lane * 4);
+      lds_copy<4>(rd, (__attribute__((address_space(3))) void*)(sring + slot * 128 + 64), lane * 4);
     }
     if (++l_qt == n_qt) {   // next head of the group, from its first row tile
       l_qt = 0;

@@ -129,6 +129,7 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
   static_assert(!PAIR || (SPLIT && !BIAS), "pairs of splits: split mode without a bias");
   using C = FCfg<DH, DV>;
   __shared__ __attribute__((aligned(16))) char smem[BIAS ? C::SMEM_B : C::SMEM];
+  debug_poison_lds(smem, sizeof(smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -347,8 +348,7 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
     const auto rs = make_rsrc(bias_w + kb, (bias_left - kb) * 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(bstage + (t & 1) * 4096 + i * 1024), 16, bdma[i], 0, 0, 0);
+      lds_copy<16>(rs, (__attribute__((address_space(3))) void*)(bstage + (t & 1) * 4096 + i * 1024), bdma[i]);
   };
   int bread[4];
 #pragma unroll
@@ -482,6 +482,7 @@ __global__ __launch_bounds__(kThreads, 2) void fewrow_kernel(FArgs a, Bias... bi
   // ---- merge the four wave states (eqs 33.4-33.5) ----
   const float l_row = l_lane + __shfl_xor(l_lane, 32, 64);
   __syncthreads();                         // V buffers are free now
+  debug_poison_lds(smem, C::MERGE);        // the merge area: only stored states are read
   float* mo_area = reinterpret_cast<float*>(smem);
   float* m_area = mo_area + kWaves * kRows * C::MO_STRIDE;
   float* l_area = m_area + kWaves * kRows;

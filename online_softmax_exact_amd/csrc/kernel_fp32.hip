@@ -74,6 +74,8 @@ __global__ __launch_bounds__(kThreads, 2) void fp32_prefill_kernel(F32Args a) {
   constexpr int MO = DV / 32;  // 32-row slices of O^T
   __shared__ float k_tile[kKeys * KP];
   __shared__ __attribute__((aligned(16))) float v_tile[kKeys * DV];
+  debug_poison_lds(k_tile, sizeof(k_tile));
+  debug_poison_lds(v_tile, sizeof(v_tile));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -283,6 +285,7 @@ __global__ __launch_bounds__(kThreads, 1) void fp32_split_kernel(F32Args a) {
   constexpr int SMEM_FL = kWaves * TILE_FL > MERGE_FL ? kWaves * TILE_FL : MERGE_FL;
   static_assert(K_FL % 4 == 0, "V tile alignment");
   __shared__ __attribute__((aligned(16))) float smem[SMEM_FL];
+  debug_poison_lds(smem, sizeof(smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -456,6 +459,7 @@ __global__ __launch_bounds__(kThreads, 1) void fp32_split_kernel(F32Args a) {
   const float l_row = l_lane + __shfl_xor(l_lane, 32);
   if (COUNT) count += __shfl_xor(count, 32);
   __syncthreads();                             // every wavefront is done with its tiles
+  debug_poison_lds(smem, MERGE_FL * 4);        // the merge area: only stored states are read
   float* const mo_area = smem;                 // [wave][row][DV]
   float* const m_area = smem + kWaves * 32 * DV;
   float* const l_area = m_area + kWaves * 32;

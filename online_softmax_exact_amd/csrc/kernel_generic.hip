@@ -28,6 +28,7 @@ __global__ __launch_bounds__(256) void generic_kernel(
     int64_t row_blocks, int64_t total_blocks, float* __restrict__ ws_o,
     float* __restrict__ ws_lse) {
   __shared__ float sq[kWaves][kMaxD];
+  debug_poison_lds(sq, sizeof(sq));
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 

@@ -94,6 +94,9 @@ __global__ __launch_bounds__(256) void merge_wide_kernel(
   __shared__ float red[4];
   __shared__ __attribute__((aligned(16))) float part[256 * 4];
   __shared__ float lpart[256];
+  debug_poison_lds(red, sizeof(red));
+  debug_poison_lds(part, sizeof(part));
+  debug_poison_lds(lpart, sizeof(lpart));
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
   n_states = sc.of(r, n_states);

@@ -145,6 +145,7 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
   constexpr bool kBiasLds = BIAS && !COUNT && PREFILL_BIAS_LDS && kRing + kBiasStage <= kLdsShare;
   constexpr bool kBiasEarly = kBiasLds && PREFILL_BIAS_EARLY;
   __shared__ __attribute__((aligned(1024))) char smem[kRing + (kBiasLds ? kBiasStage : 0)];
+  debug_poison_lds(smem, sizeof(smem));
   char* const kring = smem;
   char* const vring = smem + 2 * C::K_BYTES;
 
@@ -351,14 +352,10 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
                                static_cast<int64_t>(a.t_k - kb) * v_row_bytes);
 #pragma unroll
     for (int j = 0; j < C::K_DMA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          krs, (__attribute__((address_space(3))) void*)(kring + slot * C::K_BYTES + (wave * C::K_DMA + j) * 1024),
-          16, koff[j], 0, 0, 0);
+      lds_copy<16>(krs, (__attribute__((address_space(3))) void*)(kring + slot * C::K_BYTES + (wave * C::K_DMA + j) * 1024), koff[j]);
 #pragma unroll
     for (int j = 0; j < C::V_DMA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          vrs, (__attribute__((address_space(3))) void*)(vring + slot * C::V_BYTES + (wave * C::V_DMA + j) * 1024),
-          16, voff[j], 0, 0, 0);
+      lds_copy<16>(vrs, (__attribute__((address_space(3))) void*)(vring + slot * C::V_BYTES + (wave * C::V_DMA + j) * 1024), voff[j]);
   };
   // Wait for this wave's DMA writes, then the workgroup barrier.
   auto dma_barrier = [&]() {
@@ -504,9 +501,7 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
     const auto rs = make_rsrc(bias_w + t * kBc, bias_w_bytes - static_cast<int64_t>(t) * kBc * 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(bstage + q * 4096 + i * 1024), 16,
-          bdma[i] + 128 * q, 0, 0, 0);
+      lds_copy<16>(rs, (__attribute__((address_space(3))) void*)(bstage + q * 4096 + i * 1024), bdma[i] + 128 * q);
   };
   auto prefetch_bias = [&](int t) {
     if (kBiasLds) {
