@@ -36,6 +36,19 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_poisoning_build_exports_the_same_symbols(lib):
+    """The LDS-poisoning debug build (linked by build() beside the library)
+    loads on the host and exports the same entry points."""
+    import ctypes
+    from online_softmax_exact_amd import build as B
+    if not os.path.exists(B.POISON_LIB):
+        import __graft_entry__
+        __graft_entry__.build()
+    plib = ctypes.CDLL(B.POISON_LIB)
+    for n in declared_functions():
+        assert hasattr(plib, n), n
+
+
 def test_abi_version_and_params_layout(lib):
     assert lib.attn_abi_version() == 4
     assert lib.attn_params_sizeof() == ctypes.sizeof(_lib.Params) == 256
