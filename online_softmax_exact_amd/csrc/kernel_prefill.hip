@@ -89,6 +89,9 @@ using namespace pf;
 #ifndef PREFILL_BIAS_EARLY
 #define PREFILL_BIAS_EARLY 1           // 1: a staged block's next-tile bias copied as soon as it is read
 #endif
+#ifndef PREFILL_HILO_KEYS
+#define PREFILL_HILO_KEYS 256          // general tiles use hi + lo weights until every row has seen this many keys
+#endif
 #ifndef PREFILL_WAVES_PER_SIMD
 #define PREFILL_WAVES_PER_SIMD 2       // resident waves per SIMD the kernel is built for
 #endif
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
 
   // One query tile (128 rows of one head); a packed-sequence workgroup runs
   // it for several tiles in turn.
-  auto tile_body = [&](const int qt) {
+  auto tile_body = [&](const int qt) __attribute__((always_inline)) {
   const int row0 = qt * kBr + wave * 32;   // first row of this wave
   const int row = row0 + lr;               // this lane's row
   const bool row_ok = row < a.t_q;
@@ -757,16 +760,31 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
   // blocks past the wave's last visible key are skipped.
   auto general_step = [&](int t) {
     if (t < n_w && t >= t_w_begin) {
+      // Weights as hi + lo terms where some row of the wave may have few
+      // legal keys (its output then rests on a few weights, each of which a
+      // single bf16 rounding would shift by up to 2^-9); once every row has
+      // seen PREFILL_HILO_KEYS keys before this tile (no bias, which can mask
+      // any of them), a single product per block, as on full tiles.
+      const int before = (t * kBc < pos_w_first + 1 ? t * kBc : pos_w_first + 1) - lo_w_last;
+      const bool hilo = BIAS || PREFILL_HILO_KEYS <= 0 || before < PREFILL_HILO_KEYS;
+      // Two straight-line copies of the block loop (a branch per block
+      // between the two products costs the register allocation dearly).
+      auto blocks = [&](auto hilo_c) __attribute__((always_inline)) {
+        constexpr bool HILO = decltype(hilo_c)::value;
 #pragma unroll
-      for (int q = 0; q < kNQ; ++q) {
-        if (a.causal && t * kBc + 32 * q > pos_w_last) break;
-        if (t * kBc + 32 * q + 31 < lo_w_first) continue;   // below every row's window
-        f32x16 sv;
-        unsigned pk[8], pl[8];
-        scores_q(t & 1, q, sv);
-        general_q(t, q, sv, pk, pl);
-        pv2_q(t & 1, q, pk, pl);
-      }
+        for (int q = 0; q < kNQ; ++q) {
+          if (a.causal && t * kBc + 32 * q > pos_w_last) break;
+          if (t * kBc + 32 * q + 31 < lo_w_first) continue;   // below every row's window
+          f32x16 sv;
+          unsigned pk[8], pl[8];
+          scores_q(t & 1, q, sv);
+          general_q(t, q, sv, pk, pl);
+          if constexpr (HILO) pv2_q(t & 1, q, pk, pl);
+          else pv_q(t & 1, q, pk);
+        }
+      };
+      if (hilo) blocks(std::true_type{});
+      else blocks(std::false_type{});
     }
     advance(t, false);
   };
