@@ -90,7 +90,7 @@ using namespace pf;
 #define PREFILL_BIAS_EARLY 1           // 1: a staged block's next-tile bias copied as soon as it is read
 #endif
 #ifndef PREFILL_HILO_KEYS
-#define PREFILL_HILO_KEYS 256          // general tiles use hi + lo weights until every row has seen this many keys
+#define PREFILL_HILO_KEYS 256          // general tiles use hi + lo weights unless every row has this many legal keys
 #endif
 #ifndef PREFILL_WAVES_PER_SIMD
 #define PREFILL_WAVES_PER_SIMD 2       // resident waves per SIMD the kernel is built for
@@ -762,11 +762,13 @@ __global__ __launch_bounds__(64 * S::kWaves, PREFILL_WAVES_PER_SIMD) void prefil
     if (t < n_w && t >= t_w_begin) {
       // Weights as hi + lo terms where some row of the wave may have few
       // legal keys (its output then rests on a few weights, each of which a
-      // single bf16 rounding would shift by up to 2^-9); once every row has
-      // seen PREFILL_HILO_KEYS keys before this tile (no bias, which can mask
-      // any of them), a single product per block, as on full tiles.
-      const int before = (t * kBc < pos_w_first + 1 ? t * kBc : pos_w_first + 1) - lo_w_last;
-      const bool hilo = BIAS || PREFILL_HILO_KEYS <= 0 || before < PREFILL_HILO_KEYS;
+      // single bf16 rounding would shift by up to 2^-9); when every row has at
+      // least PREFILL_HILO_KEYS legal keys in all (no bias, which can mask any
+      // of them), a single product per block, as on full tiles.  The fewest
+      // keys of any row of the wave: at least from the last row's window
+      // start to the first row's position.
+      const int fewest = (a.t_k < pos_w_first + 1 ? a.t_k : pos_w_first + 1) - lo_w_last;
+      const bool hilo = BIAS || PREFILL_HILO_KEYS <= 0 || fewest < PREFILL_HILO_KEYS;
       // Two straight-line copies of the block loop (a branch per block
       // between the two products costs the register allocation dearly).
       auto blocks = [&](auto hilo_c) __attribute__((always_inline)) {
